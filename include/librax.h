@@ -1,0 +1,183 @@
+/*
+ * librax -- paged-KV attention over a token-granular slot pool, for AMD MI355X (gfx950).
+ *
+ * The state the calls read and write is the two-level KV memory the SGLang pages describe:
+ *
+ *   req_to_token[request_row, position] -> slot        ("A walkthrough of SGLang", Main line 4;
+ *   k_pool[slot, kv_head, d], v_pool[slot, kv_head, d]   "SGLang" notes, section "KV memory")
+ *
+ * one slot per token ("Origins: the paper and the first commit", section "Memory: a two-level
+ * pool paged by token"). Requests that share a prefix simply hold the same leading slot numbers
+ * in their table rows; nothing is copied ("Inside SGLang", Step 3, "Paged KV and the kernels
+ * that read it"). Each call handles one layer; the caller indexes layers.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All array arguments are DEVICE pointers (HIP device memory), row-major and contiguous,
+ *   except where a stride is given. Scalars are host values.
+ * - Element format `dtype`: RAX_BF16 (bfloat16, 2 bytes) or RAX_FP32 (4 bytes). K, V, Q and O
+ *   of one call share it. Index arrays are int32.
+ * - head_dim must be 64 or 128. n_q_heads must be a positive multiple of n_kv_heads; query
+ *   head h reads kv head h / (n_q_heads / n_kv_heads) (contiguous groups: grouped-query
+ *   attention, "Inside SGLang", Step 3).
+ * - `stream` is a hipStream_t (NULL = the null stream). Every call only ENQUEUES work on it:
+ *   the library never allocates, frees or synchronises, and keeps no state between calls.
+ *   Buffers must stay alive until the stream has passed the call. Calls are thread-safe.
+ * - Ownership: the caller owns every buffer, including workspaces.
+ * - Errors: a status code is returned (rax_status); no exception crosses the ABI. Arguments
+ *   are checked on the host before anything is enqueued, so a call that returns an error has
+ *   enqueued nothing. Device-resident values (lengths, slots) cannot be checked on the host:
+ *   they must satisfy the contracts stated per call (see each call); kernels clamp lengths to
+ *   the host-side maxima so that a violated length contract never indexes past a workspace.
+ * - An empty batch (batch == 0, n_new == 0, or total_extend_tokens == 0) returns RAX_OK and
+ *   enqueues nothing.
+ */
+#ifndef LIBRAX_H
+#define LIBRAX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rax_status {
+    RAX_OK = 0,
+    RAX_ERR_NULL = 1,        /* a required pointer is NULL                                    */
+    RAX_ERR_SHAPE = 2,       /* a size or count is negative, zero where it may not be, or
+                                inconsistent with another                                     */
+    RAX_ERR_DTYPE = 3,       /* unknown element format                                        */
+    RAX_ERR_UNSUPPORTED = 4, /* a valid shape this build has no kernel for (head_dim, group)  */
+    RAX_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the *_workspace_bytes figure   */
+    RAX_ERR_LAUNCH = 6       /* the HIP runtime refused the launch                            */
+} rax_status;
+
+typedef enum rax_dtype {
+    RAX_BF16 = 0,
+    RAX_FP32 = 1
+} rax_dtype;
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int rax_version(void);
+
+/* Static, human-readable name of a status code ("RAX_OK", ...); "unknown status" otherwise. */
+const char* rax_status_str(int status);
+
+/*
+ * kv_store -- write new K/V rows into pool slots by index.
+ *
+ * Defined by "Origins: the paper and the first commit", section "Execution: RadixAttention and
+ * two sets of kernels": the attention layer writes the layer's freshly computed K and V into
+ * the key and value buffers at the batch's output slot locations (out_cache_loc, "A walkthrough
+ * of SGLang", Main line 3), before the attention kernel reads the pool.
+ *
+ *   for i < n_new:  k_pool[loc[i], :, :] = k_new[i, :, :];  v_pool[loc[i], :, :] = v_new[i, :, :]
+ *
+ * Arguments
+ *   dtype        element format of k_new, v_new, k_pool, v_pool.
+ *   k_new, v_new [n_new, n_kv_heads, head_dim] rows to write.
+ *   loc          [n_new] int32 destination slots. CONTRACT: distinct and in [0, num_slots).
+ *                Out-of-range or repeated entries are undefined behaviour (not checked on the
+ *                device in release builds).
+ *   k_pool, v_pool [num_slots, n_kv_heads, head_dim] pools, written in place. No other row
+ *                changes; the copy is bit-exact.
+ * Errors: RAX_ERR_NULL, RAX_ERR_SHAPE (n_new < 0, n_new > num_slots, num_slots <= 0,
+ *   n_kv_heads <= 0), RAX_ERR_DTYPE, RAX_ERR_UNSUPPORTED (head_dim), RAX_ERR_LAUNCH.
+ */
+int rax_kv_store(int dtype, const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
+                 void* k_pool, void* v_pool, int64_t num_slots, int32_t n_kv_heads, int32_t head_dim,
+                 void* stream);
+
+/*
+ * extend_attention -- EXTEND: the new suffix tokens of each request attend causally to the
+ * request's cached prefix and to themselves.
+ *
+ * Defined by "Origins: the paper and the first commit": self-test answer 2 (only the suffix
+ * that missed the prefix cache is computed; attention reads the prefix's cached KV and the KV
+ * just computed) and section "Batching: Req, Batch and the three forward modes" (the model
+ * input is the suffix only; seq_len = prefix_len + extend_len). Per head the arithmetic is the
+ * four steps of "Inside SGLang", Step 3: scores Q K^T, times sm_scale, minus infinity above
+ * the causal diagonal, softmax along each row, times V.
+ *
+ * For request b with r = req_pool_indices[b], p = prefix_lens[b], e = extend_lens[b],
+ * s = extend_start_loc[b], suffix row i (0 <= i < e) sits at absolute position p + i and sees
+ * the keys at positions 0 .. p + i (bottom-right causal alignment, itself included):
+ *
+ *   o[s + i, h, :] = softmax_j( sm_scale * q[s + i, h, :] . K[slot_j, h / G, :] ) V[slot_j, h/G, :]
+ *   with slot_j = req_to_token[r * r2t_stride + j], j = 0 .. p + i.
+ *
+ * EVERY key, suffix included, is read from the pool: the caller must rax_kv_store the suffix
+ * rows first, on the same stream.
+ *
+ * Arguments
+ *   q, o          [total_extend_tokens, n_q_heads, head_dim]; requests back to back.
+ *   k_pool, v_pool [num_slots, n_kv_heads, head_dim].
+ *   req_to_token  request table, row stride r2t_stride (int32 elements).
+ *   req_pool_indices, prefix_lens, extend_lens, extend_start_loc   [batch] int32 (device).
+ *   max_extend_len  >= every extend_lens[b]     (host; sizes the grid)
+ *   max_seq_len     >= every p + e, <= r2t_stride (host)
+ *   sm_scale      softmax scale applied to the raw score (1/sqrt(head_dim) in the pages).
+ *   workspace     scratch of at least rax_extend_workspace_bytes(...) bytes (may be NULL when
+ *                 that figure is 0).
+ * Device-side CONTRACT: 0 <= prefix_lens[b], 0 <= extend_lens[b] <= max_extend_len,
+ *   prefix_lens[b] + extend_lens[b] <= max_seq_len, extend_start_loc[b] + extend_lens[b] <=
+ *   total_extend_tokens, the first p + e entries of each used table row are valid slots.
+ *   A request with e = 0 produces no rows.
+ * Output rounding: bf16 outputs are fp32 results rounded to nearest even.
+ * Errors: RAX_ERR_NULL, RAX_ERR_SHAPE, RAX_ERR_DTYPE, RAX_ERR_UNSUPPORTED, RAX_ERR_WORKSPACE,
+ *   RAX_ERR_LAUNCH.
+ */
+size_t rax_extend_workspace_bytes(int dtype, int32_t batch, int64_t total_extend_tokens,
+                                  int32_t max_extend_len, int32_t max_seq_len, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim);
+
+int rax_extend_attention(int dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
+                         int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                         const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                         const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
+                         int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
+                         int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float sm_scale,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * decode_attention -- DECODE: one query per request over its whole context.
+ *
+ * Defined by "Inside SGLang", Step 3, "Prefill and decode have different shapes": each request
+ * has one new query whose score row is 1 x n over every earlier token, read from the slots its
+ * table row names ("Paged KV and the kernels that read it": one query against many scattered
+ * slots). The current token's K/V must already be stored (one slot per request per step,
+ * "Origins...", "Batching"). No mask applies.
+ *
+ *   o[b, h, :] = softmax_j( sm_scale * q[b, h, :] . K[slot_j, h / G, :] ) V[slot_j, h / G, :],
+ *   slot_j = req_to_token[req_pool_indices[b] * r2t_stride + j], j = 0 .. seq_lens[b] - 1.
+ *
+ * The work is split along the key range (split-K); partial results (fp32 o and a log-sum-exp
+ * per split) go to the workspace and a second kernel merges them. The split count is a
+ * function of (batch, max_seq_len, n_kv_heads) only.
+ *
+ * Arguments
+ *   q, o          [batch, n_q_heads, head_dim].
+ *   seq_lens      [batch] int32 (device). CONTRACT: 1 <= seq_lens[b] <= max_seq_len.
+ *                 A request with seq_lens[b] <= 0 gets an all-zero output row.
+ *   max_seq_len   host bound, <= r2t_stride.
+ *   workspace     at least rax_decode_workspace_bytes(...) bytes.
+ * Errors: as extend_attention.
+ */
+size_t rax_decode_workspace_bytes(int dtype, int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim);
+
+int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
+                         int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                         const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
+                         int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                         float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Number of key splits rax_decode_attention uses for these shapes (for tests and reports). */
+int32_t rax_decode_num_splits(int dtype, int32_t batch, int32_t max_seq_len, int32_t n_kv_heads);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBRAX_H */

@@ -1,0 +1,148 @@
+// C ABI of librax: host-side argument checks, then kernel launches on the caller's stream.
+// Semantics, layouts, ownership and error behaviour of each call are documented in librax.h.
+#include "../../include/librax.h"
+#include "rax_launch.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int32_t kMaxGridYZ = 65535;
+
+bool dtype_ok(int dt) { return dt == RAX_BF16 || dt == RAX_FP32; }
+size_t elem_bytes(int dt) { return dt == RAX_BF16 ? 2 : 4; }
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+int check_heads(int32_t hq, int32_t hkv, int32_t d) {
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || hq > kMaxGridYZ) return RAX_ERR_SHAPE;
+    if (!head_dim_ok(d)) return RAX_ERR_UNSUPPORTED;
+    return RAX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rax_version(void) { return kVersion; }
+
+const char* rax_status_str(int status) {
+    switch (status) {
+        case RAX_OK: return "RAX_OK";
+        case RAX_ERR_NULL: return "RAX_ERR_NULL";
+        case RAX_ERR_SHAPE: return "RAX_ERR_SHAPE";
+        case RAX_ERR_DTYPE: return "RAX_ERR_DTYPE";
+        case RAX_ERR_UNSUPPORTED: return "RAX_ERR_UNSUPPORTED";
+        case RAX_ERR_WORKSPACE: return "RAX_ERR_WORKSPACE";
+        case RAX_ERR_LAUNCH: return "RAX_ERR_LAUNCH";
+        default: return "unknown status";
+    }
+}
+
+int rax_kv_store(int dtype, const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
+                 void* k_pool, void* v_pool, int64_t num_slots, int32_t n_kv_heads, int32_t head_dim,
+                 void* stream) {
+    if (!dtype_ok(dtype)) return RAX_ERR_DTYPE;
+    if (n_new < 0 || num_slots <= 0 || n_kv_heads <= 0 || n_new > num_slots) return RAX_ERR_SHAPE;
+    if (!head_dim_ok(head_dim)) return RAX_ERR_UNSUPPORTED;
+    if (n_new == 0) return RAX_OK;
+    if (!k_new || !v_new || !loc || !k_pool || !v_pool) return RAX_ERR_NULL;
+    const int64_t row_bytes = (int64_t)n_kv_heads * head_dim * (int64_t)elem_bytes(dtype);
+    if (n_new * (row_bytes / 16) > ((int64_t)1 << 62)) return RAX_ERR_SHAPE;
+    return rax::launch_kv_store(k_new, v_new, loc, n_new, k_pool, v_pool, row_bytes,
+                                (hipStream_t)stream) == 0 ? RAX_OK : RAX_ERR_LAUNCH;
+}
+
+size_t rax_extend_workspace_bytes(int dtype, int32_t batch, int64_t total_extend_tokens,
+                                  int32_t max_extend_len, int32_t max_seq_len, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim) {
+    (void)dtype; (void)batch; (void)total_extend_tokens; (void)max_extend_len; (void)max_seq_len;
+    (void)n_q_heads; (void)n_kv_heads; (void)head_dim;
+    return 0;
+}
+
+int rax_extend_attention(int dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
+                         int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                         const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                         const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
+                         int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
+                         int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float sm_scale,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return RAX_ERR_DTYPE;
+    if (batch < 0 || batch > kMaxGridYZ || total_extend_tokens < 0 || max_extend_len < 0 ||
+        max_seq_len < 0 || num_slots <= 0 || r2t_stride <= 0 || max_seq_len > r2t_stride ||
+        max_extend_len > max_seq_len || max_extend_len > total_extend_tokens)
+        return RAX_ERR_SHAPE;
+    int st = check_heads(n_q_heads, n_kv_heads, head_dim);
+    if (st != RAX_OK) return st;
+    const int32_t G = n_q_heads / n_kv_heads;
+    if (dtype == RAX_BF16 && !rax::extend_bf16_supported(G, head_dim)) return RAX_ERR_UNSUPPORTED;
+    if (!(sm_scale == sm_scale)) return RAX_ERR_SHAPE;
+    if (batch == 0 || total_extend_tokens == 0 || max_extend_len == 0) return RAX_OK;
+    if (!q || !o || !k_pool || !v_pool || !req_to_token || !req_pool_indices || !prefix_lens ||
+        !extend_lens || !extend_start_loc)
+        return RAX_ERR_NULL;
+    const size_t need = rax_extend_workspace_bytes(dtype, batch, total_extend_tokens, max_extend_len,
+                                                   max_seq_len, n_q_heads, n_kv_heads, head_dim);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return RAX_ERR_WORKSPACE;
+
+    rax::AttnArgs a{};
+    a.q = q; a.o = o; a.k_pool = k_pool; a.v_pool = v_pool; a.num_slots = num_slots;
+    a.r2t = req_to_token; a.r2t_stride = r2t_stride; a.req_pool_indices = req_pool_indices;
+    a.prefix_lens = prefix_lens; a.extend_lens = extend_lens; a.extend_start_loc = extend_start_loc;
+    a.total_tokens = total_extend_tokens; a.max_extend_len = max_extend_len;
+    a.seq_lens = nullptr; a.batch = batch; a.max_seq_len = max_seq_len;
+    a.n_q_heads = n_q_heads; a.n_kv_heads = n_kv_heads; a.head_dim = head_dim; a.sm_scale = sm_scale;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    const int rc = dtype == RAX_BF16 ? rax::launch_extend_bf16(a, (hipStream_t)stream)
+                                     : rax::launch_extend_fp32(a, (hipStream_t)stream);
+    return rc == 0 ? RAX_OK : RAX_ERR_LAUNCH;
+}
+
+size_t rax_decode_workspace_bytes(int dtype, int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim) {
+    if (dtype != RAX_BF16 || batch <= 0 || max_seq_len <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 ||
+        head_dim <= 0)
+        return 0;
+    return rax::decode_workspace(batch, max_seq_len, n_q_heads, n_kv_heads, head_dim);
+}
+
+int32_t rax_decode_num_splits(int dtype, int32_t batch, int32_t max_seq_len, int32_t n_kv_heads) {
+    if (dtype != RAX_BF16) return 1;
+    return rax::decode_splits(batch, max_seq_len, n_kv_heads);
+}
+
+int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
+                         int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                         const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
+                         int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                         float sm_scale, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return RAX_ERR_DTYPE;
+    if (batch < 0 || batch > kMaxGridYZ || max_seq_len < 0 || num_slots <= 0 || r2t_stride <= 0 ||
+        max_seq_len > r2t_stride)
+        return RAX_ERR_SHAPE;
+    int st = check_heads(n_q_heads, n_kv_heads, head_dim);
+    if (st != RAX_OK) return st;
+    const int32_t G = n_q_heads / n_kv_heads;
+    if (dtype == RAX_BF16 && !rax::decode_bf16_supported(G, head_dim)) return RAX_ERR_UNSUPPORTED;
+    if (!(sm_scale == sm_scale)) return RAX_ERR_SHAPE;
+    if (batch == 0) return RAX_OK;
+    if (max_seq_len == 0) return RAX_ERR_SHAPE;
+    if (!q || !o || !k_pool || !v_pool || !req_to_token || !req_pool_indices || !seq_lens)
+        return RAX_ERR_NULL;
+    const size_t need = rax_decode_workspace_bytes(dtype, batch, max_seq_len, n_q_heads, n_kv_heads,
+                                                   head_dim);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return RAX_ERR_WORKSPACE;
+
+    rax::AttnArgs a{};
+    a.q = q; a.o = o; a.k_pool = k_pool; a.v_pool = v_pool; a.num_slots = num_slots;
+    a.r2t = req_to_token; a.r2t_stride = r2t_stride; a.req_pool_indices = req_pool_indices;
+    a.prefix_lens = nullptr; a.extend_lens = nullptr; a.extend_start_loc = nullptr;
+    a.total_tokens = batch; a.max_extend_len = 0; a.seq_lens = seq_lens; a.batch = batch;
+    a.max_seq_len = max_seq_len; a.n_q_heads = n_q_heads; a.n_kv_heads = n_kv_heads;
+    a.head_dim = head_dim; a.sm_scale = sm_scale; a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    const int rc = dtype == RAX_BF16 ? rax::launch_decode_bf16(a, (hipStream_t)stream)
+                                     : rax::launch_decode_fp32(a, (hipStream_t)stream);
+    return rc == 0 ? RAX_OK : RAX_ERR_LAUNCH;
+}
+
+}  // extern "C"

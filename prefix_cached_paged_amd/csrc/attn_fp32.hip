@@ -1,0 +1,133 @@
+// EXTEND and DECODE attention in fp32 (vector ALU, fp32 arithmetic end to end).
+//
+// Same definition as the bf16 kernels ("Inside SGLang", Step 3: Q K^T, scale, causal mask,
+// row softmax, times V, over keys gathered through req_to_token), for pools stored in fp32.
+// No reduced-precision matrix instructions are used, so results stay within fp32 rounding.
+//
+// One wave per (query row, query head). Lanes take 64 keys at a time: each lane forms the full
+// dot product of the query (broadcast from LDS) with its key's row, the wave updates a running
+// max and sum, then the lanes switch to head_dim and accumulate p_j * V_j with p_j and the slot
+// broadcast by ds_bpermute. expf is used for the exponentials.
+#include "rax_device.h"
+#include "rax_launch.h"
+
+namespace rax {
+
+namespace {
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void attn_rows_fp32_kernel(
+    const float* __restrict__ q, float* __restrict__ o, const float* __restrict__ k_pool,
+    const float* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
+    const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
+    const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ extend_start_loc,
+    const int32_t* __restrict__ seq_lens, int64_t total_tokens, int32_t max_extend_len,
+    int32_t max_seq_len, int32_t Hq, int32_t Hkv, float sm_scale) {
+    constexpr int PER = D / 64;
+    __shared__ float qs[D];
+    const int lane = threadIdx.x;
+    const int h = blockIdx.y;
+    const int b = blockIdx.z;
+    const int G = Hq / Hkv;
+    const int g = h / G;
+
+    int64_t qrow;
+    int nkeys;
+    if (CAUSAL) {
+        const int i = blockIdx.x;
+        int e = min(extend_lens[b], max_extend_len);
+        const int s0 = extend_start_loc[b];
+        e = (int)min((int64_t)e, total_tokens - s0);
+        if (i >= e) return;
+        nkeys = min(prefix_lens[b] + i + 1, max_seq_len);
+        qrow = (int64_t)(s0 + i);
+    } else {
+        nkeys = min(seq_lens[b], max_seq_len);
+        qrow = b;
+    }
+    float* orow = o + (qrow * Hq + h) * D;
+    if (nkeys <= 0) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) orow[64 * k + lane] = 0.f;
+        return;
+    }
+    const float* qr = q + (qrow * Hq + h) * D;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) qs[64 * k + lane] = qr[64 * k + lane];
+    __syncthreads();
+
+    const int32_t* row = r2t + (int64_t)rpi[b] * r2t_stride;
+    const int64_t pool_row = (int64_t)Hkv * D;
+    float m = -INFINITY, lsum = 0.f;
+    float acc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+
+    for (int j0 = 0; j0 < nkeys; j0 += 64) {
+        const int j = j0 + lane;
+        const bool ok = j < nkeys;
+        const int slot = row[ok ? j : nkeys - 1];
+        const float* kr = k_pool + (int64_t)slot * pool_row + (int64_t)g * D;
+        float dot = 0.f;
+        for (int d = 0; d < D; d += 4) {
+            const float4 kv = *(const float4*)(kr + d);
+            dot = fmaf(qs[d], kv.x, dot);
+            dot = fmaf(qs[d + 1], kv.y, dot);
+            dot = fmaf(qs[d + 2], kv.z, dot);
+            dot = fmaf(qs[d + 3], kv.w, dot);
+        }
+        const float x = ok ? dot * sm_scale : -INFINITY;
+        float mx = x;
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) mx = wave_max_xor(mx, s);
+        const float m_new = fmaxf(m, mx);
+        const float alpha = expf(m - m_new);
+        m = m_new;
+        const float pj = ok ? expf(x - m) : 0.f;
+        float ps = pj;
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) ps += __shfl_xor(ps, s, kWave);
+        lsum = lsum * alpha + ps;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[k] *= alpha;
+        const int nj = min(64, nkeys - j0);
+        for (int jj = 0; jj < nj; ++jj) {
+            const float pb = __shfl(pj, jj, kWave);
+            const int sb = __shfl(slot, jj, kWave);
+            const float* vr = v_pool + (int64_t)sb * pool_row + (int64_t)g * D;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) acc[k] = fmaf(pb, vr[64 * k + lane], acc[k]);
+        }
+    }
+    const float inv = 1.f / lsum;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) orow[64 * k + lane] = acc[k] * inv;
+}
+
+template <bool CAUSAL>
+int launch_rows(const AttnArgs& a, hipStream_t stream) {
+    const unsigned gx = CAUSAL ? (unsigned)a.max_extend_len : 1u;
+    if (gx == 0 || a.batch == 0) return 0;
+    dim3 grid(gx, a.n_q_heads, a.batch);
+    if (a.head_dim == 128) {
+        hipLaunchKernelGGL((attn_rows_fp32_kernel<128, CAUSAL>), grid, dim3(64), 0, stream,
+                           (const float*)a.q, (float*)a.o, (const float*)a.k_pool, (const float*)a.v_pool,
+                           a.r2t, a.r2t_stride, a.req_pool_indices, a.prefix_lens, a.extend_lens,
+                           a.extend_start_loc, a.seq_lens, a.total_tokens, a.max_extend_len,
+                           a.max_seq_len, a.n_q_heads, a.n_kv_heads, a.sm_scale);
+    } else {
+        hipLaunchKernelGGL((attn_rows_fp32_kernel<64, CAUSAL>), grid, dim3(64), 0, stream,
+                           (const float*)a.q, (float*)a.o, (const float*)a.k_pool, (const float*)a.v_pool,
+                           a.r2t, a.r2t_stride, a.req_pool_indices, a.prefix_lens, a.extend_lens,
+                           a.extend_start_loc, a.seq_lens, a.total_tokens, a.max_extend_len,
+                           a.max_seq_len, a.n_q_heads, a.n_kv_heads, a.sm_scale);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace
+
+int launch_extend_fp32(const AttnArgs& a, hipStream_t stream) { return launch_rows<true>(a, stream); }
+int launch_decode_fp32(const AttnArgs& a, hipStream_t stream) { return launch_rows<false>(a, stream); }
+
+}  // namespace rax

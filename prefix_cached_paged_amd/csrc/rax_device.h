@@ -1,0 +1,69 @@
+// Device-side helpers shared by the librax kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rax {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+constexpr int kWave = 64;
+
+// log2(e): scores are scaled by sm_scale * log2(e) once so that the softmax uses exp2.
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two fp32 -> packed bf16x2 (round to nearest even; v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+    bf16x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Pick 16-bit element `e` (0..7, compile-time) out of a 16-byte register quad.
+template <int E>
+__device__ __forceinline__ uint32_t half_of(const uint4& v) {
+    const uint32_t w = (E / 2 == 0) ? v.x : (E / 2 == 1) ? v.y : (E / 2 == 2) ? v.z : v.w;
+    return (E & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// Same for a 4-element (8-byte) register pair.
+template <int E>
+__device__ __forceinline__ uint32_t half_of(const uint2& v) {
+    const uint32_t w = (E / 2 == 0) ? v.x : v.y;
+    return (E & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// Column E of an 8x8 (rows r[0..7]) block of 16-bit values, as one 16-byte operand:
+// out element j = r[j] element E. Pure register moves (byte permutes).
+template <int E, typename Row>
+__device__ __forceinline__ uint4 column8(const Row (&r)[8]) {
+    uint4 o;
+    o.x = half_of<E>(r[0]) | (half_of<E>(r[1]) << 16);
+    o.y = half_of<E>(r[2]) | (half_of<E>(r[3]) << 16);
+    o.z = half_of<E>(r[4]) | (half_of<E>(r[5]) << 16);
+    o.w = half_of<E>(r[6]) | (half_of<E>(r[7]) << 16);
+    return o;
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+    return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+
+}  // namespace rax

@@ -1,0 +1,57 @@
+// Internal (C++) launch interface between the C-ABI layer and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rax {
+
+// Arguments of one EXTEND or DECODE call, already validated on the host.
+struct AttnArgs {
+    const void* q;
+    void* o;
+    const void* k_pool;
+    const void* v_pool;
+    int64_t num_slots;
+    const int32_t* r2t;
+    int64_t r2t_stride;
+    const int32_t* req_pool_indices;
+    // EXTEND
+    const int32_t* prefix_lens;
+    const int32_t* extend_lens;
+    const int32_t* extend_start_loc;
+    int64_t total_tokens;
+    int32_t max_extend_len;
+    // DECODE
+    const int32_t* seq_lens;
+    // both
+    int32_t batch;
+    int32_t max_seq_len;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    float sm_scale;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+int launch_kv_store(const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
+                    void* k_pool, void* v_pool, int64_t row_bytes, hipStream_t stream);
+
+// bf16, MFMA paths.
+bool extend_bf16_supported(int32_t group, int32_t head_dim);
+int launch_extend_bf16(const AttnArgs& a, hipStream_t stream);
+
+bool decode_bf16_supported(int32_t group, int32_t head_dim);
+int32_t decode_chunk(int32_t batch, int32_t max_seq_len, int32_t n_kv_heads);
+int32_t decode_splits(int32_t batch, int32_t max_seq_len, int32_t n_kv_heads);
+size_t decode_workspace(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                        int32_t head_dim);
+int launch_decode_bf16(const AttnArgs& a, hipStream_t stream);
+
+// fp32 path (vector ALU, fp32 throughout).
+int launch_extend_fp32(const AttnArgs& a, hipStream_t stream);
+int launch_decode_fp32(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace rax

@@ -1,0 +1,187 @@
+"""Thin ctypes binding over librax.so (argument marshalling only).
+
+Every function takes torch tensors that already live on the GPU, reads their data pointers
+and shapes, and calls the C entry point of the same name on the current (or given) HIP stream.
+No arithmetic of the method happens here. Tensors of ``torch.bfloat16`` or ``torch.float32``
+select the element format. Raises ``RaxError`` with the library's status name on any error
+status, and ``RuntimeError`` if the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch  # imported before the library so that one HIP runtime serves the process
+
+__all__ = [
+    "RaxError", "BF16", "FP32", "load", "version", "kv_store", "extend_attention",
+    "decode_attention", "extend_workspace_bytes", "decode_workspace_bytes", "decode_num_splits",
+    "library_path", "declared_symbols",
+]
+
+BF16 = 0
+FP32 = 1
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "librax.h")
+_lib = None
+
+_c_i32, _c_i64, _c_sz, _c_f, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
+
+_SIGS = {
+    "rax_version": (ctypes.c_int, []),
+    "rax_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "rax_kv_store": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64, _c_i32,
+                                    _c_i32, _c_p]),
+    "rax_extend_workspace_bytes": (_c_sz, [ctypes.c_int, _c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
+                                           _c_i32]),
+    "rax_extend_attention": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64,
+                                            _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64, _c_i32, _c_i32,
+                                            _c_i32, _c_i32, _c_i32, _c_f, _c_p, _c_sz, _c_p]),
+    "rax_decode_workspace_bytes": (_c_sz, [ctypes.c_int, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "rax_decode_attention": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64,
+                                            _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f,
+                                            _c_p, _c_sz, _c_p]),
+    "rax_decode_num_splits": (_c_i32, [ctypes.c_int, _c_i32, _c_i32, _c_i32]),
+}
+
+
+class RaxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = load().rax_status_str(status).decode()
+        super().__init__(f"{where}: {name} ({status})")
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "librax.so")
+
+
+def declared_symbols() -> list[str]:
+    """Names of the functions include/librax.h declares."""
+    text = open(_HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[A-Za-z_][\w\s\*]*?)\b(rax_\w+)\s*\(", text, flags=re.M)))
+
+
+def load():
+    """Load librax.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m prefix_cached_paged_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def version() -> int:
+    return load().rax_version()
+
+
+def _dtype(*ts) -> int:
+    dt = ts[0].dtype
+    for t in ts:
+        if t.dtype != dt:
+            raise TypeError("all float tensors of one call must share a dtype")
+    if dt == torch.bfloat16:
+        return BF16
+    if dt == torch.float32:
+        return FP32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("librax takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("librax takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _idx(t):
+    if t.dtype != torch.int32:
+        raise TypeError("index tensors must be int32")
+    return _ptr(t)
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise RaxError(status, where)
+
+
+def kv_store(k_new, v_new, loc, k_pool, v_pool, stream=None):
+    """k_pool[loc[i]] = k_new[i]; v_pool[loc[i]] = v_new[i] (in place)."""
+    S, Hkv, D = k_pool.shape
+    _check(load().rax_kv_store(_dtype(k_new, v_new, k_pool, v_pool), _ptr(k_new), _ptr(v_new), _idx(loc),
+                               loc.shape[0], _ptr(k_pool), _ptr(v_pool), S, Hkv, D, _stream(stream)),
+           "rax_kv_store")
+
+
+def extend_workspace_bytes(dtype: int, batch, total_tokens, max_extend_len, max_seq_len, n_q_heads,
+                           n_kv_heads, head_dim) -> int:
+    return load().rax_extend_workspace_bytes(dtype, batch, total_tokens, max_extend_len, max_seq_len,
+                                             n_q_heads, n_kv_heads, head_dim)
+
+
+def decode_workspace_bytes(dtype: int, batch, max_seq_len, n_q_heads, n_kv_heads, head_dim) -> int:
+    return load().rax_decode_workspace_bytes(dtype, batch, max_seq_len, n_q_heads, n_kv_heads, head_dim)
+
+
+def decode_num_splits(dtype: int, batch, max_seq_len, n_kv_heads) -> int:
+    return load().rax_decode_num_splits(dtype, batch, max_seq_len, n_kv_heads)
+
+
+def _workspace(nbytes, workspace, device):
+    if nbytes == 0:
+        return workspace
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def extend_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens, extend_lens,
+                     extend_start_loc, max_extend_len, max_seq_len, sm_scale, workspace=None,
+                     stream=None):
+    """EXTEND attention of the suffix rows ``q`` into ``o`` (same shape), keys from the pool."""
+    N, Hq, D = q.shape
+    S, Hkv, Dk = k_pool.shape
+    dt = _dtype(q, o, k_pool, v_pool)
+    B = prefix_lens.shape[0]
+    need = extend_workspace_bytes(dt, B, N, max_extend_len, max_seq_len, Hq, Hkv, D)
+    workspace = _workspace(need, workspace, q.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().rax_extend_attention(dt, _ptr(q), _ptr(o), _ptr(k_pool), _ptr(v_pool), S, _idx(req_to_token),
+                                       req_to_token.shape[1], _idx(req_pool_indices), _idx(prefix_lens),
+                                       _idx(extend_lens), _idx(extend_start_loc), B, N, int(max_extend_len),
+                                       int(max_seq_len), Hq, Hkv, D, float(sm_scale), _ptr(workspace), wbytes,
+                                       _stream(stream)),
+           "rax_extend_attention")
+
+
+def decode_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, seq_lens, max_seq_len, sm_scale,
+                     workspace=None, stream=None):
+    """DECODE attention of one query per request ``q`` [B, Hq, D] into ``o``."""
+    B, Hq, D = q.shape
+    S, Hkv, Dk = k_pool.shape
+    dt = _dtype(q, o, k_pool, v_pool)
+    need = decode_workspace_bytes(dt, B, max_seq_len, Hq, Hkv, D)
+    workspace = _workspace(need, workspace, q.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().rax_decode_attention(dt, _ptr(q), _ptr(o), _ptr(k_pool), _ptr(v_pool), S, _idx(req_to_token),
+                                       req_to_token.shape[1], _idx(req_pool_indices), _idx(seq_lens), B,
+                                       int(max_seq_len), Hq, Hkv, D, float(sm_scale), _ptr(workspace), wbytes,
+                                       _stream(stream)),
+           "rax_decode_attention")

@@ -1,0 +1,117 @@
+"""CPU checks of the C ABI: the library loads, exports what the header declares, and rejects bad
+arguments on the host before anything is launched (no compute call is made here)."""
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from prefix_cached_paged_amd import rax as R
+
+pytestmark = pytest.mark.skipif(not os.path.exists(R.library_path()), reason="librax.so not built")
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def lib():
+    return R.load()
+
+
+def test_every_declared_symbol_is_exported():
+    names = R.declared_symbols()
+    assert set(names) == {"rax_version", "rax_status_str", "rax_kv_store", "rax_extend_workspace_bytes",
+                          "rax_extend_attention", "rax_decode_workspace_bytes", "rax_decode_attention",
+                          "rax_decode_num_splits"}
+    out = subprocess.run(["nm", "-D", "--defined-only", R.library_path()], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib(), n)
+
+
+def test_version_and_status_names():
+    assert lib().rax_version() == 100
+    for code, name in enumerate(["RAX_OK", "RAX_ERR_NULL", "RAX_ERR_SHAPE", "RAX_ERR_DTYPE",
+                                 "RAX_ERR_UNSUPPORTED", "RAX_ERR_WORKSPACE", "RAX_ERR_LAUNCH"]):
+        assert lib().rax_status_str(code).decode() == name
+    assert lib().rax_status_str(99).decode() == "unknown status"
+
+
+def kv_store(**kw):
+    a = dict(dtype=0, k_new=FAKE, v_new=FAKE, loc=FAKE, n_new=4, k_pool=FAKE, v_pool=FAKE, num_slots=16,
+             n_kv_heads=2, head_dim=128, stream=None)
+    a.update(kw)
+    return lib().rax_kv_store(*a.values())
+
+
+def test_kv_store_validation():
+    assert kv_store(dtype=7) == 3
+    assert kv_store(n_new=-1) == 2
+    assert kv_store(n_new=17) == 2
+    assert kv_store(num_slots=0) == 2
+    assert kv_store(n_kv_heads=0) == 2
+    assert kv_store(head_dim=96) == 4
+    assert kv_store(k_pool=None) == 1
+    assert kv_store(loc=None) == 1
+    assert kv_store(n_new=0, k_pool=None) == 0  # empty: no-op, nothing enqueued
+
+
+def extend(**kw):
+    a = dict(dtype=0, q=FAKE, o=FAKE, k_pool=FAKE, v_pool=FAKE, num_slots=1024, r2t=FAKE, r2t_stride=512,
+             rpi=FAKE, prefix=FAKE, ext=FAKE, start=FAKE, batch=2, total=64, max_ext=40, max_seq=300, hq=8,
+             hkv=2, d=128, scale=0.088, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib().rax_extend_attention(*a.values())
+
+
+def test_extend_validation():
+    assert extend(dtype=2) == 3
+    assert extend(batch=-1) == 2
+    assert extend(max_seq=600) == 2          # beyond the table row
+    assert extend(max_ext=301) == 2          # an extend longer than the longest sequence
+    assert extend(max_ext=65, total=64) == 2
+    assert extend(hq=6, hkv=4) == 2          # not a multiple
+    assert extend(d=96) == 4
+    assert extend(hq=6, hkv=2) == 4          # bf16 MFMA path needs a power-of-two group
+    assert extend(hq=64, hkv=2) == 4         # group 32 is beyond the bf16 tile
+    assert extend(scale=float("nan")) == 2
+    assert extend(q=None) == 1
+    assert extend(start=None) == 1
+    assert extend(batch=0, q=None) == 0      # empty batch
+    assert extend(total=0, max_ext=0, q=None) == 0
+
+
+def decode(**kw):
+    a = dict(dtype=0, q=FAKE, o=FAKE, k_pool=FAKE, v_pool=FAKE, num_slots=1024, r2t=FAKE, r2t_stride=512,
+             rpi=FAKE, seq=FAKE, batch=3, max_seq=300, hq=8, hkv=2, d=128, scale=0.088, ws=None, ws_bytes=0,
+             stream=None)
+    a.update(kw)
+    return lib().rax_decode_attention(*a.values())
+
+
+def test_decode_validation():
+    assert decode(dtype=5) == 3
+    assert decode(max_seq=513) == 2
+    assert decode(max_seq=0) == 2
+    assert decode(hq=8, hkv=3) == 2
+    assert decode(d=32) == 4
+    assert decode(hq=34, hkv=2) == 4         # group 17 is beyond the 16-wide head tile
+    assert decode(seq=None) == 1
+    # workspace: bf16 needs one, too small or missing is refused before any launch
+    need = lib().rax_decode_workspace_bytes(0, 3, 300, 8, 2, 128)
+    assert need > 0
+    assert decode(ws=None, ws_bytes=0) == 5
+    assert decode(ws=FAKE, ws_bytes=need - 1) == 5
+    assert decode(batch=0, q=None) == 0
+
+
+def test_decode_workspace_size():
+    for B, L, hq, hkv in [(64, 4096, 32, 8), (8, 131072, 64, 8), (1, 1, 4, 4), (128, 8192, 32, 8)]:
+        ns = lib().rax_decode_num_splits(0, B, L, hkv)
+        assert ns >= 1
+        rows = B * hq * ns
+        o_bytes = (rows * 128 * 4 + 255) // 256 * 256
+        assert lib().rax_decode_workspace_bytes(0, B, L, hq, hkv, 128) == o_bytes + rows * 4
+    assert lib().rax_decode_workspace_bytes(1, 64, 4096, 32, 8, 128) == 0   # fp32 path needs none
+    assert lib().rax_extend_workspace_bytes(0, 1, 2048, 2048, 16384, 32, 8, 128) == 0
