@@ -1,0 +1,245 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: kv_store of the step's new rows, EXTEND
+of the prefill chunk, DECODE of the running requests, all on one stream, inputs resident in
+HBM. Default workload: the mixed chunked-prefill batch (one 2,048-token chunk on a
+14,336-token cached prefix plus 128 decode requests with 1,024..8,192 tokens of context,
+32 q / 8 kv heads, head_dim 128, bf16, a 1,048,576-slot pool), which exercises every call.
+
+Prints ONE JSON line. ``value`` is the EXTEND attention throughput in TFLOP/s (algorithmic
+FLOPs: 4 * head_dim * q_heads per attended pair, masked pairs not counted); the DECODE KV
+bandwidth is reported beside it. Per-kernel durations come from HIP events recorded on the
+launch stream around each call over the timed steps.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "extend attn TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, dev_outs, budget_s: float):
+    """Time the CPU oracle (as it stands) on a bounded sample of the same workload."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    from prefix_cached_paged_amd import accounting as A
+    from prefix_cached_paged_amd.device import to_host_bits
+
+    spec = wl.spec
+    t0 = time.perf_counter()
+    kp, vp = oracle.kv_store(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.store_loc)
+    t_store = time.perf_counter() - t0
+    res = {}
+    parity = {}
+    if wl.extend is not None:
+        e = wl.extend
+        b = int(np.argmax(e.extend_lens))
+        n = int(e.extend_lens[b])
+        s0 = int(e.extend_start_loc[b])
+        # last rows first: they see the most keys; grow the sample until about half the budget
+        toks, flops, t_ext = [], 0, 0.0
+        step = 8
+        while t_ext < budget_s / 2 and len(toks) < n:
+            new = [s0 + n - 1 - i for i in range(len(toks), min(n, len(toks) + step))]
+            t1 = time.perf_counter()
+            ref = oracle.extend_attention(e.q, kp, vp, wl.req_to_token, e.req_pool_indices, e.prefix_lens,
+                                          e.extend_lens, e.extend_start_loc, spec.n_kv_heads, wl.sm_scale,
+                                          tokens=new)
+            t_ext += time.perf_counter() - t1
+            p = int(e.prefix_lens[b])
+            flops += sum(4 * spec.head_dim * spec.n_q_heads * (p + (t - s0) + 1) for t in new)
+            got = oracle.to_f64(to_host_bits(dev_outs["extend"][new]))
+            parity.setdefault("extend_max_abs", 0.0)
+            parity["extend_max_abs"] = max(parity["extend_max_abs"], float(np.max(np.abs(got - ref))))
+            toks += new
+            step *= 2
+        res["extend"] = dict(tflops=flops / t_ext / 1e12, tokens=len(toks), seconds=t_ext)
+    if wl.decode is not None:
+        d = wl.decode
+        reqs, nbytes, t_dec = [], 0, 0.0
+        order = list(range(d.batch))
+        while t_dec < budget_s / 2 and len(reqs) < d.batch:
+            new = order[len(reqs):len(reqs) + max(1, len(reqs))]
+            t1 = time.perf_counter()
+            ref = oracle.decode_attention(d.q, kp, vp, wl.req_to_token, d.req_pool_indices, d.seq_lens,
+                                          spec.n_kv_heads, wl.sm_scale, requests=new)
+            t_dec += time.perf_counter() - t1
+            nbytes += A.decode_kv_bytes(d.seq_lens[new], spec.n_kv_heads, spec.head_dim, spec.elem_bytes)
+            got = oracle.to_f64(to_host_bits(dev_outs["decode"][new]))
+            parity.setdefault("decode_max_abs", 0.0)
+            parity["decode_max_abs"] = max(parity["decode_max_abs"], float(np.max(np.abs(got - ref))))
+            reqs += new
+        res["decode"] = dict(GBps=nbytes / t_dec / 1e9, requests=len(reqs), seconds=t_dec)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    sample = []
+    if "extend" in res:
+        sample.append(f"EXTEND: last {res['extend']['tokens']} suffix rows of the chunk, all heads")
+    if "decode" in res:
+        sample.append(f"DECODE: {res['decode']['requests']} of {wl.decode.batch} requests, all heads")
+    out = dict(value=res.get("extend", {}).get("tflops"), unit="TFLOP/s", cores=threads, kind="oracle",
+               sample="; ".join(sample) + f"; float64 numpy, kv_store copy {t_store:.1f} s not counted",
+               decode_GBps=res.get("decode", {}).get("GBps"), parity_vs_gpu=parity)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4, help="workload id (1..5)")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-budget", type=float, default=16.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (see DESIGN.md for "
+              "how the path would shard); rerun with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from prefix_cached_paged_amd import accounting as A
+    from prefix_cached_paged_amd import rax
+    from prefix_cached_paged_amd import workloads as W
+    from prefix_cached_paged_amd.device import upload
+
+    rax.load()  # fails loudly if the HIP library is missing
+    cfg = args.config
+    spec = W.CONFIGS[cfg]
+    seed = args.seed if args.seed is not None else W.TIMING_SEEDS[cfg]
+    log(f"generating workload {spec.name} seed {seed}")
+    wl = W.make_workload(spec, seed)
+    log("uploading")
+    dw = upload(wl, "cuda:0")
+    dt = rax.BF16 if spec.dtype == "bf16" else rax.FP32
+    ws = None
+    if dw.dec is not None:
+        d = dw.dec
+        nb = rax.decode_workspace_bytes(dt, d["q"].shape[0], d["max_seq_len"], spec.n_q_heads, spec.n_kv_heads,
+                                        spec.head_dim)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda:0")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        rax.kv_store(dw.k_new, dw.v_new, dw.store_loc, dw.k_pool, dw.v_pool)
+        if ev is not None:
+            ev[1].record()
+        if dw.ext is not None:
+            e = dw.ext
+            rax.extend_attention(e["q"], e["o"], dw.k_pool, dw.v_pool, dw.req_to_token, e["req_pool_indices"],
+                                 e["prefix_lens"], e["extend_lens"], e["extend_start_loc"], e["max_extend_len"],
+                                 e["max_seq_len"], wl.sm_scale)
+        if ev is not None:
+            ev[2].record()
+        if dw.dec is not None:
+            d = dw.dec
+            rax.decode_attention(d["q"], d["o"], dw.k_pool, dw.v_pool, dw.req_to_token, d["req_pool_indices"],
+                                 d["seq_lens"], d["max_seq_len"], wl.sm_scale, workspace=ws)
+        if ev is not None:
+            ev[3].record()
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms = {n: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+          for i, n in enumerate(["kv_store", "extend", "decode"])}
+
+    report = {}
+    hbm = lambda nbytes, t_ms: nbytes / (t_ms * 1e-3) / 1e9
+    n_new = int(wl.store_loc.size)
+    st_bytes = A.kv_store_bytes(n_new, spec.n_kv_heads, spec.head_dim, spec.elem_bytes)
+    report["kv_store"] = dict(ms=ms["kv_store"], rows=n_new, GBps=hbm(st_bytes, ms["kv_store"]),
+                              bytes=st_bytes)
+    roofs = {}
+    if wl.extend is not None:
+        e = wl.extend
+        fl = A.extend_flops(e.prefix_lens, e.extend_lens, spec.n_q_heads, spec.head_dim)
+        tf = fl / (ms["extend"] * 1e-3) / 1e12
+        report["extend"] = dict(ms=ms["extend"], flops=fl, tflops=tf, frac=tf / PEAK_BF16_TFLOPS)
+        roofs["extend"] = dict(kernel="extend_attention", bound="mfma", achieved=tf, peak=PEAK_BF16_TFLOPS,
+                               unit="TFLOP/s", frac=tf / PEAK_BF16_TFLOPS, traffic=None,
+                               per_launch=f"{fl} algorithmic FLOP", ms=ms["extend"])
+    if wl.decode is not None:
+        d = wl.decode
+        kvb = A.decode_kv_bytes(d.seq_lens, spec.n_kv_heads, spec.head_dim, spec.elem_bytes)
+        tot = A.decode_total_bytes(d.seq_lens, d.batch, spec.n_q_heads, spec.n_kv_heads, spec.head_dim,
+                                   spec.elem_bytes)
+        gb = hbm(kvb, ms["decode"])
+        report["decode"] = dict(ms=ms["decode"], kv_bytes=kvb, kv_GBps=gb, frac=gb / PEAK_HBM_GBPS,
+                                total_GBps=hbm(tot, ms["decode"]),
+                                splits=rax.decode_num_splits(dt, d.batch, d.max_seq_len, spec.n_kv_heads))
+        roofs["decode"] = dict(kernel="decode_attention (split + merge)", bound="hbm", achieved=gb,
+                               peak=PEAK_HBM_GBPS, unit="GB/s", frac=gb / PEAK_HBM_GBPS, traffic=None,
+                               per_launch=f"{kvb} KV bytes", ms=ms["decode"])
+    dominant = max(roofs, key=lambda k: roofs[k]["ms"]) if roofs else None
+
+    if "extend" in report:
+        value, unit = report["extend"]["tflops"], "TFLOP/s"
+    else:
+        value, unit = report["decode"]["kv_GBps"], "GB/s"
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        outs = {}
+        if dw.ext is not None:
+            outs["extend"] = dw.ext["o"]
+        if dw.dec is not None:
+            outs["decode"] = dw.dec["o"]
+        cpu = cpu_baseline(wl, outs, args.cpu_budget)
+        if unit == "GB/s":
+            cpu["value"], cpu["unit"] = cpu.pop("decode_GBps"), "GB/s"
+
+    cfgd = {"workload": spec.name, "config_id": cfg, "seed": seed, "dtype": spec.dtype,
+            "q_heads": spec.n_q_heads, "kv_heads": spec.n_kv_heads, "head_dim": spec.head_dim,
+            "pool_slots": spec.num_slots}
+    if wl.extend is not None:
+        cfgd["extend"] = {"batch": wl.extend.batch, "new_tokens": wl.extend.total_tokens,
+                          "prefix_lens": sorted(set(int(x) for x in wl.extend.prefix_lens))[:4]}
+    if wl.decode is not None:
+        cfgd["decode"] = {"batch": wl.decode.batch, "mean_context": float(np.mean(wl.decode.seq_lens)),
+                          "total_context": int(np.sum(wl.decode.seq_lens))}
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": spec.dtype, "data": "synthetic", "config": cfgd,
+        "kernels": report,
+        "roofline": roofs.get(dominant),
+        "roofline_other": [roofs[k] for k in roofs if k != dominant],
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
