@@ -43,15 +43,22 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile every csrc/*.hip and link librax.so. Always recompiles. Returns the library path."""
+def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str | None = None,
+          build_dir: str | None = None) -> str:
+    """Compile every csrc/*.hip and link librax.so. Always recompiles. Returns the library path.
+
+    ``extra_flags`` (e.g. -D overrides of launch-shape constants), ``out`` and ``build_dir``
+    let a tuning sweep build variants beside the default library.
+    """
     cc = hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    lib_path = out or LIB
+    bdir = build_dir or BUILD
+    os.makedirs(bdir, exist_ok=True)
     flags = HIPCC_FLAGS + list(extra_flags or [])
     srcs = sources()
 
     def compile_one(src):
-        obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+        obj = os.path.join(bdir, os.path.basename(src)[:-4] + ".o")
         cmd = [cc, *flags, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
@@ -62,15 +69,15 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
 
     with cf.ThreadPoolExecutor(max(1, min(8, len(srcs)))) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
-    return LIB
+        print(f"built {lib_path}", file=sys.stderr)
+    return lib_path
 
 
 if __name__ == "__main__":

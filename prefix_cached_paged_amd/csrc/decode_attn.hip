@@ -34,7 +34,17 @@ namespace rax {
 
 namespace {
 
-constexpr int kDecWaves = 4;       // waves (kv heads) per workgroup
+// Launch-shape constants (overridable at build time for tuning sweeps).
+#ifndef RAX_DEC_WAVES
+#define RAX_DEC_WAVES 4
+#endif
+#ifndef RAX_DEC_TARGET_WAVES
+#define RAX_DEC_TARGET_WAVES 8192
+#endif
+#ifndef RAX_DEC_MIN_CHUNK
+#define RAX_DEC_MIN_CHUNK 256
+#endif
+constexpr int kDecWaves = RAX_DEC_WAVES;  // waves (kv heads) per workgroup
 constexpr int kDecKeysPerIter = 64;
 
 template <int D>
@@ -246,12 +256,13 @@ bool decode_bf16_supported(int32_t group, int32_t head_dim) {
 }
 
 // Keys per split: enough splits that batch * n_kv_heads * splits is in the thousands of waves
-// (256 CUs), in multiples of the 64-key iteration, between 256 and 4096 keys.
+// (256 CUs), in multiples of the 64-key iteration, between RAX_DEC_MIN_CHUNK and 4096 keys.
 int32_t decode_chunk(int32_t batch, int32_t max_seq_len, int32_t n_kv_heads) {
     const int64_t units = (int64_t)batch * n_kv_heads;
-    int64_t want = units > 0 ? ((int64_t)max_seq_len * units + 8191) / 8192 : 256;
+    const int64_t target = RAX_DEC_TARGET_WAVES;
+    int64_t want = units > 0 ? ((int64_t)max_seq_len * units + target - 1) / target : RAX_DEC_MIN_CHUNK;
     want = (want + kDecKeysPerIter - 1) / kDecKeysPerIter * kDecKeysPerIter;
-    if (want < 256) want = 256;
+    if (want < RAX_DEC_MIN_CHUNK) want = RAX_DEC_MIN_CHUNK;
     if (want > 4096) want = 4096;
     return (int32_t)want;
 }
