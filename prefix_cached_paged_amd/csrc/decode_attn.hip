@@ -39,7 +39,7 @@ namespace {
 #define RAX_DEC_WAVES 4
 #endif
 #ifndef RAX_DEC_TARGET_WAVES
-#define RAX_DEC_TARGET_WAVES 8192
+#define RAX_DEC_TARGET_WAVES 2048
 #endif
 #ifndef RAX_DEC_MIN_CHUNK
 #define RAX_DEC_MIN_CHUNK 256
@@ -56,7 +56,7 @@ __device__ __forceinline__ uint4 vcol(const VRow<D> (&r)[8]) {
 }
 
 template <int D>
-__global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(
+__global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
@@ -101,29 +101,33 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int base = k0; base < k1; base += kDecKeysPerIter) {
-        const int my_key = base + lane;
-        const int my_slot = row[my_key < k1 ? my_key : k1 - 1];
+    // Software pipeline over 64-key iterations: slot numbers are loaded two iterations ahead;
+    // the next iteration's K rows are requested as soon as this iteration's score MFMAs have
+    // consumed theirs, and its V rows as soon as P V has consumed this iteration's.
+    uint4 kr[4][S];
+    VRow<D> vr[2][8];
+#define RAX_DEC_SLOT(BASE) row[min((BASE) + lane, k1 - 1)]
+#define RAX_DEC_LOAD_K(SLOT)                                                                \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
+        const int sl_ = __shfl((SLOT), 16 * t + n16, kWave);                                \
+        const uint16_t* p_ = kbase + (int64_t)sl_ * pool_row;                               \
+        _Pragma("unroll") for (int s = 0; s < S; ++s) kr[t][s] = *(const uint4*)(p_ + 32 * s); \
+    }
+#define RAX_DEC_LOAD_V(SLOT)                                                                \
+    _Pragma("unroll") for (int u = 0; u < 2; ++u)                                           \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                         \
+        const int key_ = 32 * u + 16 * (j >> 2) + 4 * kg + (j & 3);                         \
+        const int sl_ = __shfl((SLOT), key_, kWave);                                        \
+        vr[u][j] = *(const VRow<D>*)(vbase + (int64_t)sl_ * pool_row);                      \
+    }
 
-        // K: 4 tiles of 16 keys; lane loads key 16t + n16, head_dim 32s + 8kg .. +8.
-        uint4 kr[4][S];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int sl = __shfl(my_slot, 16 * t + n16, kWave);
-            const uint16_t* p = kbase + (int64_t)sl * pool_row;
-#pragma unroll
-            for (int s = 0; s < S; ++s) kr[t][s] = *(const uint4*)(p + 32 * s);
-        }
-        // V: per 32-key block u, the 8 keys 32u + 16h + 4kg + i (h = 0,1; i = 0..3).
-        VRow<D> vr[2][8];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int key = 32 * u + 16 * (j >> 2) + 4 * kg + (j & 3);
-                const int sl = __shfl(my_slot, key, kWave);
-                vr[u][j] = *(const VRow<D>*)(vbase + (int64_t)sl * pool_row);
-            }
+    int slot_cur = RAX_DEC_SLOT(k0);
+    RAX_DEC_LOAD_K(slot_cur)
+    RAX_DEC_LOAD_V(slot_cur)
+    int slot_nxt = RAX_DEC_SLOT(k0 + kDecKeysPerIter);
+
+    for (int base = k0; base < k1; base += kDecKeysPerIter) {
+        const bool more = base + kDecKeysPerIter < k1;
 
         // S^T[key][head]: lane holds keys 16t + 4kg + i of head n16.
         f32x4 st[4];
@@ -133,19 +137,20 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(
 #pragma unroll
             for (int s = 0; s < S; ++s) st[t] = mfma16x16x32(as_bf16x8(kr[t][s]), qop[s], st[t]);
         }
+        if (more) RAX_DEC_LOAD_K(slot_nxt)
 
-        float x[4][4];
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = base + 16 * t + 4 * kg + i;
-                x[t][i] = key < k1 ? st[t][i] * scale_log2 : -INFINITY;
-                mx = fmaxf(mx, x[t][i]);
+                if (key >= k1) st[t][i] = -INFINITY;
+                mx = fmaxf(mx, st[t][i]);
             }
         mx = wave_max_xor(mx, 16);
         mx = wave_max_xor(mx, 32);
+        mx *= scale_log2;
         const float m_new = fmaxf(m, mx);
         const float alpha = fast_exp2(m - m_new);
         m = m_new;
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[t][i] = fast_exp2(x[t][i] - m);
+                p[t][i] = fast_exp2(fmaf(st[t][i], scale_log2, -m));
                 lsum += p[t][i];
             }
 
@@ -182,7 +187,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(
                 acc[7] = mfma16x16x32(as_bf16x8(vcol<D, 7>(vr[u])), pop, acc[7]);
             }
         }
+        if (more) {
+            RAX_DEC_LOAD_V(slot_nxt)
+            slot_nxt = RAX_DEC_SLOT(base + 2 * kDecKeysPerIter);
+        }
     }
+#undef RAX_DEC_SLOT
+#undef RAX_DEC_LOAD_K
+#undef RAX_DEC_LOAD_V
 
     lsum += __shfl_xor(lsum, 16, kWave);
     lsum += __shfl_xor(lsum, 32, kWave);

@@ -13,18 +13,20 @@
 //    of the G query heads sharing kv head g, token-major, so one gathered K/V tile feeds
 //    128 / G tokens x G heads. Each wave owns 32 rows.
 //  * Key tiles of 64: 256 threads gather the 64 K rows and 64 V rows (256 B per kv head per
-//    row, 16-byte loads, 16 lanes per row: coalesced) into registers one tile ahead, then store
-//    them to LDS: K row-major [key][d], V transposed [d][key] (4 keys x 8 head_dim elements
-//    per thread, transposed with register byte permutes). Both LDS arrays are XOR-swizzled in
-//    16-byte units so that the MFMA operand reads (8 consecutive rows per 8 lanes) and the
-//    stores are free or nearly free of bank conflicts.
+//    row, 16-byte loads, 16 lanes per row: coalesced). Slot numbers are loaded two tiles
+//    ahead and rows one tile ahead, so the dependent slot -> row load pair never stalls the
+//    MFMAs. Two LDS buffers, one barrier per tile. K and V are both stored row-major, XOR-
+//    swizzled in 16-byte units so that the operand reads and the stores avoid bank conflicts.
 //  * S^T = K Q^T with 32x32x16 bf16 MFMAs: keys are the M dimension (read from LDS), query
 //    rows the N dimension (Q stays in registers for the whole key loop). The C layout puts
 //    one query row per lane column, so the row max/sum are per lane plus one exchange with
 //    the other half-wave.
-//  * O^T = V^T P^T, also 32x32x16: P^T is the score C fragment converted to bf16 in place
-//    (the key order inside each 16-key step is a fixed bit permutation that the V^T layout in
-//    LDS follows), so P never leaves registers.
+//  * O^T = V^T P^T, also 32x32x16: P^T is the score C fragment converted to bf16 in place, so
+//    P never leaves registers. The V^T operand comes from the row-major V tile through the
+//    gfx950 transposed LDS read (ds_read_b64_tr_b16), in the key order the P^T fragment has.
+//  * Softmax: sm_scale * log2(e) is folded into one FMA before exp2; the accumulators are only
+//    rescaled when a row max grows by more than 2^8 (exact: P and the row sum share the
+//    reference max).
 //  * Causal mask only on the tiles that cross the diagonal; keys past the last visible key of
 //    the workgroup reuse a valid slot and are masked, so no load leaves the request's slots.
 //  * Workgroup order is XCD-aware: consecutive workgroup ids go to different XCDs, so the
@@ -43,12 +45,25 @@ constexpr int kExtBN = 64;
 constexpr int kExtThreads = 256;
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ int swz_k(int key, int unit) { return unit ^ (key & 7); }
-__device__ __forceinline__ int swz_v(int d, int unit) { return unit ^ ((d ^ (d >> 3)) & 7); }
+// In units of 2^kLazyLog2, how far a row max may rise before the accumulators are rescaled.
+constexpr float kLazyLog2 = 8.f;
 
-// Key offset (within a 16-key MFMA step) held at k-slot q of the P^T fragment: bits 2 and 3
-// swapped. The map is its own inverse.
-__device__ __forceinline__ int swap23(int q) { return (q & ~12) | ((q & 4) << 1) | ((q & 8) >> 1); }
+// LDS swizzles (16-byte units within a 256-byte row). K: unit ^ (key & 7) keeps the eight
+// consecutive rows that eight lanes read for one MFMA operand on distinct banks. V:
+// unit ^ 2 (key & 3) keeps the four rows of one transposed read (keys 4n .. 4n+3, two units
+// each) on distinct banks. Stores write whole rows, so any permutation within a row is free.
+__device__ __forceinline__ int swz_k(int key, int unit) { return unit ^ (key & 7); }
+__device__ __forceinline__ int swz_v(int key, int unit) { return unit ^ (2 * (key & 3)); }
+
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16): within each 16-lane group, lane 4j + c
+// supplies the address of four 16-bit values; lane i receives value i % 4 of the chunk of lane
+// 4j + i / 4, for j = 0..3.
+__device__ __forceinline__ uint2 ds_read_tr16_b64(const char* lds_addr) {
+    typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(lds_addr));
+    return __builtin_bit_cast(uint2, v);
+}
 
 template <int G>
 __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
@@ -61,8 +76,9 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
     constexpr int D = kExtD;
     constexpr int BQ = kExtBM / G;  // tokens per workgroup
 
-    __shared__ uint4 k_lds[kExtBN * 16];  // [key][16 units of 8 bf16]
-    __shared__ uint4 vt_lds[D * 8];       // [d][8 units of 8 keys]
+    // Two LDS buffers, each a 64-key tile of K and V, row-major [key][16 units of 8 bf16].
+    __shared__ uint4 k_lds[2][kExtBN * 16];
+    __shared__ uint4 v_lds[2][kExtBN * 16];
 
     // ---- workgroup -> (pair = b * Hkv + g, tile), XCD-aware
     const int pairs = batch * Hkv;
@@ -104,45 +120,52 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qop[s] = as_bf16x8(*(const uint4*)(q + qo_row + 16 * s + 8 * h2));
 
-    // ---- cooperative gather roles
-    const int seg = tid & 15;  // 16-byte unit of head_dim (8 elements)
-    const int grp = tid >> 4;  // 0..15
-    // K: keys grp + 16 i; V: keys 4 grp + i (i = 0..3)
-    uint4 kst[4], vst[4];
-    auto gather = [&](int j0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int kj = min(j0 + grp + 16 * i, kend - 1);
-            const int vj = min(j0 + 4 * grp + i, kend - 1);
-            const int ks = row[kj];
-            const int vs = row[vj];
-            kst[i] = *(const uint4*)(kbase + (int64_t)ks * pool_row + 8 * seg);
-            vst[i] = *(const uint4*)(vbase + (int64_t)vs * pool_row + 8 * seg);
-        }
-    };
-    // V^T position of key 4*grp + i: 16-key step (grp / 4), offset swap23(4 (grp % 4) + i).
-    const int vpos0 = 16 * (grp >> 2) + swap23(4 * (grp & 3));
-    const int vunit = vpos0 >> 3;
-    const int vhalf = (vpos0 >> 2) & 1;
-    auto to_lds = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = grp + 16 * i;
-            k_lds[key * 16 + swz_k(key, seg)] = kst[i];
-        }
-        uint2* vt2 = (uint2*)vt_lds;
-#define RAX_VT_STORE(DD)                                                                        \
-        {                                                                                       \
-            const int d = 8 * seg + DD;                                                         \
-            uint2 w;                                                                            \
-            w.x = half_of<DD>(vst[0]) | (half_of<DD>(vst[1]) << 16);                            \
-            w.y = half_of<DD>(vst[2]) | (half_of<DD>(vst[3]) << 16);                            \
-            vt2[(d * 8 + swz_v(d, vunit)) * 2 + vhalf] = w;                                     \
-        }
-        RAX_VT_STORE(0) RAX_VT_STORE(1) RAX_VT_STORE(2) RAX_VT_STORE(3)
-        RAX_VT_STORE(4) RAX_VT_STORE(5) RAX_VT_STORE(6) RAX_VT_STORE(7)
-#undef RAX_VT_STORE
-    };
+    // ---- cooperative gather: thread (seg, grp) moves 16-byte unit `seg` of keys grp + 16 i
+    const int seg = tid & 15;
+    const int grp = tid >> 4;
+    const int ntiles = (kend + kExtBN - 1) / kExtBN;
+    int slot0, slot1, slot2, slot3;
+    uint4 kst0, kst1, kst2, kst3, vst0, vst1, vst2, vst3;
+#define RAX_LOAD_SLOTS(TILE)                                                                \
+    {                                                                                       \
+        const int kb_ = (TILE) * kExtBN + grp;                                              \
+        slot0 = row[min(kb_, kend - 1)];                                                    \
+        slot1 = row[min(kb_ + 16, kend - 1)];                                               \
+        slot2 = row[min(kb_ + 32, kend - 1)];                                               \
+        slot3 = row[min(kb_ + 48, kend - 1)];                                               \
+    }
+#define RAX_GATHER()                                                                        \
+    {                                                                                       \
+        kst0 = *(const uint4*)(kbase + (int64_t)slot0 * pool_row + 8 * seg);                \
+        vst0 = *(const uint4*)(vbase + (int64_t)slot0 * pool_row + 8 * seg);                \
+        kst1 = *(const uint4*)(kbase + (int64_t)slot1 * pool_row + 8 * seg);                \
+        vst1 = *(const uint4*)(vbase + (int64_t)slot1 * pool_row + 8 * seg);                \
+        kst2 = *(const uint4*)(kbase + (int64_t)slot2 * pool_row + 8 * seg);                \
+        vst2 = *(const uint4*)(vbase + (int64_t)slot2 * pool_row + 8 * seg);                \
+        kst3 = *(const uint4*)(kbase + (int64_t)slot3 * pool_row + 8 * seg);                \
+        vst3 = *(const uint4*)(vbase + (int64_t)slot3 * pool_row + 8 * seg);                \
+    }
+#define RAX_TO_LDS(BUF)                                                                     \
+    {                                                                                       \
+        uint4* kl_ = k_lds[BUF];                                                            \
+        uint4* vl_ = v_lds[BUF];                                                            \
+        kl_[(grp + 0) * 16 + swz_k(grp + 0, seg)] = kst0;                                   \
+        vl_[(grp + 0) * 16 + swz_v(grp + 0, seg)] = vst0;                                   \
+        kl_[(grp + 16) * 16 + swz_k(grp + 16, seg)] = kst1;                                 \
+        vl_[(grp + 16) * 16 + swz_v(grp + 16, seg)] = vst1;                                 \
+        kl_[(grp + 32) * 16 + swz_k(grp + 32, seg)] = kst2;                                 \
+        vl_[(grp + 32) * 16 + swz_v(grp + 32, seg)] = vst2;                                 \
+        kl_[(grp + 48) * 16 + swz_k(grp + 48, seg)] = kst3;                                 \
+        vl_[(grp + 48) * 16 + swz_v(grp + 48, seg)] = vst3;                                 \
+    }
+
+    // ---- per-lane constants of the transposed V reads (see swz_v): 16-lane group gi holds
+    // head_dim half dh = gi & 1 and k-group h2; lane i16 = 4 jr + c reads key offset jr and
+    // head_dim 4c .. 4c+3 of that half.
+    const int i16 = lane & 15;
+    const int dh = (lane >> 4) & 1;
+    const int jr = i16 >> 2;
+    const int cc = i16 & 3;
 
     float m = -INFINITY;
     float lsum = 0.f;
@@ -152,19 +175,30 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-    const int last_q = p + t;  // last key position this row may see
-    const int diag_from = p + t0;  // tiles whose last key exceeds this need the mask
-    const int ntiles = (kend + kExtBN - 1) / kExtBN;
+    const int last_q = p + t;       // last key position this row may see
+    const int diag_from = p + t0;   // tiles whose last key exceeds this need the mask
 
-    gather(0);
+    // prologue: tile 0 in LDS buffer 0, tile 1 in registers, slots of tile 2 in registers
+    RAX_LOAD_SLOTS(0)
+    RAX_GATHER()
+    RAX_TO_LDS(0)
+    if (ntiles > 1) {
+        RAX_LOAD_SLOTS(1)
+        RAX_GATHER()
+    }
+    if (ntiles > 2) RAX_LOAD_SLOTS(2)
+
     for (int it = 0; it < ntiles; ++it) {
+        const int buf = it & 1;
         const int j0 = it * kExtBN;
-        __syncthreads();  // previous tile's LDS reads are done
-        to_lds();
-        __syncthreads();
-        if (it + 1 < ntiles) gather(j0 + kExtBN);
+        __syncthreads();  // tile `it` is complete in `buf`; the other buffer is free
+        if (it + 1 < ntiles) RAX_TO_LDS(buf ^ 1)
+        if (it + 2 < ntiles) {
+            RAX_GATHER()
+            if (it + 3 < ntiles) RAX_LOAD_SLOTS(it + 3)
+        }
 
-        // S^T: two 32-key M blocks
+        // S^T: two 32-key M blocks; st[mb][4 jj + i] is key 32 mb + 8 jj + 4 h2 + i
         f32x16 st[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
@@ -173,44 +207,50 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
             const int key = 32 * mb + col;
 #pragma unroll
             for (int s = 0; s < D / 16; ++s) {
-                const uint4 a = k_lds[key * 16 + swz_k(key, 2 * s + h2)];
+                const uint4 a = k_lds[buf][key * 16 + swz_k(key, 2 * s + h2)];
                 st[mb] = mfma32x32x16(as_bf16x8(a), qop[s], st[mb]);
             }
         }
 
-        // scale, mask, running max. st[mb][4 jj + i] is key 32 mb + 8 jj + 4 h2 + i.
-        const bool need_mask = j0 + kExtBN - 1 > diag_from;
+        // mask (diagonal tiles only) and the tile's row max of the raw scores
+        if (j0 + kExtBN - 1 > diag_from) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = j0 + 32 * mb + 8 * jj + 4 * h2 + i;
+                        if (key > last_q) st[mb][4 * jj + i] = -INFINITY;
+                    }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = st[mb][4 * jj + i] * scale_log2;
-                    if (need_mask) {
-                        const int key = j0 + 32 * mb + 8 * jj + 4 * h2 + i;
-                        x = key <= last_q ? x : -INFINITY;
-                    }
-                    st[mb][4 * jj + i] = x;
-                    mx = fmaxf(mx, x);
-                }
-        mx = wave_max_xor(mx, 32);
-        const float m_new = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - m_new);
-        m = m_new;
-        lsum *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[mb][i]);
+        mx = wave_max_xor(mx, 32) * scale_log2;
 
-        // P^T fragments: 16-key step kk uses st[kk / 2][8 (kk % 2) .. +8].
+        // Lazy rescale: the reference max m only moves when some row's max exceeds it by more
+        // than kLazyLog2 (P stays <= 2^kLazyLog2). P and the row sum use the same m, so the
+        // final division is exact whatever m is.
+        if (__any(mx > m + kLazyLog2)) {
+            const float m_new = fmaxf(m, mx);
+            const float alpha = fast_exp2(m - m_new);
+            m = m_new;
+            lsum *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+        }
+
+        // P^T fragments: 16-key step kk uses st[kk / 2][8 (kk % 2) .. +8]
         uint4 pf[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             float pv[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                pv[j] = fast_exp2(st[kk >> 1][8 * (kk & 1) + j] - m);
+                pv[j] = fast_exp2(fmaf(st[kk >> 1][8 * (kk & 1) + j], scale_log2, -m));
                 lsum += pv[j];
             }
             pf[kk].x = pack_bf16x2(pv[0], pv[1]);
@@ -219,14 +259,23 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
             pf[kk].w = pack_bf16x2(pv[6], pv[7]);
         }
 
-        // O^T[d][row] += V^T[d][keys] P^T[keys][row]
+        // O^T[d][row] += V^T[d][keys] P^T[keys][row]. The V^T operand of step kk holds, at
+        // k-slot 8 h2 + 4 a + j, key 16 kk + 8 a + 4 h2 + j: two transposed 8-byte LDS reads.
+        const char* vb = (const char*)v_lds[buf];
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-            const int d = 32 * dt + col;
+            const int unit = 4 * dt + 2 * dh + (cc >> 1);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const uint4 a = vt_lds[d * 8 + swz_v(d, 2 * kk + h2)];
-                acc[dt] = mfma32x32x16(as_bf16x8(a), as_bf16x8(pf[kk]), acc[dt]);
+                uint2 half[2];
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    const int key = 16 * kk + 8 * a + 4 * h2 + jr;
+                    const char* addr = vb + key * 256 + swz_v(key, unit) * 16 + 8 * (cc & 1);
+                    half[a] = ds_read_tr16_b64(addr);
+                }
+                const uint4 av = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
+                acc[dt] = mfma32x32x16(as_bf16x8(av), as_bf16x8(pf[kk]), acc[dt]);
             }
         }
     }
@@ -247,6 +296,10 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
             }
     }
 }
+
+#undef RAX_LOAD_SLOTS
+#undef RAX_GATHER
+#undef RAX_TO_LDS
 
 template <int G>
 int launch_g(const AttnArgs& a, hipStream_t stream) {
