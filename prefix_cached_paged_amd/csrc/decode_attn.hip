@@ -55,7 +55,17 @@ __device__ __forceinline__ uint4 vcol(const VRow<D> (&r)[8]) {
     return column8<E>(r);
 }
 
-template <int D>
+// 16 bytes at byte offset slot * row_bytes + off from a wave-uniform base.
+template <bool OFF32, typename T>
+__device__ __forceinline__ T row_load(const char* base, int slot, uint32_t row_bytes, uint32_t off) {
+    if constexpr (OFF32) {
+        return *(const T*)(base + (__umul24((uint32_t)slot, row_bytes) + off));
+    } else {
+        return *(const T*)(base + ((uint64_t)(uint32_t)slot * row_bytes + off));
+    }
+}
+
+template <int D, bool OFF32>
 __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
@@ -66,7 +76,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(
     constexpr int DT = D / 16;  // 16-row output tiles; also head_dim elements per lane per V row
 
     const int lane = threadIdx.x & 63;
-    const int g = blockIdx.y * kDecWaves + (threadIdx.x >> 6);
+    const int g = __builtin_amdgcn_readfirstlane(blockIdx.y * kDecWaves + (threadIdx.x >> 6));
     const int c = blockIdx.x;
     const int b = blockIdx.z;
     if (g >= Hkv) return;
@@ -78,9 +88,11 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(
     const int32_t* row = r2t + (int64_t)rpi[b] * r2t_stride;
     const int n16 = lane & 15;
     const int kg = lane >> 4;
-    const int64_t pool_row = (int64_t)Hkv * D;
-    const uint16_t* kbase = k_pool + (int64_t)g * D + 8 * kg;
-    const uint16_t* vbase = v_pool + (int64_t)g * D + DT * n16;
+    const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
+    const char* kbase = (const char*)k_pool + (int64_t)g * D * 2;  // wave-uniform
+    const char* vbase = (const char*)v_pool + (int64_t)g * D * 2;
+    const uint32_t k_off = 16u * kg;       // this lane's 8 head_dim elements of a K row
+    const uint32_t v_off = 2u * DT * n16;  // this lane's DT head_dim elements of a V row
 
     // B operand of S^T = K Q^T: lane holds Q[head n16][32 s + 8 kg .. +8].
     bf16x8 qop[S];
@@ -110,15 +122,15 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(
 #define RAX_DEC_LOAD_K(SLOT)                                                                \
     _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
         const int sl_ = __shfl((SLOT), 16 * t + n16, kWave);                                \
-        const uint16_t* p_ = kbase + (int64_t)sl_ * pool_row;                               \
-        _Pragma("unroll") for (int s = 0; s < S; ++s) kr[t][s] = *(const uint4*)(p_ + 32 * s); \
+        _Pragma("unroll") for (int s = 0; s < S; ++s)                                       \
+            kr[t][s] = row_load<OFF32, uint4>(kbase, sl_, row_bytes, k_off + 64u * s);      \
     }
 #define RAX_DEC_LOAD_V(SLOT)                                                                \
     _Pragma("unroll") for (int u = 0; u < 2; ++u)                                           \
     _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                         \
         const int key_ = 32 * u + 16 * (j >> 2) + 4 * kg + (j & 3);                         \
         const int sl_ = __shfl((SLOT), key_, kWave);                                        \
-        vr[u][j] = *(const VRow<D>*)(vbase + (int64_t)sl_ * pool_row);                      \
+        vr[u][j] = row_load<OFF32, VRow<D>>(vbase, sl_, row_bytes, v_off);                  \
     }
 
     int slot_cur = RAX_DEC_SLOT(k0);
@@ -304,23 +316,24 @@ int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
     const float scale_log2 = a.sm_scale * kLog2e;
     dim3 grid(ns, (a.n_kv_heads + kDecWaves - 1) / kDecWaves, a.batch);
     dim3 mgrid((a.batch * a.n_q_heads + 3) / 4);
+    const bool off32 = pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 2);
+#define RAX_DEC_SPLIT(DD, OFF)                                                                  \
+    hipLaunchKernelGGL((decode_split_kernel<DD, OFF>), grid, dim3(64 * kDecWaves), 0, stream,     \
+                       (const uint16_t*)a.q, (const uint16_t*)a.k_pool, (const uint16_t*)a.v_pool,  \
+                       a.r2t, a.r2t_stride, a.req_pool_indices, a.seq_lens, a.max_seq_len,         \
+                       a.n_q_heads, a.n_kv_heads, G, chunk, ns, scale_log2, o_part, lse)
     if (a.head_dim == 128) {
-        hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(64 * kDecWaves), 0, stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k_pool, (const uint16_t*)a.v_pool,
-                           a.r2t, a.r2t_stride, a.req_pool_indices, a.seq_lens, a.max_seq_len,
-                           a.n_q_heads, a.n_kv_heads, G, chunk, ns, scale_log2, o_part, lse);
+        if (off32) RAX_DEC_SPLIT(128, true); else RAX_DEC_SPLIT(128, false);
         if (hipGetLastError() != hipSuccess) return -1;
         hipLaunchKernelGGL(decode_merge_kernel<128>, mgrid, dim3(256), 0, stream, o_part, lse,
                            (uint16_t*)a.o, a.seq_lens, a.max_seq_len, chunk, ns, a.n_q_heads, a.batch);
     } else {
-        hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(64 * kDecWaves), 0, stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k_pool, (const uint16_t*)a.v_pool,
-                           a.r2t, a.r2t_stride, a.req_pool_indices, a.seq_lens, a.max_seq_len,
-                           a.n_q_heads, a.n_kv_heads, G, chunk, ns, scale_log2, o_part, lse);
+        if (off32) RAX_DEC_SPLIT(64, true); else RAX_DEC_SPLIT(64, false);
         if (hipGetLastError() != hipSuccess) return -1;
         hipLaunchKernelGGL(decode_merge_kernel<64>, mgrid, dim3(256), 0, stream, o_part, lse,
                            (uint16_t*)a.o, a.seq_lens, a.max_seq_len, chunk, ns, a.n_q_heads, a.batch);
     }
+#undef RAX_DEC_SPLIT
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

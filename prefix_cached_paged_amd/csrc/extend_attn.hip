@@ -27,8 +27,12 @@
 //  * Softmax: sm_scale * log2(e) is folded into one FMA before exp2; the accumulators are only
 //    rescaled when a row max grows by more than 2^8 (exact: P and the row sum share the
 //    reference max).
-//  * Causal mask only on the tiles that cross the diagonal; keys past the last visible key of
-//    the workgroup reuse a valid slot and are masked, so no load leaves the request's slots.
+//  * Causal mask only on the tiles that cross the diagonal (a separate loop, so full tiles run
+//    no mask code); keys past the last visible key of the workgroup reuse a valid slot and are
+//    masked, so no load leaves the request's slots.
+//  * Pool addressing: a per-kv-head base pointer (uniform, in SGPRs) plus a 32-bit byte offset
+//    slot * row_bytes (24-bit multiply) when the pool fits (slots * row_bytes <= 2^32, e.g. the
+//    2,097,152-slot, 8-head pool of exactly 4 GiB); 64-bit arithmetic otherwise.
 //  * Workgroup order is XCD-aware: consecutive workgroup ids go to different XCDs, so the
 //    linear id is remapped so that all tiles of one (request, kv head) run on one XCD and
 //    share its L2 for the gathered K/V; the longest (last) tiles start first.
@@ -48,12 +52,17 @@ constexpr int kXcds = 8;
 // In units of 2^kLazyLog2, how far a row max may rise before the accumulators are rescaled.
 constexpr float kLazyLog2 = 8.f;
 
-// LDS swizzles (16-byte units within a 256-byte row). K: unit ^ (key & 7) keeps the eight
-// consecutive rows that eight lanes read for one MFMA operand on distinct banks. V:
-// unit ^ 2 (key & 3) keeps the four rows of one transposed read (keys 4n .. 4n+3, two units
-// each) on distinct banks. Stores write whole rows, so any permutation within a row is free.
-__device__ __forceinline__ int swz_k(int key, int unit) { return unit ^ (key & 7); }
-__device__ __forceinline__ int swz_v(int key, int unit) { return unit ^ (2 * (key & 3)); }
+// LDS swizzles of 16-byte units within a 256-byte row (valid for 32- or 64-bank LDS).
+//  K: unit ^ (key & 15): the 16 consecutive rows that one 16-lane phase of an MFMA operand
+//     read touches land on 16 distinct units.
+//  V: bit 3 of the unit is toggled by bit 1 (the head_dim half a 16-lane group reads), then
+//     ^ 2 (key & 3): the four rows of one transposed read (keys 4n .. 4n+3, two units each)
+//     land on eight distinct units, and the two 16-lane groups of a half-wave on the other
+//     eight. Stores write whole rows, so any permutation within a row is conflict-free.
+__device__ __forceinline__ int swz_k(int key, int unit) { return unit ^ (key & 15); }
+__device__ __forceinline__ int swz_v(int key, int unit) {
+    return (unit ^ (((unit >> 1) & 1) << 3)) ^ (2 * (key & 3));
+}
 
 // Transposed LDS read (gfx950 ds_read_b64_tr_b16): within each 16-lane group, lane 4j + c
 // supplies the address of four 16-bit values; lane i receives value i % 4 of the chunk of lane
@@ -65,7 +74,17 @@ __device__ __forceinline__ uint2 ds_read_tr16_b64(const char* lds_addr) {
     return __builtin_bit_cast(uint2, v);
 }
 
-template <int G>
+// 16 bytes at byte offset slot * row_bytes + off from a uniform base.
+template <bool OFF32>
+__device__ __forceinline__ uint4 pool_load(const char* base, int slot, uint32_t row_bytes, uint32_t off) {
+    if constexpr (OFF32) {
+        return *(const uint4*)(base + (__umul24((uint32_t)slot, row_bytes) + off));
+    } else {
+        return *(const uint4*)(base + ((uint64_t)(uint32_t)slot * row_bytes + off));
+    }
+}
+
+template <int G, bool OFF32>
 __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
@@ -99,9 +118,9 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
     const int t_last = min(t0 + BQ, e) - 1;
     const int kend = min(p + t_last + 1, max_seq_len);  // keys 0 .. kend-1 are visible to someone
     const int32_t* row = r2t + (int64_t)rpi[b] * r2t_stride;
-    const int64_t pool_row = (int64_t)Hkv * D;
-    const uint16_t* kbase = k_pool + (int64_t)g * D;
-    const uint16_t* vbase = v_pool + (int64_t)g * D;
+    const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
+    const char* kbase = (const char*)k_pool + (int64_t)g * D * 2;
+    const char* vbase = (const char*)v_pool + (int64_t)g * D * 2;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -123,6 +142,7 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
     // ---- cooperative gather: thread (seg, grp) moves 16-byte unit `seg` of keys grp + 16 i
     const int seg = tid & 15;
     const int grp = tid >> 4;
+    const uint32_t seg_off = 16u * seg;
     const int ntiles = (kend + kExtBN - 1) / kExtBN;
     int slot0, slot1, slot2, slot3;
     uint4 kst0, kst1, kst2, kst3, vst0, vst1, vst2, vst3;
@@ -136,14 +156,14 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
     }
 #define RAX_GATHER()                                                                        \
     {                                                                                       \
-        kst0 = *(const uint4*)(kbase + (int64_t)slot0 * pool_row + 8 * seg);                \
-        vst0 = *(const uint4*)(vbase + (int64_t)slot0 * pool_row + 8 * seg);                \
-        kst1 = *(const uint4*)(kbase + (int64_t)slot1 * pool_row + 8 * seg);                \
-        vst1 = *(const uint4*)(vbase + (int64_t)slot1 * pool_row + 8 * seg);                \
-        kst2 = *(const uint4*)(kbase + (int64_t)slot2 * pool_row + 8 * seg);                \
-        vst2 = *(const uint4*)(vbase + (int64_t)slot2 * pool_row + 8 * seg);                \
-        kst3 = *(const uint4*)(kbase + (int64_t)slot3 * pool_row + 8 * seg);                \
-        vst3 = *(const uint4*)(vbase + (int64_t)slot3 * pool_row + 8 * seg);                \
+        kst0 = pool_load<OFF32>(kbase, slot0, row_bytes, seg_off);                          \
+        vst0 = pool_load<OFF32>(vbase, slot0, row_bytes, seg_off);                          \
+        kst1 = pool_load<OFF32>(kbase, slot1, row_bytes, seg_off);                          \
+        vst1 = pool_load<OFF32>(vbase, slot1, row_bytes, seg_off);                          \
+        kst2 = pool_load<OFF32>(kbase, slot2, row_bytes, seg_off);                          \
+        vst2 = pool_load<OFF32>(vbase, slot2, row_bytes, seg_off);                          \
+        kst3 = pool_load<OFF32>(kbase, slot3, row_bytes, seg_off);                          \
+        vst3 = pool_load<OFF32>(vbase, slot3, row_bytes, seg_off);                          \
     }
 #define RAX_TO_LDS(BUF)                                                                     \
     {                                                                                       \
@@ -159,9 +179,9 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
         vl_[(grp + 48) * 16 + swz_v(grp + 48, seg)] = vst3;                                 \
     }
 
-    // ---- per-lane constants of the transposed V reads (see swz_v): 16-lane group gi holds
-    // head_dim half dh = gi & 1 and k-group h2; lane i16 = 4 jr + c reads key offset jr and
-    // head_dim 4c .. 4c+3 of that half.
+    // ---- per-lane constants of the transposed V reads: 16-lane group gi holds head_dim half
+    // dh = gi & 1 and k-group h2; lane i16 = 4 jr + cc reads key offset jr and head_dim
+    // 4 cc .. 4 cc + 3 of that half.
     const int i16 = lane & 15;
     const int dh = (lane >> 4) & 1;
     const int jr = i16 >> 2;
@@ -175,8 +195,73 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-    const int last_q = p + t;       // last key position this row may see
-    const int diag_from = p + t0;   // tiles whose last key exceeds this need the mask
+    const int last_q = p + t;  // last key position this row may see
+    // Tiles 0 .. n_full-1 hold only keys <= p + t0, visible to every row of the workgroup.
+    const int n_full = min(ntiles, (p + t0 + 1) / kExtBN);
+
+    // One 64-key tile: stage the next tile, scores, (mask), softmax, P V.
+#define RAX_TILE(MASK)                                                                      \
+    {                                                                                       \
+        const int buf = it & 1;                                                             \
+        const int j0 = it * kExtBN;                                                         \
+        __syncthreads(); /* tile `it` is complete in `buf`; the other buffer is free */     \
+        if (it + 1 < ntiles) RAX_TO_LDS(buf ^ 1)                                            \
+        if (it + 2 < ntiles) {                                                              \
+            RAX_GATHER()                                                                    \
+            if (it + 3 < ntiles) RAX_LOAD_SLOTS(it + 3)                                     \
+        }                                                                                   \
+        f32x16 st[2];                                                                       \
+        _Pragma("unroll") for (int mb = 0; mb < 2; ++mb) {                                  \
+            _Pragma("unroll") for (int i = 0; i < 16; ++i) st[mb][i] = 0.f;                 \
+            const int key = 32 * mb + col;                                                  \
+            _Pragma("unroll") for (int s = 0; s < D / 16; ++s) {                            \
+                const uint4 a = k_lds[buf][key * 16 + swz_k(key, 2 * s + h2)];              \
+                st[mb] = mfma32x32x16(as_bf16x8(a), qop[s], st[mb]);                        \
+            }                                                                               \
+        }                                                                                   \
+        if (MASK) {                                                                         \
+            _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                \
+            _Pragma("unroll") for (int jj = 0; jj < 4; ++jj)                                \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                 \
+                if (j0 + 32 * mb + 8 * jj + 4 * h2 + i > last_q) st[mb][4 * jj + i] = -INFINITY; \
+            }                                                                               \
+        }                                                                                   \
+        float mx = -INFINITY;                                                               \
+        _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                    \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[mb][i]);           \
+        mx = wave_max_xor(mx, 32) * scale_log2;                                             \
+        if (__any(mx > m + kLazyLog2)) {                                                    \
+            const float m_new = fmaxf(m, mx);                                               \
+            const float alpha = fast_exp2(m - m_new);                                       \
+            m = m_new;                                                                      \
+            lsum *= alpha;                                                                  \
+            _Pragma("unroll") for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;         \
+        }                                                                                   \
+        uint4 pf[4];                                                                        \
+        _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                  \
+            float pv[8];                                                                    \
+            _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                 \
+                pv[j] = fast_exp2(fmaf(st[kk >> 1][8 * (kk & 1) + j], scale_log2, -m));     \
+                lsum += pv[j];                                                              \
+            }                                                                               \
+            pf[kk].x = pack_bf16x2(pv[0], pv[1]);                                           \
+            pf[kk].y = pack_bf16x2(pv[2], pv[3]);                                           \
+            pf[kk].z = pack_bf16x2(pv[4], pv[5]);                                           \
+            pf[kk].w = pack_bf16x2(pv[6], pv[7]);                                           \
+        }                                                                                   \
+        const char* vb = (const char*)v_lds[buf];                                           \
+        _Pragma("unroll") for (int dt = 0; dt < D / 32; ++dt) {                             \
+            const int unit = 4 * dt + 2 * dh + (cc >> 1);                                   \
+            _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                              \
+                const int key0 = 16 * kk + 4 * h2 + jr;                                     \
+                const uint2 h0 = ds_read_tr16_b64(vb + key0 * 256 + swz_v(key0, unit) * 16 + 8 * (cc & 1)); \
+                const int key1 = key0 + 8;                                                  \
+                const uint2 h1 = ds_read_tr16_b64(vb + key1 * 256 + swz_v(key1, unit) * 16 + 8 * (cc & 1)); \
+                const uint4 av = make_uint4(h0.x, h0.y, h1.x, h1.y);                        \
+                acc[dt] = mfma32x32x16(as_bf16x8(av), as_bf16x8(pf[kk]), acc[dt]);          \
+            }                                                                               \
+        }                                                                                   \
+    }
 
     // prologue: tile 0 in LDS buffer 0, tile 1 in registers, slots of tile 2 in registers
     RAX_LOAD_SLOTS(0)
@@ -188,97 +273,9 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
     }
     if (ntiles > 2) RAX_LOAD_SLOTS(2)
 
-    for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1;
-        const int j0 = it * kExtBN;
-        __syncthreads();  // tile `it` is complete in `buf`; the other buffer is free
-        if (it + 1 < ntiles) RAX_TO_LDS(buf ^ 1)
-        if (it + 2 < ntiles) {
-            RAX_GATHER()
-            if (it + 3 < ntiles) RAX_LOAD_SLOTS(it + 3)
-        }
-
-        // S^T: two 32-key M blocks; st[mb][4 jj + i] is key 32 mb + 8 jj + 4 h2 + i
-        f32x16 st[2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) st[mb][i] = 0.f;
-            const int key = 32 * mb + col;
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s) {
-                const uint4 a = k_lds[buf][key * 16 + swz_k(key, 2 * s + h2)];
-                st[mb] = mfma32x32x16(as_bf16x8(a), qop[s], st[mb]);
-            }
-        }
-
-        // mask (diagonal tiles only) and the tile's row max of the raw scores
-        if (j0 + kExtBN - 1 > diag_from) {
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = j0 + 32 * mb + 8 * jj + 4 * h2 + i;
-                        if (key > last_q) st[mb][4 * jj + i] = -INFINITY;
-                    }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[mb][i]);
-        mx = wave_max_xor(mx, 32) * scale_log2;
-
-        // Lazy rescale: the reference max m only moves when some row's max exceeds it by more
-        // than kLazyLog2 (P stays <= 2^kLazyLog2). P and the row sum use the same m, so the
-        // final division is exact whatever m is.
-        if (__any(mx > m + kLazyLog2)) {
-            const float m_new = fmaxf(m, mx);
-            const float alpha = fast_exp2(m - m_new);
-            m = m_new;
-            lsum *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
-        }
-
-        // P^T fragments: 16-key step kk uses st[kk / 2][8 (kk % 2) .. +8]
-        uint4 pf[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            float pv[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                pv[j] = fast_exp2(fmaf(st[kk >> 1][8 * (kk & 1) + j], scale_log2, -m));
-                lsum += pv[j];
-            }
-            pf[kk].x = pack_bf16x2(pv[0], pv[1]);
-            pf[kk].y = pack_bf16x2(pv[2], pv[3]);
-            pf[kk].z = pack_bf16x2(pv[4], pv[5]);
-            pf[kk].w = pack_bf16x2(pv[6], pv[7]);
-        }
-
-        // O^T[d][row] += V^T[d][keys] P^T[keys][row]. The V^T operand of step kk holds, at
-        // k-slot 8 h2 + 4 a + j, key 16 kk + 8 a + 4 h2 + j: two transposed 8-byte LDS reads.
-        const char* vb = (const char*)v_lds[buf];
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            const int unit = 4 * dt + 2 * dh + (cc >> 1);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                uint2 half[2];
-#pragma unroll
-                for (int a = 0; a < 2; ++a) {
-                    const int key = 16 * kk + 8 * a + 4 * h2 + jr;
-                    const char* addr = vb + key * 256 + swz_v(key, unit) * 16 + 8 * (cc & 1);
-                    half[a] = ds_read_tr16_b64(addr);
-                }
-                const uint4 av = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
-                acc[dt] = mfma32x32x16(as_bf16x8(av), as_bf16x8(pf[kk]), acc[dt]);
-            }
-        }
-    }
+    int it = 0;
+    for (; it < n_full; ++it) RAX_TILE(false)
+    for (; it < ntiles; ++it) RAX_TILE(true)
 
     lsum += __shfl_xor(lsum, 32, kWave);
     if (row_ok) {
@@ -296,12 +293,12 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
             }
     }
 }
-
 #undef RAX_LOAD_SLOTS
 #undef RAX_GATHER
 #undef RAX_TO_LDS
+#undef RAX_TILE
 
-template <int G>
+template <int G, bool OFF32>
 int launch_g(const AttnArgs& a, hipStream_t stream) {
     constexpr int BQ = kExtBM / G;
     const int tiles = (a.max_extend_len + BQ - 1) / BQ;
@@ -309,13 +306,20 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)((pairs + kXcds - 1) / kXcds) * kXcds * tiles;
     if (blocks <= 0) return 0;
     if (blocks > 0x7fffffff) return -1;
-    hipLaunchKernelGGL(extend_kernel<G>, dim3((unsigned)blocks), dim3(kExtThreads), 0, stream,
+    hipLaunchKernelGGL((extend_kernel<G, OFF32>), dim3((unsigned)blocks), dim3(kExtThreads), 0, stream,
                        (const uint16_t*)a.q, (uint16_t*)a.o, (const uint16_t*)a.k_pool,
                        (const uint16_t*)a.v_pool, a.r2t, a.r2t_stride, a.req_pool_indices,
                        a.prefix_lens, a.extend_lens, a.extend_start_loc, a.total_tokens,
                        a.max_extend_len, a.max_seq_len, a.n_q_heads, a.n_kv_heads, a.batch, tiles,
                        a.sm_scale * kLog2e);
     return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int G>
+int launch_g(const AttnArgs& a, hipStream_t stream) {
+    return pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 2)
+               ? launch_g<G, true>(a, stream)
+               : launch_g<G, false>(a, stream);
 }
 
 }  // namespace

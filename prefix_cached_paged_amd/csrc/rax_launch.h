@@ -36,6 +36,16 @@ struct AttnArgs {
     size_t workspace_bytes;
 };
 
+// True when every byte offset slot * row_bytes + (offset within the row) of the pool fits an
+// unsigned 32-bit value and slot fits 24 bits, so kernels can address rows from a uniform base
+// with 32-bit offsets and a 24-bit multiply.
+inline bool pool_fits_32bit_offsets(int64_t num_slots, int32_t n_kv_heads, int32_t head_dim,
+                                    int32_t elem_bytes) {
+    const int64_t row = (int64_t)n_kv_heads * head_dim * elem_bytes;
+    return num_slots <= ((int64_t)1 << 24) && num_slots * row <= ((int64_t)1 << 32) &&
+           row < ((int64_t)1 << 24);
+}
+
 int launch_kv_store(const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
                     void* k_pool, void* v_pool, int64_t row_bytes, hipStream_t stream);
 

@@ -167,3 +167,17 @@ def test_gqa_equals_repeated_kv_bitwise():
                        e["extend_start_loc"], e["max_extend_len"], e["max_seq_len"], wl.sm_scale)
     torch.cuda.synchronize()
     assert np.array_equal(to_host_bits(o2), a)
+
+
+@pytest.mark.timeout(600)
+def test_extend_and_decode_pool_beyond_4gib():
+    """A pool of 1,048,577 slots x 16 kv heads x 128 (4 GiB + 4 KiB per array) takes the 64-bit
+    addressing path; slots are spread over the whole pool, so rows beyond 2^32 bytes are read."""
+    spec = W.Spec("big-pool", "bf16", 64, 16, 128, 1_048_577, extend_prefix=(3000, 0), extend_lens=(100, 130),
+                  decode_lens=(2000, 5))
+    wl = W.make_workload(spec, 708)
+    say("big pool generated")
+    dw, outs = run_all(wl)
+    kp, vp = stored_pools(wl)
+    assert_close(out_f64(outs["extend"]), oracle_extend(wl, kp, vp), "bf16", "big-pool extend")
+    assert_close(out_f64(outs["decode"]), oracle_decode(wl, kp, vp), "bf16", "big-pool decode")
