@@ -1,6 +1,6 @@
 // C ABI of librax: host-side argument checks, then kernel launches on the caller's stream.
 // Semantics, layouts, ownership and error behaviour of each call are documented in librax.h.
-#include "../../include/librax.h"
+#include "librax.h"
 #include "rax_launch.h"
 
 namespace {

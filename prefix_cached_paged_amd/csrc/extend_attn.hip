@@ -8,15 +8,19 @@
 // diagonal, row softmax, times V. Evaluated blockwise with an online softmax (running max and
 // sum per row), which is an exact reformulation of the row softmax.
 //
-// Design (gfx950, wave64, 256 threads = 4 waves per workgroup):
-//  * Work item: (request b, kv head g, BM = 128 query rows). The rows are (token, head) pairs
+// Design (gfx950, wave64, 512 threads = 8 waves per workgroup, one workgroup per CU):
+//  * Work item: (request b, kv head g, BM = 256 query rows). The rows are (token, head) pairs
 //    of the G query heads sharing kv head g, token-major, so one gathered K/V tile feeds
-//    128 / G tokens x G heads. Each wave owns 32 rows.
-//  * Key tiles of 64: 256 threads gather the 64 K rows and 64 V rows (256 B per kv head per
-//    row, 16-byte loads, 16 lanes per row: coalesced). Slot numbers are loaded two tiles
-//    ahead and rows one tile ahead, so the dependent slot -> row load pair never stalls the
-//    MFMAs. Two LDS buffers, one barrier per tile. K and V are both stored row-major, XOR-
-//    swizzled in 16-byte units so that the operand reads and the stores avoid bank conflicts.
+//    256 / G tokens x G heads. Each wave owns 32 rows. Every workgroup reads the whole visible
+//    context once, so the K/V traffic is (query rows / 256) x context: the row count per
+//    workgroup is what keeps the kernel off the memory roofline.
+//  * Key tiles of 64 rows (256 B per kv head per row) are copied HBM -> LDS by the gfx950
+//    global_load_lds_dwordx4 (16 B per lane, no registers), each lane fetching the unit that
+//    the LDS swizzle stores at its destination. Three LDS buffers: tile i is consumed while
+//    tiles i+1 and i+2 are in flight; slot numbers are loaded one tile before their copy.
+//    The buffers are separate LDS objects and the loop is unrolled by three, so every read
+//    names its buffer and the compiler does not wait on copies into the other buffers. Before
+//    each barrier the wave waits (vmcnt) only for the copies of the tile it is about to read.
 //  * S^T = K Q^T with 32x32x16 bf16 MFMAs: keys are the M dimension (read from LDS), query
 //    rows the N dimension (Q stays in registers for the whole key loop). The C layout puts
 //    one query row per lane column, so the row max/sum are per lane plus one exchange with
@@ -44,9 +48,10 @@ namespace rax {
 namespace {
 
 constexpr int kExtD = 128;
-constexpr int kExtBM = 128;
+constexpr int kExtBM = 256;
 constexpr int kExtBN = 64;
-constexpr int kExtThreads = 256;
+constexpr int kExtWaves = 8;
+constexpr int kExtThreads = 64 * kExtWaves;
 constexpr int kXcds = 8;
 
 // In units of 2^kLazyLog2, how far a row max may rise before the accumulators are rescaled.
@@ -58,10 +63,15 @@ constexpr float kLazyLog2 = 8.f;
 //  V: bit 3 of the unit is toggled by bit 1 (the head_dim half a 16-lane group reads), then
 //     ^ 2 (key & 3): the four rows of one transposed read (keys 4n .. 4n+3, two units each)
 //     land on eight distinct units, and the two 16-lane groups of a half-wave on the other
-//     eight. Stores write whole rows, so any permutation within a row is conflict-free.
+//     eight.
 __device__ __forceinline__ int swz_k(int key, int unit) { return unit ^ (key & 15); }
 __device__ __forceinline__ int swz_v(int key, int unit) {
     return (unit ^ (((unit >> 1) & 1) << 3)) ^ (2 * (key & 3));
+}
+// Logical 16-byte unit stored at physical unit p of V row `key` (inverse of swz_v).
+__device__ __forceinline__ int unswz_v(int key, int p) {
+    const int t = p ^ (2 * (key & 3));
+    return t ^ (((t >> 1) & 1) << 3);
 }
 
 // Transposed LDS read (gfx950 ds_read_b64_tr_b16): within each 16-lane group, lane 4j + c
@@ -74,18 +84,32 @@ __device__ __forceinline__ uint2 ds_read_tr16_b64(const char* lds_addr) {
     return __builtin_bit_cast(uint2, v);
 }
 
-// 16 bytes at byte offset slot * row_bytes + off from a uniform base.
+// One 16-byte-per-lane HBM -> LDS copy: lane l's 16 bytes land at lds_wave_dst + 16 l
+// (gfx950 global_load_lds_dwordx4; the destination is wave-uniform).
+__device__ __forceinline__ void lds_dma16(const char* src, void* lds_wave_dst) {
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds_wave_dst, 16, 0, 0);
+}
+
 template <bool OFF32>
-__device__ __forceinline__ uint4 pool_load(const char* base, int slot, uint32_t row_bytes, uint32_t off) {
+__device__ __forceinline__ const char* pool_row_ptr(const char* base, int slot, uint32_t row_bytes,
+                                                    uint32_t off) {
     if constexpr (OFF32) {
-        return *(const uint4*)(base + (__umul24((uint32_t)slot, row_bytes) + off));
+        return base + (__umul24((uint32_t)slot, row_bytes) + off);
     } else {
-        return *(const uint4*)(base + ((uint64_t)(uint32_t)slot * row_bytes + off));
+        return base + ((uint64_t)(uint32_t)slot * row_bytes + off);
     }
 }
 
+// s_waitcnt vmcnt(N), leaving the other counters unconstrained (gfx9 encoding: vmcnt[3:0] in
+// bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
+#define RAX_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt((((N) & 15) | (((N) >> 4) << 14)) | 0x0F70)
+// Workgroup barrier that the compiler may not move memory accesses across. Copies into LDS
+// are ordered by the explicit vmcnt wait before it, reads by the operand waits of the MFMAs.
+#define RAX_BARRIER() asm volatile("s_barrier" ::: "memory")
+
 template <int G, bool OFF32>
-__global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
+__global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
@@ -95,9 +119,10 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
     constexpr int D = kExtD;
     constexpr int BQ = kExtBM / G;  // tokens per workgroup
 
-    // Two LDS buffers, each a 64-key tile of K and V, row-major [key][16 units of 8 bf16].
-    __shared__ uint4 k_lds[2][kExtBN * 16];
-    __shared__ uint4 v_lds[2][kExtBN * 16];
+    // Three K/V tile buffers, row-major [key][16 units of 8 bf16], swizzled. Separate LDS
+    // objects, each named statically below.
+    __shared__ uint4 kb0[kExtBN * 16], kb1[kExtBN * 16], kb2[kExtBN * 16];
+    __shared__ uint4 vb0[kExtBN * 16], vb1[kExtBN * 16], vb2[kExtBN * 16];
 
     // ---- workgroup -> (pair = b * Hkv + g, tile), XCD-aware
     const int pairs = batch * Hkv;
@@ -139,44 +164,41 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qop[s] = as_bf16x8(*(const uint4*)(q + qo_row + 16 * s + 8 * h2));
 
-    // ---- cooperative gather: thread (seg, grp) moves 16-byte unit `seg` of keys grp + 16 i
-    const int seg = tid & 15;
-    const int grp = tid >> 4;
-    const uint32_t seg_off = 16u * seg;
+    // ---- HBM -> LDS copies. Copy instruction i (0, 1) of wave w fills tile rows
+    // R = 8 w + 4 i + lane / 16, physical unit lane % 16 each; the lane fetches the logical
+    // unit the swizzle stores there: R & 15 = 8 (w & 1) + 4 i + prow, R & 3 = prow.
+    const int prow = lane >> 4;
+    const int punit = lane & 15;
+    const uint32_t k_src0 = 16u * (uint32_t)(punit ^ (8 * (wave & 1) + prow));
+    const uint32_t k_src1 = 16u * (uint32_t)(punit ^ (8 * (wave & 1) + 4 + prow));
+    const uint32_t v_src = 16u * (uint32_t)unswz_v(prow, punit);
     const int ntiles = (kend + kExtBN - 1) / kExtBN;
-    int slot0, slot1, slot2, slot3;
-    uint4 kst0, kst1, kst2, kst3, vst0, vst1, vst2, vst3;
-#define RAX_LOAD_SLOTS(TILE)                                                                \
+    // Slot numbers come through scalar loads at wave-uniform, clamped positions: the copies
+    // are then the only vector-memory operations in the loop, so waiting for one tile's copies
+    // (vmcnt) never waits for slot loads or for younger copies. Wave w copies tile rows
+    // 8 w .. 8 w + 7; lane row 4 i + prow takes slot number i * 4 + prow of those eight.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    int nx0, nx1, nx2, nx3, nx4, nx5, nx6, nx7;  // slots of the next tile to copy (SGPRs)
+#define RAX_SLOTS(TILE)                                                                     \
     {                                                                                       \
-        const int kb_ = (TILE) * kExtBN + grp;                                              \
-        slot0 = row[min(kb_, kend - 1)];                                                    \
-        slot1 = row[min(kb_ + 16, kend - 1)];                                               \
-        slot2 = row[min(kb_ + 32, kend - 1)];                                               \
-        slot3 = row[min(kb_ + 48, kend - 1)];                                               \
+        const int pb_ = (TILE) * kExtBN + 8 * wave_u;                                       \
+        const int lim_ = kend - 1;                                                          \
+        nx0 = row[min(pb_ + 0, lim_)]; nx1 = row[min(pb_ + 1, lim_)];                       \
+        nx2 = row[min(pb_ + 2, lim_)]; nx3 = row[min(pb_ + 3, lim_)];                       \
+        nx4 = row[min(pb_ + 4, lim_)]; nx5 = row[min(pb_ + 5, lim_)];                       \
+        nx6 = row[min(pb_ + 6, lim_)]; nx7 = row[min(pb_ + 7, lim_)];                       \
     }
-#define RAX_GATHER()                                                                        \
+    // 4 vector-memory operations per wave: K rows (i = 0, 1), then V rows.
+#define RAX_COPY(KB, VB)                                                                    \
     {                                                                                       \
-        kst0 = pool_load<OFF32>(kbase, slot0, row_bytes, seg_off);                          \
-        vst0 = pool_load<OFF32>(vbase, slot0, row_bytes, seg_off);                          \
-        kst1 = pool_load<OFF32>(kbase, slot1, row_bytes, seg_off);                          \
-        vst1 = pool_load<OFF32>(vbase, slot1, row_bytes, seg_off);                          \
-        kst2 = pool_load<OFF32>(kbase, slot2, row_bytes, seg_off);                          \
-        vst2 = pool_load<OFF32>(vbase, slot2, row_bytes, seg_off);                          \
-        kst3 = pool_load<OFF32>(kbase, slot3, row_bytes, seg_off);                          \
-        vst3 = pool_load<OFF32>(vbase, slot3, row_bytes, seg_off);                          \
-    }
-#define RAX_TO_LDS(BUF)                                                                     \
-    {                                                                                       \
-        uint4* kl_ = k_lds[BUF];                                                            \
-        uint4* vl_ = v_lds[BUF];                                                            \
-        kl_[(grp + 0) * 16 + swz_k(grp + 0, seg)] = kst0;                                   \
-        vl_[(grp + 0) * 16 + swz_v(grp + 0, seg)] = vst0;                                   \
-        kl_[(grp + 16) * 16 + swz_k(grp + 16, seg)] = kst1;                                 \
-        vl_[(grp + 16) * 16 + swz_v(grp + 16, seg)] = vst1;                                 \
-        kl_[(grp + 32) * 16 + swz_k(grp + 32, seg)] = kst2;                                 \
-        vl_[(grp + 32) * 16 + swz_v(grp + 32, seg)] = vst2;                                 \
-        kl_[(grp + 48) * 16 + swz_k(grp + 48, seg)] = kst3;                                 \
-        vl_[(grp + 48) * 16 + swz_v(grp + 48, seg)] = vst3;                                 \
+        const int sl0_ = prow == 0 ? nx0 : prow == 1 ? nx1 : prow == 2 ? nx2 : nx3;         \
+        const int sl1_ = prow == 0 ? nx4 : prow == 1 ? nx5 : prow == 2 ? nx6 : nx7;         \
+        char* kd_ = (char*)(KB) + (8 * wave_u) * 256;                                       \
+        char* vd_ = (char*)(VB) + (8 * wave_u) * 256;                                       \
+        lds_dma16(pool_row_ptr<OFF32>(kbase, sl0_, row_bytes, k_src0), kd_);                \
+        lds_dma16(pool_row_ptr<OFF32>(kbase, sl1_, row_bytes, k_src1), kd_ + 1024);         \
+        lds_dma16(pool_row_ptr<OFF32>(vbase, sl0_, row_bytes, v_src), vd_);                 \
+        lds_dma16(pool_row_ptr<OFF32>(vbase, sl1_, row_bytes, v_src), vd_ + 1024);          \
     }
 
     // ---- per-lane constants of the transposed V reads: 16-lane group gi holds head_dim half
@@ -195,35 +217,36 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-    const int last_q = p + t;  // last key position this row may see
-    // Tiles 0 .. n_full-1 hold only keys <= p + t0, visible to every row of the workgroup.
-    const int n_full = min(ntiles, (p + t0 + 1) / kExtBN);
+    const int last_q = p + t;        // last key position this row may see
+    const int diag_from = p + t0;    // a tile whose last key exceeds this needs the mask
 
-    // One 64-key tile: stage the next tile, scores, (mask), softmax, P V.
-#define RAX_TILE(MASK)                                                                      \
+    // One tile IT from buffers (KB, VB): wait for its copies, barrier, scores, (mask), softmax
+    // and P V, then start the copy of tile IT+2 into (KN, VN), whose previous contents (tile
+    // IT-1) every wave finished with before the barrier. Issuing the copy after this tile's
+    // LDS reads keeps at most two tiles of copies in flight where the reads happen, which the
+    // compiler can track without adding waits of its own.
+    // The only vector-memory operations are the copies (4 per tile), issued two tiles ahead:
+    // when tile IT is needed the younger ones are the copies of IT+1, so wait until at most 4
+    // (0 at the last tile) are outstanding.
+#define RAX_TILE(IT, KB, VB, KN, VN, MASKABLE, STEADY)                                      \
     {                                                                                       \
-        const int buf = it & 1;                                                             \
-        const int j0 = it * kExtBN;                                                         \
-        __syncthreads(); /* tile `it` is complete in `buf`; the other buffer is free */     \
-        if (it + 1 < ntiles) RAX_TO_LDS(buf ^ 1)                                            \
-        if (it + 2 < ntiles) {                                                              \
-            RAX_GATHER()                                                                    \
-            if (it + 3 < ntiles) RAX_LOAD_SLOTS(it + 3)                                     \
-        }                                                                                   \
+        if (STEADY || (IT) + 1 < ntiles) { RAX_WAIT_VMCNT(4); } else { RAX_WAIT_VMCNT(0); } \
+        RAX_BARRIER();                                                                      \
         f32x16 st[2];                                                                       \
         _Pragma("unroll") for (int mb = 0; mb < 2; ++mb) {                                  \
             _Pragma("unroll") for (int i = 0; i < 16; ++i) st[mb][i] = 0.f;                 \
             const int key = 32 * mb + col;                                                  \
             _Pragma("unroll") for (int s = 0; s < D / 16; ++s) {                            \
-                const uint4 a = k_lds[buf][key * 16 + swz_k(key, 2 * s + h2)];              \
+                const uint4 a = (KB)[key * 16 + swz_k(key, 2 * s + h2)];                    \
                 st[mb] = mfma32x32x16(as_bf16x8(a), qop[s], st[mb]);                        \
             }                                                                               \
         }                                                                                   \
-        if (MASK) {                                                                         \
+        if (MASKABLE && __builtin_amdgcn_readfirstlane((IT) * kExtBN + kExtBN - 1 > diag_from)) { \
+            const int j0_ = (IT) * kExtBN;                                                  \
             _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                \
             _Pragma("unroll") for (int jj = 0; jj < 4; ++jj)                                \
             _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                 \
-                if (j0 + 32 * mb + 8 * jj + 4 * h2 + i > last_q) st[mb][4 * jj + i] = -INFINITY; \
+                if (j0_ + 32 * mb + 8 * jj + 4 * h2 + i > last_q) st[mb][4 * jj + i] = -INFINITY; \
             }                                                                               \
         }                                                                                   \
         float mx = -INFINITY;                                                               \
@@ -249,33 +272,52 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
             pf[kk].z = pack_bf16x2(pv[4], pv[5]);                                           \
             pf[kk].w = pack_bf16x2(pv[6], pv[7]);                                           \
         }                                                                                   \
-        const char* vb = (const char*)v_lds[buf];                                           \
+        const char* vbb = (const char*)(VB);                                                \
         _Pragma("unroll") for (int dt = 0; dt < D / 32; ++dt) {                             \
             const int unit = 4 * dt + 2 * dh + (cc >> 1);                                   \
             _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                              \
                 const int key0 = 16 * kk + 4 * h2 + jr;                                     \
-                const uint2 h0 = ds_read_tr16_b64(vb + key0 * 256 + swz_v(key0, unit) * 16 + 8 * (cc & 1)); \
+                const uint2 h0 = ds_read_tr16_b64(vbb + key0 * 256 + swz_v(key0, unit) * 16 + 8 * (cc & 1)); \
                 const int key1 = key0 + 8;                                                  \
-                const uint2 h1 = ds_read_tr16_b64(vb + key1 * 256 + swz_v(key1, unit) * 16 + 8 * (cc & 1)); \
+                const uint2 h1 = ds_read_tr16_b64(vbb + key1 * 256 + swz_v(key1, unit) * 16 + 8 * (cc & 1)); \
                 const uint4 av = make_uint4(h0.x, h0.y, h1.x, h1.y);                        \
                 acc[dt] = mfma32x32x16(as_bf16x8(av), as_bf16x8(pf[kk]), acc[dt]);          \
             }                                                                               \
         }                                                                                   \
+        if (STEADY || (IT) + 2 < ntiles) {                                                  \
+            RAX_COPY(KN, VN)                                                                \
+            if (STEADY || (IT) + 3 < ntiles) RAX_SLOTS((IT) + 3)                            \
+        }                                                                                   \
     }
 
-    // prologue: tile 0 in LDS buffer 0, tile 1 in registers, slots of tile 2 in registers
-    RAX_LOAD_SLOTS(0)
-    RAX_GATHER()
-    RAX_TO_LDS(0)
+    // prologue: copies of tiles 0 and 1 in flight, slots of tile 2 loaded
+    RAX_SLOTS(0)
+    RAX_COPY(kb0, vb0)
     if (ntiles > 1) {
-        RAX_LOAD_SLOTS(1)
-        RAX_GATHER()
+        RAX_SLOTS(1)
+        RAX_COPY(kb1, vb1)
     }
-    if (ntiles > 2) RAX_LOAD_SLOTS(2)
+    if (ntiles > 2) RAX_SLOTS(2)
 
+    // Tile T lives in buffer T % 3; iteration T starts the copy of tile T+2 into buffer
+    // (T+2) % 3. Both loops advance three tiles at a time from a multiple of three.
+    const int n_full = min(ntiles, (diag_from + 1) / kExtBN);  // tiles with every key <= p + t0
     int it = 0;
-    for (; it < n_full; ++it) RAX_TILE(false)
-    for (; it < ntiles; ++it) RAX_TILE(true)
+    // Steady state: six or more tiles ahead are full and exist, so the body has no
+    // conditional copies or waits (control-flow joins with different copies in flight make
+    // the compiler add waits of its own).
+    while (it + 6 <= n_full) {
+        RAX_TILE(it, kb0, vb0, kb2, vb2, 0, 1) ++it;
+        RAX_TILE(it, kb1, vb1, kb0, vb0, 0, 1) ++it;
+        RAX_TILE(it, kb2, vb2, kb1, vb1, 0, 1) ++it;
+    }
+    while (it < ntiles) {
+        RAX_TILE(it, kb0, vb0, kb2, vb2, 1, 0) ++it;
+        if (it >= ntiles) break;
+        RAX_TILE(it, kb1, vb1, kb0, vb0, 1, 0) ++it;
+        if (it >= ntiles) break;
+        RAX_TILE(it, kb2, vb2, kb1, vb1, 1, 0) ++it;
+    }
 
     lsum += __shfl_xor(lsum, 32, kWave);
     if (row_ok) {
@@ -293,9 +335,8 @@ __global__ __launch_bounds__(kExtThreads, 2) void extend_kernel(
             }
     }
 }
-#undef RAX_LOAD_SLOTS
-#undef RAX_GATHER
-#undef RAX_TO_LDS
+#undef RAX_SLOTS
+#undef RAX_COPY
 #undef RAX_TILE
 
 template <int G, bool OFF32>
@@ -325,7 +366,8 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool extend_bf16_supported(int32_t group, int32_t head_dim) {
-    return head_dim == 128 && (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
+    return head_dim == 128 &&
+           (group == 1 || group == 2 || group == 4 || group == 8 || group == 16 || group == 32);
 }
 
 int launch_extend_bf16(const AttnArgs& a, hipStream_t stream) {
@@ -335,6 +377,7 @@ int launch_extend_bf16(const AttnArgs& a, hipStream_t stream) {
         case 4: return launch_g<4>(a, stream);
         case 8: return launch_g<8>(a, stream);
         case 16: return launch_g<16>(a, stream);
+        case 32: return launch_g<32>(a, stream);
         default: return -1;
     }
 }

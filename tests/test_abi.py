@@ -74,7 +74,7 @@ def test_extend_validation():
     assert extend(hq=6, hkv=4) == 2          # not a multiple
     assert extend(d=96) == 4
     assert extend(hq=6, hkv=2) == 4          # bf16 MFMA path needs a power-of-two group
-    assert extend(hq=64, hkv=2) == 4         # group 32 is beyond the bf16 tile
+    assert extend(hq=128, hkv=2) == 4        # group 64 is beyond the 256-row tile
     assert extend(scale=float("nan")) == 2
     assert extend(q=None) == 1
     assert extend(start=None) == 1
