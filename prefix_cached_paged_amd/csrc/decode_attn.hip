@@ -55,13 +55,36 @@ __device__ __forceinline__ uint4 vcol(const VRow<D> (&r)[8]) {
     return column8<E>(r);
 }
 
-// 16 bytes at byte offset slot * row_bytes + off from a wave-uniform base.
+#ifndef RAX_DEC_NT
+#define RAX_DEC_NT 0
+#endif
+
+// One K or V row piece (16 or 8 bytes) at byte offset slot * row_bytes + off from a
+// wave-uniform base. Every K/V byte is read once per step, so the loads can be marked
+// non-temporal (RAX_DEC_NT).
+template <typename T>
+__device__ __forceinline__ T load_piece(const char* p) {
+    if constexpr (RAX_DEC_NT) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        if constexpr (sizeof(T) == 16) {
+            const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+            return __builtin_bit_cast(T, v);
+        } else {
+            const u32x2 v = __builtin_nontemporal_load((const u32x2*)p);
+            return __builtin_bit_cast(T, v);
+        }
+    } else {
+        return *(const T*)p;
+    }
+}
+
 template <bool OFF32, typename T>
 __device__ __forceinline__ T row_load(const char* base, int slot, uint32_t row_bytes, uint32_t off) {
     if constexpr (OFF32) {
-        return *(const T*)(base + (__umul24((uint32_t)slot, row_bytes) + off));
+        return load_piece<T>(base + (__umul24((uint32_t)slot, row_bytes) + off));
     } else {
-        return *(const T*)(base + ((uint64_t)(uint32_t)slot * row_bytes + off));
+        return load_piece<T>(base + ((uint64_t)(uint32_t)slot * row_bytes + off));
     }
 }
 
