@@ -22,9 +22,12 @@
 //  * Scores S^T come out of the MFMA with the query head as the lane's column, so the
 //    softmax running max/sum is per lane; only the max over the four lane groups needs two
 //    cross-lane exchanges per 64 keys. exp2 with sm_scale*log2(e) folded into one multiply.
-//  * Key slots: one coalesced load of 64 slot numbers per 64 keys, redistributed with
-//    ds_bpermute. Keys past the chunk end reuse the last valid key's slot and get -inf scores,
-//    so no load ever leaves the request's valid slots.
+//  * Key slots: the workgroup's waves (kv heads) read the same keys, so the split's slot numbers
+//    are staged in LDS once with coalesced loads; each lane then reads the slots it needs with
+//    ds_read, off the memory-counter path of the K/V row loads. Keys past the split end reuse the
+//    last valid key's slot and get -inf scores, so no load ever leaves the request's valid slots.
+//  * Each request's context is cut into ceil(L / chunk) nearly equal splits, so split lengths
+//    differ by less than 2x across requests and no split is a short remainder.
 #include <type_traits>
 
 #include "rax_device.h"
@@ -44,8 +47,15 @@ namespace {
 #ifndef RAX_DEC_MIN_CHUNK
 #define RAX_DEC_MIN_CHUNK 256
 #endif
+#ifndef RAX_DEC_FIXED_CHUNK
+#define RAX_DEC_FIXED_CHUNK 0
+#endif
 constexpr int kDecWaves = RAX_DEC_WAVES;  // waves (kv heads) per workgroup
 constexpr int kDecKeysPerIter = 64;
+constexpr int kDecMaxChunk = 4096;  // keys per split, before the 64-key rounding of split edges
+static_assert(RAX_DEC_MIN_CHUNK % kDecKeysPerIter == 0 && RAX_DEC_MIN_CHUNK >= 256 &&
+                  RAX_DEC_MIN_CHUNK <= kDecMaxChunk,
+              "decode chunks must be multiples of 64 in [256, 4096] so that no split is empty");
 
 template <int D>
 using VRow = typename std::conditional<D == 128, uint4, uint2>::type;
@@ -88,8 +98,15 @@ __device__ __forceinline__ T row_load(const char* base, int slot, uint32_t row_b
     }
 }
 
+// Edges of split c when a context of L keys is cut into ns nearly equal splits: multiples of the
+// 64-key iteration except the final end. With ns = ceil(L / chunk) and chunk >= 256 every split
+// holds more than 64 and fewer than chunk + 64 keys.
+__device__ __forceinline__ int split_edge(int c, int L, int ns) {
+    return c >= ns ? L : kDecKeysPerIter * (int)(((int64_t)c * L) / ((int64_t)kDecKeysPerIter * ns));
+}
+
 template <int D, bool OFF32>
-__global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(
+__global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
@@ -97,18 +114,35 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(
     float* __restrict__ o_part, float* __restrict__ lse_part) {
     constexpr int S = D / 32;   // 32-wide K-dim steps of the score MFMA
     constexpr int DT = D / 16;  // 16-row output tiles; also head_dim elements per lane per V row
+    __shared__ int32_t slot_lds[kDecMaxChunk + kDecKeysPerIter];
 
-    const int lane = threadIdx.x & 63;
-    const int g = __builtin_amdgcn_readfirstlane(blockIdx.y * kDecWaves + (threadIdx.x >> 6));
     const int c = blockIdx.x;
     const int b = blockIdx.z;
-    if (g >= Hkv) return;
     const int L = min(seq_lens[b], max_seq_len);
-    const int k0 = c * chunk;
-    if (k0 >= L) return;
-    const int k1 = min(k0 + chunk, L);
+    const int ns = L > 0 ? (L + chunk - 1) / chunk : 0;
+    if (c >= ns) return;  // uniform over the workgroup
+    const int k0 = split_edge(c, L, ns);
+    const int nk = split_edge(c + 1, L, ns) - k0;
+    const int n_it = (nk + kDecKeysPerIter - 1) / kDecKeysPerIter;
 
-    const int32_t* row = r2t + (int64_t)rpi[b] * r2t_stride;
+    // The workgroup's kv heads read the same keys: stage the split's slot numbers once, padded
+    // to whole iterations with the last valid slot so that every row load stays in the request.
+    // Global-to-LDS copies (lane l of a wave writes dword l of its 64-slot block), so all of a
+    // wave's copies are in flight at once; the barrier waits for them.
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    {
+        const int32_t* row = r2t + (int64_t)rpi[b] * r2t_stride + k0;
+        for (int j = wv; j < n_it; j += kDecWaves)
+            __builtin_amdgcn_global_load_lds(
+                (__attribute__((address_space(1))) void*)(row + min(j * kDecKeysPerIter + lane, nk - 1)),
+                (__attribute__((address_space(3))) void*)(slot_lds + j * kDecKeysPerIter), 4, 0, 0);
+    }
+    __syncthreads();
+
+    const int g = __builtin_amdgcn_readfirstlane(blockIdx.y * kDecWaves + wv);
+    if (g >= Hkv) return;
+
     const int n16 = lane & 15;
     const int kg = lane >> 4;
     const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
@@ -120,12 +154,15 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(
     // B operand of S^T = K Q^T: lane holds Q[head n16][32 s + 8 kg .. +8].
     bf16x8 qop[S];
     {
+        // Columns n16 >= G are padding: load a valid head and zero it with a mask (no branch, so
+        // the four loads stay in flight together).
         const bool ok = n16 < G;
+        const uint32_t keep = ok ? 0xFFFFFFFFu : 0u;
         const uint16_t* qr = q + ((int64_t)b * Hq + (int64_t)g * G + (ok ? n16 : 0)) * D + 8 * kg;
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             uint4 v = *(const uint4*)(qr + 32 * s);
-            if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
+            v.x &= keep; v.y &= keep; v.z &= keep; v.w &= keep;
             qop[s] = as_bf16x8(v);
         }
     }
@@ -136,98 +173,99 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Software pipeline over 64-key iterations: slot numbers are loaded two iterations ahead;
-    // the next iteration's K rows are requested as soon as this iteration's score MFMAs have
-    // consumed theirs, and its V rows as soon as P V has consumed this iteration's.
+    // Software pipeline over 64-key iterations: the next iteration's K rows are requested as
+    // soon as the score MFMAs have consumed this iteration's, and its V rows as soon as P V has
+    // consumed this iteration's, so one iteration of K and V is always in flight. The steady
+    // loop is branch-free (the last iteration is peeled), which keeps the memory-counter waits
+    // exact: each wait covers only the rows about to be used.
     uint4 kr[4][S];
     VRow<D> vr[2][8];
-#define RAX_DEC_SLOT(BASE) row[min((BASE) + lane, k1 - 1)]
-#define RAX_DEC_LOAD_K(SLOT)                                                                \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
-        const int sl_ = __shfl((SLOT), 16 * t + n16, kWave);                                \
-        _Pragma("unroll") for (int s = 0; s < S; ++s)                                       \
-            kr[t][s] = row_load<OFF32, uint4>(kbase, sl_, row_bytes, k_off + 64u * s);      \
+#define RAX_DEC_SLOTS_K(IT, SK)                                                              \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) SK[t] = slot_lds[(IT) * kDecKeysPerIter + 16 * t + n16];
+#define RAX_DEC_LOAD_K(SK)                                                                   \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                            \
+    _Pragma("unroll") for (int s = 0; s < S; ++s)                                            \
+        kr[t][s] = row_load<OFF32, uint4>(kbase, SK[t], row_bytes, k_off + 64u * s);
+    // V keys of lane (n16, kg) in block u: 32u + 16h + 4kg + e for h, e in {0,1} x {0..3}.
+#define RAX_DEC_LOAD_V(IT)                                                                   \
+    _Pragma("unroll") for (int u = 0; u < 2; ++u)                                            \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                          \
+        const int4 sv_ =                                                                     \
+            *(const int4*)&slot_lds[(IT) * kDecKeysPerIter + 32 * u + 16 * h + 4 * kg];      \
+        vr[u][4 * h + 0] = row_load<OFF32, VRow<D>>(vbase, sv_.x, row_bytes, v_off);         \
+        vr[u][4 * h + 1] = row_load<OFF32, VRow<D>>(vbase, sv_.y, row_bytes, v_off);         \
+        vr[u][4 * h + 2] = row_load<OFF32, VRow<D>>(vbase, sv_.z, row_bytes, v_off);         \
+        vr[u][4 * h + 3] = row_load<OFF32, VRow<D>>(vbase, sv_.w, row_bytes, v_off);         \
     }
-#define RAX_DEC_LOAD_V(SLOT)                                                                \
-    _Pragma("unroll") for (int u = 0; u < 2; ++u)                                           \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                         \
-        const int key_ = 32 * u + 16 * (j >> 2) + 4 * kg + (j & 3);                         \
-        const int sl_ = __shfl((SLOT), key_, kWave);                                        \
-        vr[u][j] = row_load<OFF32, VRow<D>>(vbase, sl_, row_bytes, v_off);                  \
+#define RAX_DEC_ITER(IT, MORE)                                                               \
+    {                                                                                        \
+        /* S^T[key][head]: lane holds keys 16t + 4kg + i of head n16. */                     \
+        int sk_[4];                                                                          \
+        if (MORE) { RAX_DEC_SLOTS_K((IT) + 1, sk_) }                                         \
+        f32x4 st[4];                                                                         \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                      \
+            st[t] = f32x4{0.f, 0.f, 0.f, 0.f};                                               \
+            _Pragma("unroll") for (int s = 0; s < S; ++s)                                    \
+                st[t] = mfma16x16x32(as_bf16x8(kr[t][s]), qop[s], st[t]);                    \
+        }                                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        if (MORE) { RAX_DEC_LOAD_K(sk_) }                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        float mx = -INFINITY;                                                                \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t)                                        \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
+            if (!(MORE) && (IT) * kDecKeysPerIter + 16 * t + 4 * kg + i >= nk)               \
+                st[t][i] = -INFINITY;                                                        \
+            mx = fmaxf(mx, st[t][i]);                                                        \
+        }                                                                                    \
+        mx = wave_max_xor(mx, 16);                                                           \
+        mx = wave_max_xor(mx, 32);                                                           \
+        mx *= scale_log2;                                                                    \
+        const float m_new = fmaxf(m, mx);                                                    \
+        const float alpha = fast_exp2(m - m_new);                                            \
+        m = m_new;                                                                           \
+        lsum *= alpha;                                                                       \
+        _Pragma("unroll") for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;                  \
+        float p[4][4];                                                                       \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t)                                        \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
+            p[t][i] = fast_exp2(fmaf(st[t][i], scale_log2, -m));                             \
+            lsum += p[t][i];                                                                 \
+        }                                                                                    \
+        /* O^T[d][head] += V^T[d][key] P^T[key][head] per 32-key block. */                   \
+        _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                      \
+            uint4 pb;                                                                        \
+            pb.x = pack_bf16x2(p[2 * u][0], p[2 * u][1]);                                    \
+            pb.y = pack_bf16x2(p[2 * u][2], p[2 * u][3]);                                    \
+            pb.z = pack_bf16x2(p[2 * u + 1][0], p[2 * u + 1][1]);                            \
+            pb.w = pack_bf16x2(p[2 * u + 1][2], p[2 * u + 1][3]);                            \
+            const bf16x8 pop = as_bf16x8(pb);                                                \
+            acc[0] = mfma16x16x32(as_bf16x8(vcol<D, 0>(vr[u])), pop, acc[0]);                \
+            acc[1] = mfma16x16x32(as_bf16x8(vcol<D, 1>(vr[u])), pop, acc[1]);                \
+            acc[2] = mfma16x16x32(as_bf16x8(vcol<D, 2>(vr[u])), pop, acc[2]);                \
+            acc[3] = mfma16x16x32(as_bf16x8(vcol<D, 3>(vr[u])), pop, acc[3]);                \
+            if constexpr (DT == 8) {                                                         \
+                acc[4] = mfma16x16x32(as_bf16x8(vcol<D, 4>(vr[u])), pop, acc[4]);            \
+                acc[5] = mfma16x16x32(as_bf16x8(vcol<D, 5>(vr[u])), pop, acc[5]);            \
+                acc[6] = mfma16x16x32(as_bf16x8(vcol<D, 6>(vr[u])), pop, acc[6]);            \
+                acc[7] = mfma16x16x32(as_bf16x8(vcol<D, 7>(vr[u])), pop, acc[7]);            \
+            }                                                                                \
+        }                                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        if (MORE) { RAX_DEC_LOAD_V((IT) + 1) }                                               \
     }
 
-    int slot_cur = RAX_DEC_SLOT(k0);
-    RAX_DEC_LOAD_K(slot_cur)
-    RAX_DEC_LOAD_V(slot_cur)
-    int slot_nxt = RAX_DEC_SLOT(k0 + kDecKeysPerIter);
-
-    for (int base = k0; base < k1; base += kDecKeysPerIter) {
-        const bool more = base + kDecKeysPerIter < k1;
-
-        // S^T[key][head]: lane holds keys 16t + 4kg + i of head n16.
-        f32x4 st[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < S; ++s) st[t] = mfma16x16x32(as_bf16x8(kr[t][s]), qop[s], st[t]);
-        }
-        if (more) RAX_DEC_LOAD_K(slot_nxt)
-
-        float mx = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = base + 16 * t + 4 * kg + i;
-                if (key >= k1) st[t][i] = -INFINITY;
-                mx = fmaxf(mx, st[t][i]);
-            }
-        mx = wave_max_xor(mx, 16);
-        mx = wave_max_xor(mx, 32);
-        mx *= scale_log2;
-        const float m_new = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - m_new);
-        m = m_new;
-        lsum *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-
-        float p[4][4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[t][i] = fast_exp2(fmaf(st[t][i], scale_log2, -m));
-                lsum += p[t][i];
-            }
-
-        // O^T[d][head] += V^T[d][key] P^T[key][head] per 32-key block.
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            uint4 pb;
-            pb.x = pack_bf16x2(p[2 * u][0], p[2 * u][1]);
-            pb.y = pack_bf16x2(p[2 * u][2], p[2 * u][3]);
-            pb.z = pack_bf16x2(p[2 * u + 1][0], p[2 * u + 1][1]);
-            pb.w = pack_bf16x2(p[2 * u + 1][2], p[2 * u + 1][3]);
-            const bf16x8 pop = as_bf16x8(pb);
-            acc[0] = mfma16x16x32(as_bf16x8(vcol<D, 0>(vr[u])), pop, acc[0]);
-            acc[1] = mfma16x16x32(as_bf16x8(vcol<D, 1>(vr[u])), pop, acc[1]);
-            acc[2] = mfma16x16x32(as_bf16x8(vcol<D, 2>(vr[u])), pop, acc[2]);
-            acc[3] = mfma16x16x32(as_bf16x8(vcol<D, 3>(vr[u])), pop, acc[3]);
-            if constexpr (DT == 8) {
-                acc[4] = mfma16x16x32(as_bf16x8(vcol<D, 4>(vr[u])), pop, acc[4]);
-                acc[5] = mfma16x16x32(as_bf16x8(vcol<D, 5>(vr[u])), pop, acc[5]);
-                acc[6] = mfma16x16x32(as_bf16x8(vcol<D, 6>(vr[u])), pop, acc[6]);
-                acc[7] = mfma16x16x32(as_bf16x8(vcol<D, 7>(vr[u])), pop, acc[7]);
-            }
-        }
-        if (more) {
-            RAX_DEC_LOAD_V(slot_nxt)
-            slot_nxt = RAX_DEC_SLOT(base + 2 * kDecKeysPerIter);
-        }
+    {
+        int sk0[4];
+        RAX_DEC_SLOTS_K(0, sk0)
+        RAX_DEC_LOAD_K(sk0)
     }
-#undef RAX_DEC_SLOT
+    RAX_DEC_LOAD_V(0)
+    int it = 0;
+    for (; it + 1 < n_it; ++it) RAX_DEC_ITER(it, true)
+    RAX_DEC_ITER(it, false)
+#undef RAX_DEC_ITER
+#undef RAX_DEC_SLOTS_K
 #undef RAX_DEC_LOAD_K
 #undef RAX_DEC_LOAD_V
 
@@ -265,8 +303,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     const int lane = threadIdx.x & 63;
     const int b = w / Hq;
     const int L = min(seq_lens[b], max_seq_len);
-    int nc = L > 0 ? (L + chunk - 1) / chunk : 0;
-    nc = min(nc, num_splits);
+    const int nc = L > 0 ? min((L + chunk - 1) / chunk, num_splits) : 0;
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.f;
@@ -305,12 +342,17 @@ bool decode_bf16_supported(int32_t group, int32_t head_dim) {
 // Keys per split: enough splits that batch * n_kv_heads * splits is in the thousands of waves
 // (256 CUs), in multiples of the 64-key iteration, between RAX_DEC_MIN_CHUNK and 4096 keys.
 int32_t decode_chunk(int32_t batch, int32_t max_seq_len, int32_t n_kv_heads) {
+    static_assert(RAX_DEC_FIXED_CHUNK == 0 || (RAX_DEC_FIXED_CHUNK % kDecKeysPerIter == 0 &&
+                                               RAX_DEC_FIXED_CHUNK >= 256 &&
+                                               RAX_DEC_FIXED_CHUNK <= kDecMaxChunk),
+                  "fixed decode chunk must be a multiple of 64 in [256, 4096]");
+    if (RAX_DEC_FIXED_CHUNK > 0) return RAX_DEC_FIXED_CHUNK;
     const int64_t units = (int64_t)batch * n_kv_heads;
     const int64_t target = RAX_DEC_TARGET_WAVES;
     int64_t want = units > 0 ? ((int64_t)max_seq_len * units + target - 1) / target : RAX_DEC_MIN_CHUNK;
     want = (want + kDecKeysPerIter - 1) / kDecKeysPerIter * kDecKeysPerIter;
     if (want < RAX_DEC_MIN_CHUNK) want = RAX_DEC_MIN_CHUNK;
-    if (want > 4096) want = 4096;
+    if (want > kDecMaxChunk) want = kDecMaxChunk;
     return (int32_t)want;
 }
 
