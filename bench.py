@@ -29,6 +29,105 @@ METRIC = "extend attn TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
+# HBM traffic per dispatch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs summarised by
+# --pmc-summary. A kernel's figure is used only while its sources hash to what they were when
+# the counters were taken.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "mixed_chunk_hbm_traffic.txt")
+CSRC = os.path.join(ROOT, "prefix_cached_paged_amd", "csrc")
+KERNEL_SOURCES = {
+    "extend_kernel": ["extend_attn.hip", "rax_device.h", "rax_launch.h"],
+    "decode_split_kernel": ["decode_attn.hip", "rax_device.h", "rax_launch.h"],
+    "decode_merge_kernel": ["decode_attn.hip", "rax_device.h", "rax_launch.h"],
+    "decode_plan_kernel": ["decode_attn.hip", "rax_device.h", "rax_launch.h"],
+    "kv_store_kernel": ["kv_store.hip", "rax_launch.h"],
+}
+COPY_BYTES = 1 << 30
+
+
+def source_sha(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(path: str = TRAFFIC_SUMMARY) -> dict:
+    """kernel -> HBM bytes per dispatch, for kernels whose sources are unchanged."""
+    out = {}
+    if not os.path.exists(path):
+        return out
+    for line in open(path):
+        if not line.startswith("kernel="):
+            continue
+        kv = dict(f.split("=", 1) for f in line.split())
+        k = kv["kernel"]
+        if k in KERNEL_SOURCES and kv.get("source_sha") == source_sha(k):
+            out[k] = int(float(kv["hbm_bytes"]))
+    return out
+
+
+def pmc_summary(out_path: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
+                command: str):
+    """Write the traffic summary from four rocprofv3 --pmc output folders (FETCH_SIZE and
+    WRITE_SIZE for the benchmark, the same two for --copy-calibration)."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"].split("(")[0].split("<")[0].split("::")[-1], []).append(
+                        float(r["Counter_Value"]))
+        return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+
+    def copy_kib(d, counter):
+        best = 0.0
+        for k, (v, n) in per_kernel(d, counter).items():
+            if "copy" in k.lower() or "elementwise" in k.lower():
+                best = max(best, v)
+        return best
+
+    cf, cw = copy_kib(copy_fetch_dir, "FETCH_SIZE"), copy_kib(copy_write_dir, "WRITE_SIZE")
+    f_fac = COPY_BYTES / 1024 / cf
+    w_fac = COPY_BYTES / 1024 / cw
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    lines = ["# HBM traffic per dispatch (rocprofv3 --pmc), MI355X", "#",
+             "# Each counter is scaled by what it reads for a plain device copy of 1 GiB",
+             "# (bench.py --copy-calibration): bytes = KiB * 1024 * factor.", "#",
+             "# Commands (repository root on the GPU box, TMPDIR=/tmp):"]
+    lines += ["#   " + c for c in command.split(" ;; ")]
+    lines += ["#", f"calibration copy_bytes={COPY_BYTES} copy_fetch_kib={cf:.1f} copy_write_kib={cw:.1f} "
+              f"fetch_factor={f_fac:.4f} write_factor={w_fac:.4f}"]
+    for k in sorted(set(fetch) & set(write)):
+        if k not in KERNEL_SOURCES:
+            continue
+        fk, n = fetch[k]
+        wk, _ = write[k]
+        hbm = fk * 1024 * f_fac + wk * 1024 * w_fac
+        lines.append(f"kernel={k} dispatches={n} fetch_kib={fk:.1f} write_kib={wk:.1f} "
+                     f"fetch_bytes={fk * 1024 * f_fac:.0f} write_bytes={wk * 1024 * w_fac:.0f} "
+                     f"hbm_bytes={hbm:.0f} source_sha={source_sha(k)}")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def copy_calibration():
+    """A plain device copy of COPY_BYTES, three times: the reference for the PMC byte counters."""
+    import torch
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copied 3 x {COPY_BYTES} bytes", flush=True)
+
 
 def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
@@ -107,7 +206,19 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=16.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (reference for the PMC byte counters)")
+    ap.add_argument("--pmc-summary", nargs=5, metavar=("OUT", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                       "COPY_WRITE_DIR"),
+                    help="write the HBM traffic summary from rocprofv3 --pmc output folders and exit")
+    ap.add_argument("--pmc-command", default="", help="command text recorded in the traffic summary")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, command=args.pmc_command)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -180,13 +291,15 @@ def main():
     report["kv_store"] = dict(ms=ms["kv_store"], rows=n_new, GBps=hbm(st_bytes, ms["kv_store"]),
                               bytes=st_bytes)
     roofs = {}
+    traffic = read_traffic()
     if wl.extend is not None:
         e = wl.extend
         fl = A.extend_flops(e.prefix_lens, e.extend_lens, spec.n_q_heads, spec.head_dim)
         tf = fl / (ms["extend"] * 1e-3) / 1e12
         report["extend"] = dict(ms=ms["extend"], flops=fl, tflops=tf, frac=tf / PEAK_BF16_TFLOPS)
         roofs["extend"] = dict(kernel="extend_attention", bound="mfma", achieved=tf, peak=PEAK_BF16_TFLOPS,
-                               unit="TFLOP/s", frac=tf / PEAK_BF16_TFLOPS, traffic=None,
+                               unit="TFLOP/s", frac=tf / PEAK_BF16_TFLOPS,
+                               traffic=traffic.get("extend_kernel"),
                                per_launch=f"{fl} algorithmic FLOP", ms=ms["extend"])
     if wl.decode is not None:
         d = wl.decode
@@ -197,9 +310,12 @@ def main():
         report["decode"] = dict(ms=ms["decode"], kv_bytes=kvb, kv_GBps=gb, frac=gb / PEAK_HBM_GBPS,
                                 total_GBps=hbm(tot, ms["decode"]),
                                 splits=rax.decode_num_splits(dt, d.batch, d.max_seq_len, spec.n_kv_heads))
-        roofs["decode"] = dict(kernel="decode_attention (split + merge)", bound="hbm", achieved=gb,
-                               peak=PEAK_HBM_GBPS, unit="GB/s", frac=gb / PEAK_HBM_GBPS, traffic=None,
-                               per_launch=f"{kvb} KV bytes", ms=ms["decode"])
+        dec_kernels = ["decode_plan_kernel", "decode_split_kernel", "decode_merge_kernel"]
+        dec_traffic = (sum(traffic[k] for k in dec_kernels) if all(k in traffic for k in dec_kernels)
+                       else None)
+        roofs["decode"] = dict(kernel="decode_attention (plan + split + merge)", bound="hbm", achieved=gb,
+                               peak=PEAK_HBM_GBPS, unit="GB/s", frac=gb / PEAK_HBM_GBPS,
+                               traffic=dec_traffic, per_launch=f"{kvb} KV bytes", ms=ms["decode"])
     dominant = max(roofs, key=lambda k: roofs[k]["ms"]) if roofs else None
 
     if "extend" in report:

@@ -152,9 +152,13 @@ int rax_extend_attention(int dtype, const void* q, void* o, const void* k_pool, 
  *   o[b, h, :] = softmax_j( sm_scale * q[b, h, :] . K[slot_j, h / G, :] ) V[slot_j, h / G, :],
  *   slot_j = req_to_token[req_pool_indices[b] * r2t_stride + j], j = 0 .. seq_lens[b] - 1.
  *
- * The work is split along the key range (split-K); partial results (fp32 o and a log-sum-exp
- * per split) go to the workspace and a second kernel merges them. The split count is a
- * function of (batch, max_seq_len, n_kv_heads) only.
+ * The work is split along the keys (split-K) in a balanced way: a small plan kernel lays the
+ * requests' contexts end to end (each rounded up to a multiple of 64 keys) and cuts that
+ * stream into equal ranges of 256..4096 keys, one per workgroup, so that every workgroup moves
+ * the same bytes whatever the mix of context lengths. Partial results (fp32 o and a
+ * log-sum-exp per request and range) go to the workspace and a merge kernel combines them.
+ * Three kernels run on `stream` in order (plan, split, merge); the workspace holds the plan
+ * and the partials and must not be used by other work until they have run.
  *
  * Arguments
  *   q, o          [batch, n_q_heads, head_dim].
@@ -173,7 +177,9 @@ int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, 
                          int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                          float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Number of key splits rax_decode_attention uses for these shapes (for tests and reports). */
+/* Number of key ranges per group of kv heads that rax_decode_attention launches for these
+ * shapes (bf16; 1 for fp32 or empty shapes; -1 if the shapes need more than 2^31 - 1). Ranges
+ * past the end of the actual key stream exit at once. For tests and reports. */
 int32_t rax_decode_num_splits(int dtype, int32_t batch, int32_t max_seq_len, int32_t n_kv_heads);
 
 #ifdef __cplusplus

@@ -107,7 +107,8 @@ size_t rax_decode_workspace_bytes(int dtype, int32_t batch, int32_t max_seq_len,
 
 int32_t rax_decode_num_splits(int dtype, int32_t batch, int32_t max_seq_len, int32_t n_kv_heads) {
     if (dtype != RAX_BF16) return 1;
-    return rax::decode_splits(batch, max_seq_len, n_kv_heads);
+    if (batch <= 0 || max_seq_len <= 0 || n_kv_heads <= 0) return 1;
+    return rax::decode_grid(batch, max_seq_len, n_kv_heads);
 }
 
 int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
@@ -126,6 +127,8 @@ int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, 
     if (!(sm_scale == sm_scale)) return RAX_ERR_SHAPE;
     if (batch == 0) return RAX_OK;
     if (max_seq_len == 0) return RAX_ERR_SHAPE;
+    if (dtype == RAX_BF16 && rax::decode_grid(batch, max_seq_len, n_kv_heads) < 0)
+        return RAX_ERR_SHAPE;
     if (!q || !o || !k_pool || !v_pool || !req_to_token || !req_pool_indices || !seq_lens)
         return RAX_ERR_NULL;
     const size_t need = rax_decode_workspace_bytes(dtype, batch, max_seq_len, n_q_heads, n_kv_heads,

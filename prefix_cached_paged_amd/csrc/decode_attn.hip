@@ -6,13 +6,17 @@
 // byte of the context once and does ~G flops per byte, so it is bound by HBM bandwidth.
 //
 // Design (gfx950, wave64):
-//  * split-K: a wave owns (request b, kv head g, key chunk c). Chunks are sized on the host so
-//    that the grid holds thousands of waves; partial (o, lse) go to a workspace and
-//    decode_merge_kernel combines them with the usual log-sum-exp weights.
+//  * Balanced key stream. decode_plan_kernel lays the requests' contexts end to end, each
+//    rounded up to whole 64-key iterations, and cuts that stream into equal ranges of 256..4096
+//    keys, one per workgroup, so that one resident round of workgroups (2 per CU) covers it:
+//    every wave moves the same number of bytes whatever the mix of context lengths. A range
+//    may hold the tail of one request and the head of the next; each (request, range) overlap
+//    yields one partial (o, lse) in the workspace, and decode_merge_kernel combines a request's
+//    partials with log-sum-exp weights. A workgroup's waves are consecutive kv heads.
 //  * The G query heads that share kv head g are the N dimension of 16x16x32 bf16 MFMAs
 //    (grouped-query attention: one gathered K/V row feeds all G heads). Heads beyond G are
 //    zero padding; MFMA throughput is far above what the bandwidth bound needs.
-//  * No LDS. K rows are loaded straight into the MFMA A-operand layout: lane (n = lane%16,
+//  * K rows are loaded straight into the MFMA A-operand layout: lane (n = lane%16,
 //    kgrp = lane/16) holds 8 consecutive head_dim elements of key n, i.e. 16-byte loads of
 //    64 contiguous bytes per key per instruction.
 //  * V is needed with keys along the contraction. Each lane loads the 16-byte pieces of 8
@@ -22,12 +26,10 @@
 //  * Scores S^T come out of the MFMA with the query head as the lane's column, so the
 //    softmax running max/sum is per lane; only the max over the four lane groups needs two
 //    cross-lane exchanges per 64 keys. exp2 with sm_scale*log2(e) folded into one multiply.
-//  * Key slots: the workgroup's waves (kv heads) read the same keys, so the split's slot numbers
-//    are staged in LDS once with coalesced loads; each lane then reads the slots it needs with
-//    ds_read, off the memory-counter path of the K/V row loads. Keys past the split end reuse the
-//    last valid key's slot and get -inf scores, so no load ever leaves the request's valid slots.
-//  * Each request's context is cut into ceil(L / chunk) nearly equal splits, so split lengths
-//    differ by less than 2x across requests and no split is a short remainder.
+//  * Key slots: the workgroup's waves read the same keys, so the range's slot numbers are
+//    staged in LDS once with global-to-LDS copies; each lane then reads the slots it needs with
+//    ds_read, off the memory-counter path of the K/V row loads. Padding keys past a request's
+//    end reuse its last valid slot and get -inf scores, so no load leaves the request's slots.
 #include <type_traits>
 
 #include "rax_device.h"
@@ -41,21 +43,23 @@ namespace {
 #ifndef RAX_DEC_WAVES
 #define RAX_DEC_WAVES 4
 #endif
-#ifndef RAX_DEC_TARGET_WAVES
-#define RAX_DEC_TARGET_WAVES 2048
+#ifndef RAX_DEC_RESIDENT_WGS
+#define RAX_DEC_RESIDENT_WGS 512  // workgroups held at once: 2 per CU on 256 CUs
 #endif
-#ifndef RAX_DEC_MIN_CHUNK
-#define RAX_DEC_MIN_CHUNK 256
+#ifndef RAX_DEC_MIN_KEYS
+#define RAX_DEC_MIN_KEYS 256
 #endif
-#ifndef RAX_DEC_FIXED_CHUNK
-#define RAX_DEC_FIXED_CHUNK 0
+#ifndef RAX_DEC_NT
+#define RAX_DEC_NT 1
 #endif
 constexpr int kDecWaves = RAX_DEC_WAVES;  // waves (kv heads) per workgroup
 constexpr int kDecKeysPerIter = 64;
-constexpr int kDecMaxChunk = 4096;  // keys per split, before the 64-key rounding of split edges
-static_assert(RAX_DEC_MIN_CHUNK % kDecKeysPerIter == 0 && RAX_DEC_MIN_CHUNK >= 256 &&
-                  RAX_DEC_MIN_CHUNK <= kDecMaxChunk,
-              "decode chunks must be multiples of 64 in [256, 4096] so that no split is empty");
+constexpr int kDecMaxKeys = 4096;  // keys per workgroup range at most (its slots sit in LDS)
+constexpr int kDecMaxSegs = kDecMaxKeys / kDecKeysPerIter;  // requests overlapping one range
+static_assert(RAX_DEC_MIN_KEYS % kDecKeysPerIter == 0 && RAX_DEC_MIN_KEYS >= kDecKeysPerIter &&
+                  RAX_DEC_MIN_KEYS <= kDecMaxKeys,
+              "decode ranges must be whole 64-key iterations, at most 4096 keys");
+constexpr int kPlanThreads = 1024;
 
 template <int D>
 using VRow = typename std::conditional<D == 128, uint4, uint2>::type;
@@ -65,13 +69,9 @@ __device__ __forceinline__ uint4 vcol(const VRow<D> (&r)[8]) {
     return column8<E>(r);
 }
 
-#ifndef RAX_DEC_NT
-#define RAX_DEC_NT 0
-#endif
-
 // One K or V row piece (16 or 8 bytes) at byte offset slot * row_bytes + off from a
-// wave-uniform base. Every K/V byte is read once per step, so the loads can be marked
-// non-temporal (RAX_DEC_NT).
+// wave-uniform base. Every K/V byte is read once per step, so the loads are marked
+// non-temporal (RAX_DEC_NT, measured 2-6% faster on the long-context batches).
 template <typename T>
 __device__ __forceinline__ T load_piece(const char* p) {
     if constexpr (RAX_DEC_NT) {
@@ -98,49 +98,132 @@ __device__ __forceinline__ T row_load(const char* base, int slot, uint32_t row_b
     }
 }
 
-// Edges of split c when a context of L keys is cut into ns nearly equal splits: multiples of the
-// 64-key iteration except the final end. With ns = ceil(L / chunk) and chunk >= 256 every split
-// holds more than 64 and fewer than chunk + 64 keys.
-__device__ __forceinline__ int split_edge(int c, int L, int ns) {
-    return c >= ns ? L : kDecKeysPerIter * (int)(((int64_t)c * L) / ((int64_t)kDecKeysPerIter * ns));
+// Keys request b occupies in the stream: its valid keys rounded up to whole iterations.
+__device__ __forceinline__ int64_t padded_len(const int32_t* seq_lens, int b, int32_t max_seq_len) {
+    const int L = min(seq_lens[b], max_seq_len);
+    return L > 0 ? (int64_t)((L + kDecKeysPerIter - 1) / kDecKeysPerIter * kDecKeysPerIter) : 0;
 }
+
+// One workgroup. Writes P[b] = stream offset of request b (P[B] = stream length T), the range
+// length chunk = clamp(64 * ceil(T / (64 * n_target)), RAX_DEC_MIN_KEYS, 4096), the number of
+// non-empty ranges, and for each non-empty range w the request its first key belongs to.
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
+    const int32_t* __restrict__ seq_lens, int32_t B, int32_t max_seq_len, int32_t n_target,
+    int64_t* __restrict__ meta, int64_t* __restrict__ P, int32_t* __restrict__ first_req) {
+    __shared__ int64_t part[kPlanThreads];
+    const int t = threadIdx.x;
+    const int per = (B + kPlanThreads - 1) / kPlanThreads;
+    const int b0 = min(B, t * per);
+    const int b1 = min(B, b0 + per);
+    int64_t own = 0;
+    for (int b = b0; b < b1; ++b) own += padded_len(seq_lens, b, max_seq_len);
+    part[t] = own;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive scan of the thread sums
+        const int64_t v = t >= off ? part[t - off] : 0;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    const int64_t T = part[kPlanThreads - 1];
+    int64_t chunk = (T + n_target - 1) / n_target;
+    chunk = (chunk + kDecKeysPerIter - 1) / kDecKeysPerIter * kDecKeysPerIter;
+    chunk = min(max(chunk, (int64_t)RAX_DEC_MIN_KEYS), (int64_t)kDecMaxKeys);
+    int64_t run = part[t] - own;
+    for (int b = b0; b < b1; ++b) {
+        const int64_t len = padded_len(seq_lens, b, max_seq_len);
+        P[b] = run;
+        for (int64_t w = (run + chunk - 1) / chunk; w * chunk < run + len; ++w) first_req[w] = b;
+        run += len;
+    }
+    if (t == 0) {
+        P[B] = T;
+        meta[0] = T;
+        meta[1] = chunk;
+        meta[2] = (T + chunk - 1) / chunk;
+    }
+}
+
+// A (request, range) overlap: request b, its r2t row, offset of the overlap in the range, its
+// length (whole iterations), position of its first key in the request, and the request's
+// valid key count.
+struct Seg {
+    int32_t b, rpi, lo, n, pos0, len;
+};
 
 template <int D, bool OFF32>
 __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
-    int32_t Hq, int32_t Hkv, int32_t G, int32_t chunk, int32_t num_splits, float scale_log2,
-    float* __restrict__ o_part, float* __restrict__ lse_part) {
+    int32_t B, int32_t Hq, int32_t Hkv, int32_t G, int32_t groups, float scale_log2,
+    const int64_t* __restrict__ meta, const int64_t* __restrict__ P,
+    const int32_t* __restrict__ first_req, float* __restrict__ o_part,
+    float* __restrict__ lse_part) {
     constexpr int S = D / 32;   // 32-wide K-dim steps of the score MFMA
     constexpr int DT = D / 16;  // 16-row output tiles; also head_dim elements per lane per V row
-    __shared__ int32_t slot_lds[kDecMaxChunk + kDecKeysPerIter];
+    __shared__ int32_t slot_lds[kDecMaxKeys];
+    __shared__ Seg segs[kDecMaxSegs];
+    __shared__ int32_t n_seg_lds;
 
-    const int c = blockIdx.x;
-    const int b = blockIdx.z;
-    const int L = min(seq_lens[b], max_seq_len);
-    const int ns = L > 0 ? (L + chunk - 1) / chunk : 0;
-    if (c >= ns) return;  // uniform over the workgroup
-    const int k0 = split_edge(c, L, ns);
-    const int nk = split_edge(c + 1, L, ns) - k0;
-    const int n_it = (nk + kDecKeysPerIter - 1) / kDecKeysPerIter;
-
-    // The workgroup's kv heads read the same keys: stage the split's slot numbers once, padded
-    // to whole iterations with the last valid slot so that every row load stays in the request.
-    // Global-to-LDS copies (lane l of a wave writes dword l of its 64-slot block), so all of a
-    // wave's copies are in flight at once; the barrier waits for them.
+    // Groups of kv heads vary fastest, so the workgroups reading the same keys run together.
+    const int grp = blockIdx.x % groups;
+    const int w = blockIdx.x / groups;
+    const int64_t T = meta[0];
+    const int64_t chunk = meta[1];
+    if (w >= meta[2]) return;  // uniform over the workgroup
+    const int64_t s0 = (int64_t)w * chunk;
+    const int64_t s1 = min(s0 + chunk, T);
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
-    {
-        const int32_t* row = r2t + (int64_t)rpi[b] * r2t_stride + k0;
-        for (int j = wv; j < n_it; j += kDecWaves)
+
+    // Wave 0 lists the requests overlapping [s0, s1): they are consecutive from first_req[w];
+    // lane i looks at request wb + i, 64 requests per step (empty requests overlap nothing).
+    if (wv == 0) {
+        int n_seg = 0;
+        for (int wb = first_req[w]; wb < B; wb += kWave) {
+            const int bi = wb + lane;
+            int64_t pb = s1, pe = s1;
+            int rp = 0, len = 0;
+            if (bi < B) {
+                pb = P[bi];
+                pe = P[bi + 1];
+                rp = rpi[bi];
+                len = min(seq_lens[bi], max_seq_len);
+            }
+            const bool ov = bi < B && pe > pb && pe > s0 && pb < s1;
+            const uint64_t ball = __ballot(ov);
+            if (ov) {
+                const int64_t a = max(pb, s0);
+                const int64_t e = min(pe, s1);
+                const int idx = n_seg + __popcll(ball & ((1ull << lane) - 1ull));
+                segs[idx] = Seg{bi, rp, (int)(a - s0), (int)(e - a), (int)(a - pb), len};
+            }
+            n_seg += __popcll(ball);
+            if (__shfl((int)(pe >= s1), kWave - 1, kWave)) break;
+        }
+        if (lane == 0) n_seg_lds = n_seg;
+    }
+    __syncthreads();
+    const int n_seg = n_seg_lds;
+
+    // Stage the range's slot numbers: iteration block j of the range goes to wave j % waves;
+    // lane l copies the slot of key l of the block (global-to-LDS, all copies in flight at once).
+    for (int si = 0; si < n_seg; ++si) {
+        const Seg sg = segs[si];
+        const int32_t* row = r2t + (int64_t)sg.rpi * r2t_stride;
+        const int j0 = sg.lo / kDecKeysPerIter;
+        const int nb = sg.n / kDecKeysPerIter;
+        for (int j = (wv - j0 % kDecWaves + kDecWaves) % kDecWaves; j < nb; j += kDecWaves)
             __builtin_amdgcn_global_load_lds(
-                (__attribute__((address_space(1))) void*)(row + min(j * kDecKeysPerIter + lane, nk - 1)),
-                (__attribute__((address_space(3))) void*)(slot_lds + j * kDecKeysPerIter), 4, 0, 0);
+                (__attribute__((address_space(1))) void*)(
+                    row + min(sg.pos0 + j * kDecKeysPerIter + lane, sg.len - 1)),
+                (__attribute__((address_space(3))) void*)(slot_lds + sg.lo + j * kDecKeysPerIter),
+                4, 0, 0);
     }
     __syncthreads();
 
-    const int g = __builtin_amdgcn_readfirstlane(blockIdx.y * kDecWaves + wv);
+    const int g = __builtin_amdgcn_readfirstlane(grp * kDecWaves + wv);
     if (g >= Hkv) return;
 
     const int n16 = lane & 15;
@@ -150,28 +233,10 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
     const char* vbase = (const char*)v_pool + (int64_t)g * D * 2;
     const uint32_t k_off = 16u * kg;       // this lane's 8 head_dim elements of a K row
     const uint32_t v_off = 2u * DT * n16;  // this lane's DT head_dim elements of a V row
-
-    // B operand of S^T = K Q^T: lane holds Q[head n16][32 s + 8 kg .. +8].
-    bf16x8 qop[S];
-    {
-        // Columns n16 >= G are padding: load a valid head and zero it with a mask (no branch, so
-        // the four loads stay in flight together).
-        const bool ok = n16 < G;
-        const uint32_t keep = ok ? 0xFFFFFFFFu : 0u;
-        const uint16_t* qr = q + ((int64_t)b * Hq + (int64_t)g * G + (ok ? n16 : 0)) * D + 8 * kg;
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-            uint4 v = *(const uint4*)(qr + 32 * s);
-            v.x &= keep; v.y &= keep; v.z &= keep; v.w &= keep;
-            qop[s] = as_bf16x8(v);
-        }
-    }
-
-    float m = -INFINITY;
-    float lsum = 0.f;
-    f32x4 acc[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Columns n16 >= G are padding: they load a valid head and zero it with a mask (no branch,
+    // so the loads stay in flight together).
+    const bool q_ok = n16 < G;
+    const uint32_t q_keep = q_ok ? 0xFFFFFFFFu : 0u;
 
     // Software pipeline over 64-key iterations: the next iteration's K rows are requested as
     // soon as the score MFMAs have consumed this iteration's, and its V rows as soon as P V has
@@ -181,7 +246,8 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
     uint4 kr[4][S];
     VRow<D> vr[2][8];
 #define RAX_DEC_SLOTS_K(IT, SK)                                                              \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t) SK[t] = slot_lds[(IT) * kDecKeysPerIter + 16 * t + n16];
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) SK[t] =                                    \
+        slot_lds[lo + (IT) * kDecKeysPerIter + 16 * t + n16];
 #define RAX_DEC_LOAD_K(SK)                                                                   \
     _Pragma("unroll") for (int t = 0; t < 4; ++t)                                            \
     _Pragma("unroll") for (int s = 0; s < S; ++s)                                            \
@@ -191,7 +257,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
     _Pragma("unroll") for (int u = 0; u < 2; ++u)                                            \
     _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                          \
         const int4 sv_ =                                                                     \
-            *(const int4*)&slot_lds[(IT) * kDecKeysPerIter + 32 * u + 16 * h + 4 * kg];      \
+            *(const int4*)&slot_lds[lo + (IT) * kDecKeysPerIter + 32 * u + 16 * h + 4 * kg]; \
         vr[u][4 * h + 0] = row_load<OFF32, VRow<D>>(vbase, sv_.x, row_bytes, v_off);         \
         vr[u][4 * h + 1] = row_load<OFF32, VRow<D>>(vbase, sv_.y, row_bytes, v_off);         \
         vr[u][4 * h + 2] = row_load<OFF32, VRow<D>>(vbase, sv_.z, row_bytes, v_off);         \
@@ -199,9 +265,9 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
     }
 #define RAX_DEC_ITER(IT, MORE)                                                               \
     {                                                                                        \
-        /* S^T[key][head]: lane holds keys 16t + 4kg + i of head n16. */                     \
         int sk_[4];                                                                          \
         if (MORE) { RAX_DEC_SLOTS_K((IT) + 1, sk_) }                                         \
+        /* S^T[key][head]: lane holds keys 16t + 4kg + i of head n16. */                     \
         f32x4 st[4];                                                                         \
         _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                      \
             st[t] = f32x4{0.f, 0.f, 0.f, 0.f};                                               \
@@ -214,7 +280,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
         float mx = -INFINITY;                                                                \
         _Pragma("unroll") for (int t = 0; t < 4; ++t)                                        \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
-            if (!(MORE) && (IT) * kDecKeysPerIter + 16 * t + 4 * kg + i >= nk)               \
+            if (!(MORE) && (IT) * kDecKeysPerIter + 16 * t + 4 * kg + i >= n_valid)          \
                 st[t][i] = -INFINITY;                                                        \
             mx = fmaxf(mx, st[t][i]);                                                        \
         }                                                                                    \
@@ -255,82 +321,144 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
         if (MORE) { RAX_DEC_LOAD_V((IT) + 1) }                                               \
     }
 
-    {
-        int sk0[4];
-        RAX_DEC_SLOTS_K(0, sk0)
-        RAX_DEC_LOAD_K(sk0)
+    for (int si = 0; si < n_seg; ++si) {
+        const int b = __builtin_amdgcn_readfirstlane(segs[si].b);
+        const int lo = __builtin_amdgcn_readfirstlane(segs[si].lo);
+        const int n_it = __builtin_amdgcn_readfirstlane(segs[si].n) / kDecKeysPerIter;
+        // Valid keys of this overlap (at least one: every iteration block of a request's
+        // padded range starts before its end).
+        const int n_valid = __builtin_amdgcn_readfirstlane(segs[si].len) -
+                            __builtin_amdgcn_readfirstlane(segs[si].pos0);
+
+        // B operand of S^T = K Q^T: lane holds Q[head n16][32 s + 8 kg .. +8].
+        bf16x8 qop[S];
+        {
+            const uint16_t* qr =
+                q + ((int64_t)b * Hq + (int64_t)g * G + (q_ok ? n16 : 0)) * D + 8 * kg;
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                uint4 v = *(const uint4*)(qr + 32 * s);
+                v.x &= q_keep; v.y &= q_keep; v.z &= q_keep; v.w &= q_keep;
+                qop[s] = as_bf16x8(v);
+            }
+        }
+        {
+            int sk0[4];
+            RAX_DEC_SLOTS_K(0, sk0)
+            RAX_DEC_LOAD_K(sk0)
+        }
+        RAX_DEC_LOAD_V(0)
+
+        float m = -INFINITY;
+        float lsum = 0.f;
+        f32x4 acc[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        int it = 0;
+        for (; it + 1 < n_it; ++it) RAX_DEC_ITER(it, true)
+        RAX_DEC_ITER(it, false)
+
+        lsum += __shfl_xor(lsum, 16, kWave);
+        lsum += __shfl_xor(lsum, 32, kWave);
+        if (q_ok) {
+            // Partial of (request b, range w) sits at index b + w: the overlapping pairs form a
+            // monotone staircase in (b, w), so b + w never repeats.
+            const int64_t pidx = ((int64_t)b + w) * Hq + g * G + n16;
+            const float inv = 1.f / lsum;
+            float* op = o_part + pidx * D;
+            // acc[dt][i] is O^T row 4kg + i, i.e. head_dim DT*(4kg + i) + dt.
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float4* dst = (float4*)(op + DT * (4 * kg + i));
+                dst[0] = make_float4(acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv,
+                                     acc[3][i] * inv);
+                if constexpr (DT == 8)
+                    dst[1] = make_float4(acc[4][i] * inv, acc[5][i] * inv, acc[6][i] * inv,
+                                         acc[7][i] * inv);
+            }
+            if (kg == 0) lse_part[pidx] = m + __log2f(lsum);
+        }
     }
-    RAX_DEC_LOAD_V(0)
-    int it = 0;
-    for (; it + 1 < n_it; ++it) RAX_DEC_ITER(it, true)
-    RAX_DEC_ITER(it, false)
 #undef RAX_DEC_ITER
 #undef RAX_DEC_SLOTS_K
 #undef RAX_DEC_LOAD_K
 #undef RAX_DEC_LOAD_V
-
-    lsum += __shfl_xor(lsum, 16, kWave);
-    lsum += __shfl_xor(lsum, 32, kWave);
-    if (n16 < G) {
-        const int h = g * G + n16;
-        const int64_t pidx = ((int64_t)b * Hq + h) * num_splits + c;
-        const float inv = 1.f / lsum;
-        float* op = o_part + pidx * D;
-        // acc[dt][i] is O^T row 4kg + i, i.e. head_dim DT*(4kg + i) + dt.
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float4* dst = (float4*)(op + DT * (4 * kg + i));
-            dst[0] = make_float4(acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv);
-            if constexpr (DT == 8)
-                dst[1] = make_float4(acc[4][i] * inv, acc[5][i] * inv, acc[6][i] * inv, acc[7][i] * inv);
-        }
-        if (kg == 0) lse_part[pidx] = m + __log2f(lsum);
-    }
 }
 
-// One wave per (request, q head): o = sum_c 2^(lse_c - M) o_c / sum_c 2^(lse_c - M).
+// One wave per (request, q head): o = sum_c 2^(lse_c - M) o_c / sum_c 2^(lse_c - M) over the
+// request's partials, one per range its padded key span overlaps.
 template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ o_part,
-                                                           const float* __restrict__ lse_part,
-                                                           uint16_t* __restrict__ o,
-                                                           const int32_t* __restrict__ seq_lens,
-                                                           int32_t max_seq_len, int32_t chunk,
-                                                           int32_t num_splits, int32_t Hq,
-                                                           int32_t B) {
+__global__ __launch_bounds__(256) void decode_merge_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part, uint16_t* __restrict__ o,
+    const int32_t* __restrict__ seq_lens, int32_t max_seq_len, const int64_t* __restrict__ meta,
+    const int64_t* __restrict__ P, int32_t Hq, int32_t B) {
     constexpr int PER = D / 64;
-    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (w >= B * Hq) return;
+    const int wq = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wq >= B * Hq) return;
     const int lane = threadIdx.x & 63;
-    const int b = w / Hq;
+    const int b = wq / Hq;
+    const int h = wq - b * Hq;
     const int L = min(seq_lens[b], max_seq_len);
-    const int nc = L > 0 ? min((L + chunk - 1) / chunk, num_splits) : 0;
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-    if (nc > 0) {
-        const float* lp = lse_part + (int64_t)w * num_splits;
+    if (L > 0) {
+        const int64_t chunk = meta[1];
+        const int64_t w0 = P[b] / chunk;
+        const int n = (int)((P[b + 1] - 1) / chunk - w0) + 1;
+        const int64_t first = ((int64_t)b + w0) * Hq + h;  // partial c sits at first + c * Hq
         float M = -INFINITY;
-        for (int c = lane; c < nc; c += kWave) M = fmaxf(M, lp[c]);
+        for (int c = lane; c < n; c += kWave) M = fmaxf(M, lse_part[first + (int64_t)c * Hq]);
 #pragma unroll
         for (int s = 32; s >= 1; s >>= 1) M = wave_max_xor(M, s);
         float wsum = 0.f;
-        const float* op = o_part + (int64_t)w * num_splits * D + PER * lane;
-        for (int c = 0; c < nc; ++c) {
-            const float wt = fast_exp2(lp[c] - M);
+        for (int c = 0; c < n; ++c) {
+            const int64_t pi = first + (int64_t)c * Hq;
+            const float wt = fast_exp2(lse_part[pi] - M);
             wsum += wt;
+            const float* op = o_part + pi * D + PER * lane;
 #pragma unroll
-            for (int k = 0; k < PER; ++k) acc[k] += wt * op[(int64_t)c * D + k];
+            for (int k = 0; k < PER; ++k) acc[k] += wt * op[k];
         }
         const float inv = 1.f / wsum;
 #pragma unroll
         for (int k = 0; k < PER; ++k) acc[k] *= inv;
     }
-    uint16_t* dst = o + (int64_t)w * D + PER * lane;
+    uint16_t* dst = o + (int64_t)wq * D + PER * lane;
     if constexpr (PER == 2) {
         *(uint32_t*)dst = pack_bf16x2(acc[0], acc[1]);
     } else {
         *dst = (uint16_t)(pack_bf16x2(acc[0], 0.f) & 0xFFFFu);
     }
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+int32_t decode_groups(int32_t n_kv_heads) { return (n_kv_heads + kDecWaves - 1) / kDecWaves; }
+
+// Ranges per kv-head group that one resident round of workgroups covers.
+int32_t decode_target(int32_t n_kv_heads) {
+    const int32_t t = RAX_DEC_RESIDENT_WGS / decode_groups(n_kv_heads);
+    return t < 1 ? 1 : t;
+}
+
+// Workspace sections: meta (3 int64), P (batch + 1 int64), first_req (grid int32), partial o
+// (fp32, head_dim each) and lse (fp32) for (batch + grid) * n_q_heads partials.
+struct DecLayout {
+    size_t meta, P, first, o, lse, total;
+};
+
+DecLayout decode_layout(int32_t batch, int32_t grid, int32_t n_q_heads, int32_t head_dim) {
+    DecLayout l{};
+    const size_t parts = ((size_t)batch + grid) * n_q_heads;
+    l.meta = 0;
+    l.P = l.meta + 256;
+    l.first = l.P + align256(((size_t)batch + 1) * sizeof(int64_t));
+    l.o = l.first + align256((size_t)grid * sizeof(int32_t));
+    l.lse = l.o + align256(parts * head_dim * sizeof(float));
+    l.total = l.lse + parts * sizeof(float);
+    return l;
 }
 
 }  // namespace
@@ -339,64 +467,60 @@ bool decode_bf16_supported(int32_t group, int32_t head_dim) {
     return group >= 1 && group <= 16 && (head_dim == 64 || head_dim == 128);
 }
 
-// Keys per split: enough splits that batch * n_kv_heads * splits is in the thousands of waves
-// (256 CUs), in multiples of the 64-key iteration, between RAX_DEC_MIN_CHUNK and 4096 keys.
-int32_t decode_chunk(int32_t batch, int32_t max_seq_len, int32_t n_kv_heads) {
-    static_assert(RAX_DEC_FIXED_CHUNK == 0 || (RAX_DEC_FIXED_CHUNK % kDecKeysPerIter == 0 &&
-                                               RAX_DEC_FIXED_CHUNK >= 256 &&
-                                               RAX_DEC_FIXED_CHUNK <= kDecMaxChunk),
-                  "fixed decode chunk must be a multiple of 64 in [256, 4096]");
-    if (RAX_DEC_FIXED_CHUNK > 0) return RAX_DEC_FIXED_CHUNK;
-    const int64_t units = (int64_t)batch * n_kv_heads;
-    const int64_t target = RAX_DEC_TARGET_WAVES;
-    int64_t want = units > 0 ? ((int64_t)max_seq_len * units + target - 1) / target : RAX_DEC_MIN_CHUNK;
-    want = (want + kDecKeysPerIter - 1) / kDecKeysPerIter * kDecKeysPerIter;
-    if (want < RAX_DEC_MIN_CHUNK) want = RAX_DEC_MIN_CHUNK;
-    if (want > kDecMaxChunk) want = kDecMaxChunk;
-    return (int32_t)want;
-}
-
-int32_t decode_splits(int32_t batch, int32_t max_seq_len, int32_t n_kv_heads) {
-    const int32_t ck = decode_chunk(batch, max_seq_len, n_kv_heads);
-    const int32_t n = (max_seq_len + ck - 1) / ck;
-    return n < 1 ? 1 : n;
+// Ranges per kv-head group the split kernel is launched with: one resident round, or more when
+// the longest possible stream (every request at max_seq_len) needs more 4096-key ranges.
+// -1 when that would exceed the grid limit.
+int32_t decode_grid(int32_t batch, int32_t max_seq_len, int32_t n_kv_heads) {
+    const int64_t worst = (int64_t)batch * (((int64_t)max_seq_len + kDecKeysPerIter - 1) /
+                                            kDecKeysPerIter * kDecKeysPerIter);
+    int64_t n = (worst + kDecMaxKeys - 1) / kDecMaxKeys;
+    if (n < decode_target(n_kv_heads)) n = decode_target(n_kv_heads);
+    if (n * decode_groups(n_kv_heads) > INT32_MAX || n + batch > INT32_MAX) return -1;
+    return (int32_t)n;
 }
 
 size_t decode_workspace(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
                         int32_t head_dim) {
-    const size_t ns = (size_t)decode_splits(batch, max_seq_len, n_kv_heads);
-    const size_t rows = (size_t)batch * n_q_heads * ns;
-    // o partials (fp32, head_dim each), then one lse per partial; 256-byte aligned sections.
-    const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
-    return o_bytes + rows * sizeof(float);
+    const int32_t grid = decode_grid(batch, max_seq_len, n_kv_heads);
+    if (grid < 0) return 0;
+    return decode_layout(batch, grid, n_q_heads, head_dim).total;
 }
 
 int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
     const int32_t G = a.n_q_heads / a.n_kv_heads;
-    const int32_t chunk = decode_chunk(a.batch, a.max_seq_len, a.n_kv_heads);
-    const int32_t ns = decode_splits(a.batch, a.max_seq_len, a.n_kv_heads);
-    const size_t rows = (size_t)a.batch * a.n_q_heads * ns;
-    float* o_part = (float*)a.workspace;
-    float* lse = (float*)((char*)a.workspace + (rows * a.head_dim * sizeof(float) + 255) / 256 * 256);
+    const int32_t groups = decode_groups(a.n_kv_heads);
+    const int32_t grid = decode_grid(a.batch, a.max_seq_len, a.n_kv_heads);
+    if (grid < 0) return -1;
+    const DecLayout l = decode_layout(a.batch, grid, a.n_q_heads, a.head_dim);
+    char* ws = (char*)a.workspace;
+    int64_t* meta = (int64_t*)(ws + l.meta);
+    int64_t* P = (int64_t*)(ws + l.P);
+    int32_t* first = (int32_t*)(ws + l.first);
+    float* o_part = (float*)(ws + l.o);
+    float* lse = (float*)(ws + l.lse);
     const float scale_log2 = a.sm_scale * kLog2e;
-    dim3 grid(ns, (a.n_kv_heads + kDecWaves - 1) / kDecWaves, a.batch);
-    dim3 mgrid((a.batch * a.n_q_heads + 3) / 4);
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.seq_lens,
+                       a.batch, a.max_seq_len, decode_target(a.n_kv_heads), meta, P, first);
+    if (hipGetLastError() != hipSuccess) return -1;
+    const dim3 sgrid((uint32_t)grid * (uint32_t)groups);
+    const dim3 mgrid((a.batch * a.n_q_heads + 3) / 4);
     const bool off32 = pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 2);
 #define RAX_DEC_SPLIT(DD, OFF)                                                                  \
-    hipLaunchKernelGGL((decode_split_kernel<DD, OFF>), grid, dim3(64 * kDecWaves), 0, stream,     \
+    hipLaunchKernelGGL((decode_split_kernel<DD, OFF>), sgrid, dim3(64 * kDecWaves), 0, stream,    \
                        (const uint16_t*)a.q, (const uint16_t*)a.k_pool, (const uint16_t*)a.v_pool,  \
-                       a.r2t, a.r2t_stride, a.req_pool_indices, a.seq_lens, a.max_seq_len,         \
-                       a.n_q_heads, a.n_kv_heads, G, chunk, ns, scale_log2, o_part, lse)
+                       a.r2t, a.r2t_stride, a.req_pool_indices, a.seq_lens, a.max_seq_len, a.batch, \
+                       a.n_q_heads, a.n_kv_heads, G, groups, scale_log2, meta, P, first, o_part,   \
+                       lse)
     if (a.head_dim == 128) {
         if (off32) RAX_DEC_SPLIT(128, true); else RAX_DEC_SPLIT(128, false);
         if (hipGetLastError() != hipSuccess) return -1;
         hipLaunchKernelGGL(decode_merge_kernel<128>, mgrid, dim3(256), 0, stream, o_part, lse,
-                           (uint16_t*)a.o, a.seq_lens, a.max_seq_len, chunk, ns, a.n_q_heads, a.batch);
+                           (uint16_t*)a.o, a.seq_lens, a.max_seq_len, meta, P, a.n_q_heads, a.batch);
     } else {
         if (off32) RAX_DEC_SPLIT(64, true); else RAX_DEC_SPLIT(64, false);
         if (hipGetLastError() != hipSuccess) return -1;
         hipLaunchKernelGGL(decode_merge_kernel<64>, mgrid, dim3(256), 0, stream, o_part, lse,
-                           (uint16_t*)a.o, a.seq_lens, a.max_seq_len, chunk, ns, a.n_q_heads, a.batch);
+                           (uint16_t*)a.o, a.seq_lens, a.max_seq_len, meta, P, a.n_q_heads, a.batch);
     }
 #undef RAX_DEC_SPLIT
     return hipGetLastError() == hipSuccess ? 0 : -1;

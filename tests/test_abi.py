@@ -106,12 +106,21 @@ def test_decode_validation():
     assert decode(batch=0, q=None) == 0
 
 
+def a256(x):
+    return (x + 255) // 256 * 256
+
+
 def test_decode_workspace_size():
-    for B, L, hq, hkv in [(64, 4096, 32, 8), (8, 131072, 64, 8), (1, 1, 4, 4), (128, 8192, 32, 8)]:
-        ns = lib().rax_decode_num_splits(0, B, L, hkv)
-        assert ns >= 1
-        rows = B * hq * ns
-        o_bytes = (rows * 128 * 4 + 255) // 256 * 256
-        assert lib().rax_decode_workspace_bytes(0, B, L, hq, hkv, 128) == o_bytes + rows * 4
+    # ranges per kv-head group: one resident round (512 workgroups of 4 kv heads), or enough
+    # 4096-key ranges for every request at max_seq_len, whichever is larger
+    for B, L, hq, hkv in [(64, 4096, 32, 8), (8, 131072, 64, 8), (1, 1, 4, 4), (128, 8192, 32, 8),
+                          (4096, 32768, 32, 8), (16, 1000, 64, 32)]:
+        groups = (hkv + 3) // 4
+        worst = B * ((L + 63) // 64 * 64)
+        grid = max(max(1, 512 // groups), (worst + 4095) // 4096)
+        assert lib().rax_decode_num_splits(0, B, L, hkv) == grid
+        parts = (B + grid) * hq
+        want = 256 + a256((B + 1) * 8) + a256(grid * 4) + a256(parts * 128 * 4) + parts * 4
+        assert lib().rax_decode_workspace_bytes(0, B, L, hq, hkv, 128) == want
     assert lib().rax_decode_workspace_bytes(1, 64, 4096, 32, 8, 128) == 0   # fp32 path needs none
     assert lib().rax_extend_workspace_bytes(0, 1, 2048, 2048, 16384, 32, 8, 128) == 0
