@@ -25,7 +25,8 @@
 //    permuted to d = (D/16)*m + tile so that those loads are contiguous.
 //  * Scores S^T come out of the MFMA with the query head as the lane's column, so the
 //    softmax running max/sum is per lane; only the max over the four lane groups needs two
-//    cross-lane exchanges per 64 keys. exp2 with sm_scale*log2(e) folded into one multiply.
+//    cross-lane exchanges per 64 keys (permlane swaps, no LDS). exp2 with sm_scale*log2(e)
+//    folded into one multiply.
 //  * Key slots: the workgroup's waves read the same keys, so the range's slot numbers are
 //    staged in LDS once with global-to-LDS copies; each lane then reads the slots it needs with
 //    ds_read, off the memory-counter path of the K/V row loads. Padding keys past a request's
@@ -284,8 +285,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
                 st[t][i] = -INFINITY;                                                        \
             mx = fmaxf(mx, st[t][i]);                                                        \
         }                                                                                    \
-        mx = wave_max_xor(mx, 16);                                                           \
-        mx = wave_max_xor(mx, 32);                                                           \
+        mx = max_pair32(max_pair16(mx));                                                     \
         mx *= scale_log2;                                                                    \
         const float m_new = fmaxf(m, mx);                                                    \
         const float alpha = fast_exp2(m - m_new);                                            \
@@ -359,8 +359,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
         for (; it + 1 < n_it; ++it) RAX_DEC_ITER(it, true)
         RAX_DEC_ITER(it, false)
 
-        lsum += __shfl_xor(lsum, 16, kWave);
-        lsum += __shfl_xor(lsum, 32, kWave);
+        lsum = sum_pair32(sum_pair16(lsum));
         if (q_ok) {
             // Partial of (request b, range w) sits at index b + w: the overlapping pairs form a
             // monotone staircase in (b, w), so b + w never repeats.

@@ -30,7 +30,8 @@
 //    gfx950 transposed LDS read (ds_read_b64_tr_b16), in the key order the P^T fragment has.
 //  * Softmax: sm_scale * log2(e) is folded into one FMA before exp2; the accumulators are only
 //    rescaled when a row max grows by more than 2^8 (exact: P and the row sum share the
-//    reference max).
+//    reference max). The row max over the two half-waves is one permlane swap (no LDS), the
+//    row sum adds the bf16-rounded P with dot2 instructions.
 //  * Causal mask only on the tiles that cross the diagonal (a separate loop, so full tiles run
 //    no mask code); keys past the last visible key of the workgroup reuse a valid slot and are
 //    masked, so no load leaves the request's slots.
@@ -56,6 +57,14 @@ constexpr int kXcds = 8;
 
 // In units of 2^kLazyLog2, how far a row max may rise before the accumulators are rescaled.
 constexpr float kLazyLog2 = 8.f;
+
+// Row sum of the probabilities: the bf16-rounded P that P V uses, two per v_dot2c_f32_bf16
+// against (1, 1), so the normaliser sums exactly the weights applied to V.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float add_bf16x2(uint32_t pk, float acc) {
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), one, acc, false);
+}
 
 // LDS swizzles of 16-byte units within a 256-byte row (valid for 32- or 64-bank LDS).
 //  K: unit ^ (key & 15): the 16 consecutive rows that one 16-lane phase of an MFMA operand
@@ -252,7 +261,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         float mx = -INFINITY;                                                               \
         _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                    \
         _Pragma("unroll") for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[mb][i]);           \
-        mx = wave_max_xor(mx, 32) * scale_log2;                                             \
+        mx = max_pair32(mx) * scale_log2;                                             \
         if (__any(mx > m + kLazyLog2)) {                                                    \
             const float m_new = fmaxf(m, mx);                                               \
             const float alpha = fast_exp2(m - m_new);                                       \
@@ -263,14 +272,16 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         uint4 pf[4];                                                                        \
         _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                  \
             float pv[8];                                                                    \
-            _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                 \
+            _Pragma("unroll") for (int j = 0; j < 8; ++j)                                   \
                 pv[j] = fast_exp2(fmaf(st[kk >> 1][8 * (kk & 1) + j], scale_log2, -m));     \
-                lsum += pv[j];                                                              \
-            }                                                                               \
             pf[kk].x = pack_bf16x2(pv[0], pv[1]);                                           \
             pf[kk].y = pack_bf16x2(pv[2], pv[3]);                                           \
             pf[kk].z = pack_bf16x2(pv[4], pv[5]);                                           \
             pf[kk].w = pack_bf16x2(pv[6], pv[7]);                                           \
+            lsum = add_bf16x2(pf[kk].x, lsum);                                              \
+            lsum = add_bf16x2(pf[kk].y, lsum);                                              \
+            lsum = add_bf16x2(pf[kk].z, lsum);                                              \
+            lsum = add_bf16x2(pf[kk].w, lsum);                                              \
         }                                                                                   \
         const char* vbb = (const char*)(VB);                                                \
         _Pragma("unroll") for (int dt = 0; dt < D / 32; ++dt) {                             \
@@ -319,7 +330,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         RAX_TILE(it, kb2, vb2, kb1, vb1, 1, 0) ++it;
     }
 
-    lsum += __shfl_xor(lsum, 32, kWave);
+    lsum = sum_pair32(lsum);
     if (row_ok) {
         const float inv = 1.f / lsum;
         uint16_t* orow = o + qo_row;

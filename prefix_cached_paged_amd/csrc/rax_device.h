@@ -62,6 +62,23 @@ __device__ __forceinline__ uint4 column8(const Row (&r)[8]) {
     return o;
 }
 
+// The values of lanes l and l ^ 32 (pair32) or l ^ 16 (pair16), in some order, in every lane:
+// the gfx950 permlane swaps of a register with itself, one VALU operation, no LDS.
+__device__ __forceinline__ void pair32(float v, float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair16(float v, float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_pair32(float v) { float a, b; pair32(v, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float max_pair16(float v) { float a, b; pair16(v, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float sum_pair32(float v) { float a, b; pair32(v, a, b); return a + b; }
+__device__ __forceinline__ float sum_pair16(float v) { float a, b; pair16(v, a, b); return a + b; }
+
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
     return fmaxf(v, __shfl_xor(v, mask, kWave));
 }
