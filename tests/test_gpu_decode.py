@@ -135,3 +135,66 @@ def test_empty_batch_is_noop():
     R.decode_attention(d["q"][:0], d["o"][:0], dw.k_pool, dw.v_pool, dw.req_to_token, d["req_pool_indices"][:0],
                        d["seq_lens"][:0], d["max_seq_len"], wl.sm_scale)
     torch.cuda.synchronize()
+
+
+# ---- the balanced key stream: ranges that hold many requests, requests spread over many ranges,
+# empty requests, and streams long enough that the 4096-key range cap needs more than one
+# resident round of workgroups.
+
+def test_many_tiny_requests_share_ranges():
+    """3,000 requests of 1..80 keys: one 256-key range overlaps up to 64 requests."""
+    spec = W.Spec("dec-tiny-many", "bf16", 32, 8, 128, 400000, decode_batch=3000, decode_range=(1, 80))
+    wl = W.make_workload(spec, 607)
+    say(f"{spec.name}: B={wl.decode.batch} total keys={int(wl.decode.seq_lens.sum())}")
+    dw, outs = run_all(wl)
+    kp, vp = stored_pools(wl)
+    assert_close(out_f64(outs["decode"]), oracle_decode(wl, kp, vp), "bf16", spec.name)
+
+
+def test_one_long_request_among_short_ones():
+    """A 131,072-key request spans many ranges; 40 short ones share ranges with its ends."""
+    lens = (3, 64, 65, 700) * 5 + (131072,) + (1, 129, 4000, 63) * 5
+    spec = W.Spec("dec-one-long", "bf16", 32, 8, 128, 200000, decode_lens=lens)
+    wl = W.make_workload(spec, 608, "peaked")
+    dw, outs = run_all(wl)
+    kp, vp = stored_pools(wl)
+    assert_close(out_f64(outs["decode"]), oracle_decode(wl, kp, vp), "bf16", spec.name)
+
+
+def test_empty_requests_write_zeros():
+    """Requests with seq_len 0 (or below) get all-zero rows; the others are unaffected."""
+    spec = W.Spec("dec-empty", "bf16", 16, 4, 128, 60000, decode_lens=(500, 7, 3000, 64, 1, 2000, 300, 5))
+    wl = W.make_workload(spec, 609)
+    dw, outs = run_all(wl)
+    kp, vp = stored_pools(wl)
+    full = to_host_bits(outs["decode"]).copy()
+    empty = [1, 3, 4, 7]
+    sl = dw.dec["seq_lens"].clone()
+    sl[empty[:3]] = 0
+    sl[empty[3]] = -5
+    d = dw.dec
+    o2 = torch.full_like(d["o"], 7)
+    R.decode_attention(d["q"], o2, dw.k_pool, dw.v_pool, dw.req_to_token, d["req_pool_indices"], sl,
+                       d["max_seq_len"], wl.sm_scale)
+    torch.cuda.synchronize()
+    got = to_host_bits(o2)
+    assert not got[empty].any(), "empty requests must give zero rows"
+    keep = [b for b in range(wl.decode.batch) if b not in empty]
+    # the other requests see the same keys as before; their partials now sit at other places
+    assert_close(oracle.to_f64(got[keep]), oracle_decode(wl, kp, vp, requests=keep), "bf16", "non-empty")
+    assert_close(oracle.to_f64(got[keep]), oracle.to_f64(full[keep]), "bf16", "vs all-present run")
+
+
+def test_stream_longer_than_one_resident_round():
+    """520 x 4096 keys over 2 kv heads: ranges clamp at 4096 keys and the grid exceeds one
+    resident round (512 ranges); sampled requests against the oracle."""
+    spec = W.Spec("dec-rounds", "bf16", 8, 2, 64, 2200000, decode_batch=520, decode_range=(4000, 4096))
+    wl = W.make_workload(spec, 610, "peaked")
+    B, L = wl.decode.batch, wl.decode.max_seq_len
+    grid = R.decode_num_splits(R.BF16, B, L, spec.n_kv_heads)
+    say(f"{spec.name}: total keys={int(wl.decode.seq_lens.sum())} grid={grid}")
+    assert grid > 512
+    dw, outs = run_all(wl)
+    kp, vp = stored_pools(wl)
+    reqs = sorted(set([0, 1, 2, B // 2, B - 2, B - 1]) | set(np.random.default_rng(1).choice(B, 20, replace=False).tolist()))
+    assert_close(out_f64(outs["decode"])[reqs], oracle_decode(wl, kp, vp, requests=reqs), "bf16", spec.name)
