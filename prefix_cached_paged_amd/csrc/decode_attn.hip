@@ -6,13 +6,15 @@
 // byte of the context once and does ~G flops per byte, so it is bound by HBM bandwidth.
 //
 // Design (gfx950, wave64):
-//  * Balanced key stream. decode_plan_kernel lays the requests' contexts end to end, each
+//  * Balanced key stream. A plan lays the requests' contexts end to end, each
 //    rounded up to whole 64-key iterations, and cuts that stream into equal ranges of 256..4096
 //    keys, one per workgroup, so that one resident round of workgroups (2 per CU) covers it:
 //    every wave moves the same number of bytes whatever the mix of context lengths. A range
 //    may hold the tail of one request and the head of the next; each (request, range) overlap
 //    yields one partial (o, lse) in the workspace, and decode_merge_kernel combines a request's
-//    partials with log-sum-exp weights. A workgroup's waves are consecutive kv heads.
+//    partials with log-sum-exp weights. A workgroup's waves are consecutive kv heads. For
+//    batches up to 1,024 requests every split workgroup computes the plan itself (a scan in
+//    LDS); larger batches get it from decode_plan_kernel.
 //  * The G query heads that share kv head g are the N dimension of 16x16x32 bf16 MFMAs
 //    (grouped-query attention: one gathered K/V row feeds all G heads). Heads beyond G are
 //    zero padding; MFMA throughput is far above what the bandwidth bound needs.
@@ -61,6 +63,7 @@ static_assert(RAX_DEC_MIN_KEYS % kDecKeysPerIter == 0 && RAX_DEC_MIN_KEYS >= kDe
                   RAX_DEC_MIN_KEYS <= kDecMaxKeys,
               "decode ranges must be whole 64-key iterations, at most 4096 keys");
 constexpr int kPlanThreads = 1024;
+constexpr int kDecFusedBatch = 1024;  // batches up to this size need no separate plan kernel
 
 template <int D>
 using VRow = typename std::conditional<D == 128, uint4, uint2>::type;
@@ -105,6 +108,13 @@ __device__ __forceinline__ int64_t padded_len(const int32_t* seq_lens, int b, in
     return L > 0 ? (int64_t)((L + kDecKeysPerIter - 1) / kDecKeysPerIter * kDecKeysPerIter) : 0;
 }
 
+// Range length for a stream of T keys: clamp(64 * ceil(T / (64 * n_target)), min, 4096).
+__device__ __forceinline__ int64_t range_keys(int64_t T, int32_t n_target) {
+    int64_t chunk = (T + n_target - 1) / n_target;
+    chunk = (chunk + kDecKeysPerIter - 1) / kDecKeysPerIter * kDecKeysPerIter;
+    return min(max(chunk, (int64_t)RAX_DEC_MIN_KEYS), (int64_t)kDecMaxKeys);
+}
+
 // One workgroup. Writes P[b] = stream offset of request b (P[B] = stream length T), the range
 // length chunk = clamp(64 * ceil(T / (64 * n_target)), RAX_DEC_MIN_KEYS, 4096), the number of
 // non-empty ranges, and for each non-empty range w the request its first key belongs to.
@@ -127,9 +137,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
         __syncthreads();
     }
     const int64_t T = part[kPlanThreads - 1];
-    int64_t chunk = (T + n_target - 1) / n_target;
-    chunk = (chunk + kDecKeysPerIter - 1) / kDecKeysPerIter * kDecKeysPerIter;
-    chunk = min(max(chunk, (int64_t)RAX_DEC_MIN_KEYS), (int64_t)kDecMaxKeys);
+    const int64_t chunk = range_keys(T, n_target);
     int64_t run = part[t] - own;
     for (int b = b0; b < b1; ++b) {
         const int64_t len = padded_len(seq_lens, b, max_seq_len);
@@ -152,13 +160,16 @@ struct Seg {
     int32_t b, rpi, lo, n, pos0, len;
 };
 
-template <int D, bool OFF32>
+// FUSED (batch <= kDecFusedBatch): every workgroup computes the request offsets itself (a
+// scan of the padded lengths in LDS) instead of reading them from decode_plan_kernel, which is
+// then not launched; workgroup 0 writes meta and P for the merge kernel.
+template <int D, bool OFF32, bool FUSED>
 __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
-    int32_t B, int32_t Hq, int32_t Hkv, int32_t G, int32_t groups, float scale_log2,
-    const int64_t* __restrict__ meta, const int64_t* __restrict__ P,
+    int32_t B, int32_t Hq, int32_t Hkv, int32_t G, int32_t groups, int32_t n_target,
+    float scale_log2, int64_t* __restrict__ meta, int64_t* __restrict__ P,
     const int32_t* __restrict__ first_req, float* __restrict__ o_part,
     float* __restrict__ lse_part) {
     constexpr int S = D / 32;   // 32-wide K-dim steps of the score MFMA
@@ -170,25 +181,79 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
     // Groups of kv heads vary fastest, so the workgroups reading the same keys run together.
     const int grp = blockIdx.x % groups;
     const int w = blockIdx.x / groups;
-    const int64_t T = meta[0];
-    const int64_t chunk = meta[1];
-    if (w >= meta[2]) return;  // uniform over the workgroup
-    const int64_t s0 = (int64_t)w * chunk;
-    const int64_t s1 = min(s0 + chunk, T);
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
+    int64_t T, chunk, n_active;
+    const int64_t* Pr;  // request offsets: LDS (FUSED) or the plan's array
+    int b_first;
+    if constexpr (FUSED) {
+        constexpr int NT = 64 * kDecWaves;
+        __shared__ int64_t sP[kDecFusedBatch + 1];
+        __shared__ int64_t part[NT];
+        const int t = threadIdx.x;
+        const int per = (B + NT - 1) / NT;
+        const int c0 = min(B, t * per);
+        const int c1 = min(B, c0 + per);
+        int64_t own = 0;
+        for (int b = c0; b < c1; ++b) own += padded_len(seq_lens, b, max_seq_len);
+        part[t] = own;
+        __syncthreads();
+        for (int off = 1; off < NT; off <<= 1) {  // inclusive scan of the thread sums
+            const int64_t v = t >= off ? part[t - off] : 0;
+            __syncthreads();
+            part[t] += v;
+            __syncthreads();
+        }
+        T = part[NT - 1];
+        int64_t run = part[t] - own;
+        for (int b = c0; b < c1; ++b) {
+            sP[b] = run;
+            run += padded_len(seq_lens, b, max_seq_len);
+        }
+        if (t == 0) sP[B] = T;
+        chunk = range_keys(T, n_target);
+        n_active = (T + chunk - 1) / chunk;
+        __syncthreads();
+        if (blockIdx.x == 0) {
+            for (int b = t; b <= B; b += NT) P[b] = sP[b];
+            if (t == 0) {
+                meta[0] = T;
+                meta[1] = chunk;
+                meta[2] = n_active;
+            }
+        }
+        if (w >= n_active) return;  // uniform over the workgroup
+        // first request of the range: the last b with sP[b] <= s0 (it holds key s0)
+        const int64_t s0_ = (int64_t)w * chunk;
+        int lo = 0, hi = B;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (sP[mid] <= s0_) lo = mid; else hi = mid;
+        }
+        b_first = lo;
+        Pr = sP;
+    } else {
+        T = meta[0];
+        chunk = meta[1];
+        n_active = meta[2];
+        if (w >= n_active) return;  // uniform over the workgroup
+        b_first = first_req[w];
+        Pr = P;
+    }
+    const int64_t s0 = (int64_t)w * chunk;
+    const int64_t s1 = min(s0 + chunk, T);
 
-    // Wave 0 lists the requests overlapping [s0, s1): they are consecutive from first_req[w];
-    // lane i looks at request wb + i, 64 requests per step (empty requests overlap nothing).
+    // Wave 0 lists the requests overlapping [s0, s1): they are consecutive from b_first; lane i
+    // looks at request wb + i, 64 requests per step (empty requests overlap nothing).
     if (wv == 0) {
         int n_seg = 0;
-        for (int wb = first_req[w]; wb < B; wb += kWave) {
+        for (int wb = b_first; wb < B; wb += kWave) {
             const int bi = wb + lane;
             int64_t pb = s1, pe = s1;
             int rp = 0, len = 0;
             if (bi < B) {
-                pb = P[bi];
-                pe = P[bi + 1];
+                pb = Pr[bi];
+                pe = Pr[bi + 1];
                 rp = rpi[bi];
                 len = min(seq_lens[bi], max_seq_len);
             }
@@ -498,18 +563,26 @@ int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
     float* o_part = (float*)(ws + l.o);
     float* lse = (float*)(ws + l.lse);
     const float scale_log2 = a.sm_scale * kLog2e;
-    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.seq_lens,
-                       a.batch, a.max_seq_len, decode_target(a.n_kv_heads), meta, P, first);
-    if (hipGetLastError() != hipSuccess) return -1;
+    const int32_t n_target = decode_target(a.n_kv_heads);
+    const bool fused = a.batch <= kDecFusedBatch;
+    if (!fused) {
+        hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.seq_lens,
+                           a.batch, a.max_seq_len, n_target, meta, P, first);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
     const dim3 sgrid((uint32_t)grid * (uint32_t)groups);
     const dim3 mgrid((a.batch * a.n_q_heads + 3) / 4);
     const bool off32 = pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 2);
-#define RAX_DEC_SPLIT(DD, OFF)                                                                  \
-    hipLaunchKernelGGL((decode_split_kernel<DD, OFF>), sgrid, dim3(64 * kDecWaves), 0, stream,    \
+#define RAX_DEC_SPLIT3(DD, OFF, FU)                                                             \
+    hipLaunchKernelGGL((decode_split_kernel<DD, OFF, FU>), sgrid, dim3(64 * kDecWaves), 0, stream, \
                        (const uint16_t*)a.q, (const uint16_t*)a.k_pool, (const uint16_t*)a.v_pool,  \
                        a.r2t, a.r2t_stride, a.req_pool_indices, a.seq_lens, a.max_seq_len, a.batch, \
-                       a.n_q_heads, a.n_kv_heads, G, groups, scale_log2, meta, P, first, o_part,   \
-                       lse)
+                       a.n_q_heads, a.n_kv_heads, G, groups, n_target, scale_log2, meta, P, first, \
+                       o_part, lse)
+#define RAX_DEC_SPLIT(DD, OFF)                                                                  \
+    do {                                                                                        \
+        if (fused) RAX_DEC_SPLIT3(DD, OFF, true); else RAX_DEC_SPLIT3(DD, OFF, false);          \
+    } while (0)
     if (a.head_dim == 128) {
         if (off32) RAX_DEC_SPLIT(128, true); else RAX_DEC_SPLIT(128, false);
         if (hipGetLastError() != hipSuccess) return -1;
@@ -522,6 +595,7 @@ int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
                            (uint16_t*)a.o, a.seq_lens, a.max_seq_len, meta, P, a.n_q_heads, a.batch);
     }
 #undef RAX_DEC_SPLIT
+#undef RAX_DEC_SPLIT3
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
