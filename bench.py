@@ -206,6 +206,8 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=16.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step as HIP graph replays (reported beside the eager figures)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (reference for the PMC byte counters)")
     ap.add_argument("--pmc-summary", nargs=5, metavar=("OUT", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -284,6 +286,30 @@ def main():
     ms = {n: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
           for i, n in enumerate(["kv_store", "extend", "decode"])}
 
+    graph = None
+    if args.graph:
+        log("capturing one step in a HIP graph")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        gev[0].record()
+        for _ in range(args.steps):
+            g.replay()
+        gev[1].record()
+        torch.cuda.synchronize()
+        graph = dict(ms_per_step=gev[0].elapsed_time(gev[1]) / args.steps,
+                     eager_event_ms_per_step=sum(ms.values()))
+
     report = {}
     hbm = lambda nbytes, t_ms: nbytes / (t_ms * 1e-3) / 1e9
     n_new = int(wl.store_loc.size)
@@ -353,6 +379,7 @@ def main():
         "roofline": roofs.get(dominant),
         "roofline_other": [roofs[k] for k in roofs if k != dominant],
         "cpu_baseline": cpu,
+        "graph": graph,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
