@@ -18,6 +18,8 @@ What it computes is the plain definition of the method, in float64:
   of attention for one head).
 * ``decode_attention`` -- one query per request over its whole context
   ("Inside SGLang", Step 3, "Prefill and decode have different shapes").
+* ``fp8`` -- the FP8 E4M3 KV pool ("Inside SGLang", Step 6): exact decode of each byte,
+  the store's encoding (``kv_store_fp8``); the attention functions take per-pool scales.
 
 Parity status of every function is pinned by tests under ``tests/`` (brute
 force on tiny inputs, closed forms, invariants, a textbook library routine on
@@ -31,6 +33,7 @@ from .attention import (
     decode_attention,
     gather_request_kv,
 )
+from .fp8 import e4m3_bits_to_f64, e4m3_round, kv_store_fp8, quantize_bf16
 from .bruteforce import (
     extend_attention_loops,
     decode_attention_loops,
@@ -45,4 +48,8 @@ __all__ = [
     "gather_request_kv",
     "extend_attention_loops",
     "decode_attention_loops",
+    "e4m3_bits_to_f64",
+    "e4m3_round",
+    "kv_store_fp8",
+    "quantize_bf16",
 ]

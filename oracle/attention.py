@@ -82,12 +82,14 @@ def kv_store(k_pool, v_pool, k_new, v_new, loc):
     return k_out, v_out
 
 
-def gather_request_kv(k_pool, v_pool, req_to_token, row, length):
+def gather_request_kv(k_pool, v_pool, req_to_token, row, length, k_scale=1.0, v_scale=1.0):
     """Gather one request's keys and values by slot, as float64 ``[length, kv_heads, head_dim]``.
 
     The slot of the request's token ``j`` is ``req_to_token[row, j]``
     ("SGLang" notes, section "KV memory": request/position -> KV pool index ->
     KV tensors). Only the gathered rows are converted, never the whole pool.
+    FP8 pools (uint8) hold ``scale * e4m3(byte)``: the scales multiply the decoded rows
+    ("Inside SGLang", Step 6, per-tensor KV scales; 1.0 for bf16/fp32 pools).
     """
     S = k_pool.shape[0]
     if length < 0 or length > req_to_token.shape[1]:
@@ -95,7 +97,12 @@ def gather_request_kv(k_pool, v_pool, req_to_token, row, length):
     slots = np.asarray(req_to_token[row, :length], dtype=np.int64)
     if length and (slots.min() < 0 or slots.max() >= S):
         raise ValueError(f"request table row {row} names a slot outside the pool")
-    return to_f64(k_pool[slots]), to_f64(v_pool[slots])
+    kb, vb = to_f64(k_pool[slots]), to_f64(v_pool[slots])
+    if k_scale != 1.0:
+        kb = kb * float(np.float32(k_scale))
+    if v_scale != 1.0:
+        vb = vb * float(np.float32(v_scale))
+    return kb, vb
 
 
 def causal_hidden(length: int, prefix: int, rows: np.ndarray) -> np.ndarray:
@@ -117,7 +124,7 @@ def _softmax_rows_times_v(scores: np.ndarray, v: np.ndarray) -> np.ndarray:
 
 def extend_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens,
                      extend_lens, extend_start_loc, n_kv_heads, sm_scale,
-                     tokens=None, row_block=512):
+                     tokens=None, row_block=512, k_scale=1.0, v_scale=1.0):
     """EXTEND attention: each request's new suffix rows over its prefix plus themselves.
 
     Follows "Origins: the paper and the first commit": self-test answer 2 (with
@@ -167,7 +174,7 @@ def extend_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, prefix_l
             rows = np.array([i for i in range(e) if (s0 + i) in want], dtype=np.int64)
             if rows.size == 0:
                 continue
-        kb, vb = gather_request_kv(k_pool, v_pool, req_to_token, r, L)
+        kb, vb = gather_request_kv(k_pool, v_pool, req_to_token, r, L, k_scale, v_scale)
         for c0 in range(0, rows.size, row_block):
             rb = rows[c0:c0 + row_block]
             masked = causal_hidden(L, p, rb)                       # [rows, L]
@@ -187,7 +194,7 @@ def extend_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, prefix_l
 
 
 def decode_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, seq_lens,
-                     n_kv_heads, sm_scale, requests=None):
+                     n_kv_heads, sm_scale, requests=None, k_scale=1.0, v_scale=1.0):
     """DECODE attention: one query per request over positions 0 .. seq_len-1.
 
     Follows "Inside SGLang", Step 3, "Prefill and decode have different
@@ -215,7 +222,8 @@ def decode_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, seq_lens
         L = int(seq_lens[b])
         if L <= 0:
             raise ValueError(f"request {b}: a decode query needs at least one key")
-        kb, vb = gather_request_kv(k_pool, v_pool, req_to_token, int(req_pool_indices[b]), L)
+        kb, vb = gather_request_kv(k_pool, v_pool, req_to_token, int(req_pool_indices[b]), L,
+                                   k_scale, v_scale)
         for g in range(Hkv):
             heads = slice(g * G, (g + 1) * G)
             sc = (qf[b, heads, :] @ kb[:, g, :].T) * sm_scale      # [G, L]

@@ -21,10 +21,14 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def to_f64(a: np.ndarray) -> np.ndarray:
-    """float64 view of a stored array: uint16 = bfloat16 bits, float32/float64 as is."""
+    """float64 view of a stored array: uint16 = bfloat16 bits, uint8 = FP8 E4M3 bytes (unscaled),
+    float32/float64 as is."""
     a = np.asarray(a)
     if a.dtype == np.uint16:
         return bf16_bits_to_f64(a)
+    if a.dtype == np.uint8:
+        from .fp8 import e4m3_bits_to_f64
+        return e4m3_bits_to_f64(a)
     if a.dtype in (np.float32, np.float64):
         return a.astype(np.float64)
     raise TypeError(f"unsupported element format {a.dtype}")
