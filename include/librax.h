@@ -55,7 +55,8 @@ typedef enum rax_status {
 
 typedef enum rax_dtype {
     RAX_BF16 = 0,
-    RAX_FP32 = 1
+    RAX_FP32 = 1,
+    RAX_FP8_E4M3 = 2 /* K/V pool element of the *_fp8 calls (workspace queries only)   */
 } rax_dtype;
 
 /* Library version, major * 10000 + minor * 100 + patch. */
@@ -176,6 +177,36 @@ int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, 
                          const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
                          int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                          float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * FP8 KV pools -- the K and V pools hold one OCP FP8 E4M3 byte per element (no infinities; NaN
+ * only at 0x7F/0xFF; largest finite magnitude 448), and an element's value is
+ * scale * e4m3(byte) with one float scale per pool ("Inside SGLang", Step 6: with an FP8 KV
+ * cache every token costs half the bytes, attention reads the FP8 cache without a separate
+ * dequantisation pass, and a scale that the checkpoint does not provide is 1.0). Q, O and the
+ * new K/V rows given to the store stay bf16. Pools are uint8 [num_slots, n_kv_heads, head_dim];
+ * everything else as in the bf16 calls. Scales must be finite and > 0 (else RAX_ERR_SHAPE).
+ *
+ * rax_kv_store_fp8 -- as rax_kv_store, but each new bf16 element x is written as the E4M3 byte
+ *   nearest to clamp(float32(x) * r, -448, 448), ties to the even code, where r is 1/scale
+ *   computed in double and rounded once to float. Inputs must be finite (NaN inputs give an
+ *   undefined byte). Same loc contract as rax_kv_store.
+ *
+ * rax_decode_attention_fp8 -- rax_decode_attention over FP8 pools: the scores use
+ *   k_scale * e4m3(K) and the values v_scale * e4m3(V). Every E4M3 value is exactly a bf16
+ *   value, so the kernel widens the bytes in registers and applies k_scale to the scores and
+ *   v_scale to the output. Workspace: rax_decode_workspace_bytes(RAX_FP8_E4M3, ...).
+ */
+int rax_kv_store_fp8(const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
+                     void* k_pool, void* v_pool, int64_t num_slots, int32_t n_kv_heads,
+                     int32_t head_dim, float k_scale, float v_scale, void* stream);
+
+int rax_decode_attention_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
+                             int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                             const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
+                             int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                             int32_t head_dim, float sm_scale, float k_scale, float v_scale,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Number of key ranges per group of kv heads that rax_decode_attention launches for these
  * shapes (bf16; 1 for fp32 or empty shapes; -1 if the shapes need more than 2^31 - 1). Ranges

@@ -39,28 +39,33 @@ def e4m3_bits_to_f64(b: np.ndarray) -> np.ndarray:
     return np.where((bi & 0x7F) == 0x7F, np.nan, out)
 
 
-# The 127 non-negative finite values, in code order (code c holds _POS[c]); increasing.
-_POS = e4m3_bits_to_f64(np.arange(127, dtype=np.uint8))
-
-
 def e4m3_round(y: np.ndarray) -> np.ndarray:
-    """Nearest E4M3 byte of each finite value with |y| <= 448, ties to the even code."""
+    """Nearest E4M3 byte of each finite value with |y| <= 448, ties to the even code.
+
+    Written from the format: for |y| >= 2^-6 (the normal range) take the binary exponent e of
+    |y| (|y| = s * 2^e, 1 <= s < 2), round the 3-bit mantissa (s - 1) * 8 to the nearest
+    integer with ties to even, and carry into the exponent when it rounds up to 8; below 2^-6
+    round |y| / 2^-9 the same way (the subnormal step; 8 lands on the smallest normal, code 8).
+    All scalings are by powers of two, so nothing but the final rounding is inexact.
+    """
     y = np.asarray(y, dtype=np.float64)
     if not np.all(np.isfinite(y)):
         raise ValueError("E4M3 rounding takes finite values")
     a = np.abs(y)
     if np.any(a > E4M3_MAX):
         raise ValueError("values beyond 448 must be clamped before rounding")
-    hi = np.searchsorted(_POS, a, side="left")          # first code with value >= a
-    hi = np.minimum(hi, 126)
-    lo = np.maximum(hi - 1, 0)
-    d_lo = a - _POS[lo]
-    d_hi = _POS[hi] - a
-    exact = _POS[hi] == a
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
-    code = np.where(exact, hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
-    neg = np.signbit(y)
-    return np.where(neg, code | np.uint8(0x80), code).astype(np.uint8)
+    frac, exp = np.frexp(a)                      # a = frac * 2^exp, 0.5 <= frac < 1 (a > 0)
+    e = exp.astype(np.int64) - 1                 # a = (2 frac) * 2^e, 1 <= 2 frac < 2
+    m = np.rint((2.0 * frac - 1.0) * 8.0)        # 0 .. 8
+    carry = m == 8.0
+    e = np.where(carry, e + 1, e)
+    m = np.where(carry, 0.0, m)
+    normal = a >= 2.0 ** -6
+    code_n = ((e + 7) << 3) | m.astype(np.int64)
+    code_s = np.rint(a * 2.0 ** 9).astype(np.int64)
+    code = np.where(normal, code_n, code_s)
+    code = np.where(np.signbit(y), code | 0x80, code)
+    return code.astype(np.uint8)
 
 
 def reciprocal_f32(scale: float) -> np.float32:

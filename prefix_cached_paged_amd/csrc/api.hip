@@ -9,6 +9,7 @@ constexpr int kVersion = 100;  // 0.1.0
 constexpr int32_t kMaxGridYZ = 65535;
 
 bool dtype_ok(int dt) { return dt == RAX_BF16 || dt == RAX_FP32; }
+bool scale_ok(float s) { return s == s && s > 0.f && s <= 3.4028234663852886e38f; }
 size_t elem_bytes(int dt) { return dt == RAX_BF16 ? 2 : 4; }
 bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
 
@@ -99,23 +100,29 @@ int rax_extend_attention(int dtype, const void* q, void* o, const void* k_pool, 
 
 size_t rax_decode_workspace_bytes(int dtype, int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
                                   int32_t n_kv_heads, int32_t head_dim) {
-    if (dtype != RAX_BF16 || batch <= 0 || max_seq_len <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 ||
+    if ((dtype != RAX_BF16 && dtype != RAX_FP8_E4M3) || batch <= 0 || max_seq_len <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 ||
         head_dim <= 0)
         return 0;
     return rax::decode_workspace(batch, max_seq_len, n_q_heads, n_kv_heads, head_dim);
 }
 
 int32_t rax_decode_num_splits(int dtype, int32_t batch, int32_t max_seq_len, int32_t n_kv_heads) {
-    if (dtype != RAX_BF16) return 1;
+    if (dtype != RAX_BF16 && dtype != RAX_FP8_E4M3) return 1;
     if (batch <= 0 || max_seq_len <= 0 || n_kv_heads <= 0) return 1;
     return rax::decode_grid(batch, max_seq_len, n_kv_heads);
 }
 
-int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
-                         int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
-                         const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
-                         int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                         float sm_scale, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and launch shared by the bf16/fp32 and FP8-pool DECODE entry points.
+int decode_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool, const void* v_pool,
+                int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
+                int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                float sm_scale, float k_scale, float v_scale, void* workspace,
+                size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype)) return RAX_ERR_DTYPE;
     if (batch < 0 || batch > kMaxGridYZ || max_seq_len < 0 || num_slots <= 0 || r2t_stride <= 0 ||
         max_seq_len > r2t_stride)
@@ -125,6 +132,7 @@ int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, 
     const int32_t G = n_q_heads / n_kv_heads;
     if (dtype == RAX_BF16 && !rax::decode_bf16_supported(G, head_dim)) return RAX_ERR_UNSUPPORTED;
     if (!(sm_scale == sm_scale)) return RAX_ERR_SHAPE;
+    if (kv8 && (!scale_ok(k_scale) || !scale_ok(v_scale))) return RAX_ERR_SHAPE;
     if (batch == 0) return RAX_OK;
     if (max_seq_len == 0) return RAX_ERR_SHAPE;
     if (dtype == RAX_BF16 && rax::decode_grid(batch, max_seq_len, n_kv_heads) < 0)
@@ -143,9 +151,51 @@ int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, 
     a.max_seq_len = max_seq_len; a.n_q_heads = n_q_heads; a.n_kv_heads = n_kv_heads;
     a.head_dim = head_dim; a.sm_scale = sm_scale; a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
+    a.kv8 = kv8; a.k_scale = k_scale; a.v_scale = v_scale;
     const int rc = dtype == RAX_BF16 ? rax::launch_decode_bf16(a, (hipStream_t)stream)
                                      : rax::launch_decode_fp32(a, (hipStream_t)stream);
     return rc == 0 ? RAX_OK : RAX_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
+                         int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                         const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
+                         int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                         float sm_scale, void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_call(dtype, false, q, o, k_pool, v_pool, num_slots, req_to_token, r2t_stride,
+                       req_pool_indices, seq_lens, batch, max_seq_len, n_q_heads, n_kv_heads, head_dim,
+                       sm_scale, 1.f, 1.f, workspace, workspace_bytes, stream);
+}
+
+int rax_kv_store_fp8(const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
+                     void* k_pool, void* v_pool, int64_t num_slots, int32_t n_kv_heads,
+                     int32_t head_dim, float k_scale, float v_scale, void* stream) {
+    if (n_new < 0 || num_slots <= 0 || n_kv_heads <= 0 || n_new > num_slots) return RAX_ERR_SHAPE;
+    if (!head_dim_ok(head_dim)) return RAX_ERR_UNSUPPORTED;
+    if (!scale_ok(k_scale) || !scale_ok(v_scale)) return RAX_ERR_SHAPE;
+    if (n_new == 0) return RAX_OK;
+    if (!k_new || !v_new || !loc || !k_pool || !v_pool) return RAX_ERR_NULL;
+    const int64_t row_elems = (int64_t)n_kv_heads * head_dim;
+    if (n_new * (row_elems / 8) > ((int64_t)1 << 62)) return RAX_ERR_SHAPE;
+    const float k_inv = (float)(1.0 / (double)k_scale);
+    const float v_inv = (float)(1.0 / (double)v_scale);
+    return rax::launch_kv_store_fp8(k_new, v_new, loc, n_new, k_pool, v_pool, row_elems, k_inv, v_inv,
+                                    (hipStream_t)stream) == 0 ? RAX_OK : RAX_ERR_LAUNCH;
+}
+
+int rax_decode_attention_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
+                             int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                             const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
+                             int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                             int32_t head_dim, float sm_scale, float k_scale, float v_scale,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_call(RAX_BF16, true, q, o, k_pool, v_pool, num_slots, req_to_token, r2t_stride,
+                       req_pool_indices, seq_lens, batch, max_seq_len, n_q_heads, n_kv_heads, head_dim,
+                       sm_scale, k_scale, v_scale, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

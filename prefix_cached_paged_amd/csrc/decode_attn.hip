@@ -73,6 +73,41 @@ __device__ __forceinline__ uint4 vcol(const VRow<D> (&r)[8]) {
     return column8<E>(r);
 }
 
+// FP8 E4M3 pools ("Inside SGLang", Step 6): 8 (or 4) bytes per K step or V row piece, widened
+// to bf16 in registers right before the MFMA. Every E4M3 value is exactly a bf16 value, so
+// the widening (through float32) rounds nothing; the pool scales are applied to the scores
+// (K) and to the output (V) instead of to every element.
+template <bool HI>
+__device__ __forceinline__ uint32_t bf16x2_of_e4m3(uint32_t w) {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+    return pack_bf16x2(f[0], f[1]);
+}
+__device__ __forceinline__ uint4 widen8(uint2 x) {
+    return make_uint4(bf16x2_of_e4m3<false>(x.x), bf16x2_of_e4m3<true>(x.x),
+                      bf16x2_of_e4m3<false>(x.y), bf16x2_of_e4m3<true>(x.y));
+}
+__device__ __forceinline__ uint4 widen8(uint4 x) { return x; }  // bf16 pools: as stored
+__device__ __forceinline__ uint2 widen4(uint32_t x) {
+    return make_uint2(bf16x2_of_e4m3<false>(x), bf16x2_of_e4m3<true>(x));
+}
+__device__ __forceinline__ uint2 widen4(uint2 x) { return x; }
+
+// Element types of one K MFMA step (8 head_dim elements) and of a lane's V row piece (DT
+// elements), for bf16 or FP8 pools.
+template <int D, bool KV8>
+struct DecElems {
+    using K = typename std::conditional<KV8, uint2, uint4>::type;
+    using V = typename std::conditional<KV8, typename std::conditional<D == 128, uint2, uint32_t>::type,
+                                        VRow<D>>::type;
+    static constexpr int bytes = KV8 ? 1 : 2;
+};
+template <int D>
+__device__ __forceinline__ VRow<D> widen_v(typename DecElems<D, true>::V x) {
+    if constexpr (D == 128) return widen8(x); else return widen4(x);
+}
+template <int D>
+__device__ __forceinline__ VRow<D> widen_v(VRow<D> x) { return x; }
+
 // One K or V row piece (16 or 8 bytes) at byte offset slot * row_bytes + off from a
 // wave-uniform base. Every K/V byte is read once per step, so the loads are marked
 // non-temporal (RAX_DEC_NT, measured 2-6% faster on the long-context batches).
@@ -84,9 +119,11 @@ __device__ __forceinline__ T load_piece(const char* p) {
         if constexpr (sizeof(T) == 16) {
             const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
             return __builtin_bit_cast(T, v);
-        } else {
+        } else if constexpr (sizeof(T) == 8) {
             const u32x2 v = __builtin_nontemporal_load((const u32x2*)p);
             return __builtin_bit_cast(T, v);
+        } else {
+            return __builtin_nontemporal_load((const uint32_t*)p);
         }
     } else {
         return *(const T*)p;
@@ -163,13 +200,13 @@ struct Seg {
 // FUSED (batch <= kDecFusedBatch): every workgroup computes the request offsets itself (a
 // scan of the padded lengths in LDS) instead of reading them from decode_plan_kernel, which is
 // then not launched; workgroup 0 writes meta and P for the merge kernel.
-template <int D, bool OFF32, bool FUSED>
+template <int D, bool OFF32, bool FUSED, bool KV8>
 __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
     int32_t B, int32_t Hq, int32_t Hkv, int32_t G, int32_t groups, int32_t n_target,
-    float scale_log2, int64_t* __restrict__ meta, int64_t* __restrict__ P,
+    float scale_log2, float out_scale, int64_t* __restrict__ meta, int64_t* __restrict__ P,
     const int32_t* __restrict__ first_req, float* __restrict__ o_part,
     float* __restrict__ lse_part) {
     constexpr int S = D / 32;   // 32-wide K-dim steps of the score MFMA
@@ -294,11 +331,13 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
 
     const int n16 = lane & 15;
     const int kg = lane >> 4;
-    const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
-    const char* kbase = (const char*)k_pool + (int64_t)g * D * 2;  // wave-uniform
-    const char* vbase = (const char*)v_pool + (int64_t)g * D * 2;
-    const uint32_t k_off = 16u * kg;       // this lane's 8 head_dim elements of a K row
-    const uint32_t v_off = 2u * DT * n16;  // this lane's DT head_dim elements of a V row
+    using EL = DecElems<D, KV8>;
+    constexpr uint32_t es = EL::bytes;  // bytes per stored element
+    const uint32_t row_bytes = (uint32_t)Hkv * D * es;
+    const char* kbase = (const char*)k_pool + (int64_t)g * D * es;  // wave-uniform
+    const char* vbase = (const char*)v_pool + (int64_t)g * D * es;
+    const uint32_t k_off = 8u * es * kg;    // this lane's 8 head_dim elements of a K row
+    const uint32_t v_off = es * DT * n16;   // this lane's DT head_dim elements of a V row
     // Columns n16 >= G are padding: they load a valid head and zero it with a mask (no branch,
     // so the loads stay in flight together).
     const bool q_ok = n16 < G;
@@ -309,25 +348,25 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
     // consumed this iteration's, so one iteration of K and V is always in flight. The steady
     // loop is branch-free (the last iteration is peeled), which keeps the memory-counter waits
     // exact: each wait covers only the rows about to be used.
-    uint4 kr[4][S];
-    VRow<D> vr[2][8];
+    typename EL::K kr[4][S];
+    typename EL::V vr[2][8];
 #define RAX_DEC_SLOTS_K(IT, SK)                                                              \
     _Pragma("unroll") for (int t = 0; t < 4; ++t) SK[t] =                                    \
         slot_lds[lo + (IT) * kDecKeysPerIter + 16 * t + n16];
 #define RAX_DEC_LOAD_K(SK)                                                                   \
     _Pragma("unroll") for (int t = 0; t < 4; ++t)                                            \
     _Pragma("unroll") for (int s = 0; s < S; ++s)                                            \
-        kr[t][s] = row_load<OFF32, uint4>(kbase, SK[t], row_bytes, k_off + 64u * s);
+        kr[t][s] = row_load<OFF32, typename EL::K>(kbase, SK[t], row_bytes, k_off + 32u * es * s);
     // V keys of lane (n16, kg) in block u: 32u + 16h + 4kg + e for h, e in {0,1} x {0..3}.
 #define RAX_DEC_LOAD_V(IT)                                                                   \
     _Pragma("unroll") for (int u = 0; u < 2; ++u)                                            \
     _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                          \
         const int4 sv_ =                                                                     \
             *(const int4*)&slot_lds[lo + (IT) * kDecKeysPerIter + 32 * u + 16 * h + 4 * kg]; \
-        vr[u][4 * h + 0] = row_load<OFF32, VRow<D>>(vbase, sv_.x, row_bytes, v_off);         \
-        vr[u][4 * h + 1] = row_load<OFF32, VRow<D>>(vbase, sv_.y, row_bytes, v_off);         \
-        vr[u][4 * h + 2] = row_load<OFF32, VRow<D>>(vbase, sv_.z, row_bytes, v_off);         \
-        vr[u][4 * h + 3] = row_load<OFF32, VRow<D>>(vbase, sv_.w, row_bytes, v_off);         \
+        vr[u][4 * h + 0] = row_load<OFF32, typename EL::V>(vbase, sv_.x, row_bytes, v_off); \
+        vr[u][4 * h + 1] = row_load<OFF32, typename EL::V>(vbase, sv_.y, row_bytes, v_off); \
+        vr[u][4 * h + 2] = row_load<OFF32, typename EL::V>(vbase, sv_.z, row_bytes, v_off); \
+        vr[u][4 * h + 3] = row_load<OFF32, typename EL::V>(vbase, sv_.w, row_bytes, v_off); \
     }
 #define RAX_DEC_ITER(IT, MORE)                                                               \
     {                                                                                        \
@@ -338,7 +377,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
         _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                      \
             st[t] = f32x4{0.f, 0.f, 0.f, 0.f};                                               \
             _Pragma("unroll") for (int s = 0; s < S; ++s)                                    \
-                st[t] = mfma16x16x32(as_bf16x8(kr[t][s]), qop[s], st[t]);                    \
+                st[t] = mfma16x16x32(as_bf16x8(widen8(kr[t][s])), qop[s], st[t]);            \
         }                                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                   \
         if (MORE) { RAX_DEC_LOAD_K(sk_) }                                                    \
@@ -371,15 +410,17 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
             pb.z = pack_bf16x2(p[2 * u + 1][0], p[2 * u + 1][1]);                            \
             pb.w = pack_bf16x2(p[2 * u + 1][2], p[2 * u + 1][3]);                            \
             const bf16x8 pop = as_bf16x8(pb);                                                \
-            acc[0] = mfma16x16x32(as_bf16x8(vcol<D, 0>(vr[u])), pop, acc[0]);                \
-            acc[1] = mfma16x16x32(as_bf16x8(vcol<D, 1>(vr[u])), pop, acc[1]);                \
-            acc[2] = mfma16x16x32(as_bf16x8(vcol<D, 2>(vr[u])), pop, acc[2]);                \
-            acc[3] = mfma16x16x32(as_bf16x8(vcol<D, 3>(vr[u])), pop, acc[3]);                \
+            VRow<D> vw_[8];                                                                  \
+            _Pragma("unroll") for (int j = 0; j < 8; ++j) vw_[j] = widen_v<D>(vr[u][j]);     \
+            acc[0] = mfma16x16x32(as_bf16x8(vcol<D, 0>(vw_)), pop, acc[0]);                  \
+            acc[1] = mfma16x16x32(as_bf16x8(vcol<D, 1>(vw_)), pop, acc[1]);                \
+            acc[2] = mfma16x16x32(as_bf16x8(vcol<D, 2>(vw_)), pop, acc[2]);                \
+            acc[3] = mfma16x16x32(as_bf16x8(vcol<D, 3>(vw_)), pop, acc[3]);                \
             if constexpr (DT == 8) {                                                         \
-                acc[4] = mfma16x16x32(as_bf16x8(vcol<D, 4>(vr[u])), pop, acc[4]);            \
-                acc[5] = mfma16x16x32(as_bf16x8(vcol<D, 5>(vr[u])), pop, acc[5]);            \
-                acc[6] = mfma16x16x32(as_bf16x8(vcol<D, 6>(vr[u])), pop, acc[6]);            \
-                acc[7] = mfma16x16x32(as_bf16x8(vcol<D, 7>(vr[u])), pop, acc[7]);            \
+                acc[4] = mfma16x16x32(as_bf16x8(vcol<D, 4>(vw_)), pop, acc[4]);            \
+                acc[5] = mfma16x16x32(as_bf16x8(vcol<D, 5>(vw_)), pop, acc[5]);            \
+                acc[6] = mfma16x16x32(as_bf16x8(vcol<D, 6>(vw_)), pop, acc[6]);            \
+                acc[7] = mfma16x16x32(as_bf16x8(vcol<D, 7>(vw_)), pop, acc[7]);            \
             }                                                                                \
         }                                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                   \
@@ -429,7 +470,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
             // Partial of (request b, range w) sits at index b + w: the overlapping pairs form a
             // monotone staircase in (b, w), so b + w never repeats.
             const int64_t pidx = ((int64_t)b + w) * Hq + g * G + n16;
-            const float inv = 1.f / lsum;
+            const float inv = out_scale / lsum;
             float* op = o_part + pidx * D;
             // acc[dt][i] is O^T row 4kg + i, i.e. head_dim DT*(4kg + i) + dt.
 #pragma unroll
@@ -562,7 +603,8 @@ int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
     int32_t* first = (int32_t*)(ws + l.first);
     float* o_part = (float*)(ws + l.o);
     float* lse = (float*)(ws + l.lse);
-    const float scale_log2 = a.sm_scale * kLog2e;
+    const float scale_log2 = a.sm_scale * kLog2e * (a.kv8 ? a.k_scale : 1.f);
+    const float out_scale = a.kv8 ? a.v_scale : 1.f;
     const int32_t n_target = decode_target(a.n_kv_heads);
     const bool fused = a.batch <= kDecFusedBatch;
     if (!fused) {
@@ -572,13 +614,17 @@ int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
     }
     const dim3 sgrid((uint32_t)grid * (uint32_t)groups);
     const dim3 mgrid((a.batch * a.n_q_heads + 3) / 4);
-    const bool off32 = pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 2);
+    const bool off32 = pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, a.kv8 ? 1 : 2);
+#define RAX_DEC_SPLIT4(DD, OFF, FU, K8)                                                         \
+    hipLaunchKernelGGL((decode_split_kernel<DD, OFF, FU, K8>), sgrid, dim3(64 * kDecWaves), 0,   \
+                       stream, (const uint16_t*)a.q, (const uint16_t*)a.k_pool,                   \
+                       (const uint16_t*)a.v_pool, a.r2t, a.r2t_stride, a.req_pool_indices,        \
+                       a.seq_lens, a.max_seq_len, a.batch, a.n_q_heads, a.n_kv_heads, G, groups,  \
+                       n_target, scale_log2, out_scale, meta, P, first, o_part, lse)
 #define RAX_DEC_SPLIT3(DD, OFF, FU)                                                             \
-    hipLaunchKernelGGL((decode_split_kernel<DD, OFF, FU>), sgrid, dim3(64 * kDecWaves), 0, stream, \
-                       (const uint16_t*)a.q, (const uint16_t*)a.k_pool, (const uint16_t*)a.v_pool,  \
-                       a.r2t, a.r2t_stride, a.req_pool_indices, a.seq_lens, a.max_seq_len, a.batch, \
-                       a.n_q_heads, a.n_kv_heads, G, groups, n_target, scale_log2, meta, P, first, \
-                       o_part, lse)
+    do {                                                                                        \
+        if (a.kv8) RAX_DEC_SPLIT4(DD, OFF, FU, true); else RAX_DEC_SPLIT4(DD, OFF, FU, false);  \
+    } while (0)
 #define RAX_DEC_SPLIT(DD, OFF)                                                                  \
     do {                                                                                        \
         if (fused) RAX_DEC_SPLIT3(DD, OFF, true); else RAX_DEC_SPLIT3(DD, OFF, false);          \
@@ -596,6 +642,7 @@ int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
     }
 #undef RAX_DEC_SPLIT
 #undef RAX_DEC_SPLIT3
+#undef RAX_DEC_SPLIT4
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -32,6 +32,10 @@ struct AttnArgs {
     int32_t n_kv_heads;
     int32_t head_dim;
     float sm_scale;
+    // FP8 E4M3 pools (kv8): element = scale * e4m3(byte); 1 for bf16/fp32 pools.
+    bool kv8;
+    float k_scale;
+    float v_scale;
     void* workspace;
     size_t workspace_bytes;
 };
@@ -48,6 +52,10 @@ inline bool pool_fits_32bit_offsets(int64_t num_slots, int32_t n_kv_heads, int32
 
 int launch_kv_store(const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
                     void* k_pool, void* v_pool, int64_t row_bytes, hipStream_t stream);
+// bf16 rows -> FP8 E4M3 pools; k_inv / v_inv are the float32 reciprocals of the scales.
+int launch_kv_store_fp8(const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
+                        void* k_pool, void* v_pool, int64_t row_elems, float k_inv, float v_inv,
+                        hipStream_t stream);
 
 // bf16, MFMA paths.
 bool extend_bf16_supported(int32_t group, int32_t head_dim);

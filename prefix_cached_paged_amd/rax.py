@@ -18,11 +18,12 @@ import torch  # imported before the library so that one HIP runtime serves the p
 __all__ = [
     "RaxError", "BF16", "FP32", "load", "version", "kv_store", "extend_attention",
     "decode_attention", "extend_workspace_bytes", "decode_workspace_bytes", "decode_num_splits",
-    "library_path", "declared_symbols",
+    "library_path", "declared_symbols", "FP8_E4M3", "kv_store_fp8", "decode_attention_fp8",
 ]
 
 BF16 = 0
 FP32 = 1
+FP8_E4M3 = 2   # pool element of the *_fp8 calls (uint8 tensors)
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_PKG), "include", "librax.h")
 _lib = None
@@ -44,6 +45,11 @@ _SIGS = {
                                             _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f,
                                             _c_p, _c_sz, _c_p]),
     "rax_decode_num_splits": (_c_i32, [ctypes.c_int, _c_i32, _c_i32, _c_i32]),
+    "rax_kv_store_fp8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_f,
+                                        _c_f, _c_p]),
+    "rax_decode_attention_fp8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_p,
+                                                _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f, _c_f, _c_f,
+                                                _c_p, _c_sz, _c_p]),
 }
 
 
@@ -185,3 +191,40 @@ def decode_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, seq_l
                                        int(max_seq_len), Hq, Hkv, D, float(sm_scale), _ptr(workspace), wbytes,
                                        _stream(stream)),
            "rax_decode_attention")
+
+
+def _fp8_pool(t):
+    if t.dtype != torch.uint8:
+        raise TypeError("FP8 pools are uint8 tensors of E4M3 bytes")
+    return _ptr(t)
+
+
+def _bf16(t):
+    if t.dtype != torch.bfloat16:
+        raise TypeError("q, o and the new rows of the FP8 calls are bfloat16")
+    return _ptr(t)
+
+
+def kv_store_fp8(k_new, v_new, loc, k_pool, v_pool, k_scale=1.0, v_scale=1.0, stream=None):
+    """Write bf16 rows into FP8 E4M3 pools at ``loc`` (scale 1.0 when the caller has none)."""
+    S, Hkv, D = k_pool.shape
+    _check(load().rax_kv_store_fp8(_bf16(k_new), _bf16(v_new), _idx(loc), loc.shape[0], _fp8_pool(k_pool),
+                                   _fp8_pool(v_pool), S, Hkv, D, float(k_scale), float(v_scale),
+                                   _stream(stream)),
+           "rax_kv_store_fp8")
+
+
+def decode_attention_fp8(q, o, k_pool, v_pool, req_to_token, req_pool_indices, seq_lens, max_seq_len, sm_scale,
+                         k_scale=1.0, v_scale=1.0, workspace=None, stream=None):
+    """DECODE attention over FP8 E4M3 pools (bf16 ``q`` and ``o``)."""
+    B, Hq, D = q.shape
+    S, Hkv, Dk = k_pool.shape
+    need = decode_workspace_bytes(FP8_E4M3, B, int(max_seq_len), Hq, Hkv, D)
+    workspace = _workspace(need, workspace, q.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().rax_decode_attention_fp8(_bf16(q), _bf16(o), _fp8_pool(k_pool), _fp8_pool(v_pool), S,
+                                           _idx(req_to_token), req_to_token.shape[1], _idx(req_pool_indices),
+                                           _idx(seq_lens), B, int(max_seq_len), Hq, Hkv, D, float(sm_scale),
+                                           float(k_scale), float(v_scale), _ptr(workspace), wbytes,
+                                           _stream(stream)),
+           "rax_decode_attention_fp8")

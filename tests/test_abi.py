@@ -22,7 +22,7 @@ def test_every_declared_symbol_is_exported():
     names = R.declared_symbols()
     assert set(names) == {"rax_version", "rax_status_str", "rax_kv_store", "rax_extend_workspace_bytes",
                           "rax_extend_attention", "rax_decode_workspace_bytes", "rax_decode_attention",
-                          "rax_decode_num_splits"}
+                          "rax_decode_num_splits", "rax_kv_store_fp8", "rax_decode_attention_fp8"}
     out = subprocess.run(["nm", "-D", "--defined-only", R.library_path()], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for n in names:
@@ -124,3 +124,26 @@ def test_decode_workspace_size():
         assert lib().rax_decode_workspace_bytes(0, B, L, hq, hkv, 128) == want
     assert lib().rax_decode_workspace_bytes(1, 64, 4096, 32, 8, 128) == 0   # fp32 path needs none
     assert lib().rax_extend_workspace_bytes(0, 1, 2048, 2048, 16384, 32, 8, 128) == 0
+
+
+def test_fp8_calls_check_scales_and_shapes_before_launching():
+    L = lib()
+    # kv_store_fp8(k_new, v_new, loc, n_new, k_pool, v_pool, num_slots, Hkv, D, k_scale, v_scale, stream)
+    st = lambda **kw: L.rax_kv_store_fp8(kw.get("k", FAKE), FAKE, FAKE, kw.get("n", 4), FAKE, FAKE,
+                                         kw.get("S", 100), 2, kw.get("D", 128), kw.get("ks", 1.0),
+                                         kw.get("vs", 1.0), None)
+    assert st(n=0) == 0
+    assert st(ks=0.0) == 2 and st(vs=-1.0) == 2 and st(ks=float("nan")) == 2 and st(vs=float("inf")) == 2
+    assert st(D=96) == 4
+    assert st(n=200) == 2
+    assert st(k=None) == 1
+    # decode_attention_fp8(q, o, kp, vp, S, r2t, stride, rpi, seq, B, L, Hq, Hkv, D, sm, ks, vs, ws, wsb, stream)
+    need = L.rax_decode_workspace_bytes(2, 3, 300, 8, 2, 128)
+    assert need == L.rax_decode_workspace_bytes(0, 3, 300, 8, 2, 128)
+    dec = lambda **kw: L.rax_decode_attention_fp8(FAKE, FAKE, FAKE, FAKE, 1000, FAKE, 512, FAKE, FAKE,
+                                                  kw.get("B", 3), 300, 8, 2, 128, 0.1, kw.get("ks", 1.0),
+                                                  kw.get("vs", 1.0), kw.get("ws", FAKE), kw.get("wsb", need),
+                                                  None)
+    assert dec(ks=0.0) == 2 and dec(vs=float("nan")) == 2
+    assert dec(B=0) == 0
+    assert dec(ws=None, wsb=0) == 5

@@ -1,0 +1,115 @@
+"""FP8 E4M3 KV pools on the GPU against the float64 oracle.
+
+The store is compared byte for byte with ``oracle.kv_store_fp8``. For attention, the cached
+prefix/context rows are encoded by the oracle (as if an earlier step had stored them), the
+step's new rows go through the GPU store, and the GPU attention over the FP8 pools is compared
+with the oracle's attention over the same bytes and scales. Slots no request names hold the
+E4M3 NaN byte, so a read of a wrong slot poisons the output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from prefix_cached_paged_amd import rax as R
+from prefix_cached_paged_amd import workloads as W
+from prefix_cached_paged_amd.device import to_dev, to_host_bits
+
+from parity import assert_close, say
+
+pytestmark = pytest.mark.gpu
+
+NAN8 = 0x7F
+
+
+def test_store_matches_oracle_bytes():
+    rng = np.random.default_rng(701)
+    S, H, D, n = 5000, 8, 128, 777
+    for k_scale, v_scale in [(1.0, 1.0), (0.02, 0.05), (3.0, 0.7), (2.0 ** -6, 2.0 ** 5)]:
+        x = np.concatenate([rng.normal(0, 1, n * H * D // 2), rng.normal(0, 300, n * H * D // 4),
+                            rng.normal(0, 1e-3, n * H * D // 4)]).astype(np.float32)
+        rng.shuffle(x)
+        kn = (x.view(np.uint32) >> 16).astype(np.uint16).reshape(n, H, D)   # truncation: any bf16
+        vn = kn[::-1].copy()
+        kp = rng.integers(0, 256, (S, H, D), dtype=np.uint8)
+        vp = rng.integers(0, 256, (S, H, D), dtype=np.uint8)
+        loc = rng.permutation(S)[:n].astype(np.int32)
+        ref_k, ref_v = oracle.kv_store_fp8(kp, vp, kn, vn, loc, k_scale, v_scale)
+        dk, dv = to_dev(kp), to_dev(vp)
+        R.kv_store_fp8(to_dev(kn), to_dev(vn), to_dev(loc), dk, dv, k_scale, v_scale)
+        torch.cuda.synchronize()
+        assert np.array_equal(dk.cpu().numpy(), ref_k), f"K bytes differ at scale {k_scale}"
+        assert np.array_equal(dv.cpu().numpy(), ref_v), f"V bytes differ at scale {v_scale}"
+
+
+def fp8_pools(wl, k_scale, v_scale):
+    """Pools with every row a request reads (except the step's new rows) encoded by the oracle,
+    and the NaN byte elsewhere."""
+    S = wl.k_pool.shape[0]
+    kp = np.full(wl.k_pool.shape, NAN8, np.uint8)
+    vp = np.full(wl.v_pool.shape, NAN8, np.uint8)
+    reads = []
+    if wl.decode is not None:
+        reads += list(zip(wl.decode.req_pool_indices, wl.decode.seq_lens))
+    if wl.extend is not None:
+        reads += list(zip(wl.extend.req_pool_indices, wl.extend.prefix_lens + wl.extend.extend_lens))
+    used = np.unique(np.concatenate([wl.req_to_token[int(r), :int(L)] for r, L in reads]).astype(np.int64))
+    rows = np.setdiff1d(used, np.asarray(wl.store_loc, np.int64))
+    assert rows.size == 0 or rows.max() < S
+    kp[rows] = oracle.quantize_bf16(wl.k_pool[rows], k_scale)
+    vp[rows] = oracle.quantize_bf16(wl.v_pool[rows], v_scale)
+    return kp, vp
+
+
+def run_decode_fp8(wl, k_scale, v_scale):
+    kp, vp = fp8_pools(wl, k_scale, v_scale)
+    dk, dv = to_dev(kp), to_dev(vp)
+    R.kv_store_fp8(to_dev(wl.k_new), to_dev(wl.v_new), to_dev(wl.store_loc), dk, dv, k_scale, v_scale)
+    d = wl.decode
+    q = to_dev(d.q)
+    o = torch.empty_like(q)
+    R.decode_attention_fp8(q, o, dk, dv, to_dev(wl.req_to_token), to_dev(d.req_pool_indices),
+                           to_dev(d.seq_lens), d.max_seq_len, wl.sm_scale, k_scale, v_scale)
+    torch.cuda.synchronize()
+    ref_k, ref_v = oracle.kv_store_fp8(kp, vp, wl.k_new, wl.v_new, wl.store_loc, k_scale, v_scale)
+    ref = oracle.decode_attention(d.q, ref_k, ref_v, wl.req_to_token, d.req_pool_indices, d.seq_lens,
+                                  wl.spec.n_kv_heads, wl.sm_scale, k_scale=k_scale, v_scale=v_scale)
+    return oracle.to_f64(to_host_bits(o)), ref
+
+
+# Sized so that the rows each case encodes on the host stay within a few million elements.
+SPECS = [
+    W.Spec("fp8-dec-g4", "bf16", 32, 8, 128, 60000, decode_lens=(1, 2, 63, 64, 65, 257, 1000, 2500)),
+    W.Spec("fp8-dec-g1", "bf16", 8, 8, 128, 60000, decode_lens=(1, 130, 3000)),
+    W.Spec("fp8-dec-g8", "bf16", 64, 8, 128, 60000, decode_lens=(5, 513, 4000)),
+    W.Spec("fp8-dec-g16", "bf16", 16, 1, 128, 60000, decode_lens=(77, 4096, 12345)),
+    W.Spec("fp8-dec-d64", "bf16", 16, 4, 64, 60000, decode_lens=(1, 64, 999, 5000)),
+    W.Spec("fp8-dec-many", "bf16", 32, 8, 128, 60000, decode_batch=64, decode_range=(1, 120)),
+    W.Spec("fp8-dec-long", "bf16", 8, 1, 128, 120000, decode_lens=(50000, 3)),
+]
+# scales that put about 4 standard deviations at the top of the E4M3 range, and the default 1.0
+CASES = [("normal", "range"), ("normal", "one"), ("peaked", "range"), ("needle", "range")]
+
+
+@pytest.mark.parametrize("variant,scales", CASES)
+@pytest.mark.parametrize("spec", SPECS, ids=lambda s: s.name)
+def test_decode_fp8(spec, variant, scales):
+    wl = W.make_workload(spec, 702, variant)
+    if scales == "one":
+        k_scale = v_scale = 1.0
+    else:
+        k_scale = v_scale = 4 * spec.sigma / 448
+        if variant == "needle":
+            k_scale = 16.0 / 448  # the needle key is 12 sigma: keep it inside the range
+    say(f"{spec.name}/{variant}: scales {k_scale:.4g} {v_scale:.4g}")
+    got, ref = run_decode_fp8(wl, k_scale, v_scale)
+    assert_close(got, ref, "bf16", f"{spec.name}/{variant} fp8 decode")
+
+
+def test_decode_fp8_single_key_is_v_times_scale():
+    """One key: the output is v_scale * e4m3(V), the bf16 rounding of that product."""
+    spec = W.Spec("fp8-one", "bf16", 32, 8, 128, 1000, decode_lens=(1, 1, 1))
+    wl = W.make_workload(spec, 703)
+    got, ref = run_decode_fp8(wl, 0.5, 0.25)       # power-of-two scales: products exact in bf16
+    assert np.array_equal(got, ref)

@@ -64,6 +64,29 @@ def test_ties_go_to_the_even_code_and_neighbours_to_the_nearest():
     assert np.array_equal(oracle.e4m3_round(down), codes)
 
 
+def nearest_by_search(x):
+    """Brute force: the E4M3 value nearest to each x (ties to the even code), by comparing with
+    every finite code's value."""
+    v = oracle.e4m3_bits_to_f64(np.arange(127, dtype=np.uint8))
+    a = np.abs(np.asarray(x, np.float64))[:, None]
+    d = np.abs(v[None, :] - a)
+    best = d.min(axis=1, keepdims=True)
+    cand = np.where(d == best, np.arange(127)[None, :], 10 ** 6)
+    even = np.where((cand % 2 == 0) & (cand < 10 ** 6), cand, 10 ** 6).min(axis=1)
+    code = np.where(even < 10 ** 6, even, cand.min(axis=1))
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def test_rounding_matches_a_brute_force_nearest_search():
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.uniform(-448, 448, 4000), rng.normal(0, 0.02, 4000), rng.normal(0, 3, 4000),
+                        rng.uniform(-2.0 ** -5, 2.0 ** -5, 4000)])
+    v = oracle.e4m3_bits_to_f64(np.arange(127, dtype=np.uint8))
+    mids = 0.5 * (v[:-1] + v[1:])
+    x = np.concatenate([x, mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9)])
+    assert np.array_equal(oracle.e4m3_round(x), nearest_by_search(x))
+
+
 def test_encode_matches_torch_in_range():
     rng = np.random.default_rng(7)
     x = np.concatenate([rng.normal(0, 1, 20000), rng.normal(0, 100, 20000), rng.uniform(-448, 448, 20000),
