@@ -55,6 +55,9 @@ namespace {
 #ifndef RAX_DEC_NT
 #define RAX_DEC_NT 1
 #endif
+#ifndef RAX_DEC_KPI8
+#define RAX_DEC_KPI8 128  // keys per iteration with FP8 pools (64 or 128)
+#endif
 constexpr int kDecWaves = RAX_DEC_WAVES;  // waves (kv heads) per workgroup
 constexpr int kDecKeysPerIter = 64;
 constexpr int kDecMaxKeys = 4096;  // keys per workgroup range at most (its slots sit in LDS)
@@ -94,9 +97,21 @@ __device__ __forceinline__ uint2 widen4(uint2 x) { return x; }
 
 // Element types of one K MFMA step (8 head_dim elements) and of a lane's V row piece (DT
 // elements), for bf16 or FP8 pools.
+// The score contraction runs over head_dim in any order, provided K and Q use the same one.
+// With FP8 pools a lane loads 16 contiguous bytes of a K row (two MFMA steps): MFMA step s of
+// lane group kg then covers head_dim 16 kg + 64 (s / 2) + 8 (s % 2) .. +8, and the Q operand is
+// loaded in that order (bf16 pools: 8 kg + 32 s, one step per 16-byte load).
+template <bool KV8>
+__device__ __forceinline__ int k_step_elem(int s, int kg) {
+    return KV8 ? 16 * kg + 64 * (s >> 1) + 8 * (s & 1) : 8 * kg + 32 * s;
+}
+__device__ __forceinline__ uint4 k_half(uint4 x, int hi) {  // bf16x8 of 8 E4M3 bytes
+    return widen8(hi ? make_uint2(x.z, x.w) : make_uint2(x.x, x.y));
+}
+
 template <int D, bool KV8>
 struct DecElems {
-    using K = typename std::conditional<KV8, uint2, uint4>::type;
+    using K = uint4;  // one 16-byte load of a K row: 8 bf16 or 16 E4M3 elements
     using V = typename std::conditional<KV8, typename std::conditional<D == 128, uint2, uint32_t>::type,
                                         VRow<D>>::type;
     static constexpr int bytes = KV8 ? 1 : 2;
@@ -211,7 +226,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
     float* __restrict__ lse_part) {
     constexpr int S = D / 32;   // 32-wide K-dim steps of the score MFMA
     constexpr int DT = D / 16;  // 16-row output tiles; also head_dim elements per lane per V row
-    __shared__ int32_t slot_lds[kDecMaxKeys];
+    __shared__ int32_t slot_lds[kDecMaxKeys + kDecKeysPerIter];
     __shared__ Seg segs[kDecMaxSegs];
     __shared__ int32_t n_seg_lds;
 
@@ -316,7 +331,9 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
         const Seg sg = segs[si];
         const int32_t* row = r2t + (int64_t)sg.rpi * r2t_stride;
         const int j0 = sg.lo / kDecKeysPerIter;
-        const int nb = sg.n / kDecKeysPerIter;
+        // With 128-key iterations (FP8 pools) the last one may run 64 keys past the range:
+        // stage one more block of slots there (positions clamped to the request, then masked).
+        const int nb = sg.n / kDecKeysPerIter + ((KV8 && RAX_DEC_KPI8 > 64 && si == n_seg - 1) ? 1 : 0);
         for (int j = (wv - j0 % kDecWaves + kDecWaves) % kDecWaves; j < nb; j += kDecWaves)
             __builtin_amdgcn_global_load_lds(
                 (__attribute__((address_space(1))) void*)(
@@ -332,11 +349,17 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
     const int n16 = lane & 15;
     const int kg = lane >> 4;
     using EL = DecElems<D, KV8>;
+    // Keys per iteration: 64, or 128 with FP8 pools so that a wave keeps as many bytes in
+    // flight as with bf16 (the bytes per key halve). TT 16-key score tiles, UU 32-key P V steps.
+    constexpr int KPI = KV8 ? RAX_DEC_KPI8 : 64;
+    constexpr int TT = KPI / 16;
+    constexpr int UU = KPI / 32;
     constexpr uint32_t es = EL::bytes;  // bytes per stored element
     const uint32_t row_bytes = (uint32_t)Hkv * D * es;
     const char* kbase = (const char*)k_pool + (int64_t)g * D * es;  // wave-uniform
     const char* vbase = (const char*)v_pool + (int64_t)g * D * es;
-    const uint32_t k_off = 8u * es * kg;    // this lane's 8 head_dim elements of a K row
+    const uint32_t k_off = 16u * kg;        // this lane's first 16 bytes of a K row
+    constexpr int KL = KV8 ? S / 2 : S;     // 16-byte K loads per key
     const uint32_t v_off = es * DT * n16;   // this lane's DT head_dim elements of a V row
     // Columns n16 >= G are padding: they load a valid head and zero it with a mask (no branch,
     // so the loads stay in flight together).
@@ -348,21 +371,21 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
     // consumed this iteration's, so one iteration of K and V is always in flight. The steady
     // loop is branch-free (the last iteration is peeled), which keeps the memory-counter waits
     // exact: each wait covers only the rows about to be used.
-    typename EL::K kr[4][S];
-    typename EL::V vr[2][8];
+    uint4 kr[TT][KL];
+    typename EL::V vr[UU][8];
 #define RAX_DEC_SLOTS_K(IT, SK)                                                              \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t) SK[t] =                                    \
-        slot_lds[lo + (IT) * kDecKeysPerIter + 16 * t + n16];
+    _Pragma("unroll") for (int t = 0; t < TT; ++t) SK[t] =                                   \
+        slot_lds[lo + (IT) * KPI + 16 * t + n16];
 #define RAX_DEC_LOAD_K(SK)                                                                   \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                            \
-    _Pragma("unroll") for (int s = 0; s < S; ++s)                                            \
-        kr[t][s] = row_load<OFF32, typename EL::K>(kbase, SK[t], row_bytes, k_off + 32u * es * s);
+    _Pragma("unroll") for (int t = 0; t < TT; ++t)                                           \
+    _Pragma("unroll") for (int s = 0; s < KL; ++s)                                           \
+        kr[t][s] = row_load<OFF32, uint4>(kbase, SK[t], row_bytes, k_off + 64u * s);
     // V keys of lane (n16, kg) in block u: 32u + 16h + 4kg + e for h, e in {0,1} x {0..3}.
 #define RAX_DEC_LOAD_V(IT)                                                                   \
-    _Pragma("unroll") for (int u = 0; u < 2; ++u)                                            \
+    _Pragma("unroll") for (int u = 0; u < UU; ++u)                                           \
     _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                          \
         const int4 sv_ =                                                                     \
-            *(const int4*)&slot_lds[lo + (IT) * kDecKeysPerIter + 32 * u + 16 * h + 4 * kg]; \
+            *(const int4*)&slot_lds[lo + (IT) * KPI + 32 * u + 16 * h + 4 * kg];             \
         vr[u][4 * h + 0] = row_load<OFF32, typename EL::V>(vbase, sv_.x, row_bytes, v_off); \
         vr[u][4 * h + 1] = row_load<OFF32, typename EL::V>(vbase, sv_.y, row_bytes, v_off); \
         vr[u][4 * h + 2] = row_load<OFF32, typename EL::V>(vbase, sv_.z, row_bytes, v_off); \
@@ -370,22 +393,23 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
     }
 #define RAX_DEC_ITER(IT, MORE)                                                               \
     {                                                                                        \
-        int sk_[4];                                                                          \
+        int sk_[TT];                                                                         \
         if (MORE) { RAX_DEC_SLOTS_K((IT) + 1, sk_) }                                         \
         /* S^T[key][head]: lane holds keys 16t + 4kg + i of head n16. */                     \
-        f32x4 st[4];                                                                         \
-        _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                      \
+        f32x4 st[TT];                                                                        \
+        _Pragma("unroll") for (int t = 0; t < TT; ++t) {                                     \
             st[t] = f32x4{0.f, 0.f, 0.f, 0.f};                                               \
             _Pragma("unroll") for (int s = 0; s < S; ++s)                                    \
-                st[t] = mfma16x16x32(as_bf16x8(widen8(kr[t][s])), qop[s], st[t]);            \
+                st[t] = mfma16x16x32(                                                        \
+                    as_bf16x8(KV8 ? k_half(kr[t][s >> 1], s & 1) : kr[t][s]), qop[s], st[t]);  \
         }                                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                   \
         if (MORE) { RAX_DEC_LOAD_K(sk_) }                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                   \
         float mx = -INFINITY;                                                                \
-        _Pragma("unroll") for (int t = 0; t < 4; ++t)                                        \
+        _Pragma("unroll") for (int t = 0; t < TT; ++t)                                       \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
-            if (!(MORE) && (IT) * kDecKeysPerIter + 16 * t + 4 * kg + i >= n_valid)          \
+            if (!(MORE) && (IT) * KPI + 16 * t + 4 * kg + i >= n_valid)                      \
                 st[t][i] = -INFINITY;                                                        \
             mx = fmaxf(mx, st[t][i]);                                                        \
         }                                                                                    \
@@ -396,14 +420,14 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
         m = m_new;                                                                           \
         lsum *= alpha;                                                                       \
         _Pragma("unroll") for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;                  \
-        float p[4][4];                                                                       \
-        _Pragma("unroll") for (int t = 0; t < 4; ++t)                                        \
+        float p[TT][4];                                                                      \
+        _Pragma("unroll") for (int t = 0; t < TT; ++t)                                       \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
             p[t][i] = fast_exp2(fmaf(st[t][i], scale_log2, -m));                             \
             lsum += p[t][i];                                                                 \
         }                                                                                    \
         /* O^T[d][head] += V^T[d][key] P^T[key][head] per 32-key block. */                   \
-        _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                      \
+        _Pragma("unroll") for (int u = 0; u < UU; ++u) {                                     \
             uint4 pb;                                                                        \
             pb.x = pack_bf16x2(p[2 * u][0], p[2 * u][1]);                                    \
             pb.y = pack_bf16x2(p[2 * u][2], p[2 * u][3]);                                    \
@@ -430,26 +454,27 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
     for (int si = 0; si < n_seg; ++si) {
         const int b = __builtin_amdgcn_readfirstlane(segs[si].b);
         const int lo = __builtin_amdgcn_readfirstlane(segs[si].lo);
-        const int n_it = __builtin_amdgcn_readfirstlane(segs[si].n) / kDecKeysPerIter;
-        // Valid keys of this overlap (at least one: every iteration block of a request's
-        // padded range starts before its end).
-        const int n_valid = __builtin_amdgcn_readfirstlane(segs[si].len) -
-                            __builtin_amdgcn_readfirstlane(segs[si].pos0);
+        const int n_seg_keys = __builtin_amdgcn_readfirstlane(segs[si].n);
+        const int n_it = (n_seg_keys + KPI - 1) / KPI;
+        // Keys of this overlap that count: those of the request (at least one: every 64-key
+        // block of a request's padded range starts before its end) and inside the overlap.
+        const int n_valid = min(__builtin_amdgcn_readfirstlane(segs[si].len) -
+                                    __builtin_amdgcn_readfirstlane(segs[si].pos0),
+                                n_seg_keys);
 
-        // B operand of S^T = K Q^T: lane holds Q[head n16][32 s + 8 kg .. +8].
+        // B operand of S^T = K Q^T: lane holds Q[head n16][k_step_elem(s, kg) .. +8].
         bf16x8 qop[S];
         {
-            const uint16_t* qr =
-                q + ((int64_t)b * Hq + (int64_t)g * G + (q_ok ? n16 : 0)) * D + 8 * kg;
+            const uint16_t* qr = q + ((int64_t)b * Hq + (int64_t)g * G + (q_ok ? n16 : 0)) * D;
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                uint4 v = *(const uint4*)(qr + 32 * s);
+                uint4 v = *(const uint4*)(qr + k_step_elem<KV8>(s, kg));
                 v.x &= q_keep; v.y &= q_keep; v.z &= q_keep; v.w &= q_keep;
                 qop[s] = as_bf16x8(v);
             }
         }
         {
-            int sk0[4];
+            int sk0[TT];
             RAX_DEC_SLOTS_K(0, sk0)
             RAX_DEC_LOAD_K(sk0)
         }
