@@ -192,6 +192,12 @@ int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, 
  *   computed in double and rounded once to float. Inputs must be finite (NaN inputs give an
  *   undefined byte). Same loc contract as rax_kv_store.
  *
+ * rax_extend_attention_fp8 -- rax_extend_attention over FP8 pools (head_dim 128, the same
+ *   group sizes as bf16): the scores use k_scale * e4m3(K) and the values v_scale * e4m3(V).
+ *   The kernel stages the E4M3 tiles in LDS, widens them to bf16 (exact) and applies k_scale to
+ *   the scores and v_scale to the output. Workspace: rax_extend_workspace_bytes(RAX_FP8_E4M3,
+ *   ...) (0 bytes: NULL is accepted).
+ *
  * rax_decode_attention_fp8 -- rax_decode_attention over FP8 pools: the scores use
  *   k_scale * e4m3(K) and the values v_scale * e4m3(V). Every E4M3 value is exactly a bf16
  *   value, so the kernel widens the bytes in registers and applies k_scale to the scores and
@@ -200,6 +206,15 @@ int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, 
 int rax_kv_store_fp8(const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
                      void* k_pool, void* v_pool, int64_t num_slots, int32_t n_kv_heads,
                      int32_t head_dim, float k_scale, float v_scale, void* stream);
+
+int rax_extend_attention_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
+                             int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                             const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                             const int32_t* extend_lens, const int32_t* extend_start_loc,
+                             int32_t batch, int64_t total_extend_tokens, int32_t max_extend_len,
+                             int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                             int32_t head_dim, float sm_scale, float k_scale, float v_scale,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 int rax_decode_attention_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
                              int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,

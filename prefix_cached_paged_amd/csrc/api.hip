@@ -60,44 +60,6 @@ size_t rax_extend_workspace_bytes(int dtype, int32_t batch, int64_t total_extend
     return 0;
 }
 
-int rax_extend_attention(int dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
-                         int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
-                         const int32_t* req_pool_indices, const int32_t* prefix_lens,
-                         const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
-                         int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
-                         int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float sm_scale,
-                         void* workspace, size_t workspace_bytes, void* stream) {
-    if (!dtype_ok(dtype)) return RAX_ERR_DTYPE;
-    if (batch < 0 || batch > kMaxGridYZ || total_extend_tokens < 0 || max_extend_len < 0 ||
-        max_seq_len < 0 || num_slots <= 0 || r2t_stride <= 0 || max_seq_len > r2t_stride ||
-        max_extend_len > max_seq_len || max_extend_len > total_extend_tokens)
-        return RAX_ERR_SHAPE;
-    int st = check_heads(n_q_heads, n_kv_heads, head_dim);
-    if (st != RAX_OK) return st;
-    const int32_t G = n_q_heads / n_kv_heads;
-    if (dtype == RAX_BF16 && !rax::extend_bf16_supported(G, head_dim)) return RAX_ERR_UNSUPPORTED;
-    if (!(sm_scale == sm_scale)) return RAX_ERR_SHAPE;
-    if (batch == 0 || total_extend_tokens == 0 || max_extend_len == 0) return RAX_OK;
-    if (!q || !o || !k_pool || !v_pool || !req_to_token || !req_pool_indices || !prefix_lens ||
-        !extend_lens || !extend_start_loc)
-        return RAX_ERR_NULL;
-    const size_t need = rax_extend_workspace_bytes(dtype, batch, total_extend_tokens, max_extend_len,
-                                                   max_seq_len, n_q_heads, n_kv_heads, head_dim);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return RAX_ERR_WORKSPACE;
-
-    rax::AttnArgs a{};
-    a.q = q; a.o = o; a.k_pool = k_pool; a.v_pool = v_pool; a.num_slots = num_slots;
-    a.r2t = req_to_token; a.r2t_stride = r2t_stride; a.req_pool_indices = req_pool_indices;
-    a.prefix_lens = prefix_lens; a.extend_lens = extend_lens; a.extend_start_loc = extend_start_loc;
-    a.total_tokens = total_extend_tokens; a.max_extend_len = max_extend_len;
-    a.seq_lens = nullptr; a.batch = batch; a.max_seq_len = max_seq_len;
-    a.n_q_heads = n_q_heads; a.n_kv_heads = n_kv_heads; a.head_dim = head_dim; a.sm_scale = sm_scale;
-    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-    const int rc = dtype == RAX_BF16 ? rax::launch_extend_bf16(a, (hipStream_t)stream)
-                                     : rax::launch_extend_fp32(a, (hipStream_t)stream);
-    return rc == 0 ? RAX_OK : RAX_ERR_LAUNCH;
-}
-
 size_t rax_decode_workspace_bytes(int dtype, int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
                                   int32_t n_kv_heads, int32_t head_dim) {
     if ((dtype != RAX_BF16 && dtype != RAX_FP8_E4M3) || batch <= 0 || max_seq_len <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 ||
@@ -115,6 +77,48 @@ int32_t rax_decode_num_splits(int dtype, int32_t batch, int32_t max_seq_len, int
 }  // extern "C"
 
 namespace {
+
+// Checks and launch shared by the bf16/fp32 and FP8-pool EXTEND entry points.
+int extend_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool, const void* v_pool,
+                int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
+                int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
+                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float sm_scale,
+                float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    if (!dtype_ok(dtype)) return RAX_ERR_DTYPE;
+    if (batch < 0 || batch > kMaxGridYZ || total_extend_tokens < 0 || max_extend_len < 0 ||
+        max_seq_len < 0 || num_slots <= 0 || r2t_stride <= 0 || max_seq_len > r2t_stride ||
+        max_extend_len > max_seq_len || max_extend_len > total_extend_tokens)
+        return RAX_ERR_SHAPE;
+    int st = check_heads(n_q_heads, n_kv_heads, head_dim);
+    if (st != RAX_OK) return st;
+    const int32_t G = n_q_heads / n_kv_heads;
+    if (dtype == RAX_BF16 && !rax::extend_bf16_supported(G, head_dim)) return RAX_ERR_UNSUPPORTED;
+    if (!(sm_scale == sm_scale)) return RAX_ERR_SHAPE;
+    if (kv8 && (!scale_ok(k_scale) || !scale_ok(v_scale))) return RAX_ERR_SHAPE;
+    if (batch == 0 || total_extend_tokens == 0 || max_extend_len == 0) return RAX_OK;
+    if (!q || !o || !k_pool || !v_pool || !req_to_token || !req_pool_indices || !prefix_lens ||
+        !extend_lens || !extend_start_loc)
+        return RAX_ERR_NULL;
+    const size_t need = rax_extend_workspace_bytes(dtype, batch, total_extend_tokens, max_extend_len,
+                                                   max_seq_len, n_q_heads, n_kv_heads, head_dim);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return RAX_ERR_WORKSPACE;
+
+    rax::AttnArgs a{};
+    a.q = q; a.o = o; a.k_pool = k_pool; a.v_pool = v_pool; a.num_slots = num_slots;
+    a.r2t = req_to_token; a.r2t_stride = r2t_stride; a.req_pool_indices = req_pool_indices;
+    a.prefix_lens = prefix_lens; a.extend_lens = extend_lens; a.extend_start_loc = extend_start_loc;
+    a.total_tokens = total_extend_tokens; a.max_extend_len = max_extend_len;
+    a.seq_lens = nullptr; a.batch = batch; a.max_seq_len = max_seq_len;
+    a.n_q_heads = n_q_heads; a.n_kv_heads = n_kv_heads; a.head_dim = head_dim; a.sm_scale = sm_scale;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.kv8 = kv8; a.k_scale = k_scale; a.v_scale = v_scale;
+    const int rc = dtype == RAX_BF16 ? rax::launch_extend_bf16(a, (hipStream_t)stream)
+                                     : rax::launch_extend_fp32(a, (hipStream_t)stream);
+    return rc == 0 ? RAX_OK : RAX_ERR_LAUNCH;
+}
 
 // Checks and launch shared by the bf16/fp32 and FP8-pool DECODE entry points.
 int decode_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool, const void* v_pool,
@@ -196,6 +200,33 @@ int rax_decode_attention_fp8(const void* q, void* o, const void* k_pool, const v
     return decode_call(RAX_BF16, true, q, o, k_pool, v_pool, num_slots, req_to_token, r2t_stride,
                        req_pool_indices, seq_lens, batch, max_seq_len, n_q_heads, n_kv_heads, head_dim,
                        sm_scale, k_scale, v_scale, workspace, workspace_bytes, stream);
+}
+
+int rax_extend_attention(int dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
+                         int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                         const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                         const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
+                         int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
+                         int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float sm_scale,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    return extend_call(dtype, false, q, o, k_pool, v_pool, num_slots, req_to_token, r2t_stride,
+                       req_pool_indices, prefix_lens, extend_lens, extend_start_loc, batch,
+                       total_extend_tokens, max_extend_len, max_seq_len, n_q_heads, n_kv_heads,
+                       head_dim, sm_scale, 1.f, 1.f, workspace, workspace_bytes, stream);
+}
+
+int rax_extend_attention_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
+                             int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                             const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                             const int32_t* extend_lens, const int32_t* extend_start_loc,
+                             int32_t batch, int64_t total_extend_tokens, int32_t max_extend_len,
+                             int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                             int32_t head_dim, float sm_scale, float k_scale, float v_scale,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    return extend_call(RAX_BF16, true, q, o, k_pool, v_pool, num_slots, req_to_token, r2t_stride,
+                       req_pool_indices, prefix_lens, extend_lens, extend_start_loc, batch,
+                       total_extend_tokens, max_extend_len, max_seq_len, n_q_heads, n_kv_heads,
+                       head_dim, sm_scale, k_scale, v_scale, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -77,18 +77,9 @@ __device__ __forceinline__ uint4 vcol(const VRow<D> (&r)[8]) {
 }
 
 // FP8 E4M3 pools ("Inside SGLang", Step 6): 8 (or 4) bytes per K step or V row piece, widened
-// to bf16 in registers right before the MFMA. Every E4M3 value is exactly a bf16 value, so
-// the widening (through float32) rounds nothing; the pool scales are applied to the scores
-// (K) and to the output (V) instead of to every element.
-template <bool HI>
-__device__ __forceinline__ uint32_t bf16x2_of_e4m3(uint32_t w) {
-    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-    return pack_bf16x2(f[0], f[1]);
-}
-__device__ __forceinline__ uint4 widen8(uint2 x) {
-    return make_uint4(bf16x2_of_e4m3<false>(x.x), bf16x2_of_e4m3<true>(x.x),
-                      bf16x2_of_e4m3<false>(x.y), bf16x2_of_e4m3<true>(x.y));
-}
+// to bf16 in registers right before the MFMA (widen8 of 8 bytes is in rax_device.h). The pool
+// scales are applied to the scores (K) and to the output (V) instead of to every element.
+using ::rax::widen8;
 __device__ __forceinline__ uint4 widen8(uint4 x) { return x; }  // bf16 pools: as stored
 __device__ __forceinline__ uint2 widen4(uint32_t x) {
     return make_uint2(bf16x2_of_e4m3<false>(x), bf16x2_of_e4m3<true>(x));

@@ -116,22 +116,29 @@ __device__ __forceinline__ const char* pool_row_ptr(const char* base, int slot, 
 // Workgroup barrier that the compiler may not move memory accesses across. Copies into LDS
 // are ordered by the explicit vmcnt wait before it, reads by the operand waits of the MFMAs.
 #define RAX_BARRIER() asm volatile("s_barrier" ::: "memory")
+// s_waitcnt lgkmcnt(0) alone: this wave's LDS writes have completed (before a barrier after
+// which other waves read them).
+#define RAX_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
-template <int G, bool OFF32>
+template <int G, bool OFF32, bool KV8>
 __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
-    const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ k_pool,
-    const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const char* __restrict__ k_pool,
+    const char* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
     const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ extend_start_loc,
     int64_t total_tokens, int32_t max_extend_len, int32_t max_seq_len, int32_t Hq, int32_t Hkv,
-    int32_t batch, int32_t tiles, float scale_log2) {
+    int32_t batch, int32_t tiles, float scale_log2, float out_scale) {
     constexpr int D = kExtD;
     constexpr int BQ = kExtBM / G;  // tokens per workgroup
+    constexpr int EB = KV8 ? 1 : 2;  // bytes per pool element
 
     // Three K/V tile buffers, row-major [key][16 units of 8 bf16], swizzled. Separate LDS
     // objects, each named statically below.
     __shared__ uint4 kb0[kExtBN * 16], kb1[kExtBN * 16], kb2[kExtBN * 16];
     __shared__ uint4 vb0[kExtBN * 16], vb1[kExtBN * 16], vb2[kExtBN * 16];
+    // FP8 pools: three staging buffers of raw E4M3 tiles, [key][8 units of 16 bytes].
+    constexpr int SU = KV8 ? kExtBN * 8 : 1;
+    __shared__ uint4 sk0[SU], sk1[SU], sk2[SU], sv0[SU], sv1[SU], sv2[SU];
 
     // ---- workgroup -> (pair = b * Hkv + g, tile), XCD-aware
     const int pairs = batch * Hkv;
@@ -152,9 +159,9 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const int t_last = min(t0 + BQ, e) - 1;
     const int kend = min(p + t_last + 1, max_seq_len);  // keys 0 .. kend-1 are visible to someone
     const int32_t* row = r2t + (int64_t)rpi[b] * r2t_stride;
-    const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
-    const char* kbase = (const char*)k_pool + (int64_t)g * D * 2;
-    const char* vbase = (const char*)v_pool + (int64_t)g * D * 2;
+    const uint32_t row_bytes = (uint32_t)Hkv * D * EB;
+    const char* kbase = k_pool + (int64_t)g * D * EB;
+    const char* vbase = v_pool + (int64_t)g * D * EB;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -209,6 +216,35 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         lds_dma16(pool_row_ptr<OFF32>(vbase, sl0_, row_bytes, v_src), vd_);                 \
         lds_dma16(pool_row_ptr<OFF32>(vbase, sl1_, row_bytes, v_src), vd_ + 1024);          \
     }
+    // FP8 pools: a 64-key tile is 8 KB per operand, so one copy instruction per wave moves
+    // its eight rows: lane l fetches 16 bytes at offset 16 (l % 8) of row 8 w + l / 8 into
+    // staging unit 64 w + l. 2 vector-memory operations per wave per tile.
+    const int q8 = lane >> 3;
+    const uint32_t src8 = 16u * (uint32_t)(lane & 7);
+#define RAX_COPY8(SK, SV)                                                                   \
+    {                                                                                       \
+        int sl_ = nx0;                                                                      \
+        sl_ = q8 == 1 ? nx1 : sl_; sl_ = q8 == 2 ? nx2 : sl_; sl_ = q8 == 3 ? nx3 : sl_;    \
+        sl_ = q8 == 4 ? nx4 : sl_; sl_ = q8 == 5 ? nx5 : sl_; sl_ = q8 == 6 ? nx6 : sl_;    \
+        sl_ = q8 == 7 ? nx7 : sl_;                                                          \
+        lds_dma16(pool_row_ptr<OFF32>(kbase, sl_, row_bytes, src8), (char*)(SK) + wave_u * 1024); \
+        lds_dma16(pool_row_ptr<OFF32>(vbase, sl_, row_bytes, src8), (char*)(SV) + wave_u * 1024); \
+    }
+    // Each lane widens the staging unit it copied (16 E4M3 values = head_dim 16 u .. 16 u + 15
+    // of key 8 w + l / 8) into logical units 2 u and 2 u + 1 of the swizzled bf16 tile. Only
+    // the lane's own copy must have landed (vmcnt); the barrier before the tile's use makes
+    // the bf16 tile visible to the other waves.
+    const int ckey = 8 * wave + q8;
+    const int cu2 = 2 * (lane & 7);
+#define RAX_CONVERT8(SK, SV, KB, VB)                                                        \
+    {                                                                                       \
+        const uint4 k8_ = (SK)[64 * wave + lane];                                           \
+        const uint4 v8_ = (SV)[64 * wave + lane];                                           \
+        (KB)[ckey * 16 + swz_k(ckey, cu2)] = widen8(make_uint2(k8_.x, k8_.y));              \
+        (KB)[ckey * 16 + swz_k(ckey, cu2 + 1)] = widen8(make_uint2(k8_.z, k8_.w));          \
+        (VB)[ckey * 16 + swz_v(ckey, cu2)] = widen8(make_uint2(v8_.x, v8_.y));              \
+        (VB)[ckey * 16 + swz_v(ckey, cu2 + 1)] = widen8(make_uint2(v8_.z, v8_.w));          \
+    }
 
     // ---- per-lane constants of the transposed V reads: 16-lane group gi holds head_dim half
     // dh = gi & 1 and k-group h2; lane i16 = 4 jr + cc reads key offset jr and head_dim
@@ -237,10 +273,8 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // The only vector-memory operations are the copies (4 per tile), issued two tiles ahead:
     // when tile IT is needed the younger ones are the copies of IT+1, so wait until at most 4
     // (0 at the last tile) are outstanding.
-#define RAX_TILE(IT, KB, VB, KN, VN, MASKABLE, STEADY)                                      \
+#define RAX_COMPUTE(IT, KB, VB, MASKABLE)                                                   \
     {                                                                                       \
-        if (STEADY || (IT) + 1 < ntiles) { RAX_WAIT_VMCNT(4); } else { RAX_WAIT_VMCNT(0); } \
-        RAX_BARRIER();                                                                      \
         f32x16 st[2];                                                                       \
         _Pragma("unroll") for (int mb = 0; mb < 2; ++mb) {                                  \
             _Pragma("unroll") for (int i = 0; i < 16; ++i) st[mb][i] = 0.f;                 \
@@ -295,44 +329,99 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
                 acc[dt] = mfma32x32x16(as_bf16x8(av), as_bf16x8(pf[kk]), acc[dt]);          \
             }                                                                               \
         }                                                                                   \
+    }
+#define RAX_TILE(IT, KB, VB, KN, VN, MASKABLE, STEADY)                                      \
+    {                                                                                       \
+        if (STEADY || (IT) + 1 < ntiles) { RAX_WAIT_VMCNT(4); } else { RAX_WAIT_VMCNT(0); } \
+        RAX_BARRIER();                                                                      \
+        RAX_COMPUTE(IT, KB, VB, MASKABLE)                                                   \
         if (STEADY || (IT) + 2 < ntiles) {                                                  \
             RAX_COPY(KN, VN)                                                                \
             if (STEADY || (IT) + 3 < ntiles) RAX_SLOTS((IT) + 3)                            \
         }                                                                                   \
     }
-
-    // prologue: copies of tiles 0 and 1 in flight, slots of tile 2 loaded
-    RAX_SLOTS(0)
-    RAX_COPY(kb0, vb0)
-    if (ntiles > 1) {
-        RAX_SLOTS(1)
-        RAX_COPY(kb1, vb1)
+    // FP8 pools. Tile T is staged (E4M3) in buffer T % 3 and widened into bf16 buffer T % 3.
+    // Iteration IT: barrier (every wave's conversion of tile IT has landed, every wave is done
+    // with tile IT-1); compute tile IT; wait for this wave's copies of tile IT+1 (those of
+    // IT+2 stay in flight) and widen them into (KN, VN), free since tile IT-2; copy tile IT+3
+    // into staging (SN, SVN), whose tile IT this wave widened one iteration ago.
+#define RAX_TILE8(IT, KB, VB, SC, SVC, KN, VN, SN, SVN, MASKABLE, STEADY)                    \
+    {                                                                                       \
+        RAX_WAIT_LGKM0();                                                                   \
+        RAX_BARRIER();                                                                      \
+        RAX_COMPUTE(IT, KB, VB, MASKABLE)                                                   \
+        if (STEADY || (IT) + 1 < ntiles) {                                                  \
+            if (STEADY || (IT) + 2 < ntiles) { RAX_WAIT_VMCNT(2); } else { RAX_WAIT_VMCNT(0); } \
+            RAX_CONVERT8(SC, SVC, KN, VN)                                                   \
+        }                                                                                   \
+        if (STEADY || (IT) + 3 < ntiles) {                                                  \
+            RAX_COPY8(SN, SVN)                                                              \
+            if (STEADY || (IT) + 4 < ntiles) RAX_SLOTS((IT) + 4)                            \
+        }                                                                                   \
     }
-    if (ntiles > 2) RAX_SLOTS(2)
 
-    // Tile T lives in buffer T % 3; iteration T starts the copy of tile T+2 into buffer
-    // (T+2) % 3. Both loops advance three tiles at a time from a multiple of three.
     const int n_full = min(ntiles, (diag_from + 1) / kExtBN);  // tiles with every key <= p + t0
     int it = 0;
-    // Steady state: six or more tiles ahead are full and exist, so the body has no
-    // conditional copies or waits (control-flow joins with different copies in flight make
-    // the compiler add waits of its own).
-    while (it + 6 <= n_full) {
-        RAX_TILE(it, kb0, vb0, kb2, vb2, 0, 1) ++it;
-        RAX_TILE(it, kb1, vb1, kb0, vb0, 0, 1) ++it;
-        RAX_TILE(it, kb2, vb2, kb1, vb1, 0, 1) ++it;
-    }
-    while (it < ntiles) {
-        RAX_TILE(it, kb0, vb0, kb2, vb2, 1, 0) ++it;
-        if (it >= ntiles) break;
-        RAX_TILE(it, kb1, vb1, kb0, vb0, 1, 0) ++it;
-        if (it >= ntiles) break;
-        RAX_TILE(it, kb2, vb2, kb1, vb1, 1, 0) ++it;
+    if constexpr (!KV8) {
+        // prologue: copies of tiles 0 and 1 in flight, slots of tile 2 loaded
+        RAX_SLOTS(0)
+        RAX_COPY(kb0, vb0)
+        if (ntiles > 1) {
+            RAX_SLOTS(1)
+            RAX_COPY(kb1, vb1)
+        }
+        if (ntiles > 2) RAX_SLOTS(2)
+
+        // Tile T lives in buffer T % 3; iteration T starts the copy of tile T+2 into buffer
+        // (T+2) % 3. Both loops advance three tiles at a time from a multiple of three.
+        // Steady state: six or more tiles ahead are full and exist, so the body has no
+        // conditional copies or waits (control-flow joins with different copies in flight
+        // make the compiler add waits of its own).
+        while (it + 6 <= n_full) {
+            RAX_TILE(it, kb0, vb0, kb2, vb2, 0, 1) ++it;
+            RAX_TILE(it, kb1, vb1, kb0, vb0, 0, 1) ++it;
+            RAX_TILE(it, kb2, vb2, kb1, vb1, 0, 1) ++it;
+        }
+        while (it < ntiles) {
+            RAX_TILE(it, kb0, vb0, kb2, vb2, 1, 0) ++it;
+            if (it >= ntiles) break;
+            RAX_TILE(it, kb1, vb1, kb0, vb0, 1, 0) ++it;
+            if (it >= ntiles) break;
+            RAX_TILE(it, kb2, vb2, kb1, vb1, 1, 0) ++it;
+        }
+    } else {
+        // prologue: copies of tiles 0, 1, 2 issued, tile 0 widened, slots of tile 3 loaded
+        RAX_SLOTS(0)
+        RAX_COPY8(sk0, sv0)
+        if (ntiles > 1) {
+            RAX_SLOTS(1)
+            RAX_COPY8(sk1, sv1)
+        }
+        if (ntiles > 2) {
+            RAX_SLOTS(2)
+            RAX_COPY8(sk2, sv2)
+        }
+        if (ntiles > 3) RAX_SLOTS(3)
+        if (ntiles > 2) { RAX_WAIT_VMCNT(4); } else if (ntiles > 1) { RAX_WAIT_VMCNT(2); } else { RAX_WAIT_VMCNT(0); }
+        RAX_CONVERT8(sk0, sv0, kb0, vb0)
+        // Steady state: the three tiles of a step are full and tiles up to it + 6 exist.
+        while (it + 3 <= n_full && it + 7 <= ntiles) {
+            RAX_TILE8(it, kb0, vb0, sk1, sv1, kb1, vb1, sk0, sv0, 0, 1) ++it;
+            RAX_TILE8(it, kb1, vb1, sk2, sv2, kb2, vb2, sk1, sv1, 0, 1) ++it;
+            RAX_TILE8(it, kb2, vb2, sk0, sv0, kb0, vb0, sk2, sv2, 0, 1) ++it;
+        }
+        while (it < ntiles) {
+            RAX_TILE8(it, kb0, vb0, sk1, sv1, kb1, vb1, sk0, sv0, 1, 0) ++it;
+            if (it >= ntiles) break;
+            RAX_TILE8(it, kb1, vb1, sk2, sv2, kb2, vb2, sk1, sv1, 1, 0) ++it;
+            if (it >= ntiles) break;
+            RAX_TILE8(it, kb2, vb2, sk0, sv0, kb0, vb0, sk2, sv2, 1, 0) ++it;
+        }
     }
 
     lsum = sum_pair32(lsum);
     if (row_ok) {
-        const float inv = 1.f / lsum;
+        const float inv = out_scale / lsum;
         uint16_t* orow = o + qo_row;
         // acc[dt][4 jj + i] is head_dim 32 dt + 8 jj + 4 h2 + i
 #pragma unroll
@@ -349,8 +438,11 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
 #undef RAX_SLOTS
 #undef RAX_COPY
 #undef RAX_TILE
+#undef RAX_COPY8
+#undef RAX_CONVERT8
+#undef RAX_TILE8
 
-template <int G, bool OFF32>
+template <int G, bool OFF32, bool KV8>
 int launch_g(const AttnArgs& a, hipStream_t stream) {
     constexpr int BQ = kExtBM / G;
     const int tiles = (a.max_extend_len + BQ - 1) / BQ;
@@ -358,20 +450,27 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)((pairs + kXcds - 1) / kXcds) * kXcds * tiles;
     if (blocks <= 0) return 0;
     if (blocks > 0x7fffffff) return -1;
-    hipLaunchKernelGGL((extend_kernel<G, OFF32>), dim3((unsigned)blocks), dim3(kExtThreads), 0, stream,
-                       (const uint16_t*)a.q, (uint16_t*)a.o, (const uint16_t*)a.k_pool,
-                       (const uint16_t*)a.v_pool, a.r2t, a.r2t_stride, a.req_pool_indices,
+    // FP8 pools: the K scale multiplies every score, the V scale every output element.
+    const float scale_log2 = a.sm_scale * kLog2e * (KV8 ? a.k_scale : 1.f);
+    const float out_scale = KV8 ? a.v_scale : 1.f;
+    hipLaunchKernelGGL((extend_kernel<G, OFF32, KV8>), dim3((unsigned)blocks), dim3(kExtThreads), 0,
+                       stream, (const uint16_t*)a.q, (uint16_t*)a.o, (const char*)a.k_pool,
+                       (const char*)a.v_pool, a.r2t, a.r2t_stride, a.req_pool_indices,
                        a.prefix_lens, a.extend_lens, a.extend_start_loc, a.total_tokens,
                        a.max_extend_len, a.max_seq_len, a.n_q_heads, a.n_kv_heads, a.batch, tiles,
-                       a.sm_scale * kLog2e);
+                       scale_log2, out_scale);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 template <int G>
 int launch_g(const AttnArgs& a, hipStream_t stream) {
+    if (a.kv8)
+        return pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 1)
+                   ? launch_g<G, true, true>(a, stream)
+                   : launch_g<G, false, true>(a, stream);
     return pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 2)
-               ? launch_g<G, true>(a, stream)
-               : launch_g<G, false>(a, stream);
+               ? launch_g<G, true, false>(a, stream)
+               : launch_g<G, false, false>(a, stream);
 }
 
 }  // namespace

@@ -79,6 +79,19 @@ __device__ __forceinline__ float max_pair16(float v) { float a, b; pair16(v, a, 
 __device__ __forceinline__ float sum_pair32(float v) { float a, b; pair32(v, a, b); return a + b; }
 __device__ __forceinline__ float sum_pair16(float v) { float a, b; pair16(v, a, b); return a + b; }
 
+// FP8 E4M3 -> bf16: every E4M3 value (finite or NaN) is exactly a bf16 value, so widening
+// through float32 rounds nothing. bf16x2_of_e4m3<HI> widens bytes 2 HI, 2 HI + 1 of w;
+// widen8 turns 8 bytes into 8 bf16 in byte order.
+template <bool HI>
+__device__ __forceinline__ uint32_t bf16x2_of_e4m3(uint32_t w) {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+    return pack_bf16x2(f[0], f[1]);
+}
+__device__ __forceinline__ uint4 widen8(uint2 x) {
+    return make_uint4(bf16x2_of_e4m3<false>(x.x), bf16x2_of_e4m3<true>(x.x),
+                      bf16x2_of_e4m3<false>(x.y), bf16x2_of_e4m3<true>(x.y));
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
     return fmaxf(v, __shfl_xor(v, mask, kWave));
 }

@@ -47,6 +47,9 @@ _SIGS = {
     "rax_decode_num_splits": (_c_i32, [ctypes.c_int, _c_i32, _c_i32, _c_i32]),
     "rax_kv_store_fp8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_f,
                                         _c_f, _c_p]),
+    "rax_extend_attention_fp8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_p,
+                                                _c_p, _c_p, _c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                _c_i32, _c_f, _c_f, _c_f, _c_p, _c_sz, _c_p]),
     "rax_decode_attention_fp8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_p,
                                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f, _c_f, _c_f,
                                                 _c_p, _c_sz, _c_p]),
@@ -212,6 +215,25 @@ def kv_store_fp8(k_new, v_new, loc, k_pool, v_pool, k_scale=1.0, v_scale=1.0, st
                                    _fp8_pool(v_pool), S, Hkv, D, float(k_scale), float(v_scale),
                                    _stream(stream)),
            "rax_kv_store_fp8")
+
+
+def extend_attention_fp8(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens, extend_lens,
+                         extend_start_loc, max_extend_len, max_seq_len, sm_scale, k_scale=1.0, v_scale=1.0,
+                         workspace=None, stream=None):
+    """EXTEND attention over FP8 E4M3 pools (bf16 ``q`` and ``o``)."""
+    N, Hq, D = q.shape
+    S, Hkv, Dk = k_pool.shape
+    B = prefix_lens.shape[0]
+    need = extend_workspace_bytes(FP8_E4M3, B, N, max_extend_len, max_seq_len, Hq, Hkv, D)
+    workspace = _workspace(need, workspace, q.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().rax_extend_attention_fp8(_bf16(q), _bf16(o), _fp8_pool(k_pool), _fp8_pool(v_pool), S,
+                                           _idx(req_to_token), req_to_token.shape[1], _idx(req_pool_indices),
+                                           _idx(prefix_lens), _idx(extend_lens), _idx(extend_start_loc), B, N,
+                                           int(max_extend_len), int(max_seq_len), Hq, Hkv, D, float(sm_scale),
+                                           float(k_scale), float(v_scale), _ptr(workspace), wbytes,
+                                           _stream(stream)),
+           "rax_extend_attention_fp8")
 
 
 def decode_attention_fp8(q, o, k_pool, v_pool, req_to_token, req_pool_indices, seq_lens, max_seq_len, sm_scale,

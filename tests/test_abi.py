@@ -22,7 +22,8 @@ def test_every_declared_symbol_is_exported():
     names = R.declared_symbols()
     assert set(names) == {"rax_version", "rax_status_str", "rax_kv_store", "rax_extend_workspace_bytes",
                           "rax_extend_attention", "rax_decode_workspace_bytes", "rax_decode_attention",
-                          "rax_decode_num_splits", "rax_kv_store_fp8", "rax_decode_attention_fp8"}
+                          "rax_decode_num_splits", "rax_kv_store_fp8", "rax_extend_attention_fp8",
+                          "rax_decode_attention_fp8"}
     out = subprocess.run(["nm", "-D", "--defined-only", R.library_path()], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for n in names:
@@ -147,3 +148,14 @@ def test_fp8_calls_check_scales_and_shapes_before_launching():
     assert dec(ks=0.0) == 2 and dec(vs=float("nan")) == 2
     assert dec(B=0) == 0
     assert dec(ws=None, wsb=0) == 5
+    # extend_attention_fp8(q, o, kp, vp, S, r2t, stride, rpi, pre, ext, start, B, N, maxe, maxL, Hq, Hkv, D,
+    #                      sm, ks, vs, ws, wsb, stream)
+    ext = lambda **kw: L.rax_extend_attention_fp8(FAKE, FAKE, FAKE, FAKE, 1000, FAKE, 512, FAKE, FAKE, FAKE,
+                                                  FAKE, kw.get("B", 3), 100, 50, 300, kw.get("Hq", 8), 2,
+                                                  kw.get("D", 128), 0.1, kw.get("ks", 1.0), kw.get("vs", 1.0),
+                                                  None, 0, None)
+    assert ext(ks=-2.0) == 2 and ext(vs=float("inf")) == 2 and ext(ks=float("nan")) == 2
+    assert ext(B=0) == 0
+    assert ext(D=64) == 4          # FP8 EXTEND: head_dim 128 only
+    assert ext(Hq=6) == 4          # group 3 has no kernel
+    assert L.rax_extend_workspace_bytes(2, 3, 100, 50, 300, 8, 2, 128) == 0

@@ -1,4 +1,4 @@
-"""FP8 E4M3 KV pools on the GPU against the float64 oracle.
+"""FP8 E4M3 KV pools on the GPU against the float64 oracle: the store, EXTEND and DECODE.
 
 The store is compared byte for byte with ``oracle.kv_store_fp8``. For attention, the cached
 prefix/context rows are encoded by the oracle (as if an earlier step had stored them), the
@@ -113,3 +113,61 @@ def test_decode_fp8_single_key_is_v_times_scale():
     wl = W.make_workload(spec, 703)
     got, ref = run_decode_fp8(wl, 0.5, 0.25)       # power-of-two scales: products exact in bf16
     assert np.array_equal(got, ref)
+
+
+def run_extend_fp8(wl, k_scale, v_scale):
+    kp, vp = fp8_pools(wl, k_scale, v_scale)
+    dk, dv = to_dev(kp), to_dev(vp)
+    R.kv_store_fp8(to_dev(wl.k_new), to_dev(wl.v_new), to_dev(wl.store_loc), dk, dv, k_scale, v_scale)
+    e = wl.extend
+    q = to_dev(e.q)
+    o = torch.full_like(q, float("nan"))    # rows the kernel skips stay NaN
+    R.extend_attention_fp8(q, o, dk, dv, to_dev(wl.req_to_token), to_dev(e.req_pool_indices),
+                           to_dev(e.prefix_lens), to_dev(e.extend_lens), to_dev(e.extend_start_loc),
+                           int(np.max(e.extend_lens)), int(np.max(e.prefix_lens + e.extend_lens)),
+                           wl.sm_scale, k_scale, v_scale)
+    torch.cuda.synchronize()
+    ref_k, ref_v = oracle.kv_store_fp8(kp, vp, wl.k_new, wl.v_new, wl.store_loc, k_scale, v_scale)
+    ref = oracle.extend_attention(e.q, ref_k, ref_v, wl.req_to_token, e.req_pool_indices, e.prefix_lens,
+                                  e.extend_lens, e.extend_start_loc, wl.spec.n_kv_heads, wl.sm_scale,
+                                  k_scale=k_scale, v_scale=v_scale)
+    return oracle.to_f64(to_host_bits(o)), ref
+
+
+# Every group size of the kernel; contexts of 1, 2, 3 and many 64-key tiles (the prologue and
+# both loops), prefixes of 0 and off tile boundaries, suffixes that end mid-tile.
+EXT_SPECS = [
+    W.Spec("fp8-ext-g4", "bf16", 32, 8, 128, 60000, extend_prefix=(0, 1, 63, 64, 500, 1500),
+           extend_lens=(65, 1, 64, 129, 300, 257)),
+    W.Spec("fp8-ext-g1", "bf16", 4, 4, 128, 30000, extend_prefix=(0, 200, 37), extend_lens=(300, 129, 1)),
+    W.Spec("fp8-ext-g2", "bf16", 8, 4, 128, 30000, extend_prefix=(10, 0), extend_lens=(190, 64)),
+    W.Spec("fp8-ext-g8", "bf16", 64, 8, 128, 60000, extend_prefix=(1000, 5), extend_lens=(33, 200)),
+    W.Spec("fp8-ext-g16", "bf16", 16, 1, 128, 30000, extend_prefix=(129, 0, 2000), extend_lens=(20, 17, 70)),
+    W.Spec("fp8-ext-g32", "bf16", 32, 1, 128, 30000, extend_prefix=(0, 700), extend_lens=(40, 9)),
+    W.Spec("fp8-ext-short", "bf16", 32, 8, 128, 30000, extend_prefix=(0, 0, 64, 100), extend_lens=(1, 64, 64, 28)),
+]
+
+
+@pytest.mark.parametrize("variant,scales", CASES)
+@pytest.mark.parametrize("spec", EXT_SPECS, ids=lambda s: s.name)
+def test_extend_fp8(spec, variant, scales):
+    wl = W.make_workload(spec, 704, variant)
+    if scales == "one":
+        k_scale = v_scale = 1.0
+    else:
+        k_scale = v_scale = 4 * spec.sigma / 448
+        if variant == "needle":
+            k_scale = 16.0 / 448
+    say(f"{spec.name}/{variant}: scales {k_scale:.4g} {v_scale:.4g}")
+    got, ref = run_extend_fp8(wl, k_scale, v_scale)
+    assert_close(got, ref, "bf16", f"{spec.name}/{variant} fp8 extend")
+
+
+def test_extend_fp8_first_row_is_v_times_scale():
+    """A suffix row at position 0 (no prefix) sees one key: v_scale * e4m3(V) exactly."""
+    spec = W.Spec("fp8-ext-one", "bf16", 32, 8, 128, 1000, extend_prefix=(0, 0), extend_lens=(1, 5))
+    wl = W.make_workload(spec, 705)
+    got, ref = run_extend_fp8(wl, 0.5, 0.25)
+    first = np.asarray(wl.extend.extend_start_loc)
+    assert np.array_equal(got[first], ref[first])
+    assert_close(got, ref, "bf16", "fp8 extend, one key")
