@@ -5,6 +5,9 @@ of the prefill chunk, DECODE of the running requests, all on one stream, inputs 
 HBM. Default workload: the mixed chunked-prefill batch (one 2,048-token chunk on a
 14,336-token cached prefix plus 128 decode requests with 1,024..8,192 tokens of context,
 32 q / 8 kv heads, head_dim 128, bf16, a 1,048,576-slot pool), which exercises every call.
+``--kv fp8`` runs the same step over FP8 E4M3 pools (kv_store_fp8, extend_attention_fp8,
+decode_attention_fp8; per-pool scales 4 sigma / 448), the pools converted from the bf16 ones
+before timing.
 
 Prints ONE JSON line. ``value`` is the EXTEND attention throughput in TFLOP/s (algorithmic
 FLOPs: 4 * head_dim * q_heads per attended pair, masked pairs not counted); the DECODE KV
@@ -33,6 +36,7 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # --pmc-summary. A kernel's figure is used only while its sources hash to what they were when
 # the counters were taken.
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "mixed_chunk_hbm_traffic.txt")
+TRAFFIC_SUMMARY_FP8 = os.path.join(ROOT, "profiles", "mixed_chunk_fp8_hbm_traffic.txt")
 CSRC = os.path.join(ROOT, "prefix_cached_paged_amd", "csrc")
 KERNEL_SOURCES = {
     "extend_kernel": ["extend_attn.hip", "rax_device.h", "rax_launch.h"],
@@ -40,6 +44,7 @@ KERNEL_SOURCES = {
     "decode_merge_kernel": ["decode_attn.hip", "rax_device.h", "rax_launch.h"],
     "decode_plan_kernel": ["decode_attn.hip", "rax_device.h", "rax_launch.h"],
     "kv_store_kernel": ["kv_store.hip", "rax_launch.h"],
+    "kv_store_fp8_kernel": ["kv_store.hip", "rax_launch.h"],
 }
 COPY_BYTES = 1 << 30
 
@@ -133,8 +138,12 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, dev_outs, budget_s: float):
-    """Time the CPU oracle (as it stands) on a bounded sample of the same workload."""
+def cpu_baseline(wl, dev_outs, budget_s: float, kv8=None):
+    """Time the CPU oracle (as it stands) on a bounded sample of the same workload.
+
+    ``kv8 = (k_scale, v_scale)``: FP8 pools. The oracle then builds its own E4M3 pools from the
+    generator's bf16 rows (only the rows the sample reads, converted before each timed call and
+    not timed) and stores the step's new rows with its kv_store_fp8."""
     import oracle
     from threadpoolctl import threadpool_info
     from prefix_cached_paged_amd import accounting as A
@@ -142,7 +151,26 @@ def cpu_baseline(wl, dev_outs, budget_s: float):
 
     spec = wl.spec
     t0 = time.perf_counter()
-    kp, vp = oracle.kv_store(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.store_loc)
+    if kv8 is None:
+        ks = vs = 1.0
+        eb = spec.elem_bytes
+        kp, vp = oracle.kv_store(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.store_loc)
+        prep = lambda rows: None
+    else:
+        ks, vs = kv8
+        eb = 1
+        kp = np.full(wl.k_pool.shape, 0x7F, np.uint8)     # E4M3 NaN until a row is converted
+        vp = np.full(wl.v_pool.shape, 0x7F, np.uint8)
+        kp, vp = oracle.kv_store_fp8(kp, vp, wl.k_new, wl.v_new, wl.store_loc, ks, vs)
+        done = np.zeros(kp.shape[0], bool)
+        done[np.asarray(wl.store_loc, np.int64)] = True
+
+        def prep(rows):
+            rows = np.unique(np.asarray(rows, np.int64))
+            rows = rows[~done[rows]]
+            kp[rows] = oracle.quantize_bf16(wl.k_pool[rows], ks)
+            vp[rows] = oracle.quantize_bf16(wl.v_pool[rows], vs)
+            done[rows] = True
     t_store = time.perf_counter() - t0
     res = {}
     parity = {}
@@ -156,10 +184,11 @@ def cpu_baseline(wl, dev_outs, budget_s: float):
         step = 8
         while t_ext < budget_s / 2 and len(toks) < n:
             new = [s0 + n - 1 - i for i in range(len(toks), min(n, len(toks) + step))]
+            prep(wl.req_to_token[int(e.req_pool_indices[b]), :int(e.prefix_lens[b]) + n])
             t1 = time.perf_counter()
             ref = oracle.extend_attention(e.q, kp, vp, wl.req_to_token, e.req_pool_indices, e.prefix_lens,
                                           e.extend_lens, e.extend_start_loc, spec.n_kv_heads, wl.sm_scale,
-                                          tokens=new)
+                                          tokens=new, k_scale=ks, v_scale=vs)
             t_ext += time.perf_counter() - t1
             p = int(e.prefix_lens[b])
             flops += sum(4 * spec.head_dim * spec.n_q_heads * (p + (t - s0) + 1) for t in new)
@@ -175,11 +204,13 @@ def cpu_baseline(wl, dev_outs, budget_s: float):
         order = list(range(d.batch))
         while t_dec < budget_s / 2 and len(reqs) < d.batch:
             new = order[len(reqs):len(reqs) + max(1, len(reqs))]
+            if kv8 is not None:
+                prep(np.concatenate([wl.req_to_token[int(d.req_pool_indices[r]), :int(d.seq_lens[r])] for r in new]))
             t1 = time.perf_counter()
             ref = oracle.decode_attention(d.q, kp, vp, wl.req_to_token, d.req_pool_indices, d.seq_lens,
-                                          spec.n_kv_heads, wl.sm_scale, requests=new)
+                                          spec.n_kv_heads, wl.sm_scale, requests=new, k_scale=ks, v_scale=vs)
             t_dec += time.perf_counter() - t1
-            nbytes += A.decode_kv_bytes(d.seq_lens[new], spec.n_kv_heads, spec.head_dim, spec.elem_bytes)
+            nbytes += A.decode_kv_bytes(d.seq_lens[new], spec.n_kv_heads, spec.head_dim, eb)
             got = oracle.to_f64(to_host_bits(dev_outs["decode"][new]))
             parity.setdefault("decode_max_abs", 0.0)
             parity["decode_max_abs"] = max(parity["decode_max_abs"], float(np.max(np.abs(got - ref))))
@@ -191,8 +222,10 @@ def cpu_baseline(wl, dev_outs, budget_s: float):
         sample.append(f"EXTEND: last {res['extend']['tokens']} suffix rows of the chunk, all heads")
     if "decode" in res:
         sample.append(f"DECODE: {res['decode']['requests']} of {wl.decode.batch} requests, all heads")
+    store_note = (f"kv_store copy {t_store:.1f} s not counted" if kv8 is None else
+                  f"kv_store_fp8 {t_store:.1f} s and the E4M3 conversion of the sampled rows not counted")
     out = dict(value=res.get("extend", {}).get("tflops"), unit="TFLOP/s", cores=threads, kind="oracle",
-               sample="; ".join(sample) + f"; float64 numpy, kv_store copy {t_store:.1f} s not counted",
+               sample="; ".join(sample) + f"; float64 numpy, {store_note}",
                decode_GBps=res.get("decode", {}).get("GBps"), parity_vs_gpu=parity)
     return out
 
@@ -206,6 +239,8 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=16.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
+                    help="KV pool element: the workload's bf16, or FP8 E4M3 with per-pool scales")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step as HIP graph replays (reported beside the eager figures)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -243,30 +278,58 @@ def main():
     log("uploading")
     dw = upload(wl, "cuda:0")
     dt = rax.BF16 if spec.dtype == "bf16" else rax.FP32
+    kv8 = args.kv == "fp8"
+    if kv8 and spec.dtype != "bf16":
+        print("--kv fp8 needs a bf16 workload (configs 2..5)", file=sys.stderr)
+        sys.exit(2)
     ws = None
     if dw.dec is not None:
         d = dw.dec
-        nb = rax.decode_workspace_bytes(dt, d["q"].shape[0], d["max_seq_len"], spec.n_q_heads, spec.n_kv_heads,
-                                        spec.head_dim)
+        nb = rax.decode_workspace_bytes(rax.FP8_E4M3 if kv8 else dt, d["q"].shape[0], d["max_seq_len"],
+                                        spec.n_q_heads, spec.n_kv_heads, spec.head_dim)
         ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda:0")
+    k_scale = v_scale = 1.0
+    if kv8:
+        # FP8 pools converted from the bf16 ones by the library's store (set-up, not timed); the
+        # bf16 pools are freed. Scales put about 4 standard deviations at the top of E4M3.
+        k_scale = v_scale = 4.0 * spec.sigma / 448.0
+        log("converting the pools to FP8 E4M3")
+        kp8 = torch.empty(dw.k_pool.shape, dtype=torch.uint8, device="cuda:0")
+        vp8 = torch.empty_like(kp8)
+        allslots = torch.arange(kp8.shape[0], dtype=torch.int32, device="cuda:0")
+        rax.kv_store_fp8(dw.k_pool, dw.v_pool, allslots, kp8, vp8, k_scale, v_scale)
+        torch.cuda.synchronize()
+        dw.k_pool, dw.v_pool = kp8, vp8
+        del allslots
+        torch.cuda.empty_cache()
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        rax.kv_store(dw.k_new, dw.v_new, dw.store_loc, dw.k_pool, dw.v_pool)
+        if kv8:
+            rax.kv_store_fp8(dw.k_new, dw.v_new, dw.store_loc, dw.k_pool, dw.v_pool, k_scale, v_scale)
+        else:
+            rax.kv_store(dw.k_new, dw.v_new, dw.store_loc, dw.k_pool, dw.v_pool)
         if ev is not None:
             ev[1].record()
         if dw.ext is not None:
             e = dw.ext
-            rax.extend_attention(e["q"], e["o"], dw.k_pool, dw.v_pool, dw.req_to_token, e["req_pool_indices"],
-                                 e["prefix_lens"], e["extend_lens"], e["extend_start_loc"], e["max_extend_len"],
-                                 e["max_seq_len"], wl.sm_scale)
+            ea = (e["q"], e["o"], dw.k_pool, dw.v_pool, dw.req_to_token, e["req_pool_indices"], e["prefix_lens"],
+                  e["extend_lens"], e["extend_start_loc"], e["max_extend_len"], e["max_seq_len"], wl.sm_scale)
+            if kv8:
+                rax.extend_attention_fp8(*ea, k_scale, v_scale)
+            else:
+                rax.extend_attention(*ea)
         if ev is not None:
             ev[2].record()
         if dw.dec is not None:
             d = dw.dec
-            rax.decode_attention(d["q"], d["o"], dw.k_pool, dw.v_pool, dw.req_to_token, d["req_pool_indices"],
-                                 d["seq_lens"], d["max_seq_len"], wl.sm_scale, workspace=ws)
+            da = (d["q"], d["o"], dw.k_pool, dw.v_pool, dw.req_to_token, d["req_pool_indices"], d["seq_lens"],
+                  d["max_seq_len"], wl.sm_scale)
+            if kv8:
+                rax.decode_attention_fp8(*da, k_scale, v_scale, workspace=ws)
+            else:
+                rax.decode_attention(*da, workspace=ws)
         if ev is not None:
             ev[3].record()
 
@@ -313,11 +376,14 @@ def main():
     report = {}
     hbm = lambda nbytes, t_ms: nbytes / (t_ms * 1e-3) / 1e9
     n_new = int(wl.store_loc.size)
-    st_bytes = A.kv_store_bytes(n_new, spec.n_kv_heads, spec.head_dim, spec.elem_bytes)
+    pool_eb = 1 if kv8 else spec.elem_bytes
+    # bf16 store: read and write s bytes per element; FP8 store: read 2, write 1
+    st_bytes = (A.kv_store_bytes(n_new, spec.n_kv_heads, spec.head_dim, spec.elem_bytes) if not kv8 else
+                n_new * 2 * spec.n_kv_heads * spec.head_dim * 3 + 4 * n_new)
     report["kv_store"] = dict(ms=ms["kv_store"], rows=n_new, GBps=hbm(st_bytes, ms["kv_store"]),
                               bytes=st_bytes)
     roofs = {}
-    traffic = read_traffic()
+    traffic = read_traffic(TRAFFIC_SUMMARY_FP8 if kv8 else TRAFFIC_SUMMARY)
     if wl.extend is not None:
         e = wl.extend
         fl = A.extend_flops(e.prefix_lens, e.extend_lens, spec.n_q_heads, spec.head_dim)
@@ -329,13 +395,15 @@ def main():
                                per_launch=f"{fl} algorithmic FLOP", ms=ms["extend"])
     if wl.decode is not None:
         d = wl.decode
-        kvb = A.decode_kv_bytes(d.seq_lens, spec.n_kv_heads, spec.head_dim, spec.elem_bytes)
+        kvb = A.decode_kv_bytes(d.seq_lens, spec.n_kv_heads, spec.head_dim, pool_eb)
         tot = A.decode_total_bytes(d.seq_lens, d.batch, spec.n_q_heads, spec.n_kv_heads, spec.head_dim,
-                                   spec.elem_bytes)
+                                   pool_eb) if not kv8 else (
+            kvb + 4 * int(np.sum(d.seq_lens)) + 2 * d.batch * spec.n_q_heads * spec.head_dim * 2)
         gb = hbm(kvb, ms["decode"])
         report["decode"] = dict(ms=ms["decode"], kv_bytes=kvb, kv_GBps=gb, frac=gb / PEAK_HBM_GBPS,
                                 total_GBps=hbm(tot, ms["decode"]),
-                                splits=rax.decode_num_splits(dt, d.batch, d.max_seq_len, spec.n_kv_heads))
+                                splits=rax.decode_num_splits(rax.FP8_E4M3 if kv8 else dt, d.batch, d.max_seq_len,
+                                                             spec.n_kv_heads))
         # the plan kernel runs only for batches above 1,024 requests
         dec_kernels = ["decode_split_kernel", "decode_merge_kernel"]
         dec_traffic = (sum(traffic[k] for k in dec_kernels) + traffic.get("decode_plan_kernel", 0)
@@ -358,13 +426,15 @@ def main():
             outs["extend"] = dw.ext["o"]
         if dw.dec is not None:
             outs["decode"] = dw.dec["o"]
-        cpu = cpu_baseline(wl, outs, args.cpu_budget)
+        cpu = cpu_baseline(wl, outs, args.cpu_budget, kv8=(k_scale, v_scale) if kv8 else None)
         if unit == "GB/s":
             cpu["value"], cpu["unit"] = cpu.pop("decode_GBps"), "GB/s"
 
     cfgd = {"workload": spec.name, "config_id": cfg, "seed": seed, "dtype": spec.dtype,
             "q_heads": spec.n_q_heads, "kv_heads": spec.n_kv_heads, "head_dim": spec.head_dim,
-            "pool_slots": spec.num_slots}
+            "pool_slots": spec.num_slots, "kv_pool": "fp8_e4m3" if kv8 else spec.dtype}
+    if kv8:
+        cfgd["kv_scales"] = [k_scale, v_scale]
     if wl.extend is not None:
         cfgd["extend"] = {"batch": wl.extend.batch, "new_tokens": wl.extend.total_tokens,
                           "prefix_lens": sorted(set(int(x) for x in wl.extend.prefix_lens))[:4]}
