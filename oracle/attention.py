@@ -124,7 +124,7 @@ def _softmax_rows_times_v(scores: np.ndarray, v: np.ndarray) -> np.ndarray:
 
 def extend_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens,
                      extend_lens, extend_start_loc, n_kv_heads, sm_scale,
-                     tokens=None, row_block=512, k_scale=1.0, v_scale=1.0):
+                     tokens=None, row_block=512, k_scale=1.0, v_scale=1.0, suffix=None):
     """EXTEND attention: each request's new suffix rows over its prefix plus themselves.
 
     Follows "Origins: the paper and the first commit": self-test answer 2 (with
@@ -138,6 +138,15 @@ def extend_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, prefix_l
     back from ``extend_start_loc[b]``. All keys, suffix included, are read from
     the pool through ``req_to_token`` (so the suffix must already be stored).
 
+    With ``suffix = (k_new, v_new)`` (each ``[total_extend_tokens, n_kv_heads,
+    head_dim]``, rows in the order of ``q``) the keys and values of the suffix
+    positions ``p .. p + e - 1`` are those rows instead of pool rows: the ragged
+    reading of the same passages, where attention takes the prefix from the pool
+    and the suffix straight from the just-computed K/V ("Origins...", self-test
+    answer 2; "Inside SGLang", Step 3, a ragged kernel for the new tokens beside
+    a paged one for the cached prefix). Only the first ``p`` entries of the
+    request's table row are read then.
+
     Returns float64 ``[total_extend_tokens, n_q_heads, head_dim]``; with
     ``tokens`` (global row indices) only those rows are computed and returned in
     that order.
@@ -146,6 +155,12 @@ def extend_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, prefix_l
     if Hkv != n_kv_heads:
         raise ValueError("pool kv-head count does not match n_kv_heads")
     N, Hq, Dq = q.shape
+    if suffix is not None:
+        if k_scale != 1.0 or v_scale != 1.0:
+            raise ValueError("ragged suffix rows are taken with pools of the same element format")
+        for a in suffix:
+            if a.shape != (N, Hkv, D) or a.dtype != k_pool.dtype:
+                raise ValueError(f"suffix rows must be [{N}, {Hkv}, {D}] in the pool's format")
     if Dq != D:
         raise ValueError("q head_dim does not match the pool")
     if Hq % Hkv:
@@ -174,7 +189,12 @@ def extend_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, prefix_l
             rows = np.array([i for i in range(e) if (s0 + i) in want], dtype=np.int64)
             if rows.size == 0:
                 continue
-        kb, vb = gather_request_kv(k_pool, v_pool, req_to_token, r, L, k_scale, v_scale)
+        if suffix is None:
+            kb, vb = gather_request_kv(k_pool, v_pool, req_to_token, r, L, k_scale, v_scale)
+        else:
+            kp_, vp_ = gather_request_kv(k_pool, v_pool, req_to_token, r, p, k_scale, v_scale)
+            kb = np.concatenate([kp_, to_f64(suffix[0][s0:s0 + e])])
+            vb = np.concatenate([vp_, to_f64(suffix[1][s0:s0 + e])])
         for c0 in range(0, rows.size, row_block):
             rb = rows[c0:c0 + row_block]
             masked = causal_hidden(L, p, rb)                       # [rows, L]

@@ -332,6 +332,56 @@ def test_unstored_suffix_poisons_output():
     assert np.all(np.isnan(o))
 
 
+def _suffix_rows(wl):
+    """The step's new rows that belong to the EXTEND suffixes (they come first, in q's order)."""
+    n = wl.extend.total_tokens
+    return wl.k_new[:n], wl.v_new[:n]
+
+
+@pytest.mark.parametrize("seed", [35, 36])
+def test_ragged_suffix_matches_torch_sdpa(seed):
+    """Suffix keys taken from the new rows (pool suffix slots left NaN): torch's attention over
+    the prefix rows gathered by hand plus the new rows."""
+    spec = W.Spec("ragged", "bf16", 8, 2, 16, 2048, extend_prefix=(0, 1, 40, 300),
+                  extend_lens=(50, 33, 1, 64))
+    wl = W.make_workload(spec, seed)
+    kn, vn = _suffix_rows(wl)
+    got = run_extend(wl, wl.k_pool, wl.v_pool, suffix=(kn, vn))
+    e = wl.extend
+    qf = oracle.to_f64(e.q)
+    assert np.all(np.isfinite(got))
+    for b in range(e.batch):
+        p, n, s0 = int(e.prefix_lens[b]), int(e.extend_lens[b]), int(e.extend_start_loc[b])
+        slots = wl.req_to_token[int(e.req_pool_indices[b]), :p]
+        kb = np.concatenate([oracle.to_f64(wl.k_pool[slots]), oracle.to_f64(kn[s0:s0 + n])])
+        vb = np.concatenate([oracle.to_f64(wl.v_pool[slots]), oracle.to_f64(vn[s0:s0 + n])])
+        ref = _sdpa_request(qf[s0:s0 + n], kb, vb, p, wl.sm_scale)
+        np.testing.assert_allclose(got[s0:s0 + n], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("spec", TINY_SPECS[:4], ids=lambda s: s.name)
+def test_ragged_suffix_equals_stored_suffix(spec):
+    """Both readings of where the suffix K/V come from give the same result: attention over the
+    new rows equals attention over the pool after kv_store, bit for bit in float64."""
+    wl = W.make_workload(spec, 37)
+    if wl.extend is None:
+        pytest.skip("no EXTEND part")
+    kp, vp = stored(wl)
+    a = run_extend(wl, kp, vp)
+    b = run_extend(wl, wl.k_pool, wl.v_pool, suffix=_suffix_rows(wl))
+    assert np.array_equal(a, b, equal_nan=True)
+
+
+def test_ragged_suffix_rejects_bad_rows():
+    spec = W.Spec("rag-bad", "bf16", 2, 2, 4, 64, extend_prefix=(3,), extend_lens=(2,))
+    wl = W.make_workload(spec, 38)
+    kn, vn = _suffix_rows(wl)
+    with pytest.raises(ValueError):
+        run_extend(wl, wl.k_pool, wl.v_pool, suffix=(kn[:1], vn[:1]))
+    with pytest.raises(ValueError):
+        run_extend(wl, wl.k_pool, wl.v_pool, suffix=(kn.astype(np.float32), vn))
+
+
 # --------------------------------------------------------------------------- formats and constants
 
 def test_bf16_bit_patterns():
