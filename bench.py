@@ -7,7 +7,9 @@ HBM. Default workload: the mixed chunked-prefill batch (one 2,048-token chunk on
 32 q / 8 kv heads, head_dim 128, bf16, a 1,048,576-slot pool), which exercises every call.
 ``--kv fp8`` runs the same step over FP8 E4M3 pools (kv_store_fp8, extend_attention_fp8,
 decode_attention_fp8; per-pool scales 4 sigma / 448), the pools converted from the bf16 ones
-before timing.
+before timing. ``--ragged`` runs EXTEND on the ragged path: the suffix K/V read from the new
+rows and stored by the same kernel (extend_attention_ragged with store_loc); kv_store then
+writes only the decode requests' current tokens.
 
 Prints ONE JSON line. ``value`` is the EXTEND attention throughput in TFLOP/s (algorithmic
 FLOPs: 4 * head_dim * q_heads per attended pair, masked pairs not counted); the DECODE KV
@@ -241,6 +243,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
                     help="KV pool element: the workload's bf16, or FP8 E4M3 with per-pool scales")
+    ap.add_argument("--ragged", action="store_true",
+                    help="EXTEND via extend_attention_ragged with the fused store of the suffix rows")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step as HIP graph replays (reported beside the eager figures)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -279,6 +283,11 @@ def main():
     dw = upload(wl, "cuda:0")
     dt = rax.BF16 if spec.dtype == "bf16" else rax.FP32
     kv8 = args.kv == "fp8"
+    rag = args.ragged and dw.ext is not None
+    if rag and kv8:
+        print("--ragged is for bf16/fp32 pools", file=sys.stderr)
+        sys.exit(2)
+    n_ext = wl.extend.total_tokens if wl.extend is not None else 0
     if kv8 and spec.dtype != "bf16":
         print("--kv fp8 needs a bf16 workload (configs 2..5)", file=sys.stderr)
         sys.exit(2)
@@ -308,6 +317,10 @@ def main():
             ev[0].record()
         if kv8:
             rax.kv_store_fp8(dw.k_new, dw.v_new, dw.store_loc, dw.k_pool, dw.v_pool, k_scale, v_scale)
+        elif rag:
+            # the suffix rows (the first n_ext new rows) are stored by the ragged EXTEND
+            if dw.store_loc.shape[0] > n_ext:
+                rax.kv_store(dw.k_new[n_ext:], dw.v_new[n_ext:], dw.store_loc[n_ext:], dw.k_pool, dw.v_pool)
         else:
             rax.kv_store(dw.k_new, dw.v_new, dw.store_loc, dw.k_pool, dw.v_pool)
         if ev is not None:
@@ -318,6 +331,9 @@ def main():
                   e["extend_lens"], e["extend_start_loc"], e["max_extend_len"], e["max_seq_len"], wl.sm_scale)
             if kv8:
                 rax.extend_attention_fp8(*ea, k_scale, v_scale)
+            elif rag:
+                rax.extend_attention_ragged(e["q"], e["o"], dw.k_new[:n_ext], dw.v_new[:n_ext], dw.k_pool,
+                                            dw.v_pool, *ea[4:], store_loc=dw.store_loc[:n_ext])
             else:
                 rax.extend_attention(*ea)
         if ev is not None:
@@ -375,7 +391,7 @@ def main():
 
     report = {}
     hbm = lambda nbytes, t_ms: nbytes / (t_ms * 1e-3) / 1e9
-    n_new = int(wl.store_loc.size)
+    n_new = int(wl.store_loc.size) - (n_ext if rag else 0)
     pool_eb = 1 if kv8 else spec.elem_bytes
     # bf16 store: read and write s bytes per element; FP8 store: read 2, write 1
     st_bytes = (A.kv_store_bytes(n_new, spec.n_kv_heads, spec.head_dim, spec.elem_bytes) if not kv8 else
@@ -389,7 +405,8 @@ def main():
         fl = A.extend_flops(e.prefix_lens, e.extend_lens, spec.n_q_heads, spec.head_dim)
         tf = fl / (ms["extend"] * 1e-3) / 1e12
         report["extend"] = dict(ms=ms["extend"], flops=fl, tflops=tf, frac=tf / PEAK_BF16_TFLOPS)
-        roofs["extend"] = dict(kernel="extend_attention", bound="mfma", achieved=tf, peak=PEAK_BF16_TFLOPS,
+        roofs["extend"] = dict(kernel="extend_attention_ragged (fused store)" if rag else "extend_attention",
+                               bound="mfma", achieved=tf, peak=PEAK_BF16_TFLOPS,
                                unit="TFLOP/s", frac=tf / PEAK_BF16_TFLOPS,
                                traffic=traffic.get("extend_kernel"),
                                per_launch=f"{fl} algorithmic FLOP", ms=ms["extend"])
@@ -435,6 +452,8 @@ def main():
             "pool_slots": spec.num_slots, "kv_pool": "fp8_e4m3" if kv8 else spec.dtype}
     if kv8:
         cfgd["kv_scales"] = [k_scale, v_scale]
+    if rag:
+        cfgd["extend_path"] = "ragged suffix, fused store"
     if wl.extend is not None:
         cfgd["extend"] = {"batch": wl.extend.batch, "new_tokens": wl.extend.total_tokens,
                           "prefix_lens": sorted(set(int(x) for x in wl.extend.prefix_lens))[:4]}

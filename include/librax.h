@@ -142,6 +142,40 @@ int rax_extend_attention(int dtype, const void* q, void* o, const void* k_pool, 
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * extend_attention_ragged -- EXTEND with the suffix K/V taken straight from the just-computed
+ * rows, optionally storing them into the pool in the same call.
+ *
+ * The pages describe attention over "the prefix's cached KV together with the KV just
+ * computed" ("Origins...", self-test answer 2) and a ragged kernel for the new tokens beside a
+ * paged kernel for the cached prefix ("Inside SGLang", Step 3). Same result as kv_store then
+ * rax_extend_attention (the stored values are the same bits), with:
+ *
+ *   key position j < p        : K/V[req_to_token[r * r2t_stride + j], h / G, :] (the pool)
+ *   key position j = p + i    : k_new / v_new[extend_start_loc[b] + i, h / G, :]
+ *
+ * Arguments (others as rax_extend_attention)
+ *   k_new, v_new  [total_extend_tokens, n_kv_heads, head_dim], rows in the order of q (the
+ *                 suffix rows of every request, back to back). Read only.
+ *   store_loc     NULL, or [total_extend_tokens] int32 (device): when given, new row t is also
+ *                 written to pool slot store_loc[t] (the bf16 kernel stores inside the
+ *                 attention kernel; fp32 launches the copy first). The pools are written only
+ *                 then.
+ * Device-side CONTRACT: only the first p entries of each used table row are read as slots;
+ *   store_loc entries are distinct, inside the pool, and not among any request's prefix slots.
+ * Errors: as rax_extend_attention; RAX_ERR_NULL when k_new or v_new is NULL.
+ */
+int rax_extend_attention_ragged(int dtype, const void* q, void* o, const void* k_new,
+                                const void* v_new, const int32_t* store_loc, void* k_pool,
+                                void* v_pool, int64_t num_slots, const int32_t* req_to_token,
+                                int64_t r2t_stride, const int32_t* req_pool_indices,
+                                const int32_t* prefix_lens, const int32_t* extend_lens,
+                                const int32_t* extend_start_loc, int32_t batch,
+                                int64_t total_extend_tokens, int32_t max_extend_len,
+                                int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                int32_t head_dim, float sm_scale, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * decode_attention -- DECODE: one query per request over its whole context.
  *
  * Defined by "Inside SGLang", Step 3, "Prefill and decode have different shapes": each request

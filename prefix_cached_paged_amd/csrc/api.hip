@@ -86,7 +86,8 @@ int extend_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool,
                 int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
                 int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float sm_scale,
                 float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
-                void* stream) {
+                void* stream, bool ragged = false, const void* k_new = nullptr,
+                const void* v_new = nullptr, const int32_t* store_loc = nullptr) {
     if (!dtype_ok(dtype)) return RAX_ERR_DTYPE;
     if (batch < 0 || batch > kMaxGridYZ || total_extend_tokens < 0 || max_extend_len < 0 ||
         max_seq_len < 0 || num_slots <= 0 || r2t_stride <= 0 || max_seq_len > r2t_stride ||
@@ -102,6 +103,7 @@ int extend_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool,
     if (!q || !o || !k_pool || !v_pool || !req_to_token || !req_pool_indices || !prefix_lens ||
         !extend_lens || !extend_start_loc)
         return RAX_ERR_NULL;
+    if (ragged && (!k_new || !v_new)) return RAX_ERR_NULL;
     const size_t need = rax_extend_workspace_bytes(dtype, batch, total_extend_tokens, max_extend_len,
                                                    max_seq_len, n_q_heads, n_kv_heads, head_dim);
     if (need > 0 && (!workspace || workspace_bytes < need)) return RAX_ERR_WORKSPACE;
@@ -115,6 +117,7 @@ int extend_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool,
     a.n_q_heads = n_q_heads; a.n_kv_heads = n_kv_heads; a.head_dim = head_dim; a.sm_scale = sm_scale;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     a.kv8 = kv8; a.k_scale = k_scale; a.v_scale = v_scale;
+    a.ragged = ragged; a.k_new = k_new; a.v_new = v_new; a.store_loc = store_loc;
     const int rc = dtype == RAX_BF16 ? rax::launch_extend_bf16(a, (hipStream_t)stream)
                                      : rax::launch_extend_fp32(a, (hipStream_t)stream);
     return rc == 0 ? RAX_OK : RAX_ERR_LAUNCH;
@@ -227,6 +230,24 @@ int rax_extend_attention_fp8(const void* q, void* o, const void* k_pool, const v
                        req_pool_indices, prefix_lens, extend_lens, extend_start_loc, batch,
                        total_extend_tokens, max_extend_len, max_seq_len, n_q_heads, n_kv_heads,
                        head_dim, sm_scale, k_scale, v_scale, workspace, workspace_bytes, stream);
+}
+
+int rax_extend_attention_ragged(int dtype, const void* q, void* o, const void* k_new,
+                                const void* v_new, const int32_t* store_loc, void* k_pool,
+                                void* v_pool, int64_t num_slots, const int32_t* req_to_token,
+                                int64_t r2t_stride, const int32_t* req_pool_indices,
+                                const int32_t* prefix_lens, const int32_t* extend_lens,
+                                const int32_t* extend_start_loc, int32_t batch,
+                                int64_t total_extend_tokens, int32_t max_extend_len,
+                                int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                int32_t head_dim, float sm_scale, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (total_extend_tokens > 0 && store_loc && total_extend_tokens > num_slots) return RAX_ERR_SHAPE;
+    return extend_call(dtype, false, q, o, k_pool, v_pool, num_slots, req_to_token, r2t_stride,
+                       req_pool_indices, prefix_lens, extend_lens, extend_start_loc, batch,
+                       total_extend_tokens, max_extend_len, max_seq_len, n_q_heads, n_kv_heads,
+                       head_dim, sm_scale, 1.f, 1.f, workspace, workspace_bytes, stream, true, k_new,
+                       v_new, store_loc);
 }
 
 }  // extern "C"

@@ -15,10 +15,13 @@ namespace rax {
 
 namespace {
 
-template <int D, bool CAUSAL>
+// RAG (EXTEND only): key positions j >= prefix come from new row s0 + j - prefix of k_new /
+// v_new ([tokens, Hkv, D]) instead of the pool.
+template <int D, bool CAUSAL, bool RAG>
 __global__ __launch_bounds__(64) void attn_rows_fp32_kernel(
     const float* __restrict__ q, float* __restrict__ o, const float* __restrict__ k_pool,
-    const float* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
+    const float* __restrict__ v_pool, const float* __restrict__ k_new, const float* __restrict__ v_new,
+    const int32_t* __restrict__ r2t, int64_t r2t_stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
     const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ extend_start_loc,
     const int32_t* __restrict__ seq_lens, int64_t total_tokens, int32_t max_extend_len,
@@ -33,13 +36,15 @@ __global__ __launch_bounds__(64) void attn_rows_fp32_kernel(
 
     int64_t qrow;
     int nkeys;
+    int pre = 0, s0 = 0;  // RAG: prefix length and first row of the request's new rows
     if (CAUSAL) {
         const int i = blockIdx.x;
         int e = min(extend_lens[b], max_extend_len);
-        const int s0 = extend_start_loc[b];
+        s0 = extend_start_loc[b];
         e = (int)min((int64_t)e, total_tokens - s0);
         if (i >= e) return;
-        nkeys = min(prefix_lens[b] + i + 1, max_seq_len);
+        pre = prefix_lens[b];
+        nkeys = min(pre + i + 1, max_seq_len);
         qrow = (int64_t)(s0 + i);
     } else {
         nkeys = min(seq_lens[b], max_seq_len);
@@ -66,8 +71,10 @@ __global__ __launch_bounds__(64) void attn_rows_fp32_kernel(
     for (int j0 = 0; j0 < nkeys; j0 += 64) {
         const int j = j0 + lane;
         const bool ok = j < nkeys;
-        const int slot = row[ok ? j : nkeys - 1];
-        const float* kr = k_pool + (int64_t)slot * pool_row + (int64_t)g * D;
+        const int jc = ok ? j : nkeys - 1;
+        const int slot = (RAG && jc >= pre) ? 0 : row[jc];
+        const float* kr = (RAG && jc >= pre) ? k_new + (int64_t)(s0 + jc - pre) * pool_row + (int64_t)g * D
+                                             : k_pool + (int64_t)slot * pool_row + (int64_t)g * D;
         float dot = 0.f;
         for (int d = 0; d < D; d += 4) {
             const float4 kv = *(const float4*)(kr + d);
@@ -94,7 +101,9 @@ __global__ __launch_bounds__(64) void attn_rows_fp32_kernel(
         for (int jj = 0; jj < nj; ++jj) {
             const float pb = __shfl(pj, jj, kWave);
             const int sb = __shfl(slot, jj, kWave);
-            const float* vr = v_pool + (int64_t)sb * pool_row + (int64_t)g * D;
+            const int pos = j0 + jj;
+            const float* vr = (RAG && pos >= pre) ? v_new + (int64_t)(s0 + pos - pre) * pool_row + (int64_t)g * D
+                                                  : v_pool + (int64_t)sb * pool_row + (int64_t)g * D;
 #pragma unroll
             for (int k = 0; k < PER; ++k) acc[k] = fmaf(pb, vr[64 * k + lane], acc[k]);
         }
@@ -104,21 +113,21 @@ __global__ __launch_bounds__(64) void attn_rows_fp32_kernel(
     for (int k = 0; k < PER; ++k) orow[64 * k + lane] = acc[k] * inv;
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool RAG>
 int launch_rows(const AttnArgs& a, hipStream_t stream) {
     const unsigned gx = CAUSAL ? (unsigned)a.max_extend_len : 1u;
     if (gx == 0 || a.batch == 0) return 0;
     dim3 grid(gx, a.n_q_heads, a.batch);
     if (a.head_dim == 128) {
-        hipLaunchKernelGGL((attn_rows_fp32_kernel<128, CAUSAL>), grid, dim3(64), 0, stream,
+        hipLaunchKernelGGL((attn_rows_fp32_kernel<128, CAUSAL, RAG>), grid, dim3(64), 0, stream,
                            (const float*)a.q, (float*)a.o, (const float*)a.k_pool, (const float*)a.v_pool,
-                           a.r2t, a.r2t_stride, a.req_pool_indices, a.prefix_lens, a.extend_lens,
+                           (const float*)a.k_new, (const float*)a.v_new, a.r2t, a.r2t_stride, a.req_pool_indices, a.prefix_lens, a.extend_lens,
                            a.extend_start_loc, a.seq_lens, a.total_tokens, a.max_extend_len,
                            a.max_seq_len, a.n_q_heads, a.n_kv_heads, a.sm_scale);
     } else {
-        hipLaunchKernelGGL((attn_rows_fp32_kernel<64, CAUSAL>), grid, dim3(64), 0, stream,
+        hipLaunchKernelGGL((attn_rows_fp32_kernel<64, CAUSAL, RAG>), grid, dim3(64), 0, stream,
                            (const float*)a.q, (float*)a.o, (const float*)a.k_pool, (const float*)a.v_pool,
-                           a.r2t, a.r2t_stride, a.req_pool_indices, a.prefix_lens, a.extend_lens,
+                           (const float*)a.k_new, (const float*)a.v_new, a.r2t, a.r2t_stride, a.req_pool_indices, a.prefix_lens, a.extend_lens,
                            a.extend_start_loc, a.seq_lens, a.total_tokens, a.max_extend_len,
                            a.max_seq_len, a.n_q_heads, a.n_kv_heads, a.sm_scale);
     }
@@ -127,7 +136,18 @@ int launch_rows(const AttnArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-int launch_extend_fp32(const AttnArgs& a, hipStream_t stream) { return launch_rows<true>(a, stream); }
-int launch_decode_fp32(const AttnArgs& a, hipStream_t stream) { return launch_rows<false>(a, stream); }
+// Ragged fp32 EXTEND with a store: the rows are stored by the copy kernel first (no slot it
+// writes is read by the attention kernel, so the order only keeps the pool consistent).
+int launch_extend_fp32(const AttnArgs& a, hipStream_t stream) {
+    if (!a.ragged) return launch_rows<true, false>(a, stream);
+    if (a.store_loc != nullptr) {
+        const int64_t row_bytes = (int64_t)a.n_kv_heads * a.head_dim * 4;
+        if (launch_kv_store(a.k_new, a.v_new, a.store_loc, a.total_tokens, const_cast<void*>(a.k_pool),
+                            const_cast<void*>(a.v_pool), row_bytes, stream) != 0)
+            return -1;
+    }
+    return launch_rows<true, true>(a, stream);
+}
+int launch_decode_fp32(const AttnArgs& a, hipStream_t stream) { return launch_rows<false, false>(a, stream); }
 
 }  // namespace rax

@@ -110,6 +110,14 @@ __device__ __forceinline__ const char* pool_row_ptr(const char* base, int slot, 
     }
 }
 
+// Byte offset of row `idx` (a pool slot, or a new row of the ragged suffix): a 24-bit multiply
+// when both the pool and the new rows fit 32-bit offsets (OFF32), 64-bit otherwise.
+template <bool OFF32>
+__device__ __forceinline__ int64_t row_off(int idx, uint32_t row_bytes) {
+    if constexpr (OFF32) return (int64_t)__umul24((uint32_t)idx, row_bytes);
+    else return (int64_t)(uint32_t)idx * row_bytes;
+}
+
 // s_waitcnt vmcnt(N), leaving the other counters unconstrained (gfx9 encoding: vmcnt[3:0] in
 // bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
 #define RAX_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt((((N) & 15) | (((N) >> 4) << 14)) | 0x0F70)
@@ -120,10 +128,11 @@ __device__ __forceinline__ const char* pool_row_ptr(const char* base, int slot, 
 // which other waves read them).
 #define RAX_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
-template <int G, bool OFF32, bool KV8>
+template <int G, bool OFF32, bool KV8, bool RAG>
 __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const char* __restrict__ k_pool,
-    const char* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
+    const char* __restrict__ v_pool, const char* __restrict__ k_new, const char* __restrict__ v_new,
+    const int32_t* __restrict__ store_loc, const int32_t* __restrict__ r2t, int64_t r2t_stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
     const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ extend_start_loc,
     int64_t total_tokens, int32_t max_extend_len, int32_t max_seq_len, int32_t Hq, int32_t Hkv,
@@ -131,6 +140,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     constexpr int D = kExtD;
     constexpr int BQ = kExtBM / G;  // tokens per workgroup
     constexpr int EB = KV8 ? 1 : 2;  // bytes per pool element
+    static_assert(!(KV8 && RAG), "ragged suffix rows are bf16, as the pools");
 
     // Three K/V tile buffers, row-major [key][16 units of 8 bf16], swizzled. Separate LDS
     // objects, each named statically below.
@@ -162,6 +172,10 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const uint32_t row_bytes = (uint32_t)Hkv * D * EB;
     const char* kbase = k_pool + (int64_t)g * D * EB;
     const char* vbase = v_pool + (int64_t)g * D * EB;
+    // Ragged suffix: key position j >= p is new row s0 + j - p of k_new / v_new ([tokens, Hkv,
+    // D], the same row size as the pool), the prefix comes from the pool.
+    const char* knbase = RAG ? k_new + (int64_t)g * D * EB : nullptr;
+    const char* vnbase = RAG ? v_new + (int64_t)g * D * EB : nullptr;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -195,10 +209,12 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // 8 w .. 8 w + 7; lane row 4 i + prow takes slot number i * 4 + prow of those eight.
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     int nx0, nx1, nx2, nx3, nx4, nx5, nx6, nx7;  // slots of the next tile to copy (SGPRs)
+    int nxpos = 0;  // key position of the first of those eight rows
 #define RAX_SLOTS(TILE)                                                                     \
     {                                                                                       \
         const int pb_ = (TILE) * kExtBN + 8 * wave_u;                                       \
         const int lim_ = kend - 1;                                                          \
+        nxpos = pb_;                                                                        \
         nx0 = row[min(pb_ + 0, lim_)]; nx1 = row[min(pb_ + 1, lim_)];                       \
         nx2 = row[min(pb_ + 2, lim_)]; nx3 = row[min(pb_ + 3, lim_)];                       \
         nx4 = row[min(pb_ + 4, lim_)]; nx5 = row[min(pb_ + 5, lim_)];                       \
@@ -211,10 +227,24 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         const int sl1_ = prow == 0 ? nx4 : prow == 1 ? nx5 : prow == 2 ? nx6 : nx7;         \
         char* kd_ = (char*)(KB) + (8 * wave_u) * 256;                                       \
         char* vd_ = (char*)(VB) + (8 * wave_u) * 256;                                       \
-        lds_dma16(pool_row_ptr<OFF32>(kbase, sl0_, row_bytes, k_src0), kd_);                \
-        lds_dma16(pool_row_ptr<OFF32>(kbase, sl1_, row_bytes, k_src1), kd_ + 1024);         \
-        lds_dma16(pool_row_ptr<OFF32>(vbase, sl0_, row_bytes, v_src), vd_);                 \
-        lds_dma16(pool_row_ptr<OFF32>(vbase, sl1_, row_bytes, v_src), vd_ + 1024);          \
+        if constexpr (!RAG) {                                                               \
+            lds_dma16(pool_row_ptr<OFF32>(kbase, sl0_, row_bytes, k_src0), kd_);            \
+            lds_dma16(pool_row_ptr<OFF32>(kbase, sl1_, row_bytes, k_src1), kd_ + 1024);     \
+            lds_dma16(pool_row_ptr<OFF32>(vbase, sl0_, row_bytes, v_src), vd_);             \
+            lds_dma16(pool_row_ptr<OFF32>(vbase, sl1_, row_bytes, v_src), vd_ + 1024);      \
+        } else {                                                                            \
+            /* row index (pool slot or new row) and base chosen per lane, the offset */     \
+            /* product shared by K and V */                                                 \
+            const int ps0_ = min(nxpos + prow, kend - 1);                                   \
+            const int ps1_ = min(nxpos + 4 + prow, kend - 1);                               \
+            const bool n0_ = ps0_ >= p, n1_ = ps1_ >= p;                                    \
+            const int64_t r0_ = row_off<OFF32>(n0_ ? s0 + ps0_ - p : sl0_, row_bytes);      \
+            const int64_t r1_ = row_off<OFF32>(n1_ ? s0 + ps1_ - p : sl1_, row_bytes);      \
+            lds_dma16((n0_ ? knbase : kbase) + (r0_ + k_src0), kd_);                        \
+            lds_dma16((n1_ ? knbase : kbase) + (r1_ + k_src1), kd_ + 1024);                 \
+            lds_dma16((n0_ ? vnbase : vbase) + (r0_ + v_src), vd_);                         \
+            lds_dma16((n1_ ? vnbase : vbase) + (r1_ + v_src), vd_ + 1024);                  \
+        }                                                                                   \
     }
     // FP8 pools: a 64-key tile is 8 KB per operand, so one copy instruction per wave moves
     // its eight rows: lane l fetches 16 bytes at offset 16 (l % 8) of row 8 w + l / 8 into
@@ -434,6 +464,23 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
                 *(uint2*)(orow + 32 * dt + 8 * jj + 4 * h2) = w;
             }
     }
+    // Fused store of the ragged suffix: this workgroup writes kv head g of its own tokens'
+    // new rows into their pool slots (each (token, kv head) row has exactly one owner). No
+    // workgroup of this launch reads those slots: suffix keys come from the new rows, and
+    // prefix slots are disjoint from the store slots.
+    if constexpr (RAG) {
+        if (store_loc != nullptr) {
+            const int nrows = t_last - t0 + 1;
+            for (int u = tid; u < nrows * 16; u += kExtThreads) {
+                const int64_t tok = (int64_t)s0 + t0 + (u >> 4);
+                const int64_t col = (int64_t)g * D * EB + 16 * (u & 15);
+                const int64_t dst = (int64_t)store_loc[tok] * row_bytes + col;
+                const int64_t src = tok * row_bytes + col;
+                *(uint4*)((char*)k_pool + dst) = *(const uint4*)(k_new + src);
+                *(uint4*)((char*)v_pool + dst) = *(const uint4*)(v_new + src);
+            }
+        }
+    }
 }
 #undef RAX_SLOTS
 #undef RAX_COPY
@@ -442,7 +489,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
 #undef RAX_CONVERT8
 #undef RAX_TILE8
 
-template <int G, bool OFF32, bool KV8>
+template <int G, bool OFF32, bool KV8, bool RAG>
 int launch_g(const AttnArgs& a, hipStream_t stream) {
     constexpr int BQ = kExtBM / G;
     const int tiles = (a.max_extend_len + BQ - 1) / BQ;
@@ -453,9 +500,10 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
     // FP8 pools: the K scale multiplies every score, the V scale every output element.
     const float scale_log2 = a.sm_scale * kLog2e * (KV8 ? a.k_scale : 1.f);
     const float out_scale = KV8 ? a.v_scale : 1.f;
-    hipLaunchKernelGGL((extend_kernel<G, OFF32, KV8>), dim3((unsigned)blocks), dim3(kExtThreads), 0,
-                       stream, (const uint16_t*)a.q, (uint16_t*)a.o, (const char*)a.k_pool,
-                       (const char*)a.v_pool, a.r2t, a.r2t_stride, a.req_pool_indices,
+    hipLaunchKernelGGL((extend_kernel<G, OFF32, KV8, RAG>), dim3((unsigned)blocks), dim3(kExtThreads),
+                       0, stream, (const uint16_t*)a.q, (uint16_t*)a.o, (const char*)a.k_pool,
+                       (const char*)a.v_pool, (const char*)a.k_new, (const char*)a.v_new, a.store_loc,
+                       a.r2t, a.r2t_stride, a.req_pool_indices,
                        a.prefix_lens, a.extend_lens, a.extend_start_loc, a.total_tokens,
                        a.max_extend_len, a.max_seq_len, a.n_q_heads, a.n_kv_heads, a.batch, tiles,
                        scale_log2, out_scale);
@@ -464,13 +512,18 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
 
 template <int G>
 int launch_g(const AttnArgs& a, hipStream_t stream) {
-    if (a.kv8)
+    if (a.kv8) {
+        if (a.ragged) return -1;
         return pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 1)
-                   ? launch_g<G, true, true>(a, stream)
-                   : launch_g<G, false, true>(a, stream);
-    return pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 2)
-               ? launch_g<G, true, false>(a, stream)
-               : launch_g<G, false, false>(a, stream);
+                   ? launch_g<G, true, true, false>(a, stream)
+                   : launch_g<G, false, true, false>(a, stream);
+    }
+    // ragged: the new rows are addressed like pool rows (row index total_tokens - 1 at most)
+    const bool off32 = pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 2) &&
+                       (!a.ragged || pool_fits_32bit_offsets(a.total_tokens, a.n_kv_heads, a.head_dim, 2));
+    if (a.ragged)
+        return off32 ? launch_g<G, true, false, true>(a, stream) : launch_g<G, false, false, true>(a, stream);
+    return off32 ? launch_g<G, true, false, false>(a, stream) : launch_g<G, false, false, false>(a, stream);
 }
 
 }  // namespace

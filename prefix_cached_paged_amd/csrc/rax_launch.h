@@ -36,6 +36,12 @@ struct AttnArgs {
     bool kv8;
     float k_scale;
     float v_scale;
+    // Ragged EXTEND: suffix keys come from k_new / v_new ([total_tokens, Hkv, D], rows in q's
+    // order) instead of the pool; store_loc (optional) names the pool slots they are stored to.
+    bool ragged;
+    const void* k_new;
+    const void* v_new;
+    const int32_t* store_loc;
     void* workspace;
     size_t workspace_bytes;
 };

@@ -40,6 +40,10 @@ _SIGS = {
     "rax_extend_attention": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64,
                                             _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64, _c_i32, _c_i32,
                                             _c_i32, _c_i32, _c_i32, _c_f, _c_p, _c_sz, _c_p]),
+    "rax_extend_attention_ragged": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                                   _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_i32,
+                                                   _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f,
+                                                   _c_p, _c_sz, _c_p]),
     "rax_decode_workspace_bytes": (_c_sz, [ctypes.c_int, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "rax_decode_attention": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64,
                                             _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f,
@@ -178,6 +182,29 @@ def extend_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefi
                                        int(max_seq_len), Hq, Hkv, D, float(sm_scale), _ptr(workspace), wbytes,
                                        _stream(stream)),
            "rax_extend_attention")
+
+
+def extend_attention_ragged(q, o, k_new, v_new, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens,
+                            extend_lens, extend_start_loc, max_extend_len, max_seq_len, sm_scale, store_loc=None,
+                            workspace=None, stream=None):
+    """EXTEND with the suffix K/V read from ``k_new`` / ``v_new`` (rows in ``q``'s order); with
+    ``store_loc`` the rows are also written to those pool slots."""
+    N, Hq, D = q.shape
+    S, Hkv, Dk = k_pool.shape
+    dt = _dtype(q, o, k_pool, v_pool)
+    if _dtype(k_new, v_new) != dt or k_new.shape != (N, Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [tokens, n_kv_heads, head_dim] in the pool's dtype")
+    B = prefix_lens.shape[0]
+    need = extend_workspace_bytes(dt, B, N, max_extend_len, max_seq_len, Hq, Hkv, D)
+    workspace = _workspace(need, workspace, q.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().rax_extend_attention_ragged(dt, _ptr(q), _ptr(o), _ptr(k_new), _ptr(v_new),
+                                              _idx(store_loc) if store_loc is not None else None, _ptr(k_pool),
+                                              _ptr(v_pool), S, _idx(req_to_token), req_to_token.shape[1],
+                                              _idx(req_pool_indices), _idx(prefix_lens), _idx(extend_lens),
+                                              _idx(extend_start_loc), B, N, int(max_extend_len), int(max_seq_len),
+                                              Hq, Hkv, D, float(sm_scale), _ptr(workspace), wbytes, _stream(stream)),
+           "rax_extend_attention_ragged")
 
 
 def decode_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, seq_lens, max_seq_len, sm_scale,

@@ -23,7 +23,7 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"rax_version", "rax_status_str", "rax_kv_store", "rax_extend_workspace_bytes",
                           "rax_extend_attention", "rax_decode_workspace_bytes", "rax_decode_attention",
                           "rax_decode_num_splits", "rax_kv_store_fp8", "rax_extend_attention_fp8",
-                          "rax_decode_attention_fp8"}
+                          "rax_decode_attention_fp8", "rax_extend_attention_ragged"}
     out = subprocess.run(["nm", "-D", "--defined-only", R.library_path()], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for n in names:
@@ -159,3 +159,18 @@ def test_fp8_calls_check_scales_and_shapes_before_launching():
     assert ext(D=64) == 4          # FP8 EXTEND: head_dim 128 only
     assert ext(Hq=6) == 4          # group 3 has no kernel
     assert L.rax_extend_workspace_bytes(2, 3, 100, 50, 300, 8, 2, 128) == 0
+
+
+def test_ragged_extend_checks_before_launching():
+    L = lib()
+    # (dtype, q, o, k_new, v_new, store_loc, kp, vp, S, r2t, stride, rpi, pre, ext, start, B, N, maxe, maxL,
+    #  Hq, Hkv, D, sm, ws, wsb, stream)
+    rag = lambda **kw: L.rax_extend_attention_ragged(kw.get("dt", 0), FAKE, FAKE, kw.get("kn", FAKE), FAKE,
+                                                     kw.get("loc", None), FAKE, FAKE, kw.get("S", 1000), FAKE,
+                                                     512, FAKE, FAKE, FAKE, FAKE, kw.get("B", 3), kw.get("N", 100),
+                                                     50, 300, 8, 2, kw.get("D", 128), 0.1, None, 0, None)
+    assert rag(kn=None) == 1                 # no new rows
+    assert rag(B=0) == 0 and rag(kn=None, B=0) == 0
+    assert rag(dt=7) == 3
+    assert rag(D=96) == 4
+    assert rag(loc=FAKE, S=60, N=100) == 2   # more rows to store than slots
