@@ -18,6 +18,8 @@ What it computes is the plain definition of the method, in float64:
   of attention for one head).
 * ``decode_attention`` -- one query per request over its whole context
   ("Inside SGLang", Step 3, "Prefill and decode have different shapes").
+* ``paged`` -- page-granular request tables (page size P > 1, "A walkthrough of SGLang",
+  Exercises, exercise 2): position j at slot page_table[row, j // P] * P + j % P.
 * ``fp8`` -- the FP8 E4M3 KV pool ("Inside SGLang", Step 6): exact decode of each byte,
   the store's encoding (``kv_store_fp8``); the attention functions take per-pool scales.
 
@@ -34,6 +36,7 @@ from .attention import (
     gather_request_kv,
 )
 from .fp8 import e4m3_bits_to_f64, e4m3_round, kv_store_fp8, quantize_bf16
+from .paged import token_table, extend_attention_paged, decode_attention_paged
 from .bruteforce import (
     extend_attention_loops,
     decode_attention_loops,
@@ -52,4 +55,7 @@ __all__ = [
     "e4m3_round",
     "kv_store_fp8",
     "quantize_bf16",
+    "token_table",
+    "extend_attention_paged",
+    "decode_attention_paged",
 ]

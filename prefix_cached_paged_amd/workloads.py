@@ -39,6 +39,13 @@ threads fill them. bfloat16 pools hold the round-to-nearest-even bit patterns
 (``uint16``) of those float32 values. Pool slots that no request references are
 filled with NaN, so a read of a wrong slot poisons the output.
 
+Pages (``page_size`` P > 1, "A walkthrough of SGLang", Exercises, exercise 2: allocation by
+pages of P slots): step 3 draws a permutation of the S / P pages instead, each request takes
+pages in request-major order, and position j of a request lives at slot
+``page[j // P] * P + j % P``; requests with ``shared_prefix`` share the first request's prefix
+pages (the prefix length must then be a multiple of P). ``page_table[row, k]`` holds the k-th
+page of the row (-1 where unused), and ``req_to_token`` holds the same slots token by token.
+
 Variants: ``"normal"``; ``"peaked"`` (Q scaled by 8 / sigma**2 so that scaled
 scores have standard deviation about 8); ``"needle"`` (per request and kv head,
 one seeded key visible to every query of the request is set to ``NEEDLE_GAIN``
@@ -126,6 +133,7 @@ class Spec:
     decode_batch: int = 0           # or: this many DECODE requests ...
     decode_range: tuple | None = None  # ... with lengths uniform in [lo, hi]
     spare_rows: int = 4             # request-table rows no request uses (held at -1)
+    page_size: int = 1              # slots per page; 1 = token-granular (no page table)
 
     @property
     def elem_bytes(self) -> int:
@@ -190,6 +198,7 @@ class Workload:
     extend: ExtendBatch | None = None
     decode: DecodeBatch | None = None
     needles: dict = field(default_factory=dict)  # (kind, request, kv_head) -> position
+    page_table: np.ndarray | None = None  # [R, W / P] int32 when page_size > 1
 
     @property
     def sm_scale(self) -> float:
@@ -238,40 +247,68 @@ def make_workload(spec: Spec, seed: int, variant: str = "normal") -> Workload:
     r2t = np.full((R, W), -1, dtype=np.int32)
 
     # 3. slot assignment
-    slot_perm = rng.permutation(S)
-    cursor = 0
+    P = spec.page_size
+    page_table = None
+    if P == 1:
+        slot_perm = rng.permutation(S)
+        cursor = 0
 
-    def take(n):
-        nonlocal cursor
-        if cursor + n > S:
-            raise ValueError(f"workload {spec.name} needs more than {S} slots")
-        s = slot_perm[cursor:cursor + n]
-        cursor += n
-        return s
+        def take(n):
+            nonlocal cursor
+            if cursor + n > S:
+                raise ValueError(f"workload {spec.name} needs more than {S} slots")
+            s = slot_perm[cursor:cursor + n]
+            cursor += n
+            return s
+
+        def place(row, lo, n, shared_slots=None):
+            """Slots of positions lo .. lo+n-1 of a request-table row."""
+            s = take(n) if shared_slots is None else shared_slots
+            r2t[row, lo:lo + n] = s
+            return s
+    else:
+        if P < 1 or P & (P - 1) or S % P:
+            raise ValueError("page_size must be a power of two dividing the pool")
+        page_perm = rng.permutation(S // P)
+        pcur = 0
+        page_table = np.full((R, (W + P - 1) // P), -1, dtype=np.int32)
+
+        def place(row, lo, n, shared_slots=None):
+            """Slots of positions lo .. lo+n-1 of a row, taking new pages as positions reach them."""
+            nonlocal pcur
+            if shared_slots is not None:
+                page_table[row, lo // P:(lo + n) // P] = shared_slots[::P] // P
+                r2t[row, lo:lo + n] = shared_slots
+                return shared_slots
+            for k in range(lo // P, (lo + n + P - 1) // P):
+                if page_table[row, k] < 0:
+                    if pcur >= S // P:
+                        raise ValueError(f"workload {spec.name} needs more than {S // P} pages")
+                    page_table[row, k] = page_perm[pcur]
+                    pcur += 1
+            j = np.arange(lo, lo + n)
+            s = page_table[row, j // P].astype(np.int64) * P + j % P
+            r2t[row, lo:lo + n] = s
+            return s
 
     ctx_slots, new_slots = [], []
     shared = None
     for b in range(Be):
         p, e = int(ext_p[b]), int(ext_e[b])
         if spec.shared_prefix and shared is not None:
-            pre = shared
+            pre = place(ext_rows[b], 0, p, shared)
         else:
-            pre = take(p)
+            if spec.shared_prefix and p % P:
+                raise ValueError("a shared prefix must fill whole pages")
+            pre = place(ext_rows[b], 0, p)
             ctx_slots.append(pre)
             if spec.shared_prefix:
                 shared = pre
-        suf = take(e)
-        new_slots.append(suf)
-        r2t[ext_rows[b], :p] = pre
-        r2t[ext_rows[b], p:p + e] = suf
+        new_slots.append(place(ext_rows[b], p, e))
     for b in range(Bd):
         L = int(dec_L[b])
-        ctx = take(L - 1)
-        cur = take(1)
-        ctx_slots.append(ctx)
-        new_slots.append(cur)
-        r2t[dec_rows[b], :L - 1] = ctx
-        r2t[dec_rows[b], L - 1] = cur[0]
+        ctx_slots.append(place(dec_rows[b], 0, L - 1))
+        new_slots.append(place(dec_rows[b], L - 1, 1))
     ctx_slots = np.concatenate(ctx_slots) if ctx_slots else np.zeros(0, np.int64)
     new_slots = np.concatenate(new_slots) if new_slots else np.zeros(0, np.int64)
     n_ctx, n_new = ctx_slots.size, new_slots.size
@@ -355,7 +392,7 @@ def make_workload(spec: Spec, seed: int, variant: str = "normal") -> Workload:
     if Bd:
         decode = DecodeBatch(i32(dec_rows), i32(dec_L), q_dec)
     return Workload(spec, seed, variant, k_pool, v_pool, r2t, i32(new_slots), k_new, v_new,
-                    extend, decode, needles)
+                    extend, decode, needles, page_table)
 
 
 # The five workloads the method is measured on. Seeds for timing runs are
