@@ -213,6 +213,43 @@ int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, 
                          float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Page tables -- the same EXTEND and DECODE over a pool allocated in pages of P slots ("A
+ * walkthrough of SGLang", Exercises, exercise 2: the page-size option allocates and matches by
+ * pages of, e.g., 16, 32 or 64 tokens; the first version used one slot per token, "Origins:
+ * the paper and the first commit"). The request table then names one page per P positions:
+ *
+ *   slot of position j of table row r = page_table[r * pt_stride + j / P] * P + j % P
+ *
+ * (page k of a request holds its positions kP .. kP + P - 1 in order). Everything else --
+ * layouts, lengths, workspace (rax_extend/decode_workspace_bytes), outputs -- is as in the
+ * token-granular calls; with P = 1 the page table is a token table and the result is that
+ * of rax_extend_attention / rax_decode_attention.
+ *
+ * Arguments
+ *   page_table    int32 (device), row stride pt_stride entries; pt_stride * P >= max_seq_len.
+ *   page_size     P, a power of two from 1 to 2^20 (else RAX_ERR_SHAPE).
+ * Device-side CONTRACT: the entries for positions 0 .. L-1 of each used row are pages with
+ *   page * P + P <= num_slots. bf16 (MFMA kernels, head_dim 128 for EXTEND) and fp32.
+ */
+int rax_extend_attention_paged(int dtype, const void* q, void* o, const void* k_pool,
+                               const void* v_pool, int64_t num_slots, const int32_t* page_table,
+                               int64_t pt_stride, int32_t page_size,
+                               const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                               const int32_t* extend_lens, const int32_t* extend_start_loc,
+                               int32_t batch, int64_t total_extend_tokens, int32_t max_extend_len,
+                               int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                               int32_t head_dim, float sm_scale, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+int rax_decode_attention_paged(int dtype, const void* q, void* o, const void* k_pool,
+                               const void* v_pool, int64_t num_slots, const int32_t* page_table,
+                               int64_t pt_stride, int32_t page_size,
+                               const int32_t* req_pool_indices, const int32_t* seq_lens,
+                               int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t head_dim, float sm_scale,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * FP8 KV pools -- the K and V pools hold one OCP FP8 E4M3 byte per element (no infinities; NaN
  * only at 0x7F/0xFF; largest finite magnitude 448), and an element's value is
  * scale * e4m3(byte) with one float scale per pool ("Inside SGLang", Step 6: with an FP8 KV

@@ -12,6 +12,13 @@ bool dtype_ok(int dt) { return dt == RAX_BF16 || dt == RAX_FP32; }
 bool scale_ok(float s) { return s == s && s > 0.f && s <= 3.4028234663852886e38f; }
 size_t elem_bytes(int dt) { return dt == RAX_BF16 ? 2 : 4; }
 bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+// log2 of a page size (a power of two from 1 to 2^20), -1 otherwise.
+int page_shift_of(int32_t page_size) {
+    if (page_size < 1 || page_size > (1 << 20) || (page_size & (page_size - 1))) return -1;
+    int s = 0;
+    while ((1 << s) < page_size) ++s;
+    return s;
+}
 
 int check_heads(int32_t hq, int32_t hkv, int32_t d) {
     if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || hq > kMaxGridYZ) return RAX_ERR_SHAPE;
@@ -87,11 +94,13 @@ int extend_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool,
                 int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float sm_scale,
                 float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
                 void* stream, bool ragged = false, const void* k_new = nullptr,
-                const void* v_new = nullptr, const int32_t* store_loc = nullptr) {
+                const void* v_new = nullptr, const int32_t* store_loc = nullptr,
+                int32_t page_shift = 0) {
     if (!dtype_ok(dtype)) return RAX_ERR_DTYPE;
     if (batch < 0 || batch > kMaxGridYZ || total_extend_tokens < 0 || max_extend_len < 0 ||
-        max_seq_len < 0 || num_slots <= 0 || r2t_stride <= 0 || max_seq_len > r2t_stride ||
-        max_extend_len > max_seq_len || max_extend_len > total_extend_tokens)
+        max_seq_len < 0 || num_slots <= 0 || r2t_stride <= 0 ||
+        max_seq_len > (r2t_stride << page_shift) || max_extend_len > max_seq_len ||
+        max_extend_len > total_extend_tokens)
         return RAX_ERR_SHAPE;
     int st = check_heads(n_q_heads, n_kv_heads, head_dim);
     if (st != RAX_OK) return st;
@@ -118,6 +127,7 @@ int extend_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool,
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     a.kv8 = kv8; a.k_scale = k_scale; a.v_scale = v_scale;
     a.ragged = ragged; a.k_new = k_new; a.v_new = v_new; a.store_loc = store_loc;
+    a.page_shift = page_shift;
     const int rc = dtype == RAX_BF16 ? rax::launch_extend_bf16(a, (hipStream_t)stream)
                                      : rax::launch_extend_fp32(a, (hipStream_t)stream);
     return rc == 0 ? RAX_OK : RAX_ERR_LAUNCH;
@@ -129,10 +139,10 @@ int decode_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool,
                 const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
                 int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                 float sm_scale, float k_scale, float v_scale, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, int32_t page_shift = 0) {
     if (!dtype_ok(dtype)) return RAX_ERR_DTYPE;
     if (batch < 0 || batch > kMaxGridYZ || max_seq_len < 0 || num_slots <= 0 || r2t_stride <= 0 ||
-        max_seq_len > r2t_stride)
+        max_seq_len > (r2t_stride << page_shift))
         return RAX_ERR_SHAPE;
     int st = check_heads(n_q_heads, n_kv_heads, head_dim);
     if (st != RAX_OK) return st;
@@ -159,6 +169,7 @@ int decode_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool,
     a.head_dim = head_dim; a.sm_scale = sm_scale; a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
     a.kv8 = kv8; a.k_scale = k_scale; a.v_scale = v_scale;
+    a.page_shift = page_shift;
     const int rc = dtype == RAX_BF16 ? rax::launch_decode_bf16(a, (hipStream_t)stream)
                                      : rax::launch_decode_fp32(a, (hipStream_t)stream);
     return rc == 0 ? RAX_OK : RAX_ERR_LAUNCH;
@@ -248,6 +259,38 @@ int rax_extend_attention_ragged(int dtype, const void* q, void* o, const void* k
                        total_extend_tokens, max_extend_len, max_seq_len, n_q_heads, n_kv_heads,
                        head_dim, sm_scale, 1.f, 1.f, workspace, workspace_bytes, stream, true, k_new,
                        v_new, store_loc);
+}
+
+int rax_extend_attention_paged(int dtype, const void* q, void* o, const void* k_pool,
+                               const void* v_pool, int64_t num_slots, const int32_t* page_table,
+                               int64_t pt_stride, int32_t page_size,
+                               const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                               const int32_t* extend_lens, const int32_t* extend_start_loc,
+                               int32_t batch, int64_t total_extend_tokens, int32_t max_extend_len,
+                               int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                               int32_t head_dim, float sm_scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    const int ps = page_shift_of(page_size);
+    if (ps < 0 || (pt_stride > 0 && pt_stride > (INT64_MAX >> 21))) return RAX_ERR_SHAPE;
+    return extend_call(dtype, false, q, o, k_pool, v_pool, num_slots, page_table, pt_stride,
+                       req_pool_indices, prefix_lens, extend_lens, extend_start_loc, batch,
+                       total_extend_tokens, max_extend_len, max_seq_len, n_q_heads, n_kv_heads,
+                       head_dim, sm_scale, 1.f, 1.f, workspace, workspace_bytes, stream, false,
+                       nullptr, nullptr, nullptr, ps);
+}
+
+int rax_decode_attention_paged(int dtype, const void* q, void* o, const void* k_pool,
+                               const void* v_pool, int64_t num_slots, const int32_t* page_table,
+                               int64_t pt_stride, int32_t page_size,
+                               const int32_t* req_pool_indices, const int32_t* seq_lens,
+                               int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t head_dim, float sm_scale,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    const int ps = page_shift_of(page_size);
+    if (ps < 0 || (pt_stride > 0 && pt_stride > (INT64_MAX >> 21))) return RAX_ERR_SHAPE;
+    return decode_call(dtype, false, q, o, k_pool, v_pool, num_slots, page_table, pt_stride,
+                       req_pool_indices, seq_lens, batch, max_seq_len, n_q_heads, n_kv_heads, head_dim,
+                       sm_scale, 1.f, 1.f, workspace, workspace_bytes, stream, ps);
 }
 
 }  // extern "C"

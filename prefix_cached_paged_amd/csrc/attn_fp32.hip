@@ -17,7 +17,9 @@ namespace {
 
 // RAG (EXTEND only): key positions j >= prefix come from new row s0 + j - prefix of k_new /
 // v_new ([tokens, Hkv, D]) instead of the pool.
-template <int D, bool CAUSAL, bool RAG>
+// PG: r2t is a page table (page size 2^page_shift): position j lives at slot
+// r2t[row, j >> page_shift] << page_shift | (j & (2^page_shift - 1)).
+template <int D, bool CAUSAL, bool RAG, bool PG>
 __global__ __launch_bounds__(64) void attn_rows_fp32_kernel(
     const float* __restrict__ q, float* __restrict__ o, const float* __restrict__ k_pool,
     const float* __restrict__ v_pool, const float* __restrict__ k_new, const float* __restrict__ v_new,
@@ -25,7 +27,7 @@ __global__ __launch_bounds__(64) void attn_rows_fp32_kernel(
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
     const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ extend_start_loc,
     const int32_t* __restrict__ seq_lens, int64_t total_tokens, int32_t max_extend_len,
-    int32_t max_seq_len, int32_t Hq, int32_t Hkv, float sm_scale) {
+    int32_t max_seq_len, int32_t Hq, int32_t Hkv, float sm_scale, int32_t page_shift) {
     constexpr int PER = D / 64;
     __shared__ float qs[D];
     const int lane = threadIdx.x;
@@ -72,7 +74,9 @@ __global__ __launch_bounds__(64) void attn_rows_fp32_kernel(
         const int j = j0 + lane;
         const bool ok = j < nkeys;
         const int jc = ok ? j : nkeys - 1;
-        const int slot = (RAG && jc >= pre) ? 0 : row[jc];
+        const int slot = (RAG && jc >= pre) ? 0
+                         : PG ? (row[jc >> page_shift] << page_shift) | (jc & ((1 << page_shift) - 1))
+                              : row[jc];
         const float* kr = (RAG && jc >= pre) ? k_new + (int64_t)(s0 + jc - pre) * pool_row + (int64_t)g * D
                                              : k_pool + (int64_t)slot * pool_row + (int64_t)g * D;
         float dot = 0.f;
@@ -113,23 +117,23 @@ __global__ __launch_bounds__(64) void attn_rows_fp32_kernel(
     for (int k = 0; k < PER; ++k) orow[64 * k + lane] = acc[k] * inv;
 }
 
-template <bool CAUSAL, bool RAG>
+template <bool CAUSAL, bool RAG, bool PG>
 int launch_rows(const AttnArgs& a, hipStream_t stream) {
     const unsigned gx = CAUSAL ? (unsigned)a.max_extend_len : 1u;
     if (gx == 0 || a.batch == 0) return 0;
     dim3 grid(gx, a.n_q_heads, a.batch);
     if (a.head_dim == 128) {
-        hipLaunchKernelGGL((attn_rows_fp32_kernel<128, CAUSAL, RAG>), grid, dim3(64), 0, stream,
+        hipLaunchKernelGGL((attn_rows_fp32_kernel<128, CAUSAL, RAG, PG>), grid, dim3(64), 0, stream,
                            (const float*)a.q, (float*)a.o, (const float*)a.k_pool, (const float*)a.v_pool,
                            (const float*)a.k_new, (const float*)a.v_new, a.r2t, a.r2t_stride, a.req_pool_indices, a.prefix_lens, a.extend_lens,
                            a.extend_start_loc, a.seq_lens, a.total_tokens, a.max_extend_len,
-                           a.max_seq_len, a.n_q_heads, a.n_kv_heads, a.sm_scale);
+                           a.max_seq_len, a.n_q_heads, a.n_kv_heads, a.sm_scale, a.page_shift);
     } else {
-        hipLaunchKernelGGL((attn_rows_fp32_kernel<64, CAUSAL, RAG>), grid, dim3(64), 0, stream,
+        hipLaunchKernelGGL((attn_rows_fp32_kernel<64, CAUSAL, RAG, PG>), grid, dim3(64), 0, stream,
                            (const float*)a.q, (float*)a.o, (const float*)a.k_pool, (const float*)a.v_pool,
                            (const float*)a.k_new, (const float*)a.v_new, a.r2t, a.r2t_stride, a.req_pool_indices, a.prefix_lens, a.extend_lens,
                            a.extend_start_loc, a.seq_lens, a.total_tokens, a.max_extend_len,
-                           a.max_seq_len, a.n_q_heads, a.n_kv_heads, a.sm_scale);
+                           a.max_seq_len, a.n_q_heads, a.n_kv_heads, a.sm_scale, a.page_shift);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -139,15 +143,18 @@ int launch_rows(const AttnArgs& a, hipStream_t stream) {
 // Ragged fp32 EXTEND with a store: the rows are stored by the copy kernel first (no slot it
 // writes is read by the attention kernel, so the order only keeps the pool consistent).
 int launch_extend_fp32(const AttnArgs& a, hipStream_t stream) {
-    if (!a.ragged) return launch_rows<true, false>(a, stream);
+    if (a.page_shift) return a.ragged ? -1 : launch_rows<true, false, true>(a, stream);
+    if (!a.ragged) return launch_rows<true, false, false>(a, stream);
     if (a.store_loc != nullptr) {
         const int64_t row_bytes = (int64_t)a.n_kv_heads * a.head_dim * 4;
         if (launch_kv_store(a.k_new, a.v_new, a.store_loc, a.total_tokens, const_cast<void*>(a.k_pool),
                             const_cast<void*>(a.v_pool), row_bytes, stream) != 0)
             return -1;
     }
-    return launch_rows<true, true>(a, stream);
+    return launch_rows<true, true, false>(a, stream);
 }
-int launch_decode_fp32(const AttnArgs& a, hipStream_t stream) { return launch_rows<false, false>(a, stream); }
+int launch_decode_fp32(const AttnArgs& a, hipStream_t stream) {
+    return a.page_shift ? launch_rows<false, false, true>(a, stream) : launch_rows<false, false, false>(a, stream);
+}
 
 }  // namespace rax

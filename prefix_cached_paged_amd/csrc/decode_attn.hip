@@ -206,7 +206,9 @@ struct Seg {
 // FUSED (batch <= kDecFusedBatch): every workgroup computes the request offsets itself (a
 // scan of the padded lengths in LDS) instead of reading them from decode_plan_kernel, which is
 // then not launched; workgroup 0 writes meta and P for the merge kernel.
-template <int D, bool OFF32, bool FUSED, bool KV8>
+// PG: r2t is a page table (page size 2^page_shift): position j lives at slot
+// r2t[row, j >> page_shift] << page_shift | (j & (2^page_shift - 1)).
+template <int D, bool OFF32, bool FUSED, bool KV8, bool PG>
 __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
@@ -214,7 +216,8 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
     int32_t B, int32_t Hq, int32_t Hkv, int32_t G, int32_t groups, int32_t n_target,
     float scale_log2, float out_scale, int64_t* __restrict__ meta, int64_t* __restrict__ P,
     const int32_t* __restrict__ first_req, float* __restrict__ o_part,
-    float* __restrict__ lse_part) {
+    float* __restrict__ lse_part, int32_t page_shift) {
+    static_assert(!(PG && KV8), "page tables are read by the bf16 pool path");
     constexpr int S = D / 32;   // 32-wide K-dim steps of the score MFMA
     constexpr int DT = D / 16;  // 16-row output tiles; also head_dim elements per lane per V row
     __shared__ int32_t slot_lds[kDecMaxKeys + kDecKeysPerIter];
@@ -325,12 +328,19 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
         // With 128-key iterations (FP8 pools) the last one may run 64 keys past the range:
         // stage one more block of slots there (positions clamped to the request, then masked).
         const int nb = sg.n / kDecKeysPerIter + ((KV8 && RAX_DEC_KPI8 > 64 && si == n_seg - 1) ? 1 : 0);
-        for (int j = (wv - j0 % kDecWaves + kDecWaves) % kDecWaves; j < nb; j += kDecWaves)
-            __builtin_amdgcn_global_load_lds(
-                (__attribute__((address_space(1))) void*)(
-                    row + min(sg.pos0 + j * kDecKeysPerIter + lane, sg.len - 1)),
-                (__attribute__((address_space(3))) void*)(slot_lds + sg.lo + j * kDecKeysPerIter),
-                4, 0, 0);
+        for (int j = (wv - j0 % kDecWaves + kDecWaves) % kDecWaves; j < nb; j += kDecWaves) {
+            const int pos = min(sg.pos0 + j * kDecKeysPerIter + lane, sg.len - 1);
+            if constexpr (PG) {
+                // the slot is computed from the position's page entry
+                slot_lds[sg.lo + j * kDecKeysPerIter + lane] =
+                    (row[pos >> page_shift] << page_shift) | (pos & ((1 << page_shift) - 1));
+            } else {
+                __builtin_amdgcn_global_load_lds(
+                    (__attribute__((address_space(1))) void*)(row + pos),
+                    (__attribute__((address_space(3))) void*)(slot_lds + sg.lo + j * kDecKeysPerIter),
+                    4, 0, 0);
+            }
+        }
     }
     __syncthreads();
 
@@ -608,6 +618,7 @@ size_t decode_workspace(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, i
 }
 
 int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
+    if (a.kv8 && a.page_shift) return -1;
     const int32_t G = a.n_q_heads / a.n_kv_heads;
     const int32_t groups = decode_groups(a.n_kv_heads);
     const int32_t grid = decode_grid(a.batch, a.max_seq_len, a.n_kv_heads);
@@ -631,15 +642,17 @@ int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
     const dim3 sgrid((uint32_t)grid * (uint32_t)groups);
     const dim3 mgrid((a.batch * a.n_q_heads + 3) / 4);
     const bool off32 = pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, a.kv8 ? 1 : 2);
-#define RAX_DEC_SPLIT4(DD, OFF, FU, K8)                                                         \
-    hipLaunchKernelGGL((decode_split_kernel<DD, OFF, FU, K8>), sgrid, dim3(64 * kDecWaves), 0,   \
-                       stream, (const uint16_t*)a.q, (const uint16_t*)a.k_pool,                   \
+#define RAX_DEC_SPLIT4(DD, OFF, FU, K8, PGT)                                                    \
+    hipLaunchKernelGGL((decode_split_kernel<DD, OFF, FU, K8, PGT>), sgrid, dim3(64 * kDecWaves), \
+                       0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k_pool,                \
                        (const uint16_t*)a.v_pool, a.r2t, a.r2t_stride, a.req_pool_indices,        \
                        a.seq_lens, a.max_seq_len, a.batch, a.n_q_heads, a.n_kv_heads, G, groups,  \
-                       n_target, scale_log2, out_scale, meta, P, first, o_part, lse)
+                       n_target, scale_log2, out_scale, meta, P, first, o_part, lse, a.page_shift)
 #define RAX_DEC_SPLIT3(DD, OFF, FU)                                                             \
     do {                                                                                        \
-        if (a.kv8) RAX_DEC_SPLIT4(DD, OFF, FU, true); else RAX_DEC_SPLIT4(DD, OFF, FU, false);  \
+        if (a.kv8) RAX_DEC_SPLIT4(DD, OFF, FU, true, false);                                    \
+        else if (a.page_shift) RAX_DEC_SPLIT4(DD, OFF, FU, false, true);                        \
+        else RAX_DEC_SPLIT4(DD, OFF, FU, false, false);                                         \
     } while (0)
 #define RAX_DEC_SPLIT(DD, OFF)                                                                  \
     do {                                                                                        \

@@ -110,6 +110,14 @@ __device__ __forceinline__ const char* pool_row_ptr(const char* base, int slot, 
     }
 }
 
+// Slot of key position pos (wave-uniform): the table entry itself, or with a page table the
+// page's first slot plus the position within the page.
+template <bool PG>
+__device__ __forceinline__ int slot_at(const int32_t* row, int pos, int page_shift) {
+    if constexpr (PG) return (row[pos >> page_shift] << page_shift) | (pos & ((1 << page_shift) - 1));
+    else return row[pos];
+}
+
 // Byte offset of row `idx` (a pool slot, or a new row of the ragged suffix): a 24-bit multiply
 // when both the pool and the new rows fit 32-bit offsets (OFF32), 64-bit otherwise.
 template <bool OFF32>
@@ -128,7 +136,9 @@ __device__ __forceinline__ int64_t row_off(int idx, uint32_t row_bytes) {
 // which other waves read them).
 #define RAX_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
-template <int G, bool OFF32, bool KV8, bool RAG>
+// PG: the table is a page table (page size 2^page_shift): position j lives at slot
+// table[row, j >> page_shift] << page_shift | (j & (2^page_shift - 1)).
+template <int G, bool OFF32, bool KV8, bool RAG, bool PG>
 __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const char* __restrict__ k_pool,
     const char* __restrict__ v_pool, const char* __restrict__ k_new, const char* __restrict__ v_new,
@@ -136,11 +146,12 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
     const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ extend_start_loc,
     int64_t total_tokens, int32_t max_extend_len, int32_t max_seq_len, int32_t Hq, int32_t Hkv,
-    int32_t batch, int32_t tiles, float scale_log2, float out_scale) {
+    int32_t batch, int32_t tiles, float scale_log2, float out_scale, int32_t page_shift) {
     constexpr int D = kExtD;
     constexpr int BQ = kExtBM / G;  // tokens per workgroup
     constexpr int EB = KV8 ? 1 : 2;  // bytes per pool element
     static_assert(!(KV8 && RAG), "ragged suffix rows are bf16, as the pools");
+    static_assert(!(PG && (KV8 || RAG)), "page tables are read by the bf16 pool path");
 
     // Three K/V tile buffers, row-major [key][16 units of 8 bf16], swizzled. Separate LDS
     // objects, each named statically below.
@@ -215,10 +226,14 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         const int pb_ = (TILE) * kExtBN + 8 * wave_u;                                       \
         const int lim_ = kend - 1;                                                          \
         nxpos = pb_;                                                                        \
-        nx0 = row[min(pb_ + 0, lim_)]; nx1 = row[min(pb_ + 1, lim_)];                       \
-        nx2 = row[min(pb_ + 2, lim_)]; nx3 = row[min(pb_ + 3, lim_)];                       \
-        nx4 = row[min(pb_ + 4, lim_)]; nx5 = row[min(pb_ + 5, lim_)];                       \
-        nx6 = row[min(pb_ + 6, lim_)]; nx7 = row[min(pb_ + 7, lim_)];                       \
+        nx0 = slot_at<PG>(row, min(pb_ + 0, lim_), page_shift);                            \
+        nx1 = slot_at<PG>(row, min(pb_ + 1, lim_), page_shift);                            \
+        nx2 = slot_at<PG>(row, min(pb_ + 2, lim_), page_shift);                            \
+        nx3 = slot_at<PG>(row, min(pb_ + 3, lim_), page_shift);                            \
+        nx4 = slot_at<PG>(row, min(pb_ + 4, lim_), page_shift);                            \
+        nx5 = slot_at<PG>(row, min(pb_ + 5, lim_), page_shift);                            \
+        nx6 = slot_at<PG>(row, min(pb_ + 6, lim_), page_shift);                            \
+        nx7 = slot_at<PG>(row, min(pb_ + 7, lim_), page_shift);                            \
     }
     // 4 vector-memory operations per wave: K rows (i = 0, 1), then V rows.
 #define RAX_COPY(KB, VB)                                                                    \
@@ -489,7 +504,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
 #undef RAX_CONVERT8
 #undef RAX_TILE8
 
-template <int G, bool OFF32, bool KV8, bool RAG>
+template <int G, bool OFF32, bool KV8, bool RAG, bool PG>
 int launch_g(const AttnArgs& a, hipStream_t stream) {
     constexpr int BQ = kExtBM / G;
     const int tiles = (a.max_extend_len + BQ - 1) / BQ;
@@ -500,30 +515,37 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
     // FP8 pools: the K scale multiplies every score, the V scale every output element.
     const float scale_log2 = a.sm_scale * kLog2e * (KV8 ? a.k_scale : 1.f);
     const float out_scale = KV8 ? a.v_scale : 1.f;
-    hipLaunchKernelGGL((extend_kernel<G, OFF32, KV8, RAG>), dim3((unsigned)blocks), dim3(kExtThreads),
+    hipLaunchKernelGGL((extend_kernel<G, OFF32, KV8, RAG, PG>), dim3((unsigned)blocks), dim3(kExtThreads),
                        0, stream, (const uint16_t*)a.q, (uint16_t*)a.o, (const char*)a.k_pool,
                        (const char*)a.v_pool, (const char*)a.k_new, (const char*)a.v_new, a.store_loc,
                        a.r2t, a.r2t_stride, a.req_pool_indices,
                        a.prefix_lens, a.extend_lens, a.extend_start_loc, a.total_tokens,
                        a.max_extend_len, a.max_seq_len, a.n_q_heads, a.n_kv_heads, a.batch, tiles,
-                       scale_log2, out_scale);
+                       scale_log2, out_scale, a.page_shift);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 template <int G>
 int launch_g(const AttnArgs& a, hipStream_t stream) {
     if (a.kv8) {
-        if (a.ragged) return -1;
+        if (a.ragged || a.page_shift) return -1;
         return pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 1)
-                   ? launch_g<G, true, true, false>(a, stream)
-                   : launch_g<G, false, true, false>(a, stream);
+                   ? launch_g<G, true, true, false, false>(a, stream)
+                   : launch_g<G, false, true, false, false>(a, stream);
     }
     // ragged: the new rows are addressed like pool rows (row index total_tokens - 1 at most)
     const bool off32 = pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 2) &&
                        (!a.ragged || pool_fits_32bit_offsets(a.total_tokens, a.n_kv_heads, a.head_dim, 2));
-    if (a.ragged)
-        return off32 ? launch_g<G, true, false, true>(a, stream) : launch_g<G, false, false, true>(a, stream);
-    return off32 ? launch_g<G, true, false, false>(a, stream) : launch_g<G, false, false, false>(a, stream);
+    if (a.ragged) {
+        if (a.page_shift) return -1;
+        return off32 ? launch_g<G, true, false, true, false>(a, stream)
+                     : launch_g<G, false, false, true, false>(a, stream);
+    }
+    if (a.page_shift)
+        return off32 ? launch_g<G, true, false, false, true>(a, stream)
+                     : launch_g<G, false, false, false, true>(a, stream);
+    return off32 ? launch_g<G, true, false, false, false>(a, stream)
+                 : launch_g<G, false, false, false, false>(a, stream);
 }
 
 }  // namespace

@@ -42,6 +42,9 @@ struct AttnArgs {
     const void* k_new;
     const void* v_new;
     const int32_t* store_loc;
+    // Page table instead of a token table (r2t then holds pages): log2 of the page size, 0 for
+    // the token-granular table.
+    int32_t page_shift;
     void* workspace;
     size_t workspace_bytes;
 };

@@ -44,6 +44,12 @@ _SIGS = {
                                                    _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_i32,
                                                    _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f,
                                                    _c_p, _c_sz, _c_p]),
+    "rax_extend_attention_paged": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64,
+                                                  _c_i32, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64, _c_i32,
+                                                  _c_i32, _c_i32, _c_i32, _c_i32, _c_f, _c_p, _c_sz, _c_p]),
+    "rax_decode_attention_paged": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64,
+                                                  _c_i32, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                  _c_f, _c_p, _c_sz, _c_p]),
     "rax_decode_workspace_bytes": (_c_sz, [ctypes.c_int, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "rax_decode_attention": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64,
                                             _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f,
@@ -205,6 +211,41 @@ def extend_attention_ragged(q, o, k_new, v_new, k_pool, v_pool, req_to_token, re
                                               _idx(extend_start_loc), B, N, int(max_extend_len), int(max_seq_len),
                                               Hq, Hkv, D, float(sm_scale), _ptr(workspace), wbytes, _stream(stream)),
            "rax_extend_attention_ragged")
+
+
+def extend_attention_paged(q, o, k_pool, v_pool, page_table, page_size, req_pool_indices, prefix_lens,
+                           extend_lens, extend_start_loc, max_extend_len, max_seq_len, sm_scale, workspace=None,
+                           stream=None):
+    """EXTEND with keys addressed through a page table of ``page_size`` slots per page."""
+    N, Hq, D = q.shape
+    S, Hkv, Dk = k_pool.shape
+    dt = _dtype(q, o, k_pool, v_pool)
+    B = prefix_lens.shape[0]
+    need = extend_workspace_bytes(dt, B, N, max_extend_len, max_seq_len, Hq, Hkv, D)
+    workspace = _workspace(need, workspace, q.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().rax_extend_attention_paged(dt, _ptr(q), _ptr(o), _ptr(k_pool), _ptr(v_pool), S,
+                                             _idx(page_table), page_table.shape[1], int(page_size),
+                                             _idx(req_pool_indices), _idx(prefix_lens), _idx(extend_lens),
+                                             _idx(extend_start_loc), B, N, int(max_extend_len), int(max_seq_len),
+                                             Hq, Hkv, D, float(sm_scale), _ptr(workspace), wbytes, _stream(stream)),
+           "rax_extend_attention_paged")
+
+
+def decode_attention_paged(q, o, k_pool, v_pool, page_table, page_size, req_pool_indices, seq_lens, max_seq_len,
+                           sm_scale, workspace=None, stream=None):
+    """DECODE with keys addressed through a page table of ``page_size`` slots per page."""
+    B, Hq, D = q.shape
+    S, Hkv, Dk = k_pool.shape
+    dt = _dtype(q, o, k_pool, v_pool)
+    need = decode_workspace_bytes(dt, B, max_seq_len, Hq, Hkv, D)
+    workspace = _workspace(need, workspace, q.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().rax_decode_attention_paged(dt, _ptr(q), _ptr(o), _ptr(k_pool), _ptr(v_pool), S,
+                                             _idx(page_table), page_table.shape[1], int(page_size),
+                                             _idx(req_pool_indices), _idx(seq_lens), B, int(max_seq_len), Hq, Hkv,
+                                             D, float(sm_scale), _ptr(workspace), wbytes, _stream(stream)),
+           "rax_decode_attention_paged")
 
 
 def decode_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, seq_lens, max_seq_len, sm_scale,

@@ -23,7 +23,8 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"rax_version", "rax_status_str", "rax_kv_store", "rax_extend_workspace_bytes",
                           "rax_extend_attention", "rax_decode_workspace_bytes", "rax_decode_attention",
                           "rax_decode_num_splits", "rax_kv_store_fp8", "rax_extend_attention_fp8",
-                          "rax_decode_attention_fp8", "rax_extend_attention_ragged"}
+                          "rax_decode_attention_fp8", "rax_extend_attention_ragged",
+                          "rax_extend_attention_paged", "rax_decode_attention_paged"}
     out = subprocess.run(["nm", "-D", "--defined-only", R.library_path()], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for n in names:
@@ -174,3 +175,26 @@ def test_ragged_extend_checks_before_launching():
     assert rag(dt=7) == 3
     assert rag(D=96) == 4
     assert rag(loc=FAKE, S=60, N=100) == 2   # more rows to store than slots
+
+
+def test_paged_calls_check_page_size_and_table_width():
+    L = lib()
+    # (dtype, q, o, kp, vp, S, pt, pt_stride, P, rpi, pre, ext, start, B, N, maxe, maxL, Hq, Hkv, D, sm, ws, wsb, st)
+    ext = lambda **kw: L.rax_extend_attention_paged(0, FAKE, FAKE, FAKE, FAKE, 4096, kw.get("pt", FAKE),
+                                                    kw.get("stride", 32), kw.get("P", 16), FAKE, FAKE, FAKE, FAKE,
+                                                    kw.get("B", 3), 100, 50, kw.get("L", 300), 8, 2, 128, 0.1,
+                                                    None, 0, None)
+    for bad in (0, 3, 12, -16, 1 << 21):
+        assert ext(P=bad) == 2, bad
+    assert ext(L=600) == 2               # 32 pages of 16 cover 512 positions only
+    assert ext(B=0) == 0
+    assert ext(pt=None) == 1
+    # (dtype, q, o, kp, vp, S, pt, pt_stride, P, rpi, seq, B, maxL, Hq, Hkv, D, sm, ws, wsb, stream)
+    dec = lambda **kw: L.rax_decode_attention_paged(0, FAKE, FAKE, FAKE, FAKE, 4096, kw.get("pt", FAKE),
+                                                    kw.get("stride", 8), kw.get("P", 64), FAKE, FAKE,
+                                                    kw.get("B", 3), kw.get("L", 512), 8, 2, 128, 0.1, FAKE,
+                                                    1 << 30, None)
+    assert dec(P=48) == 2
+    assert dec(L=513) == 2               # 8 pages of 64
+    assert dec(B=0) == 0
+    assert dec(pt=None) == 1
