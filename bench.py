@@ -9,7 +9,8 @@ HBM. Default workload: the mixed chunked-prefill batch (one 2,048-token chunk on
 decode_attention_fp8; per-pool scales 4 sigma / 448), the pools converted from the bf16 ones
 before timing. ``--ragged`` runs EXTEND on the ragged path: the suffix K/V read from the new
 rows and stored by the same kernel (extend_attention_ragged with store_loc); kv_store then
-writes only the decode requests' current tokens.
+writes only the decode requests' current tokens. ``--page-size P`` draws the workload with
+pages of P slots and runs EXTEND and DECODE through the page table (the _paged calls).
 
 Prints ONE JSON line. ``value`` is the EXTEND attention throughput in TFLOP/s (algorithmic
 FLOPs: 4 * head_dim * q_heads per attended pair, masked pairs not counted); the DECODE KV
@@ -245,6 +246,8 @@ def main():
                     help="KV pool element: the workload's bf16, or FP8 E4M3 with per-pool scales")
     ap.add_argument("--ragged", action="store_true",
                     help="EXTEND via extend_attention_ragged with the fused store of the suffix rows")
+    ap.add_argument("--page-size", type=int, default=1,
+                    help="pool pages of this many slots, read through a page table (1 = token table)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step as HIP graph replays (reported beside the eager figures)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -276,6 +279,9 @@ def main():
     rax.load()  # fails loudly if the HIP library is missing
     cfg = args.config
     spec = W.CONFIGS[cfg]
+    if args.page_size != 1:
+        import dataclasses
+        spec = dataclasses.replace(spec, page_size=args.page_size)
     seed = args.seed if args.seed is not None else W.TIMING_SEEDS[cfg]
     log(f"generating workload {spec.name} seed {seed}")
     wl = W.make_workload(spec, seed)
@@ -284,6 +290,11 @@ def main():
     dt = rax.BF16 if spec.dtype == "bf16" else rax.FP32
     kv8 = args.kv == "fp8"
     rag = args.ragged and dw.ext is not None
+    paged = args.page_size != 1
+    if paged and (kv8 or rag):
+        print("--page-size runs the bf16/fp32 pool path only", file=sys.stderr)
+        sys.exit(2)
+    pt = torch.from_numpy(wl.page_table).to("cuda:0") if paged else None
     if rag and kv8:
         print("--ragged is for bf16/fp32 pools", file=sys.stderr)
         sys.exit(2)
@@ -334,6 +345,8 @@ def main():
             elif rag:
                 rax.extend_attention_ragged(e["q"], e["o"], dw.k_new[:n_ext], dw.v_new[:n_ext], dw.k_pool,
                                             dw.v_pool, *ea[4:], store_loc=dw.store_loc[:n_ext])
+            elif paged:
+                rax.extend_attention_paged(e["q"], e["o"], dw.k_pool, dw.v_pool, pt, args.page_size, *ea[5:])
             else:
                 rax.extend_attention(*ea)
         if ev is not None:
@@ -344,6 +357,9 @@ def main():
                   d["max_seq_len"], wl.sm_scale)
             if kv8:
                 rax.decode_attention_fp8(*da, k_scale, v_scale, workspace=ws)
+            elif paged:
+                rax.decode_attention_paged(d["q"], d["o"], dw.k_pool, dw.v_pool, pt, args.page_size, *da[5:],
+                                           workspace=ws)
             else:
                 rax.decode_attention(*da, workspace=ws)
         if ev is not None:
@@ -454,6 +470,8 @@ def main():
         cfgd["kv_scales"] = [k_scale, v_scale]
     if rag:
         cfgd["extend_path"] = "ragged suffix, fused store"
+    if paged:
+        cfgd["page_size"] = args.page_size
     if wl.extend is not None:
         cfgd["extend"] = {"batch": wl.extend.batch, "new_tokens": wl.extend.total_tokens,
                           "prefix_lens": sorted(set(int(x) for x in wl.extend.prefix_lens))[:4]}
