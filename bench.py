@@ -90,7 +90,9 @@ def pmc_summary(out_path: str, fetch_dir: str, write_dir: str, copy_fetch_dir: s
                 if r["Counter_Name"] == counter:
                     vals.setdefault(r["Kernel_Name"].split("(")[0].split("<")[0].split("::")[-1], []).append(
                         float(r["Counter_Value"]))
-        return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+        # median over dispatches: a set-up dispatch of another size (the FP8 mode converts the
+        # whole pool once with the store kernel) does not move the per-step figure
+        return {k: (float(np.median(v)), len(v)) for k, v in vals.items()}
 
     def copy_kib(d, counter):
         best = 0.0
@@ -105,7 +107,8 @@ def pmc_summary(out_path: str, fetch_dir: str, write_dir: str, copy_fetch_dir: s
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
     lines = ["# HBM traffic per dispatch (rocprofv3 --pmc), MI355X", "#",
              "# Each counter is scaled by what it reads for a plain device copy of 1 GiB",
-             "# (bench.py --copy-calibration): bytes = KiB * 1024 * factor.", "#",
+             "# (bench.py --copy-calibration): bytes = KiB * 1024 * factor. Per kernel: the median",
+             "# over its dispatches.", "#",
              "# Commands (repository root on the GPU box, TMPDIR=/tmp):"]
     lines += ["#   " + c for c in command.split(" ;; ")]
     lines += ["#", f"calibration copy_bytes={COPY_BYTES} copy_fetch_kib={cf:.1f} copy_write_kib={cw:.1f} "
