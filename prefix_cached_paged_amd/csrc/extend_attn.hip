@@ -16,11 +16,20 @@
 //    workgroup is what keeps the kernel off the memory roofline.
 //  * Key tiles of 64 rows (256 B per kv head per row) are copied HBM -> LDS by the gfx950
 //    global_load_lds_dwordx4 (16 B per lane, no registers), each lane fetching the unit that
-//    the LDS swizzle stores at its destination. Three LDS buffers: tile i is consumed while
-//    tiles i+1 and i+2 are in flight; slot numbers are loaded one tile before their copy.
-//    The buffers are separate LDS objects and the loop is unrolled by three, so every read
-//    names its buffer and the compiler does not wait on copies into the other buffers. Before
-//    each barrier the wave waits (vmcnt) only for the copies of the tile it is about to read.
+//    the LDS swizzle stores at its destination. Four LDS buffers: tile i is consumed while
+//    tiles i+1 and i+2 are in flight, and tile i-1's V is still read (ping-pong, below);
+//    slot numbers are loaded one tile before their copy. The buffers are separate LDS objects
+//    and the loop is unrolled by four, so every read names its buffer and the compiler does
+//    not wait on copies into the other buffers. Before each barrier the wave waits (vmcnt)
+//    only for the copies of the tile it is about to read.
+//  * Ping-pong: the per-tile barrier would keep the two waves of a SIMD (w and w + 4) in the
+//    same phase, both issuing MFMAs, then both the softmax. Waves 4-7 therefore lag by half a
+//    tile: in iteration i they run the softmax and P V of tile i-1, then the scores of tile i,
+//    while waves 0-3 run tile i whole; each SIMD's MFMA pipe then meets the other wave's
+//    softmax for two thirds of the iteration (+2 to +8% measured).
+//  * FP8 pools: E4M3 tiles go through three staging buffers and are widened to the bf16
+//    tiles by the lane that copied them; the compute is the same, without the ping-pong
+//    (4 bf16 buffers and 3 staging buffers would exceed the 160 KB of LDS).
 //  * S^T = K Q^T with 32x32x16 bf16 MFMAs: keys are the M dimension (read from LDS), query
 //    rows the N dimension (Q stays in registers for the whole key loop). The C layout puts
 //    one query row per lane column, so the row max/sum are per lane plus one exchange with
@@ -126,6 +135,7 @@ __device__ __forceinline__ int64_t row_off(int idx, uint32_t row_bytes) {
     else return (int64_t)(uint32_t)idx * row_bytes;
 }
 
+
 // s_waitcnt vmcnt(N), leaving the other counters unconstrained (gfx9 encoding: vmcnt[3:0] in
 // bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
 #define RAX_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt((((N) & 15) | (((N) >> 4) << 14)) | 0x0F70)
@@ -157,6 +167,8 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // objects, each named statically below.
     __shared__ uint4 kb0[kExtBN * 16], kb1[kExtBN * 16], kb2[kExtBN * 16];
     __shared__ uint4 vb0[kExtBN * 16], vb1[kExtBN * 16], vb2[kExtBN * 16];
+    // bf16 pools use a fourth buffer (ping-pong, below); FP8 pools three staging buffers.
+    __shared__ uint4 kb3[KV8 ? 1 : kExtBN * 16], vb3[KV8 ? 1 : kExtBN * 16];
     // FP8 pools: three staging buffers of raw E4M3 tiles, [key][8 units of 16 bytes].
     constexpr int SU = KV8 ? kExtBN * 8 : 1;
     __shared__ uint4 sk0[SU], sk1[SU], sk2[SU], sv0[SU], sv1[SU], sv2[SU];
@@ -310,17 +322,17 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const int last_q = p + t;        // last key position this row may see
     const int diag_from = p + t0;    // a tile whose last key exceeds this needs the mask
 
-    // One tile IT from buffers (KB, VB): wait for its copies, barrier, scores, (mask), softmax
-    // and P V, then start the copy of tile IT+2 into (KN, VN), whose previous contents (tile
-    // IT-1) every wave finished with before the barrier. Issuing the copy after this tile's
-    // LDS reads keeps at most two tiles of copies in flight where the reads happen, which the
-    // compiler can track without adding waits of its own.
-    // The only vector-memory operations are the copies (4 per tile), issued two tiles ahead:
-    // when tile IT is needed the younger ones are the copies of IT+1, so wait until at most 4
-    // (0 at the last tile) are outstanding.
-#define RAX_COMPUTE(IT, KB, VB, MASKABLE)                                                   \
+    // Per tile: scores (QK), (mask,) softmax (SM), P V (PV). An iteration waits for its tile's
+    // copies, passes the barrier, computes, then starts the copy of tile IT+2 into a buffer
+    // every wave finished with before the barrier. Issuing the copy after this tile's LDS reads
+    // keeps the copies in flight where the reads happen to buffers the compiler can tell apart,
+    // so it adds no waits of its own. The only vector-memory operations are the copies (4 per
+    // tile), issued two tiles ahead: when tile IT is needed the younger ones are the copies of
+    // IT+1, so wait until at most 4 (0 at the last tile) are outstanding.
+    f32x16 st[2];   // scores of the tile being processed
+    uint4 pf[4];    // its probabilities (bf16), the B operand of P V
+#define RAX_QK(KB)                                                                          \
     {                                                                                       \
-        f32x16 st[2];                                                                       \
         _Pragma("unroll") for (int mb = 0; mb < 2; ++mb) {                                  \
             _Pragma("unroll") for (int i = 0; i < 16; ++i) st[mb][i] = 0.f;                 \
             const int key = 32 * mb + col;                                                  \
@@ -329,6 +341,9 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
                 st[mb] = mfma32x32x16(as_bf16x8(a), qop[s], st[mb]);                        \
             }                                                                               \
         }                                                                                   \
+    }
+#define RAX_SM(IT, MASKABLE)                                                                \
+    {                                                                                       \
         if (MASKABLE && __builtin_amdgcn_readfirstlane((IT) * kExtBN + kExtBN - 1 > diag_from)) { \
             const int j0_ = (IT) * kExtBN;                                                  \
             _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                \
@@ -348,7 +363,6 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
             lsum *= alpha;                                                                  \
             _Pragma("unroll") for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;         \
         }                                                                                   \
-        uint4 pf[4];                                                                        \
         _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                  \
             float pv[8];                                                                    \
             _Pragma("unroll") for (int j = 0; j < 8; ++j)                                   \
@@ -362,6 +376,9 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
             lsum = add_bf16x2(pf[kk].z, lsum);                                              \
             lsum = add_bf16x2(pf[kk].w, lsum);                                              \
         }                                                                                   \
+    }
+#define RAX_PV(VB)                                                                          \
+    {                                                                                       \
         const char* vbb = (const char*)(VB);                                                \
         _Pragma("unroll") for (int dt = 0; dt < D / 32; ++dt) {                             \
             const int unit = 4 * dt + 2 * dh + (cc >> 1);                                   \
@@ -375,11 +392,25 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
             }                                                                               \
         }                                                                                   \
     }
-#define RAX_TILE(IT, KB, VB, KN, VN, MASKABLE, STEADY)                                      \
+#define RAX_COMPUTE(IT, KB, VB, MASKABLE) { RAX_QK(KB) RAX_SM(IT, MASKABLE) RAX_PV(VB) }
+    // Ping-pong (4 LDS buffers): waves w and w + 4 share a SIMD. Waves 0-3 run tile IT whole
+    // (scores, softmax, P V); waves 4-7 run the softmax and P V of tile IT-1 and then the
+    // scores of tile IT, so that on each SIMD one wave's MFMAs meet the other's softmax. Tile
+    // IT-1's V stays readable during iteration IT: the copy started in iteration IT goes to
+    // the buffer of tile IT-2.
+#define RAX_PTILE(LAG, IT, KB, VB, VP, KN, VN, MASKABLE, STEADY)                            \
     {                                                                                       \
         if (STEADY || (IT) + 1 < ntiles) { RAX_WAIT_VMCNT(4); } else { RAX_WAIT_VMCNT(0); } \
         RAX_BARRIER();                                                                      \
-        RAX_COMPUTE(IT, KB, VB, MASKABLE)                                                   \
+        if (LAG) {                                                                          \
+            if (!STEADY && (IT) == 0) {                                                     \
+            } else {                                                                        \
+                RAX_SM((IT) - 1, MASKABLE) RAX_PV(VP)                                       \
+            }                                                                               \
+            RAX_QK(KB)                                                                      \
+        } else {                                                                            \
+            RAX_COMPUTE(IT, KB, VB, MASKABLE)                                               \
+        }                                                                                   \
         if (STEADY || (IT) + 2 < ntiles) {                                                  \
             RAX_COPY(KN, VN)                                                                \
             if (STEADY || (IT) + 3 < ntiles) RAX_SLOTS((IT) + 3)                            \
@@ -408,7 +439,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const int n_full = min(ntiles, (diag_from + 1) / kExtBN);  // tiles with every key <= p + t0
     int it = 0;
     if constexpr (!KV8) {
-        // prologue: copies of tiles 0 and 1 in flight, slots of tile 2 loaded
+        const bool lag = __builtin_amdgcn_readfirstlane(wave) >= 4;
         RAX_SLOTS(0)
         RAX_COPY(kb0, vb0)
         if (ntiles > 1) {
@@ -416,24 +447,41 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
             RAX_COPY(kb1, vb1)
         }
         if (ntiles > 2) RAX_SLOTS(2)
-
-        // Tile T lives in buffer T % 3; iteration T starts the copy of tile T+2 into buffer
-        // (T+2) % 3. Both loops advance three tiles at a time from a multiple of three.
-        // Steady state: six or more tiles ahead are full and exist, so the body has no
-        // conditional copies or waits (control-flow joins with different copies in flight
-        // make the compiler add waits of its own).
-        while (it + 6 <= n_full) {
-            RAX_TILE(it, kb0, vb0, kb2, vb2, 0, 1) ++it;
-            RAX_TILE(it, kb1, vb1, kb0, vb0, 0, 1) ++it;
-            RAX_TILE(it, kb2, vb2, kb1, vb1, 0, 1) ++it;
+        // Tile T lives in buffer T % 4; iteration T starts the copy of tile T+2 into buffer
+        // (T+2) % 4. The first iteration is peeled (waves 4-7 have no previous tile there).
+        // One loop nest per wave group (the same barriers in the same order), so that the
+        // scores carried across iterations by waves 4-7 cost registers only there.
+#define RAX_PLOOPS(LAG)                                                                     \
+        RAX_PTILE(LAG, it, kb0, vb0, vb3, kb2, vb2, 1, 0) ++it;                              \
+        while (it + 4 <= n_full && it + 7 <= ntiles) {                                      \
+            RAX_PTILE(LAG, it, kb1, vb1, vb0, kb3, vb3, 0, 1) ++it;                          \
+            RAX_PTILE(LAG, it, kb2, vb2, vb1, kb0, vb0, 0, 1) ++it;                          \
+            RAX_PTILE(LAG, it, kb3, vb3, vb2, kb1, vb1, 0, 1) ++it;                          \
+            RAX_PTILE(LAG, it, kb0, vb0, vb3, kb2, vb2, 0, 1) ++it;                          \
+        }                                                                                   \
+        while (it < ntiles) {                                                               \
+            RAX_PTILE(LAG, it, kb1, vb1, vb0, kb3, vb3, 1, 0) ++it;                          \
+            if (it >= ntiles) break;                                                        \
+            RAX_PTILE(LAG, it, kb2, vb2, vb1, kb0, vb0, 1, 0) ++it;                          \
+            if (it >= ntiles) break;                                                        \
+            RAX_PTILE(LAG, it, kb3, vb3, vb2, kb1, vb1, 1, 0) ++it;                          \
+            if (it >= ntiles) break;                                                        \
+            RAX_PTILE(LAG, it, kb0, vb0, vb3, kb2, vb2, 1, 0) ++it;                          \
         }
-        while (it < ntiles) {
-            RAX_TILE(it, kb0, vb0, kb2, vb2, 1, 0) ++it;
-            if (it >= ntiles) break;
-            RAX_TILE(it, kb1, vb1, kb0, vb0, 1, 0) ++it;
-            if (it >= ntiles) break;
-            RAX_TILE(it, kb2, vb2, kb1, vb1, 1, 0) ++it;
+        if (lag) {
+            RAX_PLOOPS(1)
+            // softmax and P V of the last tile
+            RAX_SM(ntiles - 1, 1)
+            switch ((ntiles - 1) & 3) {
+                case 0: RAX_PV(vb0) break;
+                case 1: RAX_PV(vb1) break;
+                case 2: RAX_PV(vb2) break;
+                default: RAX_PV(vb3) break;
+            }
+        } else {
+            RAX_PLOOPS(0)
         }
+#undef RAX_PLOOPS
     } else {
         // prologue: copies of tiles 0, 1, 2 issued, tile 0 widened, slots of tile 3 loaded
         RAX_SLOTS(0)
@@ -499,7 +547,10 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
 }
 #undef RAX_SLOTS
 #undef RAX_COPY
-#undef RAX_TILE
+#undef RAX_QK
+#undef RAX_SM
+#undef RAX_PV
+#undef RAX_PTILE
 #undef RAX_COPY8
 #undef RAX_CONVERT8
 #undef RAX_TILE8
