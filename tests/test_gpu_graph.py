@@ -85,3 +85,61 @@ def test_graph_replays_match_eager(batch, ctx):
     torch.cuda.synchronize()
     assert torch.equal(bits(dw.ext["o"]), got_e), "replay with new queries differs from eager"
     assert torch.equal(bits(d["o"]), got_d), "replay with new queries differs from eager"
+
+
+def test_graph_replays_fp8_paged_ragged():
+    """The FP8, page-table and ragged (fused store) entry points under capture: three replays,
+    each bit for bit equal to the eager calls."""
+    spec = W.Spec("graph-x", "bf16", 32, 8, 128, 131072, extend_prefix=(1000, 0, 3000),
+                  extend_lens=(300, 64, 129), decode_batch=40, decode_range=(1, 2000), page_size=16)
+    wl = W.make_workload(spec, 612)
+    dw = upload(wl)
+    e, d = dw.ext, dw.dec
+    n = wl.extend.total_tokens
+    pt = torch.from_numpy(wl.page_table).cuda()
+    ks = vs = 4.0 * spec.sigma / 448
+    k8 = torch.empty(dw.k_pool.shape, dtype=torch.uint8, device="cuda")
+    v8 = torch.empty_like(k8)
+    R.kv_store(dw.k_new, dw.v_new, dw.store_loc, dw.k_pool, dw.v_pool)     # every used row of the bf16 pool
+    used = torch.unique(torch.from_numpy(wl.req_to_token[wl.req_to_token >= 0]).long()).int().cuda()
+    R.kv_store_fp8(dw.k_pool[used.long()], dw.v_pool[used.long()], used, k8, v8, ks, vs)
+    ws = torch.empty(R.decode_workspace_bytes(R.BF16, d["q"].shape[0], d["max_seq_len"], spec.n_q_heads,
+                                              spec.n_kv_heads, spec.head_dim), dtype=torch.uint8, device="cuda")
+    outs = {k: torch.empty_like(e["q"]) for k in ("e8", "ep", "er")}
+    outs.update({k: torch.empty_like(d["q"]) for k in ("d8", "dp")})
+    rest = (dw.req_to_token, e["req_pool_indices"], e["prefix_lens"], e["extend_lens"], e["extend_start_loc"],
+            e["max_extend_len"], e["max_seq_len"], wl.sm_scale)
+
+    def step():
+        R.kv_store_fp8(dw.k_new, dw.v_new, dw.store_loc, k8, v8, ks, vs)
+        R.extend_attention_fp8(e["q"], outs["e8"], k8, v8, *rest, ks, vs)
+        R.decode_attention_fp8(d["q"], outs["d8"], k8, v8, dw.req_to_token, d["req_pool_indices"], d["seq_lens"],
+                               d["max_seq_len"], wl.sm_scale, ks, vs, workspace=ws)
+        R.extend_attention_paged(e["q"], outs["ep"], dw.k_pool, dw.v_pool, pt, spec.page_size, *rest[1:])
+        R.decode_attention_paged(d["q"], outs["dp"], dw.k_pool, dw.v_pool, pt, spec.page_size,
+                                 d["req_pool_indices"], d["seq_lens"], d["max_seq_len"], wl.sm_scale, workspace=ws)
+        R.extend_attention_ragged(e["q"], outs["er"], dw.k_new[:n], dw.v_new[:n], dw.k_pool, dw.v_pool, *rest,
+                                  store_loc=dw.store_loc[:n])
+
+    step()
+    torch.cuda.synchronize()
+    ref = {k: bits(v) for k, v in outs.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for v in outs.values():
+            v.fill_(float("nan"))
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert torch.equal(bits(v), ref[k]), f"replay {r}: {k} differs from eager"
