@@ -142,9 +142,12 @@ __device__ __forceinline__ int64_t row_off(int idx, uint32_t row_bytes) {
 // Workgroup barrier that the compiler may not move memory accesses across. Copies into LDS
 // are ordered by the explicit vmcnt wait before it, reads by the operand waits of the MFMAs.
 #define RAX_BARRIER() asm volatile("s_barrier" ::: "memory")
-// s_waitcnt lgkmcnt(0) alone: this wave's LDS writes have completed (before a barrier after
-// which other waves read them).
-#define RAX_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+// Barrier after which other waves read this wave's LDS writes: the wait for them and the
+// barrier are one statement, so no write can be scheduled between the two.
+#define RAX_WRITES_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+// This wave's LDS reads have returned before anything after this point is issued: a copy into
+// an LDS buffer the wave has just read (the FP8 staging ring) must not overtake those reads.
+#define RAX_READS_DONE() asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory")
 
 // PG: the table is a page table (page size 2^page_shift): position j lives at slot
 // table[row, j >> page_shift] << page_shift | (j & (2^page_shift - 1)).
@@ -167,11 +170,11 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // objects, each named statically below.
     __shared__ uint4 kb0[kExtBN * 16], kb1[kExtBN * 16], kb2[kExtBN * 16];
     __shared__ uint4 vb0[kExtBN * 16], vb1[kExtBN * 16], vb2[kExtBN * 16];
-    // bf16 pools use a fourth buffer (ping-pong, below); FP8 pools three staging buffers.
-    __shared__ uint4 kb3[KV8 ? 1 : kExtBN * 16], vb3[KV8 ? 1 : kExtBN * 16];
-    // FP8 pools: three staging buffers of raw E4M3 tiles, [key][8 units of 16 bytes].
+    __shared__ uint4 kb3[kExtBN * 16], vb3[kExtBN * 16];  // fourth buffer (ping-pong, below)
+    // FP8 pools: two staging buffers of raw E4M3 tiles, [key][8 units of 16 bytes] (with the
+    // four bf16 buffers, 160 KB of LDS).
     constexpr int SU = KV8 ? kExtBN * 8 : 1;
-    __shared__ uint4 sk0[SU], sk1[SU], sk2[SU], sv0[SU], sv1[SU], sv2[SU];
+    __shared__ uint4 sk0[SU], sk1[SU], sv0[SU], sv1[SU];
 
     // ---- workgroup -> (pair = b * Hkv + g, tile), XCD-aware
     const int pairs = batch * Hkv;
@@ -398,10 +401,8 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // scores of tile IT, so that on each SIMD one wave's MFMAs meet the other's softmax. Tile
     // IT-1's V stays readable during iteration IT: the copy started in iteration IT goes to
     // the buffer of tile IT-2.
-#define RAX_PTILE(LAG, IT, KB, VB, VP, KN, VN, MASKABLE, STEADY)                            \
+#define RAX_PCOMPUTE(LAG, IT, KB, VB, VP, MASKABLE, STEADY)                                 \
     {                                                                                       \
-        if (STEADY || (IT) + 1 < ntiles) { RAX_WAIT_VMCNT(4); } else { RAX_WAIT_VMCNT(0); } \
-        RAX_BARRIER();                                                                      \
         if (LAG) {                                                                          \
             if (!STEADY && (IT) == 0) {                                                     \
             } else {                                                                        \
@@ -411,35 +412,55 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         } else {                                                                            \
             RAX_COMPUTE(IT, KB, VB, MASKABLE)                                               \
         }                                                                                   \
+    }
+#define RAX_PTILE(LAG, IT, KB, VB, VP, KN, VN, MASKABLE, STEADY)                            \
+    {                                                                                       \
+        if (STEADY || (IT) + 1 < ntiles) { RAX_WAIT_VMCNT(4); } else { RAX_WAIT_VMCNT(0); } \
+        RAX_BARRIER();                                                                      \
+        RAX_PCOMPUTE(LAG, IT, KB, VB, VP, MASKABLE, STEADY)                                 \
         if (STEADY || (IT) + 2 < ntiles) {                                                  \
             RAX_COPY(KN, VN)                                                                \
             if (STEADY || (IT) + 3 < ntiles) RAX_SLOTS((IT) + 3)                            \
         }                                                                                   \
     }
-    // FP8 pools. Tile T is staged (E4M3) in buffer T % 3 and widened into bf16 buffer T % 3.
-    // Iteration IT: barrier (every wave's conversion of tile IT has landed, every wave is done
-    // with tile IT-1); compute tile IT; wait for this wave's copies of tile IT+1 (those of
-    // IT+2 stay in flight) and widen them into (KN, VN), free since tile IT-2; copy tile IT+3
-    // into staging (SN, SVN), whose tile IT this wave widened one iteration ago.
-#define RAX_TILE8(IT, KB, VB, SC, SVC, KN, VN, SN, SVN, MASKABLE, STEADY)                    \
+    // FP8 pools: tile T is staged (E4M3) in buffer T % 2 and widened into bf16 buffer T % 4.
+    // Iteration IT: barrier (every wave's widening of tile IT has landed, every wave is done
+    // with iteration IT-1); compute as above; wait for this wave's copies of tile IT+1 (those
+    // of IT+2 stay in flight) and widen them from staging (SC, SVC) into (KN, VN), free since
+    // tile IT-3; then, once the staging reads have returned, copy tile IT+3 into the staging
+    // buffer just emptied (the compiler may otherwise issue the copy before the widening has
+    // consumed the reads, and a copy that hits in L2 can land first).
+#define RAX_PTILE8(LAG, IT, KB, VB, VP, SC, SVC, KN, VN, MASKABLE, STEADY)                  \
     {                                                                                       \
-        RAX_WAIT_LGKM0();                                                                   \
-        RAX_BARRIER();                                                                      \
-        RAX_COMPUTE(IT, KB, VB, MASKABLE)                                                   \
+        RAX_WRITES_BARRIER();                                                               \
+        RAX_PCOMPUTE(LAG, IT, KB, VB, VP, MASKABLE, STEADY)                                 \
         if (STEADY || (IT) + 1 < ntiles) {                                                  \
             if (STEADY || (IT) + 2 < ntiles) { RAX_WAIT_VMCNT(2); } else { RAX_WAIT_VMCNT(0); } \
             RAX_CONVERT8(SC, SVC, KN, VN)                                                   \
         }                                                                                   \
         if (STEADY || (IT) + 3 < ntiles) {                                                  \
-            RAX_COPY8(SN, SVN)                                                              \
+            RAX_READS_DONE();                                                               \
+            RAX_COPY8(SC, SVC)                                                              \
             if (STEADY || (IT) + 4 < ntiles) RAX_SLOTS((IT) + 4)                            \
         }                                                                                   \
     }
 
     const int n_full = min(ntiles, (diag_from + 1) / kExtBN);  // tiles with every key <= p + t0
     int it = 0;
+    const bool lag = __builtin_amdgcn_readfirstlane(wave) >= 4;
+    // waves 4-7 after their loop: softmax and P V of the last tile (inside their branch, so
+    // the scores stay dead after the softmax for waves 0-3)
+#define RAX_LAG_TAIL()                                                                      \
+    {                                                                                       \
+        RAX_SM(ntiles - 1, 1)                                                               \
+        switch ((ntiles - 1) & 3) {                                                         \
+            case 0: RAX_PV(vb0) break;                                                      \
+            case 1: RAX_PV(vb1) break;                                                      \
+            case 2: RAX_PV(vb2) break;                                                      \
+            default: RAX_PV(vb3) break;                                                     \
+        }                                                                                   \
+    }
     if constexpr (!KV8) {
-        const bool lag = __builtin_amdgcn_readfirstlane(wave) >= 4;
         RAX_SLOTS(0)
         RAX_COPY(kb0, vb0)
         if (ntiles > 1) {
@@ -470,48 +491,54 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         }
         if (lag) {
             RAX_PLOOPS(1)
-            // softmax and P V of the last tile
-            RAX_SM(ntiles - 1, 1)
-            switch ((ntiles - 1) & 3) {
-                case 0: RAX_PV(vb0) break;
-                case 1: RAX_PV(vb1) break;
-                case 2: RAX_PV(vb2) break;
-                default: RAX_PV(vb3) break;
-            }
+            RAX_LAG_TAIL()
         } else {
             RAX_PLOOPS(0)
         }
 #undef RAX_PLOOPS
     } else {
-        // prologue: copies of tiles 0, 1, 2 issued, tile 0 widened, slots of tile 3 loaded
+        // prologue: copies of tiles 0 and 1 issued, tile 0 widened, the copy of tile 2 issued
+        // into its emptied staging buffer, slots of tile 3 loaded
         RAX_SLOTS(0)
         RAX_COPY8(sk0, sv0)
         if (ntiles > 1) {
             RAX_SLOTS(1)
             RAX_COPY8(sk1, sv1)
         }
-        if (ntiles > 2) {
-            RAX_SLOTS(2)
-            RAX_COPY8(sk2, sv2)
-        }
-        if (ntiles > 3) RAX_SLOTS(3)
-        if (ntiles > 2) { RAX_WAIT_VMCNT(4); } else if (ntiles > 1) { RAX_WAIT_VMCNT(2); } else { RAX_WAIT_VMCNT(0); }
+        if (ntiles > 2) RAX_SLOTS(2)
+        if (ntiles > 1) { RAX_WAIT_VMCNT(2); } else { RAX_WAIT_VMCNT(0); }
         RAX_CONVERT8(sk0, sv0, kb0, vb0)
-        // Steady state: the three tiles of a step are full and tiles up to it + 6 exist.
-        while (it + 3 <= n_full && it + 7 <= ntiles) {
-            RAX_TILE8(it, kb0, vb0, sk1, sv1, kb1, vb1, sk0, sv0, 0, 1) ++it;
-            RAX_TILE8(it, kb1, vb1, sk2, sv2, kb2, vb2, sk1, sv1, 0, 1) ++it;
-            RAX_TILE8(it, kb2, vb2, sk0, sv0, kb0, vb0, sk2, sv2, 0, 1) ++it;
+        if (ntiles > 2) {
+            RAX_READS_DONE();
+            RAX_COPY8(sk0, sv0)
+            if (ntiles > 3) RAX_SLOTS(3)
         }
-        while (it < ntiles) {
-            RAX_TILE8(it, kb0, vb0, sk1, sv1, kb1, vb1, sk0, sv0, 1, 0) ++it;
-            if (it >= ntiles) break;
-            RAX_TILE8(it, kb1, vb1, sk2, sv2, kb2, vb2, sk1, sv1, 1, 0) ++it;
-            if (it >= ntiles) break;
-            RAX_TILE8(it, kb2, vb2, sk0, sv0, kb0, vb0, sk2, sv2, 1, 0) ++it;
+        // Tile T: staging T % 2, bf16 buffer T % 4; the first iteration is peeled.
+#define RAX_PLOOPS8(LAG)                                                                    \
+        RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, kb1, vb1, 1, 0) ++it;                   \
+        while (it + 4 <= n_full && it + 8 <= ntiles) {                                      \
+            RAX_PTILE8(LAG, it, kb1, vb1, vb0, sk0, sv0, kb2, vb2, 0, 1) ++it;               \
+            RAX_PTILE8(LAG, it, kb2, vb2, vb1, sk1, sv1, kb3, vb3, 0, 1) ++it;               \
+            RAX_PTILE8(LAG, it, kb3, vb3, vb2, sk0, sv0, kb0, vb0, 0, 1) ++it;               \
+            RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, kb1, vb1, 0, 1) ++it;               \
+        }                                                                                   \
+        while (it < ntiles) {                                                               \
+            RAX_PTILE8(LAG, it, kb1, vb1, vb0, sk0, sv0, kb2, vb2, 1, 0) ++it;               \
+            if (it >= ntiles) break;                                                        \
+            RAX_PTILE8(LAG, it, kb2, vb2, vb1, sk1, sv1, kb3, vb3, 1, 0) ++it;               \
+            if (it >= ntiles) break;                                                        \
+            RAX_PTILE8(LAG, it, kb3, vb3, vb2, sk0, sv0, kb0, vb0, 1, 0) ++it;               \
+            if (it >= ntiles) break;                                                        \
+            RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, kb1, vb1, 1, 0) ++it;               \
         }
+        if (lag) {
+            RAX_PLOOPS8(1)
+            RAX_LAG_TAIL()
+        } else {
+            RAX_PLOOPS8(0)
+        }
+#undef RAX_PLOOPS8
     }
-
     lsum = sum_pair32(lsum);
     if (row_ok) {
         const float inv = out_scale / lsum;
@@ -553,7 +580,9 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
 #undef RAX_PTILE
 #undef RAX_COPY8
 #undef RAX_CONVERT8
-#undef RAX_TILE8
+#undef RAX_PTILE8
+#undef RAX_PCOMPUTE
+#undef RAX_LAG_TAIL
 
 template <int G, bool OFF32, bool KV8, bool RAG, bool PG>
 int launch_g(const AttnArgs& a, hipStream_t stream) {
