@@ -72,13 +72,14 @@ size_t rax_decode_workspace_bytes(int dtype, int32_t batch, int32_t max_seq_len,
     if ((dtype != RAX_BF16 && dtype != RAX_FP8_E4M3) || batch <= 0 || max_seq_len <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 ||
         head_dim <= 0)
         return 0;
-    return rax::decode_workspace(batch, max_seq_len, n_q_heads, n_kv_heads, head_dim);
+    return rax::decode_workspace(batch, max_seq_len, n_q_heads, n_kv_heads, head_dim,
+                                 dtype == RAX_FP8_E4M3);
 }
 
 int32_t rax_decode_num_splits(int dtype, int32_t batch, int32_t max_seq_len, int32_t n_kv_heads) {
     if (dtype != RAX_BF16 && dtype != RAX_FP8_E4M3) return 1;
     if (batch <= 0 || max_seq_len <= 0 || n_kv_heads <= 0) return 1;
-    return rax::decode_grid(batch, max_seq_len, n_kv_heads);
+    return rax::decode_grid(batch, max_seq_len, n_kv_heads, dtype == RAX_FP8_E4M3);
 }
 
 }  // extern "C"
@@ -152,12 +153,12 @@ int decode_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool,
     if (kv8 && (!scale_ok(k_scale) || !scale_ok(v_scale))) return RAX_ERR_SHAPE;
     if (batch == 0) return RAX_OK;
     if (max_seq_len == 0) return RAX_ERR_SHAPE;
-    if (dtype == RAX_BF16 && rax::decode_grid(batch, max_seq_len, n_kv_heads) < 0)
+    if (dtype == RAX_BF16 && rax::decode_grid(batch, max_seq_len, n_kv_heads, kv8) < 0)
         return RAX_ERR_SHAPE;
     if (!q || !o || !k_pool || !v_pool || !req_to_token || !req_pool_indices || !seq_lens)
         return RAX_ERR_NULL;
-    const size_t need = rax_decode_workspace_bytes(dtype, batch, max_seq_len, n_q_heads, n_kv_heads,
-                                                   head_dim);
+    const size_t need = rax_decode_workspace_bytes(kv8 ? RAX_FP8_E4M3 : dtype, batch, max_seq_len,
+                                                   n_q_heads, n_kv_heads, head_dim);
     if (need > 0 && (!workspace || workspace_bytes < need)) return RAX_ERR_WORKSPACE;
 
     rax::AttnArgs a{};

@@ -46,8 +46,18 @@ namespace {
 #ifndef RAX_DEC_WAVES
 #define RAX_DEC_WAVES 4
 #endif
-#ifndef RAX_DEC_RESIDENT_WGS
-#define RAX_DEC_RESIDENT_WGS 512  // workgroups held at once: 2 per CU on 256 CUs
+// Split workgroups resident per CU (the register budget: 3 allows 168 VGPRs, 2 allows 256)
+// and keys per iteration, for bf16 and for FP8 pools. bf16: 32-key iterations at 3 workgroups
+// per CU; FP8: 128-key iterations (a wave keeps as many bytes in flight as at 64 bf16 keys)
+// at 2 per CU, where they fit without spills.
+#ifndef RAX_DEC_WGS_PER_CU
+#define RAX_DEC_WGS_PER_CU 3
+#endif
+#ifndef RAX_DEC_WGS_PER_CU8
+#define RAX_DEC_WGS_PER_CU8 2
+#endif
+#ifndef RAX_DEC_KPI16
+#define RAX_DEC_KPI16 32
 #endif
 #ifndef RAX_DEC_MIN_KEYS
 #define RAX_DEC_MIN_KEYS 256
@@ -56,7 +66,7 @@ namespace {
 #define RAX_DEC_NT 1
 #endif
 #ifndef RAX_DEC_KPI8
-#define RAX_DEC_KPI8 128  // keys per iteration with FP8 pools (64 or 128)
+#define RAX_DEC_KPI8 128
 #endif
 constexpr int kDecWaves = RAX_DEC_WAVES;  // waves (kv heads) per workgroup
 constexpr int kDecKeysPerIter = 64;
@@ -209,7 +219,7 @@ struct Seg {
 // PG: r2t is a page table (page size 2^page_shift): position j lives at slot
 // r2t[row, j >> page_shift] << page_shift | (j & (2^page_shift - 1)).
 template <int D, bool OFF32, bool FUSED, bool KV8, bool PG>
-__global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_kernel(
+__global__ __launch_bounds__(64 * kDecWaves, KV8 ? RAX_DEC_WGS_PER_CU8 : RAX_DEC_WGS_PER_CU) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
@@ -350,9 +360,9 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
     const int n16 = lane & 15;
     const int kg = lane >> 4;
     using EL = DecElems<D, KV8>;
-    // Keys per iteration: 64, or 128 with FP8 pools so that a wave keeps as many bytes in
-    // flight as with bf16 (the bytes per key halve). TT 16-key score tiles, UU 32-key P V steps.
-    constexpr int KPI = KV8 ? RAX_DEC_KPI8 : 64;
+    // Keys per iteration (see RAX_DEC_KPI16 / RAX_DEC_KPI8): TT 16-key score tiles, UU 32-key
+    // P V steps.
+    constexpr int KPI = KV8 ? RAX_DEC_KPI8 : RAX_DEC_KPI16;
     constexpr int TT = KPI / 16;
     constexpr int UU = KPI / 32;
     constexpr uint32_t es = EL::bytes;  // bytes per stored element
@@ -456,12 +466,14 @@ __global__ __launch_bounds__(64 * kDecWaves, 8 / kDecWaves) void decode_split_ke
         const int b = __builtin_amdgcn_readfirstlane(segs[si].b);
         const int lo = __builtin_amdgcn_readfirstlane(segs[si].lo);
         const int n_seg_keys = __builtin_amdgcn_readfirstlane(segs[si].n);
-        const int n_it = (n_seg_keys + KPI - 1) / KPI;
         // Keys of this overlap that count: those of the request (at least one: every 64-key
         // block of a request's padded range starts before its end) and inside the overlap.
         const int n_valid = min(__builtin_amdgcn_readfirstlane(segs[si].len) -
                                     __builtin_amdgcn_readfirstlane(segs[si].pos0),
                                 n_seg_keys);
+        // Iterations up to the last valid key: only the last one can hold padding keys (which
+        // the mask removes), whatever the iteration width.
+        const int n_it = (n_valid + KPI - 1) / KPI;
 
         // B operand of S^T = K Q^T: lane holds Q[head n16][k_step_elem(s, kg) .. +8].
         bf16x8 qop[S];
@@ -568,9 +580,10 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 int32_t decode_groups(int32_t n_kv_heads) { return (n_kv_heads + kDecWaves - 1) / kDecWaves; }
 
-// Ranges per kv-head group that one resident round of workgroups covers.
-int32_t decode_target(int32_t n_kv_heads) {
-    const int32_t t = RAX_DEC_RESIDENT_WGS / decode_groups(n_kv_heads);
+// Ranges per kv-head group that one resident round of workgroups (256 CUs) covers.
+int32_t decode_target(int32_t n_kv_heads, bool kv8) {
+    const int32_t resident = 256 * (kv8 ? RAX_DEC_WGS_PER_CU8 : RAX_DEC_WGS_PER_CU);
+    const int32_t t = resident / decode_groups(n_kv_heads);
     return t < 1 ? 1 : t;
 }
 
@@ -601,18 +614,18 @@ bool decode_bf16_supported(int32_t group, int32_t head_dim) {
 // Ranges per kv-head group the split kernel is launched with: one resident round, or more when
 // the longest possible stream (every request at max_seq_len) needs more 4096-key ranges.
 // -1 when that would exceed the grid limit.
-int32_t decode_grid(int32_t batch, int32_t max_seq_len, int32_t n_kv_heads) {
+int32_t decode_grid(int32_t batch, int32_t max_seq_len, int32_t n_kv_heads, bool kv8) {
     const int64_t worst = (int64_t)batch * (((int64_t)max_seq_len + kDecKeysPerIter - 1) /
                                             kDecKeysPerIter * kDecKeysPerIter);
     int64_t n = (worst + kDecMaxKeys - 1) / kDecMaxKeys;
-    if (n < decode_target(n_kv_heads)) n = decode_target(n_kv_heads);
+    if (n < decode_target(n_kv_heads, kv8)) n = decode_target(n_kv_heads, kv8);
     if (n * decode_groups(n_kv_heads) > INT32_MAX || n + batch > INT32_MAX) return -1;
     return (int32_t)n;
 }
 
 size_t decode_workspace(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
-                        int32_t head_dim) {
-    const int32_t grid = decode_grid(batch, max_seq_len, n_kv_heads);
+                        int32_t head_dim, bool kv8) {
+    const int32_t grid = decode_grid(batch, max_seq_len, n_kv_heads, kv8);
     if (grid < 0) return 0;
     return decode_layout(batch, grid, n_q_heads, head_dim).total;
 }
@@ -621,7 +634,7 @@ int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
     if (a.kv8 && a.page_shift) return -1;
     const int32_t G = a.n_q_heads / a.n_kv_heads;
     const int32_t groups = decode_groups(a.n_kv_heads);
-    const int32_t grid = decode_grid(a.batch, a.max_seq_len, a.n_kv_heads);
+    const int32_t grid = decode_grid(a.batch, a.max_seq_len, a.n_kv_heads, a.kv8);
     if (grid < 0) return -1;
     const DecLayout l = decode_layout(a.batch, grid, a.n_q_heads, a.head_dim);
     char* ws = (char*)a.workspace;
@@ -632,7 +645,7 @@ int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
     float* lse = (float*)(ws + l.lse);
     const float scale_log2 = a.sm_scale * kLog2e * (a.kv8 ? a.k_scale : 1.f);
     const float out_scale = a.kv8 ? a.v_scale : 1.f;
-    const int32_t n_target = decode_target(a.n_kv_heads);
+    const int32_t n_target = decode_target(a.n_kv_heads, a.kv8);
     const bool fused = a.batch <= kDecFusedBatch;
     if (!fused) {
         hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.seq_lens,

@@ -71,10 +71,11 @@ bool extend_bf16_supported(int32_t group, int32_t head_dim);
 int launch_extend_bf16(const AttnArgs& a, hipStream_t stream);
 
 bool decode_bf16_supported(int32_t group, int32_t head_dim);
-// Key ranges per group of kv heads the split kernel is launched with; -1 if too many.
-int32_t decode_grid(int32_t batch, int32_t max_seq_len, int32_t n_kv_heads);
+// Key ranges per group of kv heads the split kernel is launched with (bf16 or FP8 pools, which
+// differ in resident workgroups); -1 if too many.
+int32_t decode_grid(int32_t batch, int32_t max_seq_len, int32_t n_kv_heads, bool kv8);
 size_t decode_workspace(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
-                        int32_t head_dim);
+                        int32_t head_dim, bool kv8);
 int launch_decode_bf16(const AttnArgs& a, hipStream_t stream);
 
 // fp32 path (vector ALU, fp32 throughout).

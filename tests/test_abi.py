@@ -113,17 +113,19 @@ def a256(x):
 
 
 def test_decode_workspace_size():
-    # ranges per kv-head group: one resident round (512 workgroups of 4 kv heads), or enough
-    # 4096-key ranges for every request at max_seq_len, whichever is larger
+    # ranges per kv-head group: one resident round (768 workgroups of 4 kv heads for bf16 pools,
+    # 512 for FP8 pools), or enough 4096-key ranges for every request at max_seq_len, whichever
+    # is larger
     for B, L, hq, hkv in [(64, 4096, 32, 8), (8, 131072, 64, 8), (1, 1, 4, 4), (128, 8192, 32, 8),
                           (4096, 32768, 32, 8), (16, 1000, 64, 32)]:
-        groups = (hkv + 3) // 4
-        worst = B * ((L + 63) // 64 * 64)
-        grid = max(max(1, 512 // groups), (worst + 4095) // 4096)
-        assert lib().rax_decode_num_splits(0, B, L, hkv) == grid
-        parts = (B + grid) * hq
-        want = 256 + a256((B + 1) * 8) + a256(grid * 4) + a256(parts * 128 * 4) + parts * 4
-        assert lib().rax_decode_workspace_bytes(0, B, L, hq, hkv, 128) == want
+        for dtype, resident in ((0, 768), (2, 512)):
+            groups = (hkv + 3) // 4
+            worst = B * ((L + 63) // 64 * 64)
+            grid = max(max(1, resident // groups), (worst + 4095) // 4096)
+            assert lib().rax_decode_num_splits(dtype, B, L, hkv) == grid
+            parts = (B + grid) * hq
+            want = 256 + a256((B + 1) * 8) + a256(grid * 4) + a256(parts * 128 * 4) + parts * 4
+            assert lib().rax_decode_workspace_bytes(dtype, B, L, hq, hkv, 128) == want
     assert lib().rax_decode_workspace_bytes(1, 64, 4096, 32, 8, 128) == 0   # fp32 path needs none
     assert lib().rax_extend_workspace_bytes(0, 1, 2048, 2048, 16384, 32, 8, 128) == 0
 
@@ -141,7 +143,8 @@ def test_fp8_calls_check_scales_and_shapes_before_launching():
     assert st(k=None) == 1
     # decode_attention_fp8(q, o, kp, vp, S, r2t, stride, rpi, seq, B, L, Hq, Hkv, D, sm, ks, vs, ws, wsb, stream)
     need = L.rax_decode_workspace_bytes(2, 3, 300, 8, 2, 128)
-    assert need == L.rax_decode_workspace_bytes(0, 3, 300, 8, 2, 128)
+    # FP8 pools keep fewer split workgroups resident (wider iterations), so need at most as much
+    assert 0 < need <= L.rax_decode_workspace_bytes(0, 3, 300, 8, 2, 128)
     dec = lambda **kw: L.rax_decode_attention_fp8(FAKE, FAKE, FAKE, FAKE, 1000, FAKE, 512, FAKE, FAKE,
                                                   kw.get("B", 3), 300, 8, 2, 128, 0.1, kw.get("ks", 1.0),
                                                   kw.get("vs", 1.0), kw.get("ws", FAKE), kw.get("wsb", need),
