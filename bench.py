@@ -11,6 +11,9 @@ before timing. ``--ragged`` runs EXTEND on the ragged path: the suffix K/V read 
 rows and stored by the same kernel (extend_attention_ragged with store_loc); kv_store then
 writes only the decode requests' current tokens. ``--page-size P`` draws the workload with
 pages of P slots and runs EXTEND and DECODE through the page table (the _paged calls).
+``--cold`` sweeps a 1 GiB buffer (read and write, four times the 256 MB last-level cache)
+before every step, outside the kernels' event windows, so the per-kernel figures are
+cold-cache ones; ms_per_step then includes the sweeps.
 
 Prints ONE JSON line. ``value`` is the EXTEND attention throughput in TFLOP/s (algorithmic
 FLOPs: 4 * head_dim * q_heads per attended pair, masked pairs not counted); the DECODE KV
@@ -251,6 +254,8 @@ def main():
                     help="EXTEND via extend_attention_ragged with the fused store of the suffix rows")
     ap.add_argument("--page-size", type=int, default=1,
                     help="pool pages of this many slots, read through a page table (1 = token table)")
+    ap.add_argument("--cold", action="store_true",
+                    help="sweep 1 GiB through the caches before every step (per-kernel times are then cold)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step as HIP graph replays (reported beside the eager figures)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -326,7 +331,12 @@ def main():
         del allslots
         torch.cuda.empty_cache()
 
+    flush = torch.empty(COPY_BYTES // 2, dtype=torch.uint8, device="cuda:0") if args.cold else None
+    flush2 = torch.empty_like(flush) if args.cold else None
+
     def step(ev=None):
+        if flush is not None:
+            flush2.copy_(flush)   # 512 MiB read + 512 MiB written: evicts the step's data
         if ev is not None:
             ev[0].record()
         if kv8:
@@ -475,6 +485,8 @@ def main():
         cfgd["extend_path"] = "ragged suffix, fused store"
     if paged:
         cfgd["page_size"] = args.page_size
+    if args.cold:
+        cfgd["caches"] = "cold: 1 GiB swept before every step"
     if wl.extend is not None:
         cfgd["extend"] = {"batch": wl.extend.batch, "new_tokens": wl.extend.total_tokens,
                           "prefix_lens": sorted(set(int(x) for x in wl.extend.prefix_lens))[:4]}
