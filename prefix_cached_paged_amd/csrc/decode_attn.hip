@@ -7,8 +7,9 @@
 //
 // Design (gfx950, wave64):
 //  * Balanced key stream. A plan lays the requests' contexts end to end, each
-//    rounded up to whole 64-key iterations, and cuts that stream into equal ranges of 256..4096
-//    keys, one per workgroup, so that one resident round of workgroups (2 per CU) covers it:
+//    rounded up to whole 64-key blocks, and cuts that stream into equal ranges of 256..4096
+//    keys, one per workgroup, so that one resident round of workgroups (3 per CU over bf16
+//    pools, 2 over FP8 pools) covers it:
 //    every wave moves the same number of bytes whatever the mix of context lengths. A range
 //    may hold the tail of one request and the head of the next; each (request, range) overlap
 //    yields one partial (o, lse) in the workspace, and decode_merge_kernel combines a request's
@@ -27,8 +28,10 @@
 //    permuted to d = (D/16)*m + tile so that those loads are contiguous.
 //  * Scores S^T come out of the MFMA with the query head as the lane's column, so the
 //    softmax running max/sum is per lane; only the max over the four lane groups needs two
-//    cross-lane exchanges per 64 keys (permlane swaps, no LDS). exp2 with sm_scale*log2(e)
+//    cross-lane exchanges per iteration (permlane swaps, no LDS). exp2 with sm_scale*log2(e)
 //    folded into one multiply.
+//  * Iterations of 32 keys over bf16 pools (168 VGPRs: 3 waves per SIMD) and 128 keys over
+//    FP8 pools (2 waves per SIMD, as many bytes in flight per wave as 64 bf16 keys).
 //  * Key slots: the workgroup's waves read the same keys, so the range's slot numbers are
 //    staged in LDS once with global-to-LDS copies; each lane then reads the slots it needs with
 //    ds_read, off the memory-counter path of the K/V row loads. Padding keys past a request's
@@ -377,7 +380,7 @@ __global__ __launch_bounds__(64 * kDecWaves, KV8 ? RAX_DEC_WGS_PER_CU8 : RAX_DEC
     const bool q_ok = n16 < G;
     const uint32_t q_keep = q_ok ? 0xFFFFFFFFu : 0u;
 
-    // Software pipeline over 64-key iterations: the next iteration's K rows are requested as
+    // Software pipeline over KPI-key iterations: the next iteration's K rows are requested as
     // soon as the score MFMAs have consumed this iteration's, and its V rows as soon as P V has
     // consumed this iteration's, so one iteration of K and V is always in flight. The steady
     // loop is branch-free (the last iteration is peeled), which keeps the memory-counter waits
