@@ -56,11 +56,18 @@ COPY_BYTES = 1 << 30
 
 
 def source_sha(kernel: str) -> str:
+    """Hash of the kernel's sources with comments and blank lines removed (an edit of a comment
+    does not change the kernel the counters were taken on)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 
