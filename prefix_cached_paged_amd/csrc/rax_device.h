@@ -79,13 +79,14 @@ __device__ __forceinline__ float max_pair16(float v) { float a, b; pair16(v, a, 
 __device__ __forceinline__ float sum_pair32(float v) { float a, b; pair32(v, a, b); return a + b; }
 __device__ __forceinline__ float sum_pair16(float v) { float a, b; pair16(v, a, b); return a + b; }
 
-// FP8 E4M3 -> bf16: every E4M3 value (finite or NaN) is exactly a bf16 value, so widening
-// through float32 rounds nothing. bf16x2_of_e4m3<HI> widens bytes 2 HI, 2 HI + 1 of w;
-// widen8 turns 8 bytes into 8 bf16 in byte order.
+// FP8 E4M3 -> bf16: every E4M3 value (finite or NaN) is exactly a bf16 value, so the widening
+// rounds nothing. bf16x2_of_e4m3<HI> widens bytes 2 HI, 2 HI + 1 of w in one gfx950
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1 (the same bits as v_cvt_pk_f32_fp8 followed by
+// v_cvt_pk_bf16_f32, for all 2^16 byte pairs of either half); widen8 turns 8 bytes into 8 bf16
+// in byte order.
 template <bool HI>
 __device__ __forceinline__ uint32_t bf16x2_of_e4m3(uint32_t w) {
-    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-    return pack_bf16x2(f[0], f[1]);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
 }
 __device__ __forceinline__ uint4 widen8(uint2 x) {
     return make_uint4(bf16x2_of_e4m3<false>(x.x), bf16x2_of_e4m3<true>(x.x),
