@@ -533,13 +533,20 @@ __global__ __launch_bounds__(64 * kDecWaves, KV8 ? RAX_DEC_WGS_PER_CU8 : RAX_DEC
 }
 
 // One wave per (request, q head): o = sum_c 2^(lse_c - M) o_c / sum_c 2^(lse_c - M) over the
-// request's partials, one per range its padded key span overlaps.
+// request's partials, one per range its padded key span overlaps. Lane c % 64 holds partial c's
+// lse and weight; the o rows of kMergeRows partials are loaded together (the first block goes
+// out with the lse loads), so a request's partials cost one memory round trip per block rather
+// than one per partial. The rows are accumulated in partial order.
+constexpr int kMergeRows = 8;
+
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part, uint16_t* __restrict__ o,
     const int32_t* __restrict__ seq_lens, int32_t max_seq_len, const int64_t* __restrict__ meta,
     const int64_t* __restrict__ P, int32_t Hq, int32_t B) {
     constexpr int PER = D / 64;
+    constexpr int U = kMergeRows;
+    using Piece = typename std::conditional<PER == 2, float2, float>::type;
     const int wq = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (wq >= B * Hq) return;
     const int lane = threadIdx.x & 63;
@@ -554,20 +561,47 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
         const int64_t w0 = P[b] / chunk;
         const int n = (int)((P[b + 1] - 1) / chunk - w0) + 1;
         const int64_t first = ((int64_t)b + w0) * Hq + h;  // partial c sits at first + c * Hq
-        float M = -INFINITY;
-        for (int c = lane; c < n; c += kWave) M = fmaxf(M, lse_part[first + (int64_t)c * Hq]);
+        // Partial c's piece of this lane: o_part[(first + c * Hq) * D + PER * lane ..].
+        const Piece* orow = (const Piece*)(o_part + first * D) + lane;
+        const int64_t ostep = (int64_t)Hq * D / PER;
+        Piece v[U];
+        // Rows c .. c + U - 1, indices past the last partial clamped to it (their weight is 0).
+        auto load_rows = [&](int c) {
+#pragma unroll
+            for (int k = 0; k < U; ++k) v[k] = orow[(int64_t)min(c + k, n - 1) * ostep];
+        };
+        load_rows(0);
+        const float lse_own = lane < n ? lse_part[first + (int64_t)lane * Hq] : -INFINITY;
+        float M = lse_own;
+        for (int c = lane + kWave; c < n; c += kWave) M = fmaxf(M, lse_part[first + (int64_t)c * Hq]);
 #pragma unroll
         for (int s = 32; s >= 1; s >>= 1) M = wave_max_xor(M, s);
-        float wsum = 0.f;
-        for (int c = 0; c < n; ++c) {
-            const int64_t pi = first + (int64_t)c * Hq;
-            const float wt = fast_exp2(lse_part[pi] - M);
-            wsum += wt;
-            const float* op = o_part + pi * D + PER * lane;
+        float wpart = 0.f;
+        for (int c0 = 0; c0 < n; c0 += kWave) {
+            const int c = c0 + lane;
+            const float lc =
+                c0 == 0 ? lse_own : (c < n ? lse_part[first + (int64_t)c * Hq] : -INFINITY);
+            const float wt = fast_exp2(lc - M);  // 0 in lanes past the last partial
+            wpart += wt;
+            const int m = min(kWave, n - c0);
+            for (int j = 0; j < m; j += U) {
+                if (c0 + j > 0) load_rows(c0 + j);
 #pragma unroll
-            for (int k = 0; k < PER; ++k) acc[k] += wt * op[k];
+                for (int k = 0; k < U; ++k) {
+                    const float wk =
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), j + k));
+                    if constexpr (PER == 2) {
+                        acc[0] += wk * v[k].x;
+                        acc[1] += wk * v[k].y;
+                    } else {
+                        acc[0] += wk * v[k];
+                    }
+                }
+            }
         }
-        const float inv = 1.f / wsum;
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) wpart += __shfl_xor(wpart, s, kWave);
+        const float inv = 1.f / wpart;
 #pragma unroll
         for (int k = 0; k < PER; ++k) acc[k] *= inv;
     }
