@@ -19,6 +19,7 @@ __all__ = [
     "RaxError", "BF16", "FP32", "load", "version", "kv_store", "extend_attention",
     "decode_attention", "extend_workspace_bytes", "decode_workspace_bytes", "decode_num_splits",
     "library_path", "declared_symbols", "FP8_E4M3", "kv_store_fp8", "decode_attention_fp8",
+    "extend_attention_fp8", "extend_attention_ragged", "extend_attention_paged", "decode_attention_paged",
 ]
 
 BF16 = 0
@@ -131,9 +132,50 @@ def _idx(t):
     return _ptr(t)
 
 
-def _stream(stream):
-    s = stream if stream is not None else torch.cuda.current_stream()
+def _stream(stream, device=None):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
     return s.cuda_stream
+
+
+def _expect(ok: bool, what: str):
+    if not ok:
+        raise ValueError(what)
+
+
+def _same_device(*ts):
+    dev = ts[0].device
+    _expect(all(t is None or t.device == dev for t in ts), "all tensors of one call must be on one device")
+
+
+def _attn_shapes(q, o, k_pool, v_pool):
+    """Shapes the C entry points cannot see (they take one head_dim and the pool's slot count):
+    q and o alike, K and V pools alike, one head_dim, every tensor on q's device."""
+    _expect(q.dim() == 3 and o.shape == q.shape, "q and o must be [rows, n_q_heads, head_dim] alike")
+    _expect(k_pool.dim() == 3 and v_pool.shape == k_pool.shape,
+            "k_pool and v_pool must be [num_slots, n_kv_heads, head_dim] alike")
+    _expect(k_pool.shape[2] == q.shape[2], "the pools' head_dim differs from q's")
+    _same_device(q, o, k_pool, v_pool)
+    N, Hq, D = q.shape
+    S, Hkv, _ = k_pool.shape
+    return N, Hq, D, S, Hkv
+
+
+def _per_request(B, *ts):
+    _expect(all(t.dim() == 1 and t.shape[0] == B for t in ts), f"per-request arrays must have {B} entries")
+
+
+def _table(t):
+    _expect(t.dim() == 2, "the request / page table must be 2-D [rows, stride]")
+    return t.shape[1]
+
+
+def _rows(k_new, v_new, loc, k_pool, v_pool):
+    _expect(k_new.dim() == 3 and v_new.shape == k_new.shape,
+            "k_new and v_new must be [n, n_kv_heads, head_dim] alike")
+    _expect(k_pool.dim() == 3 and v_pool.shape == k_pool.shape and tuple(k_new.shape[1:]) == tuple(k_pool.shape[1:]),
+            "k_pool and v_pool must be [num_slots, n_kv_heads, head_dim] alike, with the rows' heads and head_dim")
+    _expect(loc.dim() == 1 and loc.shape[0] <= k_new.shape[0], "loc must be 1-D with at most one entry per row")
+    _same_device(k_new, v_new, loc, k_pool, v_pool)
 
 
 def _check(status: int, where: str):
@@ -143,9 +185,10 @@ def _check(status: int, where: str):
 
 def kv_store(k_new, v_new, loc, k_pool, v_pool, stream=None):
     """k_pool[loc[i]] = k_new[i]; v_pool[loc[i]] = v_new[i] (in place)."""
+    _rows(k_new, v_new, loc, k_pool, v_pool)
     S, Hkv, D = k_pool.shape
     _check(load().rax_kv_store(_dtype(k_new, v_new, k_pool, v_pool), _ptr(k_new), _ptr(v_new), _idx(loc),
-                               loc.shape[0], _ptr(k_pool), _ptr(v_pool), S, Hkv, D, _stream(stream)),
+                               loc.shape[0], _ptr(k_pool), _ptr(v_pool), S, Hkv, D, _stream(stream, k_pool.device)),
            "rax_kv_store")
 
 
@@ -175,10 +218,11 @@ def extend_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefi
                      extend_start_loc, max_extend_len, max_seq_len, sm_scale, workspace=None,
                      stream=None):
     """EXTEND attention of the suffix rows ``q`` into ``o`` (same shape), keys from the pool."""
-    N, Hq, D = q.shape
-    S, Hkv, Dk = k_pool.shape
+    N, Hq, D, S, Hkv = _attn_shapes(q, o, k_pool, v_pool)
     dt = _dtype(q, o, k_pool, v_pool)
     B = prefix_lens.shape[0]
+    _per_request(B, req_pool_indices, prefix_lens, extend_lens, extend_start_loc)
+    _table(req_to_token)
     need = extend_workspace_bytes(dt, B, N, max_extend_len, max_seq_len, Hq, Hkv, D)
     workspace = _workspace(need, workspace, q.device)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -186,7 +230,7 @@ def extend_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefi
                                        req_to_token.shape[1], _idx(req_pool_indices), _idx(prefix_lens),
                                        _idx(extend_lens), _idx(extend_start_loc), B, N, int(max_extend_len),
                                        int(max_seq_len), Hq, Hkv, D, float(sm_scale), _ptr(workspace), wbytes,
-                                       _stream(stream)),
+                                       _stream(stream, q.device)),
            "rax_extend_attention")
 
 
@@ -195,12 +239,16 @@ def extend_attention_ragged(q, o, k_new, v_new, k_pool, v_pool, req_to_token, re
                             workspace=None, stream=None):
     """EXTEND with the suffix K/V read from ``k_new`` / ``v_new`` (rows in ``q``'s order); with
     ``store_loc`` the rows are also written to those pool slots."""
-    N, Hq, D = q.shape
-    S, Hkv, Dk = k_pool.shape
+    N, Hq, D, S, Hkv = _attn_shapes(q, o, k_pool, v_pool)
     dt = _dtype(q, o, k_pool, v_pool)
     if _dtype(k_new, v_new) != dt or k_new.shape != (N, Hkv, D) or v_new.shape != k_new.shape:
         raise ValueError("k_new / v_new must be [tokens, n_kv_heads, head_dim] in the pool's dtype")
+    _expect(store_loc is None or (store_loc.dim() == 1 and store_loc.shape[0] == N),
+            "store_loc must hold one slot per suffix row")
+    _same_device(q, k_new, v_new, store_loc)
     B = prefix_lens.shape[0]
+    _per_request(B, req_pool_indices, prefix_lens, extend_lens, extend_start_loc)
+    _table(req_to_token)
     need = extend_workspace_bytes(dt, B, N, max_extend_len, max_seq_len, Hq, Hkv, D)
     workspace = _workspace(need, workspace, q.device)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -209,7 +257,8 @@ def extend_attention_ragged(q, o, k_new, v_new, k_pool, v_pool, req_to_token, re
                                               _ptr(v_pool), S, _idx(req_to_token), req_to_token.shape[1],
                                               _idx(req_pool_indices), _idx(prefix_lens), _idx(extend_lens),
                                               _idx(extend_start_loc), B, N, int(max_extend_len), int(max_seq_len),
-                                              Hq, Hkv, D, float(sm_scale), _ptr(workspace), wbytes, _stream(stream)),
+                                              Hq, Hkv, D, float(sm_scale), _ptr(workspace), wbytes,
+                                              _stream(stream, q.device)),
            "rax_extend_attention_ragged")
 
 
@@ -217,10 +266,11 @@ def extend_attention_paged(q, o, k_pool, v_pool, page_table, page_size, req_pool
                            extend_lens, extend_start_loc, max_extend_len, max_seq_len, sm_scale, workspace=None,
                            stream=None):
     """EXTEND with keys addressed through a page table of ``page_size`` slots per page."""
-    N, Hq, D = q.shape
-    S, Hkv, Dk = k_pool.shape
+    N, Hq, D, S, Hkv = _attn_shapes(q, o, k_pool, v_pool)
     dt = _dtype(q, o, k_pool, v_pool)
     B = prefix_lens.shape[0]
+    _per_request(B, req_pool_indices, prefix_lens, extend_lens, extend_start_loc)
+    _table(page_table)
     need = extend_workspace_bytes(dt, B, N, max_extend_len, max_seq_len, Hq, Hkv, D)
     workspace = _workspace(need, workspace, q.device)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -228,39 +278,42 @@ def extend_attention_paged(q, o, k_pool, v_pool, page_table, page_size, req_pool
                                              _idx(page_table), page_table.shape[1], int(page_size),
                                              _idx(req_pool_indices), _idx(prefix_lens), _idx(extend_lens),
                                              _idx(extend_start_loc), B, N, int(max_extend_len), int(max_seq_len),
-                                             Hq, Hkv, D, float(sm_scale), _ptr(workspace), wbytes, _stream(stream)),
+                                             Hq, Hkv, D, float(sm_scale), _ptr(workspace), wbytes,
+                                             _stream(stream, q.device)),
            "rax_extend_attention_paged")
 
 
 def decode_attention_paged(q, o, k_pool, v_pool, page_table, page_size, req_pool_indices, seq_lens, max_seq_len,
                            sm_scale, workspace=None, stream=None):
     """DECODE with keys addressed through a page table of ``page_size`` slots per page."""
-    B, Hq, D = q.shape
-    S, Hkv, Dk = k_pool.shape
+    B, Hq, D, S, Hkv = _attn_shapes(q, o, k_pool, v_pool)
     dt = _dtype(q, o, k_pool, v_pool)
+    _per_request(B, req_pool_indices, seq_lens)
+    _table(page_table)
     need = decode_workspace_bytes(dt, B, max_seq_len, Hq, Hkv, D)
     workspace = _workspace(need, workspace, q.device)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().rax_decode_attention_paged(dt, _ptr(q), _ptr(o), _ptr(k_pool), _ptr(v_pool), S,
                                              _idx(page_table), page_table.shape[1], int(page_size),
                                              _idx(req_pool_indices), _idx(seq_lens), B, int(max_seq_len), Hq, Hkv,
-                                             D, float(sm_scale), _ptr(workspace), wbytes, _stream(stream)),
+                                             D, float(sm_scale), _ptr(workspace), wbytes, _stream(stream, q.device)),
            "rax_decode_attention_paged")
 
 
 def decode_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, seq_lens, max_seq_len, sm_scale,
                      workspace=None, stream=None):
     """DECODE attention of one query per request ``q`` [B, Hq, D] into ``o``."""
-    B, Hq, D = q.shape
-    S, Hkv, Dk = k_pool.shape
+    B, Hq, D, S, Hkv = _attn_shapes(q, o, k_pool, v_pool)
     dt = _dtype(q, o, k_pool, v_pool)
+    _per_request(B, req_pool_indices, seq_lens)
+    _table(req_to_token)
     need = decode_workspace_bytes(dt, B, max_seq_len, Hq, Hkv, D)
     workspace = _workspace(need, workspace, q.device)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().rax_decode_attention(dt, _ptr(q), _ptr(o), _ptr(k_pool), _ptr(v_pool), S, _idx(req_to_token),
                                        req_to_token.shape[1], _idx(req_pool_indices), _idx(seq_lens), B,
                                        int(max_seq_len), Hq, Hkv, D, float(sm_scale), _ptr(workspace), wbytes,
-                                       _stream(stream)),
+                                       _stream(stream, q.device)),
            "rax_decode_attention")
 
 
@@ -278,10 +331,11 @@ def _bf16(t):
 
 def kv_store_fp8(k_new, v_new, loc, k_pool, v_pool, k_scale=1.0, v_scale=1.0, stream=None):
     """Write bf16 rows into FP8 E4M3 pools at ``loc`` (scale 1.0 when the caller has none)."""
+    _rows(k_new, v_new, loc, k_pool, v_pool)
     S, Hkv, D = k_pool.shape
     _check(load().rax_kv_store_fp8(_bf16(k_new), _bf16(v_new), _idx(loc), loc.shape[0], _fp8_pool(k_pool),
                                    _fp8_pool(v_pool), S, Hkv, D, float(k_scale), float(v_scale),
-                                   _stream(stream)),
+                                   _stream(stream, k_pool.device)),
            "rax_kv_store_fp8")
 
 
@@ -289,9 +343,10 @@ def extend_attention_fp8(q, o, k_pool, v_pool, req_to_token, req_pool_indices, p
                          extend_start_loc, max_extend_len, max_seq_len, sm_scale, k_scale=1.0, v_scale=1.0,
                          workspace=None, stream=None):
     """EXTEND attention over FP8 E4M3 pools (bf16 ``q`` and ``o``)."""
-    N, Hq, D = q.shape
-    S, Hkv, Dk = k_pool.shape
+    N, Hq, D, S, Hkv = _attn_shapes(q, o, k_pool, v_pool)
     B = prefix_lens.shape[0]
+    _per_request(B, req_pool_indices, prefix_lens, extend_lens, extend_start_loc)
+    _table(req_to_token)
     need = extend_workspace_bytes(FP8_E4M3, B, N, max_extend_len, max_seq_len, Hq, Hkv, D)
     workspace = _workspace(need, workspace, q.device)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -300,15 +355,16 @@ def extend_attention_fp8(q, o, k_pool, v_pool, req_to_token, req_pool_indices, p
                                            _idx(prefix_lens), _idx(extend_lens), _idx(extend_start_loc), B, N,
                                            int(max_extend_len), int(max_seq_len), Hq, Hkv, D, float(sm_scale),
                                            float(k_scale), float(v_scale), _ptr(workspace), wbytes,
-                                           _stream(stream)),
+                                           _stream(stream, q.device)),
            "rax_extend_attention_fp8")
 
 
 def decode_attention_fp8(q, o, k_pool, v_pool, req_to_token, req_pool_indices, seq_lens, max_seq_len, sm_scale,
                          k_scale=1.0, v_scale=1.0, workspace=None, stream=None):
     """DECODE attention over FP8 E4M3 pools (bf16 ``q`` and ``o``)."""
-    B, Hq, D = q.shape
-    S, Hkv, Dk = k_pool.shape
+    B, Hq, D, S, Hkv = _attn_shapes(q, o, k_pool, v_pool)
+    _per_request(B, req_pool_indices, seq_lens)
+    _table(req_to_token)
     need = decode_workspace_bytes(FP8_E4M3, B, int(max_seq_len), Hq, Hkv, D)
     workspace = _workspace(need, workspace, q.device)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -316,5 +372,5 @@ def decode_attention_fp8(q, o, k_pool, v_pool, req_to_token, req_pool_indices, s
                                            _idx(req_to_token), req_to_token.shape[1], _idx(req_pool_indices),
                                            _idx(seq_lens), B, int(max_seq_len), Hq, Hkv, D, float(sm_scale),
                                            float(k_scale), float(v_scale), _ptr(workspace), wbytes,
-                                           _stream(stream)),
+                                           _stream(stream, q.device)),
            "rax_decode_attention_fp8")

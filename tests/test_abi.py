@@ -201,3 +201,36 @@ def test_paged_calls_check_page_size_and_table_width():
     assert dec(L=513) == 2               # 8 pages of 64
     assert dec(B=0) == 0
     assert dec(pt=None) == 1
+
+
+def test_binding_checks_what_the_abi_cannot_see():
+    """The C calls take one head_dim, one row count and the per-request arrays' length from the
+    batch size; the binding compares the tensors' own shapes first (host tensors suffice: the
+    checks run before any device pointer is taken)."""
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros(6, 8, 128, dtype=bf)
+    kp = torch.zeros(32, 2, 128, dtype=bf)
+    r2t = torch.zeros(2, 16, dtype=torch.int32)
+    ints = lambda n: torch.zeros(n, dtype=torch.int32)
+    ext = lambda q, o, kp, vp, per: R.extend_attention(q, o, kp, vp, r2t, *per, 3, 16, 0.1)
+    with pytest.raises(ValueError, match="head_dim"):
+        ext(q, torch.zeros_like(q), torch.zeros(32, 2, 64, dtype=bf), torch.zeros(32, 2, 64, dtype=bf), [ints(2)] * 4)
+    with pytest.raises(ValueError, match="q and o"):
+        ext(q, torch.zeros(6, 8, 64, dtype=bf), kp, torch.zeros_like(kp), [ints(2)] * 4)
+    with pytest.raises(ValueError, match="k_pool and v_pool"):
+        ext(q, torch.zeros_like(q), kp, torch.zeros(31, 2, 128, dtype=bf), [ints(2)] * 4)
+    with pytest.raises(ValueError, match="per-request"):
+        ext(q, torch.zeros_like(q), kp, torch.zeros_like(kp), [ints(2), ints(2), ints(3), ints(2)])
+    with pytest.raises(ValueError, match="2-D"):
+        R.decode_attention(q, torch.zeros_like(q), kp, torch.zeros_like(kp), ints(16), ints(6), ints(6), 16, 0.1)
+    with pytest.raises(ValueError, match="per-request"):
+        R.decode_attention(q, torch.zeros_like(q), kp, torch.zeros_like(kp), r2t, ints(6), ints(5), 16, 0.1)
+    with pytest.raises(ValueError, match="loc"):
+        R.kv_store(torch.zeros(3, 2, 128, dtype=bf), torch.zeros(3, 2, 128, dtype=bf), ints(4), kp, torch.zeros_like(kp))
+    with pytest.raises(ValueError, match="head_dim"):
+        R.kv_store(torch.zeros(3, 2, 64, dtype=bf), torch.zeros(3, 2, 64, dtype=bf), ints(3), kp, torch.zeros_like(kp))
+    with pytest.raises(ValueError, match="store_loc"):
+        R.extend_attention_ragged(q, torch.zeros_like(q), torch.zeros(6, 2, 128, dtype=bf),
+                                  torch.zeros(6, 2, 128, dtype=bf), kp, torch.zeros_like(kp), r2t, ints(2), ints(2),
+                                  ints(2), ints(2), 3, 16, 0.1, store_loc=ints(5))
