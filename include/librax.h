@@ -20,6 +20,10 @@
  * - head_dim must be 64 or 128. n_q_heads must be a positive multiple of n_kv_heads; query
  *   head h reads kv head h / (n_q_heads / n_kv_heads) (contiguous groups: grouped-query
  *   attention, "Inside SGLang", Step 3).
+ * - Kernels exist for (group G = n_q_heads / n_kv_heads): fp32 EXTEND and DECODE, any G and
+ *   head_dim 64 or 128; bf16 (and FP8-pool) EXTEND, head_dim 128 and G in {1, 2, 4, 8, 16, 32};
+ *   bf16 (and FP8-pool) DECODE, head_dim 64 or 128 and G from 1 to 16. Any other valid shape
+ *   returns RAX_ERR_UNSUPPORTED before anything is enqueued.
  * - `stream` is a hipStream_t (NULL = the null stream). Every call only ENQUEUES work on it:
  *   the library never allocates, frees or synchronises, and keeps no state between calls.
  *   Buffers must stay alive until the stream has passed the call. Calls are thread-safe.

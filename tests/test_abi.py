@@ -77,6 +77,9 @@ def test_extend_validation():
     assert extend(d=96) == 4
     assert extend(hq=6, hkv=2) == 4          # bf16 MFMA path needs a power-of-two group
     assert extend(hq=128, hkv=2) == 4        # group 64 is beyond the 256-row tile
+    assert extend(d=64) == 4                 # bf16 EXTEND has a head_dim 128 kernel only
+    assert extend(dtype=1, d=64, batch=0, q=None) == 0           # fp32: head_dim 64 ...
+    assert extend(dtype=1, hq=6, hkv=2, batch=0, q=None) == 0    # ... and any group
     assert extend(scale=float("nan")) == 2
     assert extend(q=None) == 1
     assert extend(start=None) == 1
@@ -99,6 +102,8 @@ def test_decode_validation():
     assert decode(hq=8, hkv=3) == 2
     assert decode(d=32) == 4
     assert decode(hq=34, hkv=2) == 4         # group 17 is beyond the 16-wide head tile
+    assert decode(dtype=1, hq=34, hkv=2, batch=0, q=None) == 0   # fp32: any group
+    assert decode(d=64, batch=0, q=None) == 0                     # bf16 DECODE: head_dim 64 too
     assert decode(seq=None) == 1
     # workspace: bf16 needs one, too small or missing is refused before any launch
     need = lib().rax_decode_workspace_bytes(0, 3, 300, 8, 2, 128)
