@@ -83,8 +83,8 @@ const char* rax_status_str(int status);
  *   dtype        element format of k_new, v_new, k_pool, v_pool.
  *   k_new, v_new [n_new, n_kv_heads, head_dim] rows to write.
  *   loc          [n_new] int32 destination slots. CONTRACT: distinct and in [0, num_slots).
- *                Out-of-range or repeated entries are undefined behaviour (not checked on the
- *                device in release builds).
+ *                Out-of-range or repeated entries are undefined behaviour (not checked by this
+ *                call; rax_check_kv_store counts them).
  *   k_pool, v_pool [num_slots, n_kv_heads, head_dim] pools, written in place. No other row
  *                changes; the copy is bit-exact.
  * Errors: RAX_ERR_NULL, RAX_ERR_SHAPE (n_new < 0, n_new > num_slots, num_slots <= 0,
@@ -302,6 +302,71 @@ int rax_decode_attention_fp8(const void* q, void* o, const void* k_pool, const v
  * shapes (bf16; 1 for fp32 or empty shapes; -1 if the shapes need more than 2^31 - 1). Ranges
  * past the end of the actual key stream exit at once. For tests and reports. */
 int32_t rax_decode_num_splits(int dtype, int32_t batch, int32_t max_seq_len, int32_t n_kv_heads);
+
+/*
+ * Debug checks of the device-side contracts -- for callers that want the contracts above
+ * verified (the attention and store calls themselves trust their index arrays).
+ *
+ * Each check enqueues kernels on `stream` that read the index arrays a call would be given,
+ * only inside the bounds of the host arguments (never through an index that fails its check),
+ * and writes to `counts` (device int32[RAX_CHECK_COUNT], zeroed by the check itself) the number
+ * of entries that break each contract:
+ *
+ *   RAX_CHECK_LENGTH     requests whose lengths or start break the call's CONTRACT (EXTEND:
+ *                        0 <= p, 0 <= e <= max_extend_len, p + e <= max_seq_len, 0 <= s,
+ *                        s + e <= total_extend_tokens; DECODE: seq_lens[b] <= max_seq_len);
+ *                        their positions are not examined further.
+ *   RAX_CHECK_ROW        requests with valid lengths that read keys, whose
+ *                        req_pool_indices[b] lies outside [0, table_rows); their positions are
+ *                        not examined further.
+ *   RAX_CHECK_SLOT       positions the call reads whose slot (token table) or page (page
+ *                        table: page * P + P <= num_slots) lies outside the pool; for the
+ *                        store checks, loc / store_loc entries outside [0, num_slots).
+ *   RAX_CHECK_DUPLICATE  loc / store_loc entries equal to an earlier entry.
+ *   RAX_CHECK_OVERLAP    positions a ragged call reads from the pool whose slot is also one
+ *                        of its store_loc slots.
+ *
+ * The positions a call reads: EXTEND 0 .. p + e - 1 (0 .. p - 1 for the ragged call), for
+ * requests with e > 0; DECODE 0 .. seq_lens[b] - 1. All zero means the arrays satisfy the
+ * contracts the checks cover. Counts are per entry and wrap past 2^31 - 1.
+ *
+ * Arguments (as the call being checked, plus)
+ *   table_rows   rows of req_to_token / page_table (stride table_stride entries).
+ *   page_size    1 for a token table, else the page size (a power of two up to 2^20).
+ *   workspace    the duplicate and overlap checks' bitmap, rax_check_workspace_bytes(num_slots)
+ *                bytes: needed by rax_check_kv_store, and by rax_check_extend when store_loc is
+ *                given; contents are overwritten.
+ *   counts       device int32[RAX_CHECK_COUNT], written by the check.
+ * Errors: RAX_ERR_NULL, RAX_ERR_SHAPE (as the checked call, plus page_size, table_rows <= 0
+ *   with batch > 0, max_seq_len > table_stride * page_size, store_loc without ragged),
+ *   RAX_ERR_WORKSPACE, RAX_ERR_LAUNCH. Like every call they only enqueue work: read `counts`
+ *   after the stream has passed them.
+ */
+typedef enum rax_check_item {
+    RAX_CHECK_LENGTH = 0,
+    RAX_CHECK_ROW = 1,
+    RAX_CHECK_SLOT = 2,
+    RAX_CHECK_DUPLICATE = 3,
+    RAX_CHECK_OVERLAP = 4,
+    RAX_CHECK_COUNT = 5
+} rax_check_item;
+
+size_t rax_check_workspace_bytes(int64_t num_slots);
+
+int rax_check_kv_store(const int32_t* loc, int64_t n_new, int64_t num_slots, void* workspace,
+                       size_t workspace_bytes, int32_t* counts, void* stream);
+
+int rax_check_extend(const int32_t* table, int64_t table_rows, int64_t table_stride,
+                     int32_t page_size, const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                     const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
+                     int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
+                     int64_t num_slots, int32_t ragged, const int32_t* store_loc, void* workspace,
+                     size_t workspace_bytes, int32_t* counts, void* stream);
+
+int rax_check_decode(const int32_t* table, int64_t table_rows, int64_t table_stride,
+                     int32_t page_size, const int32_t* req_pool_indices, const int32_t* seq_lens,
+                     int32_t batch, int32_t max_seq_len, int64_t num_slots, int32_t* counts,
+                     void* stream);
 
 #ifdef __cplusplus
 }

@@ -2,6 +2,7 @@
 // Semantics, layouts, ownership and error behaviour of each call are documented in librax.h.
 #include "librax.h"
 #include "rax_launch.h"
+#include "rax_check.h"
 
 namespace {
 
@@ -292,6 +293,80 @@ int rax_decode_attention_paged(int dtype, const void* q, void* o, const void* k_
     return decode_call(dtype, false, q, o, k_pool, v_pool, num_slots, page_table, pt_stride,
                        req_pool_indices, seq_lens, batch, max_seq_len, n_q_heads, n_kv_heads, head_dim,
                        sm_scale, 1.f, 1.f, workspace, workspace_bytes, stream, ps);
+}
+
+}  // extern "C"
+
+static_assert(RAX_CHECK_LENGTH == rax::kCheckLength && RAX_CHECK_ROW == rax::kCheckRow &&
+                  RAX_CHECK_SLOT == rax::kCheckSlot && RAX_CHECK_DUPLICATE == rax::kCheckDuplicate &&
+                  RAX_CHECK_OVERLAP == rax::kCheckOverlap && RAX_CHECK_COUNT == rax::kCheckCount,
+              "rax_check_item and the kernels' counters must agree");
+
+namespace {
+
+// Host checks and launch shared by rax_check_extend and rax_check_decode.
+int check_requests(bool ext, const int32_t* table, int64_t table_rows, int64_t table_stride,
+                   int32_t page_size, const int32_t* rpi, const int32_t* lens_a,
+                   const int32_t* lens_b, const int32_t* start, int32_t batch, int64_t total,
+                   int32_t max_ext, int32_t max_seq, int64_t num_slots, bool ragged,
+                   const int32_t* store_loc, void* workspace, size_t workspace_bytes,
+                   int32_t* counts, void* stream) {
+    const int ps = page_shift_of(page_size);
+    if (ps < 0 || batch < 0 || table_stride <= 0 || table_stride > (INT64_MAX >> 21) ||
+        max_seq < 0 || max_seq > (table_stride << ps) || num_slots <= 0 || total < 0 ||
+        max_ext < 0 || (batch > 0 && table_rows <= 0) || (store_loc && !ragged))
+        return RAX_ERR_SHAPE;
+    if (!counts) return RAX_ERR_NULL;
+    if (batch > 0 && (!table || !rpi || !lens_a || (ext && (!lens_b || !start)))) return RAX_ERR_NULL;
+    const bool marks = store_loc != nullptr && total > 0;
+    if (marks && (!workspace || workspace_bytes < rax_check_workspace_bytes(num_slots)))
+        return RAX_ERR_WORKSPACE;
+    rax::CheckArgs c{};
+    c.table = table; c.table_rows = table_rows; c.stride = table_stride; c.page_shift = ps;
+    c.rpi = rpi; c.lens_a = lens_a; c.lens_b = ext ? lens_b : nullptr; c.start = ext ? start : nullptr;
+    c.total = total; c.max_ext = max_ext; c.max_seq = max_seq; c.num_slots = num_slots;
+    c.ragged = ragged; c.store_loc = marks ? store_loc : nullptr; c.bitmap = workspace;
+    c.counts = counts; c.batch = batch;
+    return rax::launch_check_requests(c, (hipStream_t)stream) == 0 ? RAX_OK : RAX_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rax_check_workspace_bytes(int64_t num_slots) {
+    return num_slots > 0 ? (size_t)rax::check_bitmap_words(num_slots) * sizeof(uint32_t) : 0;
+}
+
+int rax_check_kv_store(const int32_t* loc, int64_t n_new, int64_t num_slots, void* workspace,
+                       size_t workspace_bytes, int32_t* counts, void* stream) {
+    if (n_new < 0 || num_slots <= 0) return RAX_ERR_SHAPE;
+    if (!counts || (n_new > 0 && !loc)) return RAX_ERR_NULL;
+    if (!workspace || workspace_bytes < rax_check_workspace_bytes(num_slots)) return RAX_ERR_WORKSPACE;
+    return rax::launch_check_store(loc, n_new, num_slots, workspace, counts, (hipStream_t)stream) == 0
+               ? RAX_OK
+               : RAX_ERR_LAUNCH;
+}
+
+int rax_check_extend(const int32_t* table, int64_t table_rows, int64_t table_stride,
+                     int32_t page_size, const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                     const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
+                     int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
+                     int64_t num_slots, int32_t ragged, const int32_t* store_loc, void* workspace,
+                     size_t workspace_bytes, int32_t* counts, void* stream) {
+    return check_requests(true, table, table_rows, table_stride, page_size, req_pool_indices,
+                          prefix_lens, extend_lens, extend_start_loc, batch, total_extend_tokens,
+                          max_extend_len, max_seq_len, num_slots, ragged != 0, store_loc, workspace,
+                          workspace_bytes, counts, stream);
+}
+
+int rax_check_decode(const int32_t* table, int64_t table_rows, int64_t table_stride,
+                     int32_t page_size, const int32_t* req_pool_indices, const int32_t* seq_lens,
+                     int32_t batch, int32_t max_seq_len, int64_t num_slots, int32_t* counts,
+                     void* stream) {
+    return check_requests(false, table, table_rows, table_stride, page_size, req_pool_indices,
+                          seq_lens, nullptr, nullptr, batch, 0, 0, max_seq_len, num_slots, false,
+                          nullptr, nullptr, 0, counts, stream);
 }
 
 }  // extern "C"

@@ -20,6 +20,7 @@ __all__ = [
     "decode_attention", "extend_workspace_bytes", "decode_workspace_bytes", "decode_num_splits",
     "library_path", "declared_symbols", "FP8_E4M3", "kv_store_fp8", "decode_attention_fp8",
     "extend_attention_fp8", "extend_attention_ragged", "extend_attention_paged", "decode_attention_paged",
+    "CHECK_ITEMS", "check_kv_store", "check_extend", "check_decode",
 ]
 
 BF16 = 0
@@ -64,6 +65,12 @@ _SIGS = {
     "rax_decode_attention_fp8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_p,
                                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f, _c_f, _c_f,
                                                 _c_p, _c_sz, _c_p]),
+    "rax_check_workspace_bytes": (_c_sz, [_c_i64]),
+    "rax_check_kv_store": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_sz, _c_p, _c_p]),
+    "rax_check_extend": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64,
+                                        _c_i32, _c_i32, _c_i64, _c_i32, _c_p, _c_p, _c_sz, _c_p, _c_p]),
+    "rax_check_decode": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_i32, _c_i32, _c_i64, _c_p,
+                                        _c_p]),
 }
 
 
@@ -374,3 +381,62 @@ def decode_attention_fp8(q, o, k_pool, v_pool, req_to_token, req_pool_indices, s
                                            float(k_scale), float(v_scale), _ptr(workspace), wbytes,
                                            _stream(stream, q.device)),
            "rax_decode_attention_fp8")
+
+
+# Debug checks of the device-side contracts: counts per kind (order of rax_check_item).
+CHECK_ITEMS = ("length", "row", "slot", "duplicate", "overlap")
+
+
+def _counts_dict(counts):
+    return dict(zip(CHECK_ITEMS, (int(x) for x in counts.cpu().tolist())))  # waits for the stream
+
+
+def _check_bitmap(num_slots, device):
+    return torch.empty(load().rax_check_workspace_bytes(int(num_slots)), dtype=torch.uint8, device=device)
+
+
+def check_kv_store(loc, num_slots, stream=None):
+    """Counts of ``loc`` entries outside [0, num_slots) ("slot") and repeats ("duplicate")."""
+    _expect(loc.dim() == 1, "loc must be 1-D")
+    counts = torch.empty(len(CHECK_ITEMS), dtype=torch.int32, device=loc.device)
+    ws = _check_bitmap(num_slots, loc.device)
+    _check(load().rax_check_kv_store(_idx(loc), loc.shape[0], int(num_slots), _ptr(ws), ws.numel(), _ptr(counts),
+                                     _stream(stream, loc.device)),
+           "rax_check_kv_store")
+    return _counts_dict(counts)
+
+
+def check_extend(table, req_pool_indices, prefix_lens, extend_lens, extend_start_loc, total_tokens, max_extend_len,
+                 max_seq_len, num_slots, page_size=1, ragged=False, store_loc=None, stream=None):
+    """Contract breaks in the index arrays of an EXTEND call (token or page ``table``; the ragged
+    call reads only the prefix from the pool, and ``store_loc`` adds the duplicate / overlap
+    checks of its store)."""
+    B = prefix_lens.shape[0]
+    _per_request(B, req_pool_indices, prefix_lens, extend_lens, extend_start_loc)
+    _expect(store_loc is None or (store_loc.dim() == 1 and store_loc.shape[0] == int(total_tokens)),
+            "store_loc must hold one slot per suffix row")
+    _same_device(table, req_pool_indices, prefix_lens, extend_lens, extend_start_loc, store_loc)
+    stride = _table(table)
+    counts = torch.empty(len(CHECK_ITEMS), dtype=torch.int32, device=table.device)
+    ws = _check_bitmap(num_slots, table.device) if store_loc is not None else None
+    _check(load().rax_check_extend(_idx(table), table.shape[0], stride, int(page_size), _idx(req_pool_indices),
+                                   _idx(prefix_lens), _idx(extend_lens), _idx(extend_start_loc), B, int(total_tokens),
+                                   int(max_extend_len), int(max_seq_len), int(num_slots), int(bool(ragged)),
+                                   _idx(store_loc) if store_loc is not None else None, _ptr(ws),
+                                   ws.numel() if ws is not None else 0, _ptr(counts), _stream(stream, table.device)),
+           "rax_check_extend")
+    return _counts_dict(counts)
+
+
+def check_decode(table, req_pool_indices, seq_lens, max_seq_len, num_slots, page_size=1, stream=None):
+    """Contract breaks in the index arrays of a DECODE call (token or page ``table``)."""
+    B = seq_lens.shape[0]
+    _per_request(B, req_pool_indices, seq_lens)
+    _same_device(table, req_pool_indices, seq_lens)
+    stride = _table(table)
+    counts = torch.empty(len(CHECK_ITEMS), dtype=torch.int32, device=table.device)
+    _check(load().rax_check_decode(_idx(table), table.shape[0], stride, int(page_size), _idx(req_pool_indices),
+                                   _idx(seq_lens), B, int(max_seq_len), int(num_slots), _ptr(counts),
+                                   _stream(stream, table.device)),
+           "rax_check_decode")
+    return _counts_dict(counts)

@@ -24,7 +24,9 @@ def test_every_declared_symbol_is_exported():
                           "rax_extend_attention", "rax_decode_workspace_bytes", "rax_decode_attention",
                           "rax_decode_num_splits", "rax_kv_store_fp8", "rax_extend_attention_fp8",
                           "rax_decode_attention_fp8", "rax_extend_attention_ragged",
-                          "rax_extend_attention_paged", "rax_decode_attention_paged"}
+                          "rax_extend_attention_paged", "rax_decode_attention_paged",
+                          "rax_check_workspace_bytes", "rax_check_kv_store", "rax_check_extend",
+                          "rax_check_decode"}
     out = subprocess.run(["nm", "-D", "--defined-only", R.library_path()], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for n in names:
@@ -239,3 +241,47 @@ def test_binding_checks_what_the_abi_cannot_see():
         R.extend_attention_ragged(q, torch.zeros_like(q), torch.zeros(6, 2, 128, dtype=bf),
                                   torch.zeros(6, 2, 128, dtype=bf), kp, torch.zeros_like(kp), r2t, ints(2), ints(2),
                                   ints(2), ints(2), 3, 16, 0.1, store_loc=ints(5))
+
+
+def test_check_calls_validate_before_launching():
+    L = lib()
+    assert L.rax_check_workspace_bytes(1) == 4 and L.rax_check_workspace_bytes(33) == 8
+    assert L.rax_check_workspace_bytes(0) == 0
+    ws = L.rax_check_workspace_bytes(1024)
+    # kv_store: shapes, counts, workspace
+    assert L.rax_check_kv_store(FAKE, -1, 1024, FAKE, ws, FAKE, None) == 2
+    assert L.rax_check_kv_store(FAKE, 4, 0, FAKE, ws, FAKE, None) == 2
+    assert L.rax_check_kv_store(FAKE, 4, 1024, FAKE, ws, None, None) == 1
+    assert L.rax_check_kv_store(None, 4, 1024, FAKE, ws, FAKE, None) == 1
+    assert L.rax_check_kv_store(FAKE, 4, 1024, FAKE, ws - 1, FAKE, None) == 5
+    assert L.rax_check_kv_store(FAKE, 4, 1024, None, ws, FAKE, None) == 5
+
+    def ext(**kw):
+        a = dict(table=FAKE, rows=4, stride=512, page=1, rpi=FAKE, p=FAKE, e=FAKE, s=FAKE, batch=3, total=64,
+                 max_ext=64, max_seq=300, slots=1024, ragged=0, store=None, ws=None, ws_bytes=0, counts=FAKE,
+                 stream=None)
+        a.update(kw)
+        return L.rax_check_extend(*a.values())
+
+    assert ext(page=3) == 2                      # not a power of two
+    assert ext(page=1 << 21) == 2
+    assert ext(max_seq=513) == 2                 # past the table row
+    assert ext(page=4, stride=64, max_seq=257) == 2
+    assert ext(rows=0) == 2
+    assert ext(store=FAKE) == 2                  # a store without the ragged call
+    assert ext(counts=None) == 1
+    assert ext(e=None) == 1
+    assert ext(ragged=1, store=FAKE) == 5        # the overlap check needs the bitmap
+    assert ext(ragged=1, store=FAKE, ws=FAKE, ws_bytes=ws - 1) == 5
+
+    def dec(**kw):
+        a = dict(table=FAKE, rows=4, stride=512, page=1, rpi=FAKE, seq=FAKE, batch=3, max_seq=300, slots=1024,
+                 counts=FAKE, stream=None)
+        a.update(kw)
+        return L.rax_check_decode(*a.values())
+
+    assert dec(page=0) == 2
+    assert dec(max_seq=600) == 2
+    assert dec(slots=0) == 2
+    assert dec(seq=None) == 1
+    assert dec(counts=None) == 1
