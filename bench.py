@@ -119,7 +119,7 @@ def pmc_summary(out_path: str, fetch_dir: str, write_dir: str, copy_fetch_dir: s
              "# Each counter is scaled by what it reads for a plain device copy of 1 GiB",
              "# (bench.py --copy-calibration): bytes = KiB * 1024 * factor. Per kernel: the median",
              "# over its dispatches.", "#",
-             "# Commands (repository root on the GPU box, TMPDIR=/tmp):"]
+             "# Commands (from the repository root, TMPDIR=/tmp):"]
     lines += ["#   " + c for c in command.split(" ;; ")]
     lines += ["#", f"calibration copy_bytes={COPY_BYTES} copy_fetch_kib={cf:.1f} copy_write_kib={cw:.1f} "
               f"fetch_factor={f_fac:.4f} write_factor={w_fac:.4f}"]
@@ -281,8 +281,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (see DESIGN.md for "
-              "how the path would shard); rerun with --gpus 1", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: librax has no multi-GPU path; rerun with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

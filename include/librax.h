@@ -52,7 +52,7 @@ typedef enum rax_status {
     RAX_ERR_SHAPE = 2,       /* a size or count is negative, zero where it may not be, or
                                 inconsistent with another                                     */
     RAX_ERR_DTYPE = 3,       /* unknown element format                                        */
-    RAX_ERR_UNSUPPORTED = 4, /* a valid shape this build has no kernel for (head_dim, group)  */
+    RAX_ERR_UNSUPPORTED = 4, /* a valid shape with no kernel in the library (head_dim, group) */
     RAX_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the *_workspace_bytes figure   */
     RAX_ERR_LAUNCH = 6       /* the HIP runtime refused the launch                            */
 } rax_status;
