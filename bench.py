@@ -315,7 +315,7 @@ def main():
         sys.exit(2)
     n_ext = wl.extend.total_tokens if wl.extend is not None else 0
     if kv8 and spec.dtype != "bf16":
-        print("--kv fp8 needs a bf16 workload (configs 2..5)", file=sys.stderr)
+        print("--kv fp8 needs a bf16 workload (--config 2 to 5)", file=sys.stderr)
         sys.exit(2)
     ws = None
     if dw.dec is not None:
@@ -435,9 +435,10 @@ def main():
     report["kv_store"] = dict(ms=ms["kv_store"], rows=n_new, GBps=hbm(st_bytes, ms["kv_store"]),
                               bytes=st_bytes)
     roofs = {}
-    # The traffic summaries were counted on the default step (workload 4 with its timing seed,
-    # token table, pool-reading EXTEND, warm caches) over bf16 or FP8 pools; graph replay runs the same
-    # kernels on the same data. Any other workload or mode has no counted traffic: null.
+    # The traffic summaries were counted on the default step (the mixed chunked-prefill batch,
+    # --config 4, with its timing seed; token table, pool-reading EXTEND, warm caches) over bf16
+    # or FP8 pools; graph replay runs the same kernels on the same data. Any other workload or
+    # mode has no counted traffic: null.
     counted = cfg == 4 and seed == W.TIMING_SEEDS[4] and not rag and not paged and not args.cold
     traffic = read_traffic(TRAFFIC_SUMMARY_FP8 if kv8 else TRAFFIC_SUMMARY) if counted else {}
     if wl.extend is not None:

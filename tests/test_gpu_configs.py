@@ -32,7 +32,7 @@ def sampled_tokens(wl, n_random, rng):
 
 def check(cfg, seed, variant, n_tok, n_req):
     spec = W.CONFIGS[cfg]
-    say(f"config {cfg} seed {seed} {variant}: generating")
+    say(f"{spec.name} seed {seed} {variant}: generating")
     wl = W.make_workload(spec, seed, variant)
     say("running kv_store + extend + decode")
     dw, outs = run_all(wl)
@@ -53,11 +53,11 @@ def check(cfg, seed, variant, n_tok, n_req):
 
 @pytest.mark.timeout(1200)
 @pytest.mark.parametrize("seed_off,variant", [(0, "normal"), (100, "peaked")])
-def test_config4_mixed_batch(seed_off, variant):
+def test_mixed_chunk_batch(seed_off, variant):
     check(4, W.TIMING_SEEDS[4] + seed_off, variant, n_tok=24, n_req=24)
 
 
 @pytest.mark.timeout(1200)
 @pytest.mark.parametrize("seed_off,variant", [(0, "normal"), (100, "needle")])
-def test_config5_long_context(seed_off, variant):
+def test_long_context_batch(seed_off, variant):
     check(5, W.TIMING_SEEDS[5] + seed_off, variant, n_tok=6, n_req=8)

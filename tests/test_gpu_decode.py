@@ -48,23 +48,23 @@ def test_decode_fp32(spec):
 
 
 @pytest.mark.parametrize("seed_off", [0, 100, 200])
-def test_decode_config2_full(seed_off):
+def test_decode_64req_full(seed_off):
     """64 requests, contexts 512..4096, 32 q / 8 kv heads: every output against the oracle."""
     spec = W.CONFIGS[2]
     wl = W.make_workload(spec, W.TIMING_SEEDS[2] + seed_off)
-    say(f"config 2 seed {W.TIMING_SEEDS[2] + seed_off}: generated")
+    say(f"{spec.name} seed {W.TIMING_SEEDS[2] + seed_off}: generated")
     dw, outs = run_all(wl)
     kp, vp = stored_pools(wl)
-    assert_close(out_f64(outs["decode"]), oracle_decode(wl, kp, vp), "bf16", f"config2 seed+{seed_off}")
+    assert_close(out_f64(outs["decode"]), oracle_decode(wl, kp, vp), "bf16", f"{spec.name} seed+{seed_off}")
 
 
 @pytest.mark.parametrize("variant", ["normal", "peaked"])
-def test_decode_config2_variants(variant):
+def test_decode_64req_variants(variant):
     spec = W.CONFIGS[2]
     wl = W.make_workload(spec, W.TIMING_SEEDS[2], variant)
     dw, outs = run_all(wl)
     kp, vp = stored_pools(wl)
-    assert_close(out_f64(outs["decode"]), oracle_decode(wl, kp, vp), "bf16", f"config2/{variant}")
+    assert_close(out_f64(outs["decode"]), oracle_decode(wl, kp, vp), "bf16", f"{spec.name}/{variant}")
 
 
 def test_single_key_returns_value_bitwise():

@@ -39,13 +39,13 @@ def test_extend_small(spec, variant):
 
 
 @pytest.mark.parametrize("seed_off", [0, 100, 200])
-def test_extend_config1_fp32(seed_off):
+def test_extend_tiny_fp32(seed_off):
     """Tiny EXTEND in fp32: prefixes {0,16,64,128}, extends {32,16,8,1}, 4 heads, d=64: all rows."""
     spec = W.CONFIGS[1]
     wl = W.make_workload(spec, W.TIMING_SEEDS[1] + seed_off)
     dw, outs = run_all(wl)
     kp, vp = stored_pools(wl)
-    assert_close(out_f64(outs["extend"]), oracle_extend(wl, kp, vp), "fp32", f"config1 seed+{seed_off}")
+    assert_close(out_f64(outs["extend"]), oracle_extend(wl, kp, vp), "fp32", f"{spec.name} seed+{seed_off}")
 
 
 @pytest.mark.parametrize("spec", [
@@ -75,17 +75,17 @@ def _sample_tokens(wl, per_request, rng):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("seed_off", [0, 100])
-def test_extend_config3_sampled(seed_off):
+def test_extend_shared_prefix_sampled(seed_off):
     """Shared 4,096-token prefix, 32 requests x 256 new tokens: sampled rows of 8 requests."""
     spec = W.CONFIGS[3]
     wl = W.make_workload(spec, W.TIMING_SEEDS[3] + seed_off)
-    say("config 3 generated")
+    say(f"{spec.name} generated")
     dw, outs = run_all(wl)
     kp, vp = stored_pools(wl)
     rng = np.random.default_rng(seed_off)
     toks = [t for t in _sample_tokens(wl, 12, rng) if t // 256 in (0, 1, 5, 13, 20, 27, 30, 31)]
     got = out_f64(outs["extend"])[toks]
-    assert_close(got, oracle_extend(wl, kp, vp, tokens=toks), "bf16", f"config3 seed+{seed_off}")
+    assert_close(got, oracle_extend(wl, kp, vp, tokens=toks), "bf16", f"{spec.name} seed+{seed_off}")
 
 
 def test_extend_one_token_matches_decode():
