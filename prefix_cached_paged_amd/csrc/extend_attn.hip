@@ -491,7 +491,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         // scores carried across iterations by waves 4-7 cost registers only there.
 #define RAX_PLOOPS(LAG)                                                                     \
         RAX_PTILE(LAG, it, kb0, vb0, vb3, kb2, vb2, 1, 0) ++it;                              \
-        while (it + 4 <= n_full && it + 7 <= ntiles) {                                      \
+        while (it + 4 <= n_full) {                                                          \
             RAX_PTILE(LAG, it, kb1, vb1, vb0, kb3, vb3, 0, 1) ++it;                          \
             RAX_PTILE(LAG, it, kb2, vb2, vb1, kb0, vb0, 0, 1) ++it;                          \
             RAX_PTILE(LAG, it, kb3, vb3, vb2, kb1, vb1, 0, 1) ++it;                          \
@@ -512,6 +512,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         } else {
             RAX_PLOOPS(0)
         }
+        RAX_WAIT_VMCNT(0);  // the copies past the end land before the workgroup's LDS is reused
 #undef RAX_PLOOPS
     } else {
         // prologue: copies of tiles 0 and 1 issued, tile 0 widened, the copy of tile 2 issued
