@@ -534,7 +534,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         // Tile T: staging T % 2, bf16 buffer T % 4; the first iteration is peeled.
 #define RAX_PLOOPS8(LAG)                                                                    \
         RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, kb1, vb1, 1, 0) ++it;                   \
-        while (it + 4 <= n_full && it + 8 <= ntiles) {                                      \
+        while (it + 4 <= n_full) {                                                          \
             RAX_PTILE8(LAG, it, kb1, vb1, vb0, sk0, sv0, kb2, vb2, 0, 1) ++it;               \
             RAX_PTILE8(LAG, it, kb2, vb2, vb1, sk1, sv1, kb3, vb3, 0, 1) ++it;               \
             RAX_PTILE8(LAG, it, kb3, vb3, vb2, sk0, sv0, kb0, vb0, 0, 1) ++it;               \
@@ -555,6 +555,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         } else {
             RAX_PLOOPS8(0)
         }
+        RAX_WAIT_VMCNT(0);  // as for bf16 pools: copies past the end land before LDS is reused
 #undef RAX_PLOOPS8
     }
     lsum = sum_pair32(lsum);
