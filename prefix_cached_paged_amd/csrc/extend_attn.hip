@@ -331,7 +331,11 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // keeps the copies in flight where the reads happen to buffers the compiler can tell apart,
     // so it adds no waits of its own. The only vector-memory operations are the copies (4 per
     // tile), issued two tiles ahead: when tile IT is needed the younger ones are the copies of
-    // IT+1, so wait until at most 4 (0 at the last tile) are outstanding.
+    // IT+1, so wait until at most 4 are outstanding (0 at the last tile of the masked tail,
+    // whose copies stop at the last tile). The unmasked steady loop copies unconditionally, also
+    // past the last tile (positions clamp to the last key; the buffers are not read again), and
+    // runs until fewer than four full tiles remain; the copies still in flight after the loops
+    // are drained before the workgroup ends.
     f32x16 st[2];   // scores of the tile being processed
     uint4 pf[4];    // its probabilities (bf16), the B operand of P V
 #define RAX_QK(KB)                                                                          \
