@@ -120,12 +120,12 @@ def a256(x):
 
 
 def test_decode_workspace_size():
-    # ranges per kv-head group: one resident round (768 workgroups of 4 kv heads for bf16 pools,
-    # 512 for FP8 pools), or enough 4096-key ranges for every request at max_seq_len, whichever
-    # is larger
+    # ranges per kv-head group: one resident round (768 workgroups of 4 kv heads, 3 per CU, for
+    # bf16 and FP8 pools alike), or enough 4096-key ranges for every request at max_seq_len,
+    # whichever is larger
     for B, L, hq, hkv in [(64, 4096, 32, 8), (8, 131072, 64, 8), (1, 1, 4, 4), (128, 8192, 32, 8),
                           (4096, 32768, 32, 8), (16, 1000, 64, 32)]:
-        for dtype, resident in ((0, 768), (2, 512)):
+        for dtype, resident in ((0, 768), (2, 768)):
             groups = (hkv + 3) // 4
             worst = B * ((L + 63) // 64 * 64)
             grid = max(max(1, resident // groups), (worst + 4095) // 4096)
