@@ -7,7 +7,8 @@
 // One wave per (query row, query head). Lanes take 64 keys at a time: each lane forms the full
 // dot product of the query (broadcast from LDS) with its key's row, the wave updates a running
 // max and sum, then the lanes switch to head_dim and accumulate p_j * V_j with p_j and the slot
-// broadcast by ds_bpermute. expf is used for the exponentials.
+// broadcast by ds_bpermute, loading the V rows of 8 keys at a time. expf is used for the
+// exponentials.
 #include "rax_device.h"
 #include "rax_launch.h"
 
@@ -101,15 +102,25 @@ __global__ __launch_bounds__(64) void attn_rows_fp32_kernel(
         lsum = lsum * alpha + ps;
 #pragma unroll
         for (int k = 0; k < PER; ++k) acc[k] *= alpha;
+        // P V, 8 keys at a time: their V rows are loaded together, then added in key order.
+        // Keys past the last one (lanes without a key) carry p = 0 and a clamped valid row.
         const int nj = min(64, nkeys - j0);
-        for (int jj = 0; jj < nj; ++jj) {
-            const float pb = __shfl(pj, jj, kWave);
-            const int sb = __shfl(slot, jj, kWave);
-            const int pos = j0 + jj;
-            const float* vr = (RAG && pos >= pre) ? v_new + (int64_t)(s0 + pos - pre) * pool_row + (int64_t)g * D
-                                                  : v_pool + (int64_t)sb * pool_row + (int64_t)g * D;
+        for (int jj = 0; jj < nj; jj += 8) {
+            float pb[8], vv[8][PER];
 #pragma unroll
-            for (int k = 0; k < PER; ++k) acc[k] = fmaf(pb, vr[64 * k + lane], acc[k]);
+            for (int u = 0; u < 8; ++u) {
+                pb[u] = __shfl(pj, jj + u, kWave);
+                const int sb = __shfl(slot, jj + u, kWave);
+                const int pos = min(j0 + jj + u, nkeys - 1);
+                const float* vr = (RAG && pos >= pre) ? v_new + (int64_t)(s0 + pos - pre) * pool_row + (int64_t)g * D
+                                                      : v_pool + (int64_t)sb * pool_row + (int64_t)g * D;
+#pragma unroll
+                for (int k = 0; k < PER; ++k) vv[u][k] = vr[64 * k + lane];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int k = 0; k < PER; ++k) acc[k] = fmaf(pb[u], vv[u][k], acc[k]);
         }
     }
     const float inv = 1.f / lsum;
