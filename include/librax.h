@@ -191,13 +191,15 @@ int rax_extend_attention_ragged(int dtype, const void* q, void* o, const void* k
  *   o[b, h, :] = softmax_j( sm_scale * q[b, h, :] . K[slot_j, h / G, :] ) V[slot_j, h / G, :],
  *   slot_j = req_to_token[req_pool_indices[b] * r2t_stride + j], j = 0 .. seq_lens[b] - 1.
  *
- * The work is split along the keys (split-K) in a balanced way: a small plan kernel lays the
+ * The work is split along the keys (split-K) in a balanced way: a plan lays the
  * requests' contexts end to end (each rounded up to a multiple of 64 keys) and cuts that
  * stream into equal ranges of 256..4096 keys, one per workgroup, so that every workgroup moves
  * the same bytes whatever the mix of context lengths. Partial results (fp32 o and a
  * log-sum-exp per request and range) go to the workspace and a merge kernel combines them.
- * Three kernels run on `stream` in order (plan, split, merge); the workspace holds the plan
- * and the partials and must not be used by other work until they have run.
+ * The kernels run on `stream` in order: split (which computes the plan itself for batches up
+ * to 1,024 requests; larger batches get a separate plan kernel first), then merge. The
+ * workspace holds the plan and the partials and must not be used by other work until they
+ * have run.
  *
  * Arguments
  *   q, o          [batch, n_q_heads, head_dim].
