@@ -87,6 +87,8 @@ SPECS = [
     W.Spec("fp8-dec-d64", "bf16", 16, 4, 64, 60000, decode_lens=(1, 64, 999, 5000)),
     W.Spec("fp8-dec-many", "bf16", 32, 8, 128, 60000, decode_batch=64, decode_range=(1, 120)),
     W.Spec("fp8-dec-long", "bf16", 8, 1, 128, 120000, decode_lens=(50000, 3)),
+    # more than 1,024 requests: the plan runs as its own kernel before the split
+    W.Spec("fp8-dec-plan", "bf16", 8, 2, 128, 30000, decode_batch=1500, decode_range=(1, 16)),
 ]
 # scales that put about 4 standard deviations at the top of the E4M3 range, and the default 1.0
 CASES = [("normal", "range"), ("normal", "one"), ("peaked", "range"), ("needle", "range")]
