@@ -1,4 +1,5 @@
-"""Pools above 4 GiB for the FP8, page-table and ragged calls (the 64-bit addressing kernels).
+"""Pools above 4 GiB for the token-table, FP8, page-table and ragged calls (the 64-bit addressing
+kernels).
 
 A small seeded workload is spread over a large device pool by an affine slot map
 s -> a * s + b (for page tables, pages p -> a * p + b, positions inside a page unchanged), so
@@ -121,3 +122,38 @@ def test_paged_and_ragged_pool_beyond_4gib():
     # the fused store wrote the suffix rows at their mapped slots
     got = to_host_bits(dk[loc[:n].long()])
     assert np.array_equal(got, wl.k_new[:n])
+
+
+def test_token_table_pool_beyond_4gib():
+    """bf16 pools read through the token table (the pool-reading EXTEND and DECODE) with rows
+    beyond byte 2^32: the 64-bit addressing form of the bf16 kernels."""
+    spec = W.Spec("big-tok", "bf16", 32, 8, 128, 40000, extend_prefix=(3000, 0), extend_lens=(200, 130),
+                  decode_lens=(2500, 7, 600))
+    wl = W.make_workload(spec, 813)
+    n_big, a, b = 2_400_000, 59, 11              # 4.9 GB per bf16 pool; max slot 2,359,952
+    assert (40000 - 1) * a + b < n_big and (40000 - 1) * a + b > (1 << 32) // (8 * 128 * 2)
+    say("big bf16 token-table pools: filling on the device")
+    dk = big_pool(wl.k_pool, n_big, a, b, None)
+    dv = big_pool(wl.v_pool, n_big, a, b, None)
+    r2t = to_dev(remap(wl.req_to_token, a, b))
+    R.kv_store(to_dev(wl.k_new), to_dev(wl.v_new), to_dev(remap(wl.store_loc, a, b)), dk, dv)
+    e, d = wl.extend, wl.decode
+    qe, qd = to_dev(e.q), to_dev(d.q)
+    oe, od = torch.empty_like(qe), torch.empty_like(qd)
+    say("big bf16 token-table pools: extend and decode")
+    R.extend_attention(qe, oe, dk, dv, r2t, to_dev(e.req_pool_indices), to_dev(e.prefix_lens),
+                       to_dev(e.extend_lens), to_dev(e.extend_start_loc), e.max_extend_len, e.max_seq_len,
+                       wl.sm_scale)
+    R.decode_attention(qd, od, dk, dv, r2t, to_dev(d.req_pool_indices), to_dev(d.seq_lens), d.max_seq_len,
+                       wl.sm_scale)
+    torch.cuda.synchronize()
+    kp, vp = oracle.kv_store(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.store_loc)
+    ref_e = oracle.extend_attention(e.q, kp, vp, wl.req_to_token, e.req_pool_indices, e.prefix_lens, e.extend_lens,
+                                    e.extend_start_loc, spec.n_kv_heads, wl.sm_scale)
+    ref_d = oracle.decode_attention(d.q, kp, vp, wl.req_to_token, d.req_pool_indices, d.seq_lens, spec.n_kv_heads,
+                                    wl.sm_scale)
+    assert_close(oracle.to_f64(to_host_bits(oe)), ref_e, "bf16", "big token-table extend")
+    assert_close(oracle.to_f64(to_host_bits(od)), ref_d, "bf16", "big token-table decode")
+    # rows beyond byte 2^32 are among those read
+    used = remap(wl.req_to_token[wl.req_to_token >= 0], a, b).astype(np.int64)
+    assert (used * 8 * 128 * 2 >= (1 << 32)).sum() > 100
