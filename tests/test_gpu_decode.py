@@ -22,6 +22,8 @@ SMALL = [
     W.Spec("dec-g16", "bf16", 16, 1, 128, 100000, decode_lens=(77, 4096, 12345)),
     W.Spec("dec-d64", "bf16", 16, 4, 64, 100000, decode_lens=(1, 64, 999, 5000)),
     W.Spec("dec-many", "bf16", 32, 8, 128, 400000, decode_batch=96, decode_range=(1, 3000)),
+    # head_dim 64 with more than 1,024 requests: the separate plan kernel
+    W.Spec("dec-d64-plan", "bf16", 16, 4, 64, 100000, decode_batch=1200, decode_range=(1, 40)),
 ]
 
 
