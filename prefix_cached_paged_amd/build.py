@@ -80,5 +80,26 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
     return lib_path
 
 
+C_ABI_SRC = os.path.join(ROOT, "tests", "c_abi", "single_key.c")
+C_ABI_BIN = os.path.join(ROOT, "tests", "c_abi", "single_key")
+
+
+def build_c_abi_check(verbose: bool = False) -> str:
+    """Compile the plain-C test program against include/librax.h and librax.so (host code only:
+    gcc, the HIP runtime API headers and libamdhip64; the library is found next to the package
+    at run time)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c11", "-O1", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include",
+           f"-I{os.path.join(ROOT, 'include')}", C_ABI_SRC, "-o", C_ABI_BIN, f"-L{rocm}/lib", "-lamdhip64",
+           f"-L{PKG}", "-l:librax.so", f"-Wl,-rpath,{rocm}/lib", "-Wl,-rpath,$ORIGIN/../../prefix_cached_paged_amd"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C test program failed to build:\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {C_ABI_BIN}", file=sys.stderr)
+    return C_ABI_BIN
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_c_abi_check(verbose=True)
