@@ -263,6 +263,8 @@ def main():
                     help="pool pages of this many slots, read through a page table (1 = token table)")
     ap.add_argument("--cold", action="store_true",
                     help="sweep 1 GiB through the caches before every step (per-kernel times are then cold)")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="skip timing a plain bf16 GEMM (torch.matmul) as the box's practical MFMA ceiling")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step as HIP graph replays (reported beside the eager figures)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -398,8 +400,11 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    ms = {n: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
-          for i, n in enumerate(["kv_store", "extend", "decode"])}
+    per_step = {n: [evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]
+                for i, n in enumerate(["kv_store", "extend", "decode"])}
+    ms = {n: float(np.mean(v)) for n, v in per_step.items()}
+    spread = {n: dict(median=float(np.median(v)), p10=float(np.percentile(v, 10)), p90=float(np.percentile(v, 90)))
+              for n, v in per_step.items()}
 
     graph = None
     if args.graph:
@@ -425,6 +430,27 @@ def main():
         graph = dict(ms_per_step=gev[0].elapsed_time(gev[1]) / args.steps,
                      eager_event_ms_per_step=sum(ms.values()))
 
+    mfma_ceiling = None
+    if not args.no_mfma_ceiling and dw.ext is not None:
+        # A large bf16 GEMM (hipBLASLt through torch.matmul, contiguous 2-D operands): what a
+        # library contraction reaches on this machine, at the clock sustained MFMA load runs at. Shown
+        # beside the EXTEND figure; the roofline fraction stays against the published peak.
+        n = 8192
+        a_ = torch.randn(n, n, device="cuda:0").to(torch.bfloat16)
+        b_ = torch.randn(n, n, device="cuda:0").to(torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a_, b_)
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        gev[0].record()
+        for _ in range(10):
+            torch.matmul(a_, b_)
+        gev[1].record()
+        torch.cuda.synchronize()
+        gms = gev[0].elapsed_time(gev[1]) / 10
+        mfma_ceiling = dict(kind="torch.matmul bf16 8192x8192x8192 (hipBLASLt)", ms=gms,
+                            tflops=2 * n ** 3 / (gms * 1e-3) / 1e12)
+        del a_, b_
+
     report = {}
     hbm = lambda nbytes, t_ms: nbytes / (t_ms * 1e-3) / 1e9
     n_new = int(wl.store_loc.size) - (n_ext if rag else 0)
@@ -432,7 +458,8 @@ def main():
     # bf16 store: read and write s bytes per element; FP8 store: read 2, write 1
     st_bytes = (A.kv_store_bytes(n_new, spec.n_kv_heads, spec.head_dim, spec.elem_bytes) if not kv8 else
                 n_new * 2 * spec.n_kv_heads * spec.head_dim * 3 + 4 * n_new)
-    report["kv_store"] = dict(ms=ms["kv_store"], rows=n_new, GBps=hbm(st_bytes, ms["kv_store"]),
+    report["kv_store"] = dict(ms=ms["kv_store"], ms_spread=spread["kv_store"], rows=n_new,
+                              GBps=hbm(st_bytes, ms["kv_store"]),
                               bytes=st_bytes)
     roofs = {}
     # The traffic summaries were counted on the default step (the mixed chunked-prefill batch,
@@ -445,7 +472,8 @@ def main():
         e = wl.extend
         fl = A.extend_flops(e.prefix_lens, e.extend_lens, spec.n_q_heads, spec.head_dim)
         tf = fl / (ms["extend"] * 1e-3) / 1e12
-        report["extend"] = dict(ms=ms["extend"], flops=fl, tflops=tf, frac=tf / PEAK_BF16_TFLOPS)
+        report["extend"] = dict(ms=ms["extend"], ms_spread=spread["extend"], flops=fl, tflops=tf,
+                                frac=tf / PEAK_BF16_TFLOPS)
         roofs["extend"] = dict(kernel="extend_attention_ragged (fused store)" if rag else "extend_attention",
                                bound="mfma", achieved=tf, peak=PEAK_BF16_TFLOPS,
                                unit="TFLOP/s", frac=tf / PEAK_BF16_TFLOPS,
@@ -458,7 +486,7 @@ def main():
                                    pool_eb) if not kv8 else (
             kvb + 4 * int(np.sum(d.seq_lens)) + 2 * d.batch * spec.n_q_heads * spec.head_dim * 2)
         gb = hbm(kvb, ms["decode"])
-        report["decode"] = dict(ms=ms["decode"], kv_bytes=kvb, kv_GBps=gb, frac=gb / PEAK_HBM_GBPS,
+        report["decode"] = dict(ms=ms["decode"], ms_spread=spread["decode"], kv_bytes=kvb, kv_GBps=gb, frac=gb / PEAK_HBM_GBPS,
                                 total_GBps=hbm(tot, ms["decode"]),
                                 splits=rax.decode_num_splits(rax.FP8_E4M3 if kv8 else dt, d.batch, d.max_seq_len,
                                                              spec.n_kv_heads))
@@ -514,6 +542,7 @@ def main():
         "roofline_other": [roofs[k] for k in roofs if k != dominant],
         "cpu_baseline": cpu,
         "graph": graph,
+        "mfma_ceiling": mfma_ceiling,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
