@@ -264,7 +264,8 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="sweep 1 GiB through the caches before every step (per-kernel times are then cold)")
     ap.add_argument("--no-mfma-ceiling", action="store_true",
-                    help="skip timing a plain bf16 GEMM (torch.matmul) as the box's practical MFMA ceiling")
+                    help="skip timing a plain bf16 GEMM (torch.matmul) and a torch gather of the DECODE rows "
+                         "as the box's practical MFMA and gather ceilings")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step as HIP graph replays (reported beside the eager figures)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -451,6 +452,30 @@ def main():
                             tflops=2 * n ** 3 / (gms * 1e-3) / 1e12)
         del a_, b_
 
+    gather_ceiling = None
+    if not args.no_mfma_ceiling and dw.dec is not None and not kv8 and not paged:
+        # The DECODE call's K and V rows gathered by slot with torch.index_select (a library
+        # gather-copy of the same random rows): its read rate is comparable to the DECODE KV GB/s.
+        d = wl.decode
+        rows = np.concatenate([wl.req_to_token[r, :L] for r, L in zip(d.req_pool_indices, d.seq_lens)])
+        slots = torch.from_numpy(rows.astype(np.int64)).to("cuda:0")
+        kf = dw.k_pool.view(dw.k_pool.shape[0], -1)
+        vf = dw.v_pool.view(dw.v_pool.shape[0], -1)
+        for _ in range(2):
+            gk, gv = torch.index_select(kf, 0, slots), torch.index_select(vf, 0, slots)
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        gev[0].record()
+        for _ in range(5):
+            torch.index_select(kf, 0, slots, out=gk)
+            torch.index_select(vf, 0, slots, out=gv)
+        gev[1].record()
+        torch.cuda.synchronize()
+        gms = gev[0].elapsed_time(gev[1]) / 5
+        nb = 2 * gk.numel() * gk.element_size()
+        gather_ceiling = dict(kind="torch.index_select of the DECODE call's K and V rows", ms=gms,
+                              read_GBps=nb / (gms * 1e-3) / 1e9, read_plus_write_GBps=2 * nb / (gms * 1e-3) / 1e9)
+        del gk, gv, slots
+
     report = {}
     hbm = lambda nbytes, t_ms: nbytes / (t_ms * 1e-3) / 1e9
     n_new = int(wl.store_loc.size) - (n_ext if rag else 0)
@@ -543,6 +568,7 @@ def main():
         "cpu_baseline": cpu,
         "graph": graph,
         "mfma_ceiling": mfma_ceiling,
+        "gather_ceiling": gather_ceiling,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
