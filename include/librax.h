@@ -42,6 +42,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* The HIP runtime's stream handle. Declared here so that plain C callers need no HIP headers;
+ * it is the same type hip_runtime_api.h defines (a repeated identical typedef is valid C11 and
+ * C++), so a hipStream_t from the runtime passes unchanged. */
+#ifndef HIP_INCLUDE_HIP_HIP_RUNTIME_API_H
+typedef struct ihipStream_t* hipStream_t;
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -67,7 +74,7 @@ typedef enum rax_dtype {
 int rax_version(void);
 
 /* Static, human-readable name of a status code ("RAX_OK", ...); "unknown status" otherwise. */
-const char* rax_status_str(int status);
+const char* rax_status_str(rax_status status);
 
 /*
  * kv_store -- write new K/V rows into pool slots by index.
@@ -90,9 +97,9 @@ const char* rax_status_str(int status);
  * Errors: RAX_ERR_NULL, RAX_ERR_SHAPE (n_new < 0, n_new > num_slots, num_slots <= 0,
  *   n_kv_heads <= 0), RAX_ERR_DTYPE, RAX_ERR_UNSUPPORTED (head_dim), RAX_ERR_LAUNCH.
  */
-int rax_kv_store(int dtype, const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
-                 void* k_pool, void* v_pool, int64_t num_slots, int32_t n_kv_heads, int32_t head_dim,
-                 void* stream);
+rax_status rax_kv_store(rax_dtype dtype, const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
+                        void* k_pool, void* v_pool, int64_t num_slots, int32_t n_kv_heads, int32_t head_dim,
+                        hipStream_t stream);
 
 /*
  * extend_attention -- EXTEND: the new suffix tokens of each request attend causally to the
@@ -133,17 +140,17 @@ int rax_kv_store(int dtype, const void* k_new, const void* v_new, const int32_t*
  * Errors: RAX_ERR_NULL, RAX_ERR_SHAPE, RAX_ERR_DTYPE, RAX_ERR_UNSUPPORTED, RAX_ERR_WORKSPACE,
  *   RAX_ERR_LAUNCH.
  */
-size_t rax_extend_workspace_bytes(int dtype, int32_t batch, int64_t total_extend_tokens,
+size_t rax_extend_workspace_bytes(rax_dtype dtype, int32_t batch, int64_t total_extend_tokens,
                                   int32_t max_extend_len, int32_t max_seq_len, int32_t n_q_heads,
                                   int32_t n_kv_heads, int32_t head_dim);
 
-int rax_extend_attention(int dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
-                         int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
-                         const int32_t* req_pool_indices, const int32_t* prefix_lens,
-                         const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
-                         int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
-                         int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float sm_scale,
-                         void* workspace, size_t workspace_bytes, void* stream);
+rax_status rax_extend_attention(rax_dtype dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
+                                int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                                const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
+                                int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
+                                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float sm_scale,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * extend_attention_ragged -- EXTEND with the suffix K/V taken straight from the just-computed
@@ -168,16 +175,16 @@ int rax_extend_attention(int dtype, const void* q, void* o, const void* k_pool, 
  *   store_loc entries are distinct, inside the pool, and not among any request's prefix slots.
  * Errors: as rax_extend_attention; RAX_ERR_NULL when k_new or v_new is NULL.
  */
-int rax_extend_attention_ragged(int dtype, const void* q, void* o, const void* k_new,
-                                const void* v_new, const int32_t* store_loc, void* k_pool,
-                                void* v_pool, int64_t num_slots, const int32_t* req_to_token,
-                                int64_t r2t_stride, const int32_t* req_pool_indices,
-                                const int32_t* prefix_lens, const int32_t* extend_lens,
-                                const int32_t* extend_start_loc, int32_t batch,
-                                int64_t total_extend_tokens, int32_t max_extend_len,
-                                int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
-                                int32_t head_dim, float sm_scale, void* workspace,
-                                size_t workspace_bytes, void* stream);
+rax_status rax_extend_attention_ragged(rax_dtype dtype, const void* q, void* o, const void* k_new,
+                                       const void* v_new, const int32_t* store_loc, void* k_pool,
+                                       void* v_pool, int64_t num_slots, const int32_t* req_to_token,
+                                       int64_t r2t_stride, const int32_t* req_pool_indices,
+                                       const int32_t* prefix_lens, const int32_t* extend_lens,
+                                       const int32_t* extend_start_loc, int32_t batch,
+                                       int64_t total_extend_tokens, int32_t max_extend_len,
+                                       int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                       int32_t head_dim, float sm_scale, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
 
 /*
  * decode_attention -- DECODE: one query per request over its whole context.
@@ -209,14 +216,14 @@ int rax_extend_attention_ragged(int dtype, const void* q, void* o, const void* k
  *   workspace     at least rax_decode_workspace_bytes(...) bytes.
  * Errors: as extend_attention.
  */
-size_t rax_decode_workspace_bytes(int dtype, int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+size_t rax_decode_workspace_bytes(rax_dtype dtype, int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
                                   int32_t n_kv_heads, int32_t head_dim);
 
-int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
-                         int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
-                         const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
-                         int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                         float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
+rax_status rax_decode_attention(rax_dtype dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
+                                int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                                const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
+                                int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                float sm_scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Page tables -- the same EXTEND and DECODE over a pool allocated in pages of P slots ("A
@@ -237,23 +244,23 @@ int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, 
  * Device-side CONTRACT: the entries for positions 0 .. L-1 of each used row are pages with
  *   page * P + P <= num_slots. bf16 (MFMA kernels, head_dim 128 for EXTEND) and fp32.
  */
-int rax_extend_attention_paged(int dtype, const void* q, void* o, const void* k_pool,
-                               const void* v_pool, int64_t num_slots, const int32_t* page_table,
-                               int64_t pt_stride, int32_t page_size,
-                               const int32_t* req_pool_indices, const int32_t* prefix_lens,
-                               const int32_t* extend_lens, const int32_t* extend_start_loc,
-                               int32_t batch, int64_t total_extend_tokens, int32_t max_extend_len,
-                               int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
-                               int32_t head_dim, float sm_scale, void* workspace,
-                               size_t workspace_bytes, void* stream);
+rax_status rax_extend_attention_paged(rax_dtype dtype, const void* q, void* o, const void* k_pool,
+                                      const void* v_pool, int64_t num_slots, const int32_t* page_table,
+                                      int64_t pt_stride, int32_t page_size,
+                                      const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                      const int32_t* extend_lens, const int32_t* extend_start_loc,
+                                      int32_t batch, int64_t total_extend_tokens, int32_t max_extend_len,
+                                      int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                      int32_t head_dim, float sm_scale, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
 
-int rax_decode_attention_paged(int dtype, const void* q, void* o, const void* k_pool,
-                               const void* v_pool, int64_t num_slots, const int32_t* page_table,
-                               int64_t pt_stride, int32_t page_size,
-                               const int32_t* req_pool_indices, const int32_t* seq_lens,
-                               int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
-                               int32_t n_kv_heads, int32_t head_dim, float sm_scale,
-                               void* workspace, size_t workspace_bytes, void* stream);
+rax_status rax_decode_attention_paged(rax_dtype dtype, const void* q, void* o, const void* k_pool,
+                                      const void* v_pool, int64_t num_slots, const int32_t* page_table,
+                                      int64_t pt_stride, int32_t page_size,
+                                      const int32_t* req_pool_indices, const int32_t* seq_lens,
+                                      int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                                      int32_t n_kv_heads, int32_t head_dim, float sm_scale,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * FP8 KV pools -- the K and V pools hold one OCP FP8 E4M3 byte per element (no infinities; NaN
@@ -280,30 +287,30 @@ int rax_decode_attention_paged(int dtype, const void* q, void* o, const void* k_
  *   value, so the kernel widens the bytes in registers and applies k_scale to the scores and
  *   v_scale to the output. Workspace: rax_decode_workspace_bytes(RAX_FP8_E4M3, ...).
  */
-int rax_kv_store_fp8(const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
-                     void* k_pool, void* v_pool, int64_t num_slots, int32_t n_kv_heads,
-                     int32_t head_dim, float k_scale, float v_scale, void* stream);
+rax_status rax_kv_store_fp8(const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
+                            void* k_pool, void* v_pool, int64_t num_slots, int32_t n_kv_heads,
+                            int32_t head_dim, float k_scale, float v_scale, hipStream_t stream);
 
-int rax_extend_attention_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
-                             int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
-                             const int32_t* req_pool_indices, const int32_t* prefix_lens,
-                             const int32_t* extend_lens, const int32_t* extend_start_loc,
-                             int32_t batch, int64_t total_extend_tokens, int32_t max_extend_len,
-                             int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
-                             int32_t head_dim, float sm_scale, float k_scale, float v_scale,
-                             void* workspace, size_t workspace_bytes, void* stream);
+rax_status rax_extend_attention_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                    int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                                    const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                    const int32_t* extend_lens, const int32_t* extend_start_loc,
+                                    int32_t batch, int64_t total_extend_tokens, int32_t max_extend_len,
+                                    int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t head_dim, float sm_scale, float k_scale, float v_scale,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-int rax_decode_attention_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
-                             int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
-                             const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
-                             int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
-                             int32_t head_dim, float sm_scale, float k_scale, float v_scale,
-                             void* workspace, size_t workspace_bytes, void* stream);
+rax_status rax_decode_attention_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                    int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                                    const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
+                                    int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t head_dim, float sm_scale, float k_scale, float v_scale,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Number of key ranges per group of kv heads that rax_decode_attention launches for these
  * shapes (bf16; 1 for fp32 or empty shapes; -1 if the shapes need more than 2^31 - 1). Ranges
  * past the end of the actual key stream exit at once. For tests and reports. */
-int32_t rax_decode_num_splits(int dtype, int32_t batch, int32_t max_seq_len, int32_t n_kv_heads);
+int32_t rax_decode_num_splits(rax_dtype dtype, int32_t batch, int32_t max_seq_len, int32_t n_kv_heads);
 
 /*
  * Debug checks of the device-side contracts -- for callers that want the contracts above
@@ -355,20 +362,20 @@ typedef enum rax_check_item {
 
 size_t rax_check_workspace_bytes(int64_t num_slots);
 
-int rax_check_kv_store(const int32_t* loc, int64_t n_new, int64_t num_slots, void* workspace,
-                       size_t workspace_bytes, int32_t* counts, void* stream);
+rax_status rax_check_kv_store(const int32_t* loc, int64_t n_new, int64_t num_slots, void* workspace,
+                              size_t workspace_bytes, int32_t* counts, hipStream_t stream);
 
-int rax_check_extend(const int32_t* table, int64_t table_rows, int64_t table_stride,
-                     int32_t page_size, const int32_t* req_pool_indices, const int32_t* prefix_lens,
-                     const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
-                     int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
-                     int64_t num_slots, int32_t ragged, const int32_t* store_loc, void* workspace,
-                     size_t workspace_bytes, int32_t* counts, void* stream);
+rax_status rax_check_extend(const int32_t* table, int64_t table_rows, int64_t table_stride,
+                            int32_t page_size, const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                            const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
+                            int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
+                            int64_t num_slots, int32_t ragged, const int32_t* store_loc, void* workspace,
+                            size_t workspace_bytes, int32_t* counts, hipStream_t stream);
 
-int rax_check_decode(const int32_t* table, int64_t table_rows, int64_t table_stride,
-                     int32_t page_size, const int32_t* req_pool_indices, const int32_t* seq_lens,
-                     int32_t batch, int32_t max_seq_len, int64_t num_slots, int32_t* counts,
-                     void* stream);
+rax_status rax_check_decode(const int32_t* table, int64_t table_rows, int64_t table_stride,
+                            int32_t page_size, const int32_t* req_pool_indices, const int32_t* seq_lens,
+                            int32_t batch, int32_t max_seq_len, int64_t num_slots, int32_t* counts,
+                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ int page_shift_of(int32_t page_size) {
     return s;
 }
 
-int check_heads(int32_t hq, int32_t hkv, int32_t d) {
+rax_status check_heads(int32_t hq, int32_t hkv, int32_t d) {
     if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || hq > kMaxGridYZ) return RAX_ERR_SHAPE;
     if (!head_dim_ok(d)) return RAX_ERR_UNSUPPORTED;
     return RAX_OK;
@@ -33,7 +33,7 @@ extern "C" {
 
 int rax_version(void) { return kVersion; }
 
-const char* rax_status_str(int status) {
+const char* rax_status_str(rax_status status) {
     switch (status) {
         case RAX_OK: return "RAX_OK";
         case RAX_ERR_NULL: return "RAX_ERR_NULL";
@@ -46,9 +46,9 @@ const char* rax_status_str(int status) {
     }
 }
 
-int rax_kv_store(int dtype, const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
-                 void* k_pool, void* v_pool, int64_t num_slots, int32_t n_kv_heads, int32_t head_dim,
-                 void* stream) {
+rax_status rax_kv_store(rax_dtype dtype, const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
+                        void* k_pool, void* v_pool, int64_t num_slots, int32_t n_kv_heads, int32_t head_dim,
+                        hipStream_t stream) {
     if (!dtype_ok(dtype)) return RAX_ERR_DTYPE;
     if (n_new < 0 || num_slots <= 0 || n_kv_heads <= 0 || n_new > num_slots) return RAX_ERR_SHAPE;
     if (!head_dim_ok(head_dim)) return RAX_ERR_UNSUPPORTED;
@@ -60,7 +60,7 @@ int rax_kv_store(int dtype, const void* k_new, const void* v_new, const int32_t*
                                 (hipStream_t)stream) == 0 ? RAX_OK : RAX_ERR_LAUNCH;
 }
 
-size_t rax_extend_workspace_bytes(int dtype, int32_t batch, int64_t total_extend_tokens,
+size_t rax_extend_workspace_bytes(rax_dtype dtype, int32_t batch, int64_t total_extend_tokens,
                                   int32_t max_extend_len, int32_t max_seq_len, int32_t n_q_heads,
                                   int32_t n_kv_heads, int32_t head_dim) {
     (void)dtype; (void)batch; (void)total_extend_tokens; (void)max_extend_len; (void)max_seq_len;
@@ -68,7 +68,7 @@ size_t rax_extend_workspace_bytes(int dtype, int32_t batch, int64_t total_extend
     return 0;
 }
 
-size_t rax_decode_workspace_bytes(int dtype, int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+size_t rax_decode_workspace_bytes(rax_dtype dtype, int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
                                   int32_t n_kv_heads, int32_t head_dim) {
     if ((dtype != RAX_BF16 && dtype != RAX_FP8_E4M3) || batch <= 0 || max_seq_len <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 ||
         head_dim <= 0)
@@ -77,7 +77,7 @@ size_t rax_decode_workspace_bytes(int dtype, int32_t batch, int32_t max_seq_len,
                                  dtype == RAX_FP8_E4M3);
 }
 
-int32_t rax_decode_num_splits(int dtype, int32_t batch, int32_t max_seq_len, int32_t n_kv_heads) {
+int32_t rax_decode_num_splits(rax_dtype dtype, int32_t batch, int32_t max_seq_len, int32_t n_kv_heads) {
     if (dtype != RAX_BF16 && dtype != RAX_FP8_E4M3) return 1;
     if (batch <= 0 || max_seq_len <= 0 || n_kv_heads <= 0) return 1;
     return rax::decode_grid(batch, max_seq_len, n_kv_heads, dtype == RAX_FP8_E4M3);
@@ -88,14 +88,14 @@ int32_t rax_decode_num_splits(int dtype, int32_t batch, int32_t max_seq_len, int
 namespace {
 
 // Checks and launch shared by the bf16/fp32 and FP8-pool EXTEND entry points.
-int extend_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool, const void* v_pool,
+rax_status extend_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool, const void* v_pool,
                 int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
                 const int32_t* req_pool_indices, const int32_t* prefix_lens,
                 const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
                 int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
                 int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float sm_scale,
                 float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
-                void* stream, bool ragged = false, const void* k_new = nullptr,
+                hipStream_t stream, bool ragged = false, const void* k_new = nullptr,
                 const void* v_new = nullptr, const int32_t* store_loc = nullptr,
                 int32_t page_shift = 0) {
     if (!dtype_ok(dtype)) return RAX_ERR_DTYPE;
@@ -104,7 +104,7 @@ int extend_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool,
         max_seq_len > (r2t_stride << page_shift) || max_extend_len > max_seq_len ||
         max_extend_len > total_extend_tokens)
         return RAX_ERR_SHAPE;
-    int st = check_heads(n_q_heads, n_kv_heads, head_dim);
+    const rax_status st = check_heads(n_q_heads, n_kv_heads, head_dim);
     if (st != RAX_OK) return st;
     const int32_t G = n_q_heads / n_kv_heads;
     if (dtype == RAX_BF16 && !rax::extend_bf16_supported(G, head_dim)) return RAX_ERR_UNSUPPORTED;
@@ -115,7 +115,7 @@ int extend_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool,
         !extend_lens || !extend_start_loc)
         return RAX_ERR_NULL;
     if (ragged && (!k_new || !v_new)) return RAX_ERR_NULL;
-    const size_t need = rax_extend_workspace_bytes(dtype, batch, total_extend_tokens, max_extend_len,
+    const size_t need = rax_extend_workspace_bytes((rax_dtype)dtype, batch, total_extend_tokens, max_extend_len,
                                                    max_seq_len, n_q_heads, n_kv_heads, head_dim);
     if (need > 0 && (!workspace || workspace_bytes < need)) return RAX_ERR_WORKSPACE;
 
@@ -136,17 +136,17 @@ int extend_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool,
 }
 
 // Checks and launch shared by the bf16/fp32 and FP8-pool DECODE entry points.
-int decode_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool, const void* v_pool,
+rax_status decode_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool, const void* v_pool,
                 int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
                 const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
                 int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                 float sm_scale, float k_scale, float v_scale, void* workspace,
-                size_t workspace_bytes, void* stream, int32_t page_shift = 0) {
+                size_t workspace_bytes, hipStream_t stream, int32_t page_shift = 0) {
     if (!dtype_ok(dtype)) return RAX_ERR_DTYPE;
     if (batch < 0 || batch > kMaxGridYZ || max_seq_len < 0 || num_slots <= 0 || r2t_stride <= 0 ||
         max_seq_len > (r2t_stride << page_shift))
         return RAX_ERR_SHAPE;
-    int st = check_heads(n_q_heads, n_kv_heads, head_dim);
+    const rax_status st = check_heads(n_q_heads, n_kv_heads, head_dim);
     if (st != RAX_OK) return st;
     const int32_t G = n_q_heads / n_kv_heads;
     if (dtype == RAX_BF16 && !rax::decode_bf16_supported(G, head_dim)) return RAX_ERR_UNSUPPORTED;
@@ -158,7 +158,7 @@ int decode_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool,
         return RAX_ERR_SHAPE;
     if (!q || !o || !k_pool || !v_pool || !req_to_token || !req_pool_indices || !seq_lens)
         return RAX_ERR_NULL;
-    const size_t need = rax_decode_workspace_bytes(kv8 ? RAX_FP8_E4M3 : dtype, batch, max_seq_len,
+    const size_t need = rax_decode_workspace_bytes(kv8 ? RAX_FP8_E4M3 : (rax_dtype)dtype, batch, max_seq_len,
                                                    n_q_heads, n_kv_heads, head_dim);
     if (need > 0 && (!workspace || workspace_bytes < need)) return RAX_ERR_WORKSPACE;
 
@@ -181,19 +181,19 @@ int decode_call(int dtype, bool kv8, const void* q, void* o, const void* k_pool,
 
 extern "C" {
 
-int rax_decode_attention(int dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
-                         int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
-                         const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
-                         int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                         float sm_scale, void* workspace, size_t workspace_bytes, void* stream) {
+rax_status rax_decode_attention(rax_dtype dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
+                                int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                                const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
+                                int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                float sm_scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return decode_call(dtype, false, q, o, k_pool, v_pool, num_slots, req_to_token, r2t_stride,
                        req_pool_indices, seq_lens, batch, max_seq_len, n_q_heads, n_kv_heads, head_dim,
                        sm_scale, 1.f, 1.f, workspace, workspace_bytes, stream);
 }
 
-int rax_kv_store_fp8(const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
-                     void* k_pool, void* v_pool, int64_t num_slots, int32_t n_kv_heads,
-                     int32_t head_dim, float k_scale, float v_scale, void* stream) {
+rax_status rax_kv_store_fp8(const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,
+                            void* k_pool, void* v_pool, int64_t num_slots, int32_t n_kv_heads,
+                            int32_t head_dim, float k_scale, float v_scale, hipStream_t stream) {
     if (n_new < 0 || num_slots <= 0 || n_kv_heads <= 0 || n_new > num_slots) return RAX_ERR_SHAPE;
     if (!head_dim_ok(head_dim)) return RAX_ERR_UNSUPPORTED;
     if (!scale_ok(k_scale) || !scale_ok(v_scale)) return RAX_ERR_SHAPE;
@@ -207,54 +207,54 @@ int rax_kv_store_fp8(const void* k_new, const void* v_new, const int32_t* loc, i
                                     (hipStream_t)stream) == 0 ? RAX_OK : RAX_ERR_LAUNCH;
 }
 
-int rax_decode_attention_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
-                             int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
-                             const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
-                             int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
-                             int32_t head_dim, float sm_scale, float k_scale, float v_scale,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+rax_status rax_decode_attention_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                    int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                                    const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
+                                    int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t head_dim, float sm_scale, float k_scale, float v_scale,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return decode_call(RAX_BF16, true, q, o, k_pool, v_pool, num_slots, req_to_token, r2t_stride,
                        req_pool_indices, seq_lens, batch, max_seq_len, n_q_heads, n_kv_heads, head_dim,
                        sm_scale, k_scale, v_scale, workspace, workspace_bytes, stream);
 }
 
-int rax_extend_attention(int dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
-                         int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
-                         const int32_t* req_pool_indices, const int32_t* prefix_lens,
-                         const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
-                         int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
-                         int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float sm_scale,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+rax_status rax_extend_attention(rax_dtype dtype, const void* q, void* o, const void* k_pool, const void* v_pool,
+                                int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                                const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
+                                int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
+                                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float sm_scale,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return extend_call(dtype, false, q, o, k_pool, v_pool, num_slots, req_to_token, r2t_stride,
                        req_pool_indices, prefix_lens, extend_lens, extend_start_loc, batch,
                        total_extend_tokens, max_extend_len, max_seq_len, n_q_heads, n_kv_heads,
                        head_dim, sm_scale, 1.f, 1.f, workspace, workspace_bytes, stream);
 }
 
-int rax_extend_attention_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
-                             int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
-                             const int32_t* req_pool_indices, const int32_t* prefix_lens,
-                             const int32_t* extend_lens, const int32_t* extend_start_loc,
-                             int32_t batch, int64_t total_extend_tokens, int32_t max_extend_len,
-                             int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
-                             int32_t head_dim, float sm_scale, float k_scale, float v_scale,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+rax_status rax_extend_attention_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                    int64_t num_slots, const int32_t* req_to_token, int64_t r2t_stride,
+                                    const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                    const int32_t* extend_lens, const int32_t* extend_start_loc,
+                                    int32_t batch, int64_t total_extend_tokens, int32_t max_extend_len,
+                                    int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t head_dim, float sm_scale, float k_scale, float v_scale,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return extend_call(RAX_BF16, true, q, o, k_pool, v_pool, num_slots, req_to_token, r2t_stride,
                        req_pool_indices, prefix_lens, extend_lens, extend_start_loc, batch,
                        total_extend_tokens, max_extend_len, max_seq_len, n_q_heads, n_kv_heads,
                        head_dim, sm_scale, k_scale, v_scale, workspace, workspace_bytes, stream);
 }
 
-int rax_extend_attention_ragged(int dtype, const void* q, void* o, const void* k_new,
-                                const void* v_new, const int32_t* store_loc, void* k_pool,
-                                void* v_pool, int64_t num_slots, const int32_t* req_to_token,
-                                int64_t r2t_stride, const int32_t* req_pool_indices,
-                                const int32_t* prefix_lens, const int32_t* extend_lens,
-                                const int32_t* extend_start_loc, int32_t batch,
-                                int64_t total_extend_tokens, int32_t max_extend_len,
-                                int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
-                                int32_t head_dim, float sm_scale, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+rax_status rax_extend_attention_ragged(rax_dtype dtype, const void* q, void* o, const void* k_new,
+                                       const void* v_new, const int32_t* store_loc, void* k_pool,
+                                       void* v_pool, int64_t num_slots, const int32_t* req_to_token,
+                                       int64_t r2t_stride, const int32_t* req_pool_indices,
+                                       const int32_t* prefix_lens, const int32_t* extend_lens,
+                                       const int32_t* extend_start_loc, int32_t batch,
+                                       int64_t total_extend_tokens, int32_t max_extend_len,
+                                       int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                       int32_t head_dim, float sm_scale, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
     if (total_extend_tokens > 0 && store_loc && total_extend_tokens > num_slots) return RAX_ERR_SHAPE;
     return extend_call(dtype, false, q, o, k_pool, v_pool, num_slots, req_to_token, r2t_stride,
                        req_pool_indices, prefix_lens, extend_lens, extend_start_loc, batch,
@@ -263,15 +263,15 @@ int rax_extend_attention_ragged(int dtype, const void* q, void* o, const void* k
                        v_new, store_loc);
 }
 
-int rax_extend_attention_paged(int dtype, const void* q, void* o, const void* k_pool,
-                               const void* v_pool, int64_t num_slots, const int32_t* page_table,
-                               int64_t pt_stride, int32_t page_size,
-                               const int32_t* req_pool_indices, const int32_t* prefix_lens,
-                               const int32_t* extend_lens, const int32_t* extend_start_loc,
-                               int32_t batch, int64_t total_extend_tokens, int32_t max_extend_len,
-                               int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
-                               int32_t head_dim, float sm_scale, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+rax_status rax_extend_attention_paged(rax_dtype dtype, const void* q, void* o, const void* k_pool,
+                                      const void* v_pool, int64_t num_slots, const int32_t* page_table,
+                                      int64_t pt_stride, int32_t page_size,
+                                      const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                      const int32_t* extend_lens, const int32_t* extend_start_loc,
+                                      int32_t batch, int64_t total_extend_tokens, int32_t max_extend_len,
+                                      int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                      int32_t head_dim, float sm_scale, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
     const int ps = page_shift_of(page_size);
     if (ps < 0 || (pt_stride > 0 && pt_stride > (INT64_MAX >> 21))) return RAX_ERR_SHAPE;
     return extend_call(dtype, false, q, o, k_pool, v_pool, num_slots, page_table, pt_stride,
@@ -281,13 +281,13 @@ int rax_extend_attention_paged(int dtype, const void* q, void* o, const void* k_
                        nullptr, nullptr, nullptr, ps);
 }
 
-int rax_decode_attention_paged(int dtype, const void* q, void* o, const void* k_pool,
-                               const void* v_pool, int64_t num_slots, const int32_t* page_table,
-                               int64_t pt_stride, int32_t page_size,
-                               const int32_t* req_pool_indices, const int32_t* seq_lens,
-                               int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
-                               int32_t n_kv_heads, int32_t head_dim, float sm_scale,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+rax_status rax_decode_attention_paged(rax_dtype dtype, const void* q, void* o, const void* k_pool,
+                                      const void* v_pool, int64_t num_slots, const int32_t* page_table,
+                                      int64_t pt_stride, int32_t page_size,
+                                      const int32_t* req_pool_indices, const int32_t* seq_lens,
+                                      int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                                      int32_t n_kv_heads, int32_t head_dim, float sm_scale,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
     const int ps = page_shift_of(page_size);
     if (ps < 0 || (pt_stride > 0 && pt_stride > (INT64_MAX >> 21))) return RAX_ERR_SHAPE;
     return decode_call(dtype, false, q, o, k_pool, v_pool, num_slots, page_table, pt_stride,
@@ -305,12 +305,12 @@ static_assert(RAX_CHECK_LENGTH == rax::kCheckLength && RAX_CHECK_ROW == rax::kCh
 namespace {
 
 // Host checks and launch shared by rax_check_extend and rax_check_decode.
-int check_requests(bool ext, const int32_t* table, int64_t table_rows, int64_t table_stride,
+rax_status check_requests(bool ext, const int32_t* table, int64_t table_rows, int64_t table_stride,
                    int32_t page_size, const int32_t* rpi, const int32_t* lens_a,
                    const int32_t* lens_b, const int32_t* start, int32_t batch, int64_t total,
                    int32_t max_ext, int32_t max_seq, int64_t num_slots, bool ragged,
                    const int32_t* store_loc, void* workspace, size_t workspace_bytes,
-                   int32_t* counts, void* stream) {
+                   int32_t* counts, hipStream_t stream) {
     const int ps = page_shift_of(page_size);
     if (ps < 0 || batch < 0 || table_stride <= 0 || table_stride > (INT64_MAX >> 21) ||
         max_seq < 0 || max_seq > (table_stride << ps) || num_slots <= 0 || total < 0 ||
@@ -338,8 +338,8 @@ size_t rax_check_workspace_bytes(int64_t num_slots) {
     return num_slots > 0 ? (size_t)rax::check_bitmap_words(num_slots) * sizeof(uint32_t) : 0;
 }
 
-int rax_check_kv_store(const int32_t* loc, int64_t n_new, int64_t num_slots, void* workspace,
-                       size_t workspace_bytes, int32_t* counts, void* stream) {
+rax_status rax_check_kv_store(const int32_t* loc, int64_t n_new, int64_t num_slots, void* workspace,
+                              size_t workspace_bytes, int32_t* counts, hipStream_t stream) {
     if (n_new < 0 || num_slots <= 0) return RAX_ERR_SHAPE;
     if (!counts || (n_new > 0 && !loc)) return RAX_ERR_NULL;
     if (!workspace || workspace_bytes < rax_check_workspace_bytes(num_slots)) return RAX_ERR_WORKSPACE;
@@ -348,22 +348,22 @@ int rax_check_kv_store(const int32_t* loc, int64_t n_new, int64_t num_slots, voi
                : RAX_ERR_LAUNCH;
 }
 
-int rax_check_extend(const int32_t* table, int64_t table_rows, int64_t table_stride,
-                     int32_t page_size, const int32_t* req_pool_indices, const int32_t* prefix_lens,
-                     const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
-                     int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
-                     int64_t num_slots, int32_t ragged, const int32_t* store_loc, void* workspace,
-                     size_t workspace_bytes, int32_t* counts, void* stream) {
+rax_status rax_check_extend(const int32_t* table, int64_t table_rows, int64_t table_stride,
+                            int32_t page_size, const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                            const int32_t* extend_lens, const int32_t* extend_start_loc, int32_t batch,
+                            int64_t total_extend_tokens, int32_t max_extend_len, int32_t max_seq_len,
+                            int64_t num_slots, int32_t ragged, const int32_t* store_loc, void* workspace,
+                            size_t workspace_bytes, int32_t* counts, hipStream_t stream) {
     return check_requests(true, table, table_rows, table_stride, page_size, req_pool_indices,
                           prefix_lens, extend_lens, extend_start_loc, batch, total_extend_tokens,
                           max_extend_len, max_seq_len, num_slots, ragged != 0, store_loc, workspace,
                           workspace_bytes, counts, stream);
 }
 
-int rax_check_decode(const int32_t* table, int64_t table_rows, int64_t table_stride,
-                     int32_t page_size, const int32_t* req_pool_indices, const int32_t* seq_lens,
-                     int32_t batch, int32_t max_seq_len, int64_t num_slots, int32_t* counts,
-                     void* stream) {
+rax_status rax_check_decode(const int32_t* table, int64_t table_rows, int64_t table_stride,
+                            int32_t page_size, const int32_t* req_pool_indices, const int32_t* seq_lens,
+                            int32_t batch, int32_t max_seq_len, int64_t num_slots, int32_t* counts,
+                            hipStream_t stream) {
     return check_requests(false, table, table_rows, table_stride, page_size, req_pool_indices,
                           seq_lens, nullptr, nullptr, batch, 0, 0, max_seq_len, num_slots, false,
                           nullptr, nullptr, 0, counts, stream);
