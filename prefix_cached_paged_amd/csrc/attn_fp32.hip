@@ -9,6 +9,13 @@
 // max and sum, then the lanes switch to head_dim and accumulate p_j * V_j with p_j and the slot
 // broadcast by ds_bpermute, loading the V rows of 8 keys at a time. expf is used for the
 // exponentials.
+//
+// The scores, the running max and the exponent argument s_j - m are formed in double precision;
+// everything from the weights on (p_j, the row sum, P V) is fp32. The softmax turns an absolute
+// error in a score into a relative error of its weight, and an fp32 score of magnitude ~50 (a
+// sharply peaked row) already carries ~2e-6 of rounding, which moves O(1) outputs by ~1e-5. The
+// argument s_j - m of the keys that carry weight is small, so its single rounding to fp32 is
+// harmless; downstream the errors stay relative to the weights.
 #include "rax_device.h"
 #include "rax_launch.h"
 
@@ -66,7 +73,8 @@ __global__ __launch_bounds__(64) void attn_rows_fp32_kernel(
 
     const int32_t* row = r2t + (int64_t)rpi[b] * r2t_stride;
     const int64_t pool_row = (int64_t)Hkv * D;
-    float m = -INFINITY, lsum = 0.f;
+    double m = -INFINITY;
+    float lsum = 0.f;
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.f;
@@ -80,22 +88,22 @@ __global__ __launch_bounds__(64) void attn_rows_fp32_kernel(
                               : row[jc];
         const float* kr = (RAG && jc >= pre) ? k_new + (int64_t)(s0 + jc - pre) * pool_row + (int64_t)g * D
                                              : k_pool + (int64_t)slot * pool_row + (int64_t)g * D;
-        float dot = 0.f;
+        double dot = 0.0;  // products of two fp32 values are exact in double
         for (int d = 0; d < D; d += 4) {
             const float4 kv = *(const float4*)(kr + d);
-            dot = fmaf(qs[d], kv.x, dot);
-            dot = fmaf(qs[d + 1], kv.y, dot);
-            dot = fmaf(qs[d + 2], kv.z, dot);
-            dot = fmaf(qs[d + 3], kv.w, dot);
+            dot = fma((double)qs[d], (double)kv.x, dot);
+            dot = fma((double)qs[d + 1], (double)kv.y, dot);
+            dot = fma((double)qs[d + 2], (double)kv.z, dot);
+            dot = fma((double)qs[d + 3], (double)kv.w, dot);
         }
-        const float x = ok ? dot * sm_scale : -INFINITY;
-        float mx = x;
+        const double x = ok ? dot * (double)sm_scale : -INFINITY;
+        double mx = x;
 #pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) mx = wave_max_xor(mx, s);
-        const float m_new = fmaxf(m, mx);
-        const float alpha = expf(m - m_new);
+        for (int s = 32; s >= 1; s >>= 1) mx = fmax(mx, __shfl_xor(mx, s, kWave));
+        const double m_new = fmax(m, mx);
+        const float alpha = expf((float)(m - m_new));  // m = -inf at the first block: alpha = 0
         m = m_new;
-        const float pj = ok ? expf(x - m) : 0.f;
+        const float pj = ok ? expf((float)(x - m)) : 0.f;
         float ps = pj;
 #pragma unroll
         for (int s = 32; s >= 1; s >>= 1) ps += __shfl_xor(ps, s, kWave);

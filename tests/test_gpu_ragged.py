@@ -52,11 +52,6 @@ def run_ragged(dw, wl, store_loc):
 @pytest.mark.parametrize("variant", ["normal", "peaked"])
 @pytest.mark.parametrize("spec", SPECS, ids=lambda s: s.name)
 def test_ragged_extend(spec, variant, fused_store):
-    if spec.dtype == "fp32" and variant == "peaked":
-        # The fp32 bound (1e-5 absolute) is stated for O(1) outputs. Peaked scores reach about
-        # +-50, whose fp32 rounding (2^-24 relative) alone moves the O(4) outputs by ~1e-5 in
-        # any fp32 kernel; this case is compared bitwise with the pool-reading kernel below.
-        pytest.skip("fp32 peaked: checked bitwise against kv_store + extend_attention instead")
     wl = W.make_workload(spec, 801, variant)
     e = wl.extend
     n = e.total_tokens
