@@ -82,7 +82,18 @@ def kv_store(k_pool, v_pool, k_new, v_new, loc):
     return k_out, v_out
 
 
-def gather_request_kv(k_pool, v_pool, req_to_token, row, length, k_scale=1.0, v_scale=1.0):
+def _heads(kv_heads, Hkv):
+    """The kv heads to compute: all of them, or the listed subset (in that order)."""
+    if kv_heads is None:
+        return list(range(Hkv))
+    sel = [int(g) for g in kv_heads]
+    if any(g < 0 or g >= Hkv for g in sel):
+        raise ValueError("kv_heads lists a head outside the pool")
+    return sel
+
+
+def gather_request_kv(k_pool, v_pool, req_to_token, row, length, k_scale=1.0, v_scale=1.0,
+                      kv_heads=None):
     """Gather one request's keys and values by slot, as float64 ``[length, kv_heads, head_dim]``.
 
     The slot of the request's token ``j`` is ``req_to_token[row, j]``
@@ -90,6 +101,7 @@ def gather_request_kv(k_pool, v_pool, req_to_token, row, length, k_scale=1.0, v_
     KV tensors). Only the gathered rows are converted, never the whole pool.
     FP8 pools (uint8) hold ``scale * e4m3(byte)``: the scales multiply the decoded rows
     ("Inside SGLang", Step 6, per-tensor KV scales; 1.0 for bf16/fp32 pools).
+    With ``kv_heads`` only those heads are gathered, in that order (axis 1).
     """
     S = k_pool.shape[0]
     if length < 0 or length > req_to_token.shape[1]:
@@ -97,7 +109,11 @@ def gather_request_kv(k_pool, v_pool, req_to_token, row, length, k_scale=1.0, v_
     slots = np.asarray(req_to_token[row, :length], dtype=np.int64)
     if length and (slots.min() < 0 or slots.max() >= S):
         raise ValueError(f"request table row {row} names a slot outside the pool")
-    kb, vb = to_f64(k_pool[slots]), to_f64(v_pool[slots])
+    if kv_heads is None:
+        kb, vb = to_f64(k_pool[slots]), to_f64(v_pool[slots])
+    else:
+        sel = np.asarray(kv_heads, dtype=np.int64)[None, :]
+        kb, vb = to_f64(k_pool[slots[:, None], sel]), to_f64(v_pool[slots[:, None], sel])
     if k_scale != 1.0:
         kb = kb * float(np.float32(k_scale))
     if v_scale != 1.0:
@@ -124,7 +140,8 @@ def _softmax_rows_times_v(scores: np.ndarray, v: np.ndarray) -> np.ndarray:
 
 def extend_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens,
                      extend_lens, extend_start_loc, n_kv_heads, sm_scale,
-                     tokens=None, row_block=512, k_scale=1.0, v_scale=1.0, suffix=None):
+                     tokens=None, row_block=512, k_scale=1.0, v_scale=1.0, suffix=None,
+                     kv_heads=None):
     """EXTEND attention: each request's new suffix rows over its prefix plus themselves.
 
     Follows "Origins: the paper and the first commit": self-test answer 2 (with
@@ -149,7 +166,8 @@ def extend_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, prefix_l
 
     Returns float64 ``[total_extend_tokens, n_q_heads, head_dim]``; with
     ``tokens`` (global row indices) only those rows are computed and returned in
-    that order.
+    that order. With ``kv_heads`` only the query heads of those kv heads are
+    computed; the other heads stay NaN.
     """
     S, Hkv, D = _check_pool(k_pool, v_pool)
     if Hkv != n_kv_heads:
@@ -166,6 +184,7 @@ def extend_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, prefix_l
     if Hq % Hkv:
         raise ValueError("n_q_heads must be a multiple of n_kv_heads")
     G = Hq // Hkv
+    sel = _heads(kv_heads, Hkv)
     qf = to_f64(q)
     B = len(req_pool_indices)
     want = None
@@ -190,20 +209,20 @@ def extend_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, prefix_l
             if rows.size == 0:
                 continue
         if suffix is None:
-            kb, vb = gather_request_kv(k_pool, v_pool, req_to_token, r, L, k_scale, v_scale)
+            kb, vb = gather_request_kv(k_pool, v_pool, req_to_token, r, L, k_scale, v_scale, sel)
         else:
-            kp_, vp_ = gather_request_kv(k_pool, v_pool, req_to_token, r, p, k_scale, v_scale)
-            kb = np.concatenate([kp_, to_f64(suffix[0][s0:s0 + e])])
-            vb = np.concatenate([vp_, to_f64(suffix[1][s0:s0 + e])])
+            kp_, vp_ = gather_request_kv(k_pool, v_pool, req_to_token, r, p, k_scale, v_scale, sel)
+            kb = np.concatenate([kp_, to_f64(suffix[0][s0:s0 + e][:, sel])])
+            vb = np.concatenate([vp_, to_f64(suffix[1][s0:s0 + e][:, sel])])
         for c0 in range(0, rows.size, row_block):
             rb = rows[c0:c0 + row_block]
             masked = causal_hidden(L, p, rb)                       # [rows, L]
-            for g in range(Hkv):
+            for gi, g in enumerate(sel):
                 heads = slice(g * G, (g + 1) * G)
                 qg = qf[s0 + rb, heads, :].transpose(1, 0, 2)      # [G, rows, D]
-                sc = (qg @ kb[:, g, :].T) * sm_scale               # [G, rows, L]
+                sc = (qg @ kb[:, gi, :].T) * sm_scale              # [G, rows, L]
                 sc[:, masked] = -np.inf
-                og = _softmax_rows_times_v(sc, vb[:, g, :])        # [G, rows, D]
+                og = _softmax_rows_times_v(sc, vb[:, gi, :])       # [G, rows, D]
                 og = og.transpose(1, 0, 2)                         # [rows, G, D]
                 if want is None:
                     out[s0 + rb, heads, :] = og
@@ -214,7 +233,7 @@ def extend_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, prefix_l
 
 
 def decode_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, seq_lens,
-                     n_kv_heads, sm_scale, requests=None, k_scale=1.0, v_scale=1.0):
+                     n_kv_heads, sm_scale, requests=None, k_scale=1.0, v_scale=1.0, kv_heads=None):
     """DECODE attention: one query per request over positions 0 .. seq_len-1.
 
     Follows "Inside SGLang", Step 3, "Prefill and decode have different
@@ -226,7 +245,8 @@ def decode_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, seq_lens
     step), so no mask applies.
 
     ``q`` is ``[batch, n_q_heads, head_dim]``. Returns float64 of the same shape
-    (or only the listed ``requests``, in that order).
+    (or only the listed ``requests``, in that order). With ``kv_heads`` only the
+    query heads of those kv heads are computed; the other heads stay NaN.
     """
     S, Hkv, D = _check_pool(k_pool, v_pool)
     if Hkv != n_kv_heads:
@@ -235,6 +255,7 @@ def decode_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, seq_lens
     if Dq != D or Hq % Hkv:
         raise ValueError("bad q shape")
     G = Hq // Hkv
+    sel = _heads(kv_heads, Hkv)
     qf = to_f64(q)
     reqs = range(B) if requests is None else [int(b) for b in requests]
     out = np.full((len(reqs), Hq, D), np.nan)
@@ -243,9 +264,9 @@ def decode_attention(q, k_pool, v_pool, req_to_token, req_pool_indices, seq_lens
         if L <= 0:
             raise ValueError(f"request {b}: a decode query needs at least one key")
         kb, vb = gather_request_kv(k_pool, v_pool, req_to_token, int(req_pool_indices[b]), L,
-                                   k_scale, v_scale)
-        for g in range(Hkv):
+                                   k_scale, v_scale, sel)
+        for gi, g in enumerate(sel):
             heads = slice(g * G, (g + 1) * G)
-            sc = (qf[b, heads, :] @ kb[:, g, :].T) * sm_scale      # [G, L]
-            out[k, heads, :] = _softmax_rows_times_v(sc, vb[:, g, :])
+            sc = (qf[b, heads, :] @ kb[:, gi, :].T) * sm_scale     # [G, L]
+            out[k, heads, :] = _softmax_rows_times_v(sc, vb[:, gi, :])
     return out

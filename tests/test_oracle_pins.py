@@ -451,3 +451,27 @@ def test_planted_oracle_mistakes_are_caught(monkeypatch, mutation):
         monkeypatch.setattr(oatt, "_softmax_rows_times_v", tv)
     got = run_extend(wl, kp, vp)
     assert not np.allclose(got, ref, rtol=0, atol=1e-6, equal_nan=False)
+
+
+# --------------------------------------------------------------------------- kv-head subsets
+
+@pytest.mark.parametrize("spec", TINY_SPECS[1:4], ids=lambda s: s.name)
+def test_kv_head_subset_is_a_slice_of_the_full_result(spec):
+    """Computing only some kv heads (the unit the CPU baseline's worker processes take) gives the
+    full computation's values for their query heads, bit for bit, and NaN for the others; the
+    ragged reading takes the same subset of the new rows."""
+    wl = W.make_workload(spec, 41)
+    kp, vp = stored(wl)
+    Hkv, G = spec.n_kv_heads, spec.n_q_heads // spec.n_kv_heads
+    full_e, full_d = run_extend(wl, kp, vp), run_decode(wl, kp, vp)
+    full_r = run_extend(wl, wl.k_pool, wl.v_pool, suffix=_suffix_rows(wl))
+    for sel in ([Hkv - 1], list(range(Hkv))[::-1]):
+        heads = np.concatenate([np.arange(g * G, (g + 1) * G) for g in sel])
+        rest = np.setdiff1d(np.arange(spec.n_q_heads), heads)
+        for full, part in ((full_e, run_extend(wl, kp, vp, kv_heads=sel)),
+                           (full_d, run_decode(wl, kp, vp, kv_heads=sel)),
+                           (full_r, run_extend(wl, wl.k_pool, wl.v_pool, suffix=_suffix_rows(wl), kv_heads=sel))):
+            assert np.array_equal(part[:, heads], full[:, heads], equal_nan=True)
+            assert np.all(np.isnan(part[:, rest]))
+    with pytest.raises(ValueError):
+        run_decode(wl, kp, vp, kv_heads=[Hkv])
