@@ -213,11 +213,16 @@ def decode_num_splits(dtype: int, batch, max_seq_len, n_kv_heads) -> int:
     return load().rax_decode_num_splits(dtype, batch, max_seq_len, n_kv_heads)
 
 
-def _workspace(nbytes, workspace, device):
+def _workspace(nbytes, workspace, device, stream=None):
+    """The caller's workspace, or a new one. A new block is tied to the launch stream
+    (``record_stream``): the caching allocator then does not hand it to other work until that
+    stream has passed the kernels that write and read it, although the tensor itself is dropped
+    when the call returns."""
     if nbytes == 0:
         return workspace
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        workspace.record_stream(stream if stream is not None else torch.cuda.current_stream(device))
     return workspace
 
 
@@ -231,7 +236,7 @@ def extend_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefi
     _per_request(B, req_pool_indices, prefix_lens, extend_lens, extend_start_loc)
     _table(req_to_token)
     need = extend_workspace_bytes(dt, B, N, max_extend_len, max_seq_len, Hq, Hkv, D)
-    workspace = _workspace(need, workspace, q.device)
+    workspace = _workspace(need, workspace, q.device, stream)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().rax_extend_attention(dt, _ptr(q), _ptr(o), _ptr(k_pool), _ptr(v_pool), S, _idx(req_to_token),
                                        req_to_token.shape[1], _idx(req_pool_indices), _idx(prefix_lens),
@@ -257,7 +262,7 @@ def extend_attention_ragged(q, o, k_new, v_new, k_pool, v_pool, req_to_token, re
     _per_request(B, req_pool_indices, prefix_lens, extend_lens, extend_start_loc)
     _table(req_to_token)
     need = extend_workspace_bytes(dt, B, N, max_extend_len, max_seq_len, Hq, Hkv, D)
-    workspace = _workspace(need, workspace, q.device)
+    workspace = _workspace(need, workspace, q.device, stream)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().rax_extend_attention_ragged(dt, _ptr(q), _ptr(o), _ptr(k_new), _ptr(v_new),
                                               _idx(store_loc) if store_loc is not None else None, _ptr(k_pool),
@@ -279,7 +284,7 @@ def extend_attention_paged(q, o, k_pool, v_pool, page_table, page_size, req_pool
     _per_request(B, req_pool_indices, prefix_lens, extend_lens, extend_start_loc)
     _table(page_table)
     need = extend_workspace_bytes(dt, B, N, max_extend_len, max_seq_len, Hq, Hkv, D)
-    workspace = _workspace(need, workspace, q.device)
+    workspace = _workspace(need, workspace, q.device, stream)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().rax_extend_attention_paged(dt, _ptr(q), _ptr(o), _ptr(k_pool), _ptr(v_pool), S,
                                              _idx(page_table), page_table.shape[1], int(page_size),
@@ -298,7 +303,7 @@ def decode_attention_paged(q, o, k_pool, v_pool, page_table, page_size, req_pool
     _per_request(B, req_pool_indices, seq_lens)
     _table(page_table)
     need = decode_workspace_bytes(dt, B, max_seq_len, Hq, Hkv, D)
-    workspace = _workspace(need, workspace, q.device)
+    workspace = _workspace(need, workspace, q.device, stream)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().rax_decode_attention_paged(dt, _ptr(q), _ptr(o), _ptr(k_pool), _ptr(v_pool), S,
                                              _idx(page_table), page_table.shape[1], int(page_size),
@@ -315,7 +320,7 @@ def decode_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, seq_l
     _per_request(B, req_pool_indices, seq_lens)
     _table(req_to_token)
     need = decode_workspace_bytes(dt, B, max_seq_len, Hq, Hkv, D)
-    workspace = _workspace(need, workspace, q.device)
+    workspace = _workspace(need, workspace, q.device, stream)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().rax_decode_attention(dt, _ptr(q), _ptr(o), _ptr(k_pool), _ptr(v_pool), S, _idx(req_to_token),
                                        req_to_token.shape[1], _idx(req_pool_indices), _idx(seq_lens), B,
@@ -355,7 +360,7 @@ def extend_attention_fp8(q, o, k_pool, v_pool, req_to_token, req_pool_indices, p
     _per_request(B, req_pool_indices, prefix_lens, extend_lens, extend_start_loc)
     _table(req_to_token)
     need = extend_workspace_bytes(FP8_E4M3, B, N, max_extend_len, max_seq_len, Hq, Hkv, D)
-    workspace = _workspace(need, workspace, q.device)
+    workspace = _workspace(need, workspace, q.device, stream)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().rax_extend_attention_fp8(_bf16(q), _bf16(o), _fp8_pool(k_pool), _fp8_pool(v_pool), S,
                                            _idx(req_to_token), req_to_token.shape[1], _idx(req_pool_indices),
@@ -373,7 +378,7 @@ def decode_attention_fp8(q, o, k_pool, v_pool, req_to_token, req_pool_indices, s
     _per_request(B, req_pool_indices, seq_lens)
     _table(req_to_token)
     need = decode_workspace_bytes(FP8_E4M3, B, int(max_seq_len), Hq, Hkv, D)
-    workspace = _workspace(need, workspace, q.device)
+    workspace = _workspace(need, workspace, q.device, stream)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().rax_decode_attention_fp8(_bf16(q), _bf16(o), _fp8_pool(k_pool), _fp8_pool(v_pool), S,
                                            _idx(req_to_token), req_to_token.shape[1], _idx(req_pool_indices),

@@ -38,15 +38,16 @@ def test_decode_small(spec, variant):
     assert_close(out_f64(outs["decode"]), oracle_decode(wl, kp, vp), spec.dtype, f"{spec.name}/{variant}")
 
 
+@pytest.mark.parametrize("variant", ["normal", "peaked", "needle"])
 @pytest.mark.parametrize("spec", [
     W.Spec("dec-fp32-d64", "fp32", 4, 4, 64, 20000, decode_lens=(1, 64, 65, 1000, 3000)),
     W.Spec("dec-fp32-d128-g3", "fp32", 12, 4, 128, 20000, decode_lens=(2, 500, 4100)),
 ], ids=lambda s: s.name)
-def test_decode_fp32(spec):
-    wl = W.make_workload(spec, 602)
+def test_decode_fp32(spec, variant):
+    wl = W.make_workload(spec, 602, variant)
     dw, outs = run_all(wl)
     kp, vp = stored_pools(wl)
-    assert_close(out_f64(outs["decode"]), oracle_decode(wl, kp, vp), "fp32", spec.name)
+    assert_close(out_f64(outs["decode"]), oracle_decode(wl, kp, vp), "fp32", f"{spec.name}/{variant}")
 
 
 @pytest.mark.parametrize("seed_off", [0, 100, 200])
@@ -60,7 +61,7 @@ def test_decode_64req_full(seed_off):
     assert_close(out_f64(outs["decode"]), oracle_decode(wl, kp, vp), "bf16", f"{spec.name} seed+{seed_off}")
 
 
-@pytest.mark.parametrize("variant", ["normal", "peaked"])
+@pytest.mark.parametrize("variant", ["normal", "peaked", "needle"])
 def test_decode_64req_variants(variant):
     spec = W.CONFIGS[2]
     wl = W.make_workload(spec, W.TIMING_SEEDS[2], variant)
@@ -200,3 +201,26 @@ def test_stream_longer_than_one_resident_round():
     kp, vp = stored_pools(wl)
     reqs = sorted(set([0, 1, 2, B // 2, B - 2, B - 1]) | set(np.random.default_rng(1).choice(B, 20, replace=False).tolist()))
     assert_close(out_f64(outs["decode"])[reqs], oracle_decode(wl, kp, vp, requests=reqs), "bf16", spec.name)
+
+
+def test_decode_on_a_side_stream_keeps_its_workspace():
+    """The binding allocates the workspace on the caller's behalf and the kernels run on a side
+    stream; right after the call returns, a new allocation of the same size on the current
+    stream is filled. The workspace block must not be handed out again before the side stream
+    has passed the DECODE kernels: the result still matches the oracle."""
+    spec = W.Spec("side-stream", "bf16", 32, 8, 128, 200000, decode_lens=(3000, 9000, 20000, 513, 64))
+    wl = W.make_workload(spec, 611)
+    dw = upload(wl)
+    store(dw)
+    x = dw.dec
+    nb = R.decode_workspace_bytes(R.BF16, wl.decode.batch, x["max_seq_len"], 32, 8, 128)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    x["o"].record_stream(side)
+    R.decode_attention(x["q"], x["o"], dw.k_pool, dw.v_pool, dw.req_to_token, x["req_pool_indices"],
+                       x["seq_lens"], x["max_seq_len"], wl.sm_scale, stream=side)
+    junk = torch.empty(nb, dtype=torch.uint8, device=x["q"].device)
+    junk.fill_(0xFF)
+    torch.cuda.synchronize()
+    kp, vp = stored_pools(wl)
+    assert_close(out_f64(x["o"]), oracle_decode(wl, kp, vp), "bf16", "decode on a side stream")
