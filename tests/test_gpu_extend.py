@@ -59,35 +59,6 @@ def test_extend_fp32(spec):
     assert_close(out_f64(outs["extend"]), oracle_extend(wl, kp, vp), "fp32", spec.name)
 
 
-def _sample_tokens(wl, per_request, rng):
-    e = wl.extend
-    toks = []
-    for b in range(e.batch):
-        n = int(e.extend_lens[b])
-        if n == 0:
-            continue
-        s0 = int(e.extend_start_loc[b])
-        pick = {0, n - 1, min(n - 1, 127), min(n - 1, 128)}
-        pick |= set(rng.choice(n, size=min(n, per_request), replace=False).tolist())
-        toks += [s0 + i for i in sorted(pick)]
-    return toks
-
-
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("seed_off", [0, 100])
-def test_extend_shared_prefix_sampled(seed_off):
-    """Shared 4,096-token prefix, 32 requests x 256 new tokens: sampled rows of 8 requests."""
-    spec = W.CONFIGS[3]
-    wl = W.make_workload(spec, W.TIMING_SEEDS[3] + seed_off)
-    say(f"{spec.name} generated")
-    dw, outs = run_all(wl)
-    kp, vp = stored_pools(wl)
-    rng = np.random.default_rng(seed_off)
-    toks = [t for t in _sample_tokens(wl, 12, rng) if t // 256 in (0, 1, 5, 13, 20, 27, 30, 31)]
-    got = out_f64(outs["extend"])[toks]
-    assert_close(got, oracle_extend(wl, kp, vp, tokens=toks), "bf16", f"{spec.name} seed+{seed_off}")
-
-
 def test_extend_one_token_matches_decode():
     """EXTEND with e = 1 on prefix p and DECODE over p + 1 keys agree (two different kernels)."""
     spec = W.Spec("e1", "bf16", 32, 8, 128, 50000, extend_prefix=(0, 63, 64, 2000), extend_lens=(1, 1, 1, 1))
