@@ -2,9 +2,13 @@
 
 One step = one pass of the whole path over one batch: kv_store of the step's new rows, EXTEND
 of the prefill chunk, DECODE of the running requests, all on one stream, inputs resident in
-HBM. Default workload: the mixed chunked-prefill batch (one 2,048-token chunk on a
-14,336-token cached prefix plus 128 decode requests with 1,024..8,192 tokens of context,
-32 q / 8 kv heads, head_dim 128, bf16, a 1,048,576-slot pool), which exercises every call.
+HBM. Default workload: the long-context step (one EXTEND of 8,192 new tokens on a
+65,536-token cached prefix plus 8 decode requests with 32,768..131,072 tokens of context,
+64 q / 8 kv heads, head_dim 128, bf16, values N(0, 0.5), a 2,097,152-slot pool of 4 GiB per
+K and V), the largest workload, which exercises every call. ``--config 4`` is the mixed
+chunked-prefill batch (a 2,048-token chunk on a 14,336-token prefix plus 128 decode requests
+of 1,024..8,192 tokens, 32 q / 8 kv heads, a 1,048,576-slot pool); ``--config 2`` and ``3``
+the 64-request decode batch and the shared-prefix EXTEND.
 ``--kv fp8`` runs the same step over FP8 E4M3 pools (kv_store_fp8, extend_attention_fp8,
 decode_attention_fp8; per-pool scales 4 sigma / 448), the pools converted from the bf16 ones
 before timing. ``--ragged`` runs EXTEND on the ragged path: the suffix K/V read from the new
@@ -17,8 +21,10 @@ cold-cache ones; ms_per_step then includes the sweeps.
 
 Prints ONE JSON line. ``value`` is the EXTEND attention throughput in TFLOP/s (algorithmic
 FLOPs: 4 * head_dim * q_heads per attended pair, masked pairs not counted); the DECODE KV
-bandwidth is reported beside it. Per-kernel durations come from HIP events recorded on the
-launch stream around each call over the timed steps.
+bandwidth is reported beside it (workloads without EXTEND report it as ``value``). Per-kernel
+durations come from HIP events recorded on the launch stream around each call over the timed
+steps. ``cpu_baseline`` is the float64 oracle timed on a bounded sample of the same workload
+in worker processes on the host's cores (see CpuOracle).
 """
 
 from __future__ import annotations
@@ -39,10 +45,17 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 # HBM traffic per dispatch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs summarised by
-# --pmc-summary. A kernel's figure is used only while its sources hash to what they were when
-# the counters were taken.
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "mixed_chunk_hbm_traffic.txt")
-TRAFFIC_SUMMARY_FP8 = os.path.join(ROOT, "profiles", "mixed_chunk_fp8_hbm_traffic.txt")
+# --pmc-summary, per (workload id, KV pool element); each was counted on that workload's timing
+# seed with the token table, the pool-reading EXTEND and warm caches. A kernel's figure is used
+# only while its sources hash to what they were when the counters were taken.
+TRAFFIC_SUMMARIES = {
+    (2, "bf16"): "decode_64req_hbm_traffic.txt",
+    (3, "bf16"): "shared_prefix_hbm_traffic.txt",
+    (4, "bf16"): "mixed_chunk_hbm_traffic.txt",
+    (4, "fp8"): "mixed_chunk_fp8_hbm_traffic.txt",
+    (5, "bf16"): "long_context_hbm_traffic.txt",
+}
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", TRAFFIC_SUMMARIES[(4, "bf16")])
 CSRC = os.path.join(ROOT, "prefix_cached_paged_amd", "csrc")
 KERNEL_SOURCES = {
     "extend_kernel": ["extend_attn.hip", "rax_device.h", "rax_launch.h"],
@@ -154,96 +167,208 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, dev_outs, budget_s: float, kv8=None):
-    """Time the CPU oracle (as it stands) on a bounded sample of the same workload.
+def cpu_model() -> str:
+    """The host CPU's model name (what lscpu prints as "Model name")."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    ``kv8 = (k_scale, v_scale)``: FP8 pools. The oracle then builds its own E4M3 pools from the
-    generator's bf16 rows (only the rows the sample reads, converted before each timed call and
-    not timed) and stores the step's new rows with its kv_store_fp8."""
+
+def cpu_workers() -> tuple[int, int]:
+    """(workers, affinity CPUs): one worker process per CPU this process may run on, capped by
+    the OMP_NUM_THREADS share when the environment sets one (the host's share for one GPU)."""
+    aff = len(os.sched_getaffinity(0))
+    n = aff
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n), aff
+
+
+# What the forked oracle workers read (copy-on-write from the parent): workload, stored pools,
+# scales. Set before the pool is forked.
+_CPU = {}
+
+
+def _cpu_worker_init():
+    from threadpoolctl import threadpool_limits
+    _CPU["limit"] = threadpool_limits(1)   # one BLAS thread per worker process
+
+
+def _cpu_call(kind, idx, g):
     import oracle
-    from threadpoolctl import threadpool_info
-    from prefix_cached_paged_amd import accounting as A
-    from prefix_cached_paged_amd.device import to_host_bits
-
+    wl, kp, vp, ks, vs = _CPU["wl"], _CPU["kp"], _CPU["vp"], _CPU["ks"], _CPU["vs"]
     spec = wl.spec
-    t0 = time.perf_counter()
-    if kv8 is None:
-        ks = vs = 1.0
-        eb = spec.elem_bytes
-        kp, vp = oracle.kv_store(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.store_loc)
-        prep = lambda rows: None
-    else:
-        ks, vs = kv8
-        eb = 1
-        kp = np.full(wl.k_pool.shape, 0x7F, np.uint8)     # E4M3 NaN until a row is converted
-        vp = np.full(wl.v_pool.shape, 0x7F, np.uint8)
-        kp, vp = oracle.kv_store_fp8(kp, vp, wl.k_new, wl.v_new, wl.store_loc, ks, vs)
-        done = np.zeros(kp.shape[0], bool)
-        done[np.asarray(wl.store_loc, np.int64)] = True
-
-        def prep(rows):
-            rows = np.unique(np.asarray(rows, np.int64))
-            rows = rows[~done[rows]]
-            kp[rows] = oracle.quantize_bf16(wl.k_pool[rows], ks)
-            vp[rows] = oracle.quantize_bf16(wl.v_pool[rows], vs)
-            done[rows] = True
-    t_store = time.perf_counter() - t0
-    res = {}
-    parity = {}
-    if wl.extend is not None:
+    if kind == "extend":
         e = wl.extend
-        b = int(np.argmax(e.extend_lens))
-        n = int(e.extend_lens[b])
-        s0 = int(e.extend_start_loc[b])
-        # last rows first: they see the most keys; grow the sample until about half the budget
-        toks, flops, t_ext = [], 0, 0.0
-        step = 8
-        while t_ext < budget_s / 2 and len(toks) < n:
-            new = [s0 + n - 1 - i for i in range(len(toks), min(n, len(toks) + step))]
-            prep(wl.req_to_token[int(e.req_pool_indices[b]), :int(e.prefix_lens[b]) + n])
-            t1 = time.perf_counter()
-            ref = oracle.extend_attention(e.q, kp, vp, wl.req_to_token, e.req_pool_indices, e.prefix_lens,
-                                          e.extend_lens, e.extend_start_loc, spec.n_kv_heads, wl.sm_scale,
-                                          tokens=new, k_scale=ks, v_scale=vs)
-            t_ext += time.perf_counter() - t1
-            p = int(e.prefix_lens[b])
-            flops += sum(4 * spec.head_dim * spec.n_q_heads * (p + (t - s0) + 1) for t in new)
-            got = oracle.to_f64(to_host_bits(dev_outs["extend"][new]))
-            parity.setdefault("extend_max_abs", 0.0)
-            parity["extend_max_abs"] = max(parity["extend_max_abs"], float(np.max(np.abs(got - ref))))
-            toks += new
-            step *= 2
-        res["extend"] = dict(tflops=flops / t_ext / 1e12, tokens=len(toks), seconds=t_ext)
-    if wl.decode is not None:
-        d = wl.decode
-        reqs, nbytes, t_dec = [], 0, 0.0
-        order = list(range(d.batch))
-        while t_dec < budget_s / 2 and len(reqs) < d.batch:
-            new = order[len(reqs):len(reqs) + max(1, len(reqs))]
-            if kv8 is not None:
-                prep(np.concatenate([wl.req_to_token[int(d.req_pool_indices[r]), :int(d.seq_lens[r])] for r in new]))
-            t1 = time.perf_counter()
-            ref = oracle.decode_attention(d.q, kp, vp, wl.req_to_token, d.req_pool_indices, d.seq_lens,
-                                          spec.n_kv_heads, wl.sm_scale, requests=new, k_scale=ks, v_scale=vs)
-            t_dec += time.perf_counter() - t1
-            nbytes += A.decode_kv_bytes(d.seq_lens[new], spec.n_kv_heads, spec.head_dim, eb)
-            got = oracle.to_f64(to_host_bits(dev_outs["decode"][new]))
-            parity.setdefault("decode_max_abs", 0.0)
-            parity["decode_max_abs"] = max(parity["decode_max_abs"], float(np.max(np.abs(got - ref))))
-            reqs += new
-        res["decode"] = dict(GBps=nbytes / t_dec / 1e9, requests=len(reqs), seconds=t_dec)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    sample = []
-    if "extend" in res:
-        sample.append(f"EXTEND: last {res['extend']['tokens']} suffix rows of the chunk, all heads")
-    if "decode" in res:
-        sample.append(f"DECODE: {res['decode']['requests']} of {wl.decode.batch} requests, all heads")
-    store_note = (f"kv_store copy {t_store:.1f} s not counted" if kv8 is None else
-                  f"kv_store_fp8 {t_store:.1f} s and the E4M3 conversion of the sampled rows not counted")
-    out = dict(value=res.get("extend", {}).get("tflops"), unit="TFLOP/s", cores=threads, kind="oracle",
-               sample="; ".join(sample) + f"; float64 numpy, {store_note}",
-               decode_GBps=res.get("decode", {}).get("GBps"), parity_vs_gpu=parity)
-    return out
+        return oracle.extend_attention(e.q, kp, vp, wl.req_to_token, e.req_pool_indices, e.prefix_lens,
+                                       e.extend_lens, e.extend_start_loc, spec.n_kv_heads, wl.sm_scale,
+                                       tokens=idx, k_scale=ks, v_scale=vs, kv_heads=[g])
+    d = wl.decode
+    return oracle.decode_attention(d.q, kp, vp, wl.req_to_token, d.req_pool_indices, d.seq_lens,
+                                   spec.n_kv_heads, wl.sm_scale, requests=idx, k_scale=ks, v_scale=vs,
+                                   kv_heads=[g])
+
+
+def _cpu_task(task):
+    kind, idx, g = task
+    G = _CPU["wl"].spec.n_q_heads // _CPU["wl"].spec.n_kv_heads
+    out = _cpu_call(kind, idx, g)
+    return kind, idx, g, out[:, g * G:(g + 1) * G]
+
+
+class CpuOracle:
+    """The float64 oracle, as it stands, timed on the host's cores beside the GPU.
+
+    Work is split into (rows or request, kv head) units run by a pool of worker processes, one
+    BLAS thread each. The pool is forked before the GPU is initialised (the workers share the
+    workload copy-on-write and never touch the GPU). A short single-thread calibration sizes a
+    bounded sample of the same workload so that each call's sample takes about half of
+    ``budget_s`` of wall time on the pool: EXTEND the last suffix rows (they see the most keys),
+    DECODE whole requests in order. ``kv8 = (k_scale, v_scale)``: FP8 pools; the oracle then
+    builds its own E4M3 rows of the sample from the generator's bf16 rows (not timed) and stores
+    the step's new rows with its kv_store_fp8.
+    """
+
+    def __init__(self, wl, budget_s: float, kv8=None):
+        import multiprocessing as mp
+
+        import oracle
+        from threadpoolctl import threadpool_limits
+        from prefix_cached_paged_amd import accounting as A
+
+        self.wl, self.spec = wl, wl.spec
+        self.kv8 = kv8
+        spec = self.spec
+        t0 = time.perf_counter()
+        if kv8 is None:
+            ks = vs = 1.0
+            self.eb = spec.elem_bytes
+            kp, vp = oracle.kv_store(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.store_loc)
+            prep = lambda rows: None
+        else:
+            ks, vs = kv8
+            self.eb = 1
+            kp = np.full(wl.k_pool.shape, 0x7F, np.uint8)     # E4M3 NaN until a row is converted
+            vp = np.full(wl.v_pool.shape, 0x7F, np.uint8)
+            kp, vp = oracle.kv_store_fp8(kp, vp, wl.k_new, wl.v_new, wl.store_loc, ks, vs)
+            done = np.zeros(kp.shape[0], bool)
+            done[np.asarray(wl.store_loc, np.int64)] = True
+
+            def prep(rows):
+                rows = np.unique(np.asarray(rows, np.int64))
+                rows = rows[~done[rows]]
+                kp[rows] = oracle.quantize_bf16(wl.k_pool[rows], ks)
+                vp[rows] = oracle.quantize_bf16(wl.v_pool[rows], vs)
+                done[rows] = True
+        self.t_store = time.perf_counter() - t0
+        _CPU.update(wl=wl, kp=kp, vp=vp, ks=ks, vs=vs)
+        self.workers, self.affinity = cpu_workers()
+        wall = budget_s / 2
+        Hkv, Hq, D = spec.n_kv_heads, spec.n_q_heads, spec.head_dim
+        G = Hq // Hkv
+        self.tasks = {}
+        self.work = {}
+
+        def timed(kind, idx):       # best of two single-thread calls on kv head 0
+            best = float("inf")
+            for _ in range(2):
+                t = time.perf_counter()
+                _cpu_call(kind, idx, 0)
+                best = min(best, time.perf_counter() - t)
+            return best
+
+        with threadpool_limits(1):
+            if wl.extend is not None:
+                e = wl.extend
+                order = sorted(range(e.batch), key=lambda b: -int(e.extend_lens[b]))
+                order = [b for b in order if int(e.extend_lens[b]) > 0]
+                row_flops = lambda b, i: 4 * D * Hq * (int(e.prefix_lens[b]) + i + 1)
+                b0 = order[0]
+                r0 = int(e.req_pool_indices[b0])
+                prep(wl.req_to_token[r0, :int(e.prefix_lens[b0]) + int(e.extend_lens[b0])])
+                last = int(e.extend_start_loc[b0]) + int(e.extend_lens[b0]) - 1
+                rate = row_flops(b0, int(e.extend_lens[b0]) - 1) / Hkv / timed("extend", [last])
+                target = rate * self.workers * wall
+                toks, flops = [], 0
+                for b in order:                     # last rows first, request after request
+                    n, s0 = int(e.extend_lens[b]), int(e.extend_start_loc[b])
+                    prep(wl.req_to_token[int(e.req_pool_indices[b]), :int(e.prefix_lens[b]) + n])
+                    for i in range(n - 1, -1, -1):
+                        if flops >= target:
+                            break
+                        toks.append(s0 + i)
+                        flops += row_flops(b, i)
+                    if flops >= target:
+                        break
+                chunks = max(1, min(len(toks), -(-2 * self.workers // Hkv)))
+                parts = [sorted(toks[c::chunks]) for c in range(chunks)]
+                self.tasks["extend"] = [("extend", part, g) for part in parts for g in range(Hkv)]
+                self.work["extend"] = (flops, len(toks), sorted(toks))
+            if wl.decode is not None:
+                d = wl.decode
+                reqs, nbytes = [], 0
+                prep(wl.req_to_token[int(d.req_pool_indices[0]), :int(d.seq_lens[0])])
+                rate = A.decode_kv_bytes(d.seq_lens[:1], 1, D, self.eb) / timed("decode", [0])
+                target = rate * self.workers * wall
+                for b in range(d.batch):
+                    if nbytes >= target:
+                        break
+                    prep(wl.req_to_token[int(d.req_pool_indices[b]), :int(d.seq_lens[b])])
+                    reqs.append(b)
+                    nbytes += A.decode_kv_bytes(d.seq_lens[b:b + 1], Hkv, D, self.eb)
+                self.tasks["decode"] = [("decode", [b], g) for b in reqs for g in range(Hkv)]
+                self.work["decode"] = (nbytes, len(reqs), reqs)
+            # fork the workers now, before anything initialises the GPU in this process
+            self.pool = mp.get_context("fork").Pool(self.workers, initializer=_cpu_worker_init)
+
+    def run(self, dev_outs) -> dict:
+        from prefix_cached_paged_amd.device import to_host_bits
+        import oracle
+
+        spec = self.spec
+        G = spec.n_q_heads // spec.n_kv_heads
+        res, parity = {}, {}
+        for kind in ("extend", "decode"):
+            if kind not in self.tasks:
+                continue
+            t0 = time.perf_counter()
+            outs = list(self.pool.imap_unordered(_cpu_task, self.tasks[kind]))
+            wall = time.perf_counter() - t0
+            work, count, idx = self.work[kind]
+            got = oracle.to_f64(to_host_bits(dev_outs[kind][idx]))
+            pos = {t: i for i, t in enumerate(idx)}
+            err = 0.0
+            for _, part, g, ref in outs:
+                rows = [pos[t] for t in part]
+                err = max(err, float(np.max(np.abs(got[rows, g * G:(g + 1) * G] - ref))))
+            parity[f"{kind}_max_abs"] = err
+            if kind == "extend":
+                res[kind] = dict(tflops=work / wall / 1e12, tokens=count, seconds=wall)
+            else:
+                res[kind] = dict(GBps=work / wall / 1e9, requests=count, seconds=wall)
+        sample = []
+        if "extend" in res:
+            sample.append(f"EXTEND: last {res['extend']['tokens']} suffix rows, all heads "
+                          f"({res['extend']['seconds']:.1f} s wall)")
+        if "decode" in res:
+            sample.append(f"DECODE: {res['decode']['requests']} of {self.wl.decode.batch} requests, all heads "
+                          f"({res['decode']['seconds']:.1f} s wall)")
+        store_note = (f"kv_store copy {self.t_store:.1f} s not counted" if self.kv8 is None else
+                      f"kv_store_fp8 {self.t_store:.1f} s and the E4M3 conversion of the sampled rows not counted")
+        return dict(value=res.get("extend", {}).get("tflops"), unit="TFLOP/s", cores=self.workers, kind="oracle",
+                    sample="; ".join(sample) + f"; float64 numpy in {self.workers} worker processes over "
+                    f"(rows or request, kv head), one BLAS thread each; {store_note}",
+                    cpu_model=cpu_model(), affinity_cpus=self.affinity,
+                    decode_GBps=res.get("decode", {}).get("GBps"), parity_vs_gpu=parity)
+
+    def close(self):
+        self.pool.terminate()
+        self.pool.join()
 
 
 def main():
@@ -251,9 +376,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=4, help="workload id (1..5)")
+    ap.add_argument("--config", type=int, default=5, help="workload id (1..5)")
     ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--cpu-budget", type=float, default=16.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=16.0,
+                    help="seconds of wall time for the CPU oracle's samples (about half per call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
                     help="KV pool element: the workload's bf16, or FP8 E4M3 with per-pool scales")
@@ -290,47 +416,55 @@ def main():
 
     import torch
     from prefix_cached_paged_amd import accounting as A
-    from prefix_cached_paged_amd import rax
     from prefix_cached_paged_amd import workloads as W
-    from prefix_cached_paged_amd.device import upload
 
-    rax.load()  # fails loudly if the HIP library is missing
     cfg = args.config
     spec = W.CONFIGS[cfg]
     if args.page_size != 1:
         import dataclasses
         spec = dataclasses.replace(spec, page_size=args.page_size)
-    seed = args.seed if args.seed is not None else W.TIMING_SEEDS[cfg]
-    log(f"generating workload {spec.name} seed {seed}")
-    wl = W.make_workload(spec, seed)
-    log("uploading")
-    dw = upload(wl, "cuda:0")
-    dt = rax.BF16 if spec.dtype == "bf16" else rax.FP32
     kv8 = args.kv == "fp8"
-    rag = args.ragged and dw.ext is not None
     paged = args.page_size != 1
-    if paged and (kv8 or rag):
+    if paged and (kv8 or args.ragged):
         print("--page-size runs the bf16/fp32 pool path only", file=sys.stderr)
         sys.exit(2)
-    pt = torch.from_numpy(wl.page_table).to("cuda:0") if paged else None
-    if rag and kv8:
+    if args.ragged and kv8:
         print("--ragged is for bf16/fp32 pools", file=sys.stderr)
         sys.exit(2)
-    n_ext = wl.extend.total_tokens if wl.extend is not None else 0
     if kv8 and spec.dtype != "bf16":
         print("--kv fp8 needs a bf16 workload (--config 2 to 5)", file=sys.stderr)
         sys.exit(2)
+    # FP8 pools: scales put about 4 standard deviations at the top of E4M3.
+    k_scale = v_scale = 4.0 * spec.sigma / 448.0 if kv8 else 1.0
+    seed = args.seed if args.seed is not None else W.TIMING_SEEDS[cfg]
+    log(f"generating workload {spec.name} seed {seed}")
+    wl = W.make_workload(spec, seed)
+
+    # The CPU oracle's worker processes are forked here, before this process touches the GPU.
+    cpu_oracle = None
+    if not args.no_cpu_baseline:
+        log("preparing the CPU oracle (store, calibration, worker pool)")
+        cpu_oracle = CpuOracle(wl, args.cpu_budget, kv8=(k_scale, v_scale) if kv8 else None)
+
+    from prefix_cached_paged_amd import rax
+    from prefix_cached_paged_amd.device import upload
+
+    rax.load()  # fails loudly if the HIP library is missing
+    log("uploading")
+    dw = upload(wl, "cuda:0")
+    dt = rax.BF16 if spec.dtype == "bf16" else rax.FP32
+    rag = args.ragged and dw.ext is not None
+    pt = torch.from_numpy(wl.page_table).to("cuda:0") if paged else None
+    n_ext = wl.extend.total_tokens if wl.extend is not None else 0
     ws = None
     if dw.dec is not None:
         d = dw.dec
         nb = rax.decode_workspace_bytes(rax.FP8_E4M3 if kv8 else dt, d["q"].shape[0], d["max_seq_len"],
                                         spec.n_q_heads, spec.n_kv_heads, spec.head_dim)
         ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda:0")
-    k_scale = v_scale = 1.0
     if kv8:
         # FP8 pools converted from the bf16 ones by the library's store (set-up, not timed); the
-        # bf16 pools are freed. Scales put about 4 standard deviations at the top of E4M3.
-        k_scale = v_scale = 4.0 * spec.sigma / 448.0
+        # bf16 pools are freed.
         log("converting the pools to FP8 E4M3")
         kp8 = torch.empty(dw.k_pool.shape, dtype=torch.uint8, device="cuda:0")
         vp8 = torch.empty_like(kp8)
@@ -487,12 +621,12 @@ def main():
                               GBps=hbm(st_bytes, ms["kv_store"]),
                               bytes=st_bytes)
     roofs = {}
-    # The traffic summaries were counted on the default step (the mixed chunked-prefill batch,
-    # --config 4, with its timing seed; token table, pool-reading EXTEND, warm caches) over bf16
-    # or FP8 pools; graph replay runs the same kernels on the same data. Any other workload or
-    # mode has no counted traffic: null.
-    counted = cfg == 4 and seed == W.TIMING_SEEDS[4] and not rag and not paged and not args.cold
-    traffic = read_traffic(TRAFFIC_SUMMARY_FP8 if kv8 else TRAFFIC_SUMMARY) if counted else {}
+    # A traffic summary counts only for the run it was taken on (its workload with the timing
+    # seed; token table, pool-reading EXTEND, warm caches, the same pool element); graph replay
+    # runs the same kernels on the same data. Any other workload or mode: null.
+    summary = TRAFFIC_SUMMARIES.get((cfg, "fp8" if kv8 else spec.dtype))
+    counted = (summary is not None and seed == W.TIMING_SEEDS[cfg] and not rag and not paged and not args.cold)
+    traffic = read_traffic(os.path.join(ROOT, "profiles", summary)) if counted else {}
     if wl.extend is not None:
         e = wl.extend
         fl = A.extend_flops(e.prefix_lens, e.extend_lens, spec.n_q_heads, spec.head_dim)
@@ -530,14 +664,17 @@ def main():
         value, unit = report["decode"]["kv_GBps"], "GB/s"
 
     cpu = None
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a sample")
+    if cpu_oracle is not None:
+        log(f"timing the CPU oracle on a sample ({cpu_oracle.workers} worker processes)")
         outs = {}
         if dw.ext is not None:
             outs["extend"] = dw.ext["o"]
         if dw.dec is not None:
             outs["decode"] = dw.dec["o"]
-        cpu = cpu_baseline(wl, outs, args.cpu_budget, kv8=(k_scale, v_scale) if kv8 else None)
+        try:
+            cpu = cpu_oracle.run(outs)
+        finally:
+            cpu_oracle.close()
         if unit == "GB/s":
             cpu["value"], cpu["unit"] = cpu.pop("decode_GBps"), "GB/s"
 
