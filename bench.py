@@ -270,9 +270,7 @@ class CpuOracle:
         self.workers, self.affinity = cpu_workers()
         wall = budget_s / 2
         Hkv, Hq, D = spec.n_kv_heads, spec.n_q_heads, spec.head_dim
-        G = Hq // Hkv
-        self.tasks = {}
-        self.work = {}
+        self.plan = {}
 
         def timed(kind, idx):       # best of two single-thread calls on kv head 0
             best = float("inf")
@@ -282,49 +280,53 @@ class CpuOracle:
                 best = min(best, time.perf_counter() - t)
             return best
 
+        self.wall = wall
         with threadpool_limits(1):
             if wl.extend is not None:
                 e = wl.extend
                 order = sorted(range(e.batch), key=lambda b: -int(e.extend_lens[b]))
                 order = [b for b in order if int(e.extend_lens[b]) > 0]
-                row_flops = lambda b, i: 4 * D * Hq * (int(e.prefix_lens[b]) + i + 1)
-                b0 = order[0]
-                r0 = int(e.req_pool_indices[b0])
-                prep(wl.req_to_token[r0, :int(e.prefix_lens[b0]) + int(e.extend_lens[b0])])
-                last = int(e.extend_start_loc[b0]) + int(e.extend_lens[b0]) - 1
-                rate = row_flops(b0, int(e.extend_lens[b0]) - 1) / Hkv / timed("extend", [last])
-                target = rate * self.workers * wall
-                toks, flops = [], 0
-                for b in order:                     # last rows first, request after request
-                    n, s0 = int(e.extend_lens[b]), int(e.extend_start_loc[b])
-                    prep(wl.req_to_token[int(e.req_pool_indices[b]), :int(e.prefix_lens[b]) + n])
-                    for i in range(n - 1, -1, -1):
-                        if flops >= target:
-                            break
-                        toks.append(s0 + i)
-                        flops += row_flops(b, i)
-                    if flops >= target:
-                        break
-                chunks = max(1, min(len(toks), -(-2 * self.workers // Hkv)))
-                parts = [sorted(toks[c::chunks]) for c in range(chunks)]
-                self.tasks["extend"] = [("extend", part, g) for part in parts for g in range(Hkv)]
-                self.work["extend"] = (flops, len(toks), sorted(toks))
+                for b in order:     # FP8: every row a sampled EXTEND row may read, before the fork
+                    prep(wl.req_to_token[int(e.req_pool_indices[b]), :int(e.prefix_lens[b]) + int(e.extend_lens[b])])
+                # candidate rows, most keys first: the last rows of each request, request after request
+                self.ext_rows = [(int(e.extend_start_loc[b]) + i, 4 * D * Hq * (int(e.prefix_lens[b]) + i + 1))
+                                 for b in order for i in range(int(e.extend_lens[b]) - 1, -1, -1)]
+                tok, fl = self.ext_rows[0]
+                rate = fl / Hkv / timed("extend", [tok])
+                self.plan["extend"] = self._extend_plan(rate * self.workers * wall)
             if wl.decode is not None:
                 d = wl.decode
-                reqs, nbytes = [], 0
-                prep(wl.req_to_token[int(d.req_pool_indices[0]), :int(d.seq_lens[0])])
-                rate = A.decode_kv_bytes(d.seq_lens[:1], 1, D, self.eb) / timed("decode", [0])
-                target = rate * self.workers * wall
                 for b in range(d.batch):
-                    if nbytes >= target:
-                        break
                     prep(wl.req_to_token[int(d.req_pool_indices[b]), :int(d.seq_lens[b])])
-                    reqs.append(b)
-                    nbytes += A.decode_kv_bytes(d.seq_lens[b:b + 1], Hkv, D, self.eb)
-                self.tasks["decode"] = [("decode", [b], g) for b in reqs for g in range(Hkv)]
-                self.work["decode"] = (nbytes, len(reqs), reqs)
+                rate = A.decode_kv_bytes(d.seq_lens[:1], 1, D, self.eb) / timed("decode", [0])
+                self.plan["decode"] = self._decode_plan(rate * self.workers * wall)
             # fork the workers now, before anything initialises the GPU in this process
             self.pool = mp.get_context("fork").Pool(self.workers, initializer=_cpu_worker_init)
+
+    def _extend_plan(self, target_flops):
+        """Tasks, FLOPs, row count and rows of an EXTEND sample of about target_flops."""
+        Hkv = self.spec.n_kv_heads
+        toks, flops = [], 0
+        for tok, fl in self.ext_rows:
+            if flops >= target_flops:
+                break
+            toks.append(tok)
+            flops += fl
+        chunks = max(1, min(len(toks), -(-2 * self.workers // Hkv)))
+        parts = [sorted(toks[c::chunks]) for c in range(chunks)]
+        return [("extend", part, g) for part in parts for g in range(Hkv)], flops, len(toks), sorted(toks)
+
+    def _decode_plan(self, target_bytes):
+        """Tasks, KV bytes, request count and requests of a DECODE sample of about target_bytes."""
+        from prefix_cached_paged_amd import accounting as A
+        d, Hkv, D = self.wl.decode, self.spec.n_kv_heads, self.spec.head_dim
+        reqs, nbytes = [], 0
+        for b in range(d.batch):
+            if nbytes >= target_bytes:
+                break
+            reqs.append(b)
+            nbytes += A.decode_kv_bytes(d.seq_lens[b:b + 1], Hkv, D, self.eb)
+        return [("decode", [b], g) for b in reqs for g in range(Hkv)], nbytes, len(reqs), reqs
 
     def run(self, dev_outs) -> dict:
         from prefix_cached_paged_amd.device import to_host_bits
@@ -334,12 +336,31 @@ class CpuOracle:
         G = spec.n_q_heads // spec.n_kv_heads
         res, parity = {}, {}
         for kind in ("extend", "decode"):
-            if kind not in self.tasks:
+            if kind not in self.plan:
                 continue
-            t0 = time.perf_counter()
-            outs = list(self.pool.imap_unordered(_cpu_task, self.tasks[kind]))
-            wall = time.perf_counter() - t0
-            work, count, idx = self.work[kind]
+            # The calibration was one single-thread call; the first pool run measures the real
+            # rate, and a sample far below the wall-time target is grown from it and run again
+            # (only the last run is reported). A DECODE sample that is the whole batch is
+            # repeated until the runs add up to the target, and their mean is reported.
+            tasks, work, count, idx = self.plan[kind]
+            runs = []
+            while True:
+                t0 = time.perf_counter()
+                outs = list(self.pool.imap_unordered(_cpu_task, tasks))
+                runs.append(time.perf_counter() - t0)
+                grow = self.wall / runs[-1]
+                if kind == "extend" and grow > 2 and count < len(self.ext_rows) and len(runs) == 1:
+                    tasks, work, count, idx = self._extend_plan(work * grow * 0.9)
+                    runs = []
+                    continue
+                if kind == "decode" and grow > 2 and count < self.wl.decode.batch and len(runs) == 1:
+                    tasks, work, count, idx = self._decode_plan(work * grow * 0.9)
+                    runs = []
+                    continue
+                if kind == "decode" and count == self.wl.decode.batch and sum(runs) < self.wall and len(runs) < 20:
+                    continue
+                break
+            wall = float(np.mean(runs))
             got = oracle.to_f64(to_host_bits(dev_outs[kind][idx]))
             pos = {t: i for i, t in enumerate(idx)}
             err = 0.0
@@ -348,16 +369,16 @@ class CpuOracle:
                 err = max(err, float(np.max(np.abs(got[rows, g * G:(g + 1) * G] - ref))))
             parity[f"{kind}_max_abs"] = err
             if kind == "extend":
-                res[kind] = dict(tflops=work / wall / 1e12, tokens=count, seconds=wall)
+                res[kind] = dict(tflops=work / wall / 1e12, tokens=count, seconds=wall, runs=len(runs))
             else:
-                res[kind] = dict(GBps=work / wall / 1e9, requests=count, seconds=wall)
+                res[kind] = dict(GBps=work / wall / 1e9, requests=count, seconds=wall, runs=len(runs))
         sample = []
         if "extend" in res:
             sample.append(f"EXTEND: last {res['extend']['tokens']} suffix rows, all heads "
                           f"({res['extend']['seconds']:.1f} s wall)")
         if "decode" in res:
             sample.append(f"DECODE: {res['decode']['requests']} of {self.wl.decode.batch} requests, all heads "
-                          f"({res['decode']['seconds']:.1f} s wall)")
+                          f"({res['decode']['seconds']:.2f} s wall, mean of {res['decode']['runs']} runs)")
         store_note = (f"kv_store copy {self.t_store:.1f} s not counted" if self.kv8 is None else
                       f"kv_store_fp8 {self.t_store:.1f} s and the E4M3 conversion of the sampled rows not counted")
         return dict(value=res.get("extend", {}).get("tflops"), unit="TFLOP/s", cores=self.workers, kind="oracle",
