@@ -61,7 +61,9 @@ typedef enum rax_status {
     RAX_ERR_DTYPE = 3,       /* unknown element format                                        */
     RAX_ERR_UNSUPPORTED = 4, /* a valid shape with no kernel in the library (head_dim, group) */
     RAX_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the *_workspace_bytes figure   */
-    RAX_ERR_LAUNCH = 6       /* the HIP runtime refused the launch                            */
+    RAX_ERR_LAUNCH = 6,      /* the HIP runtime refused the launch                            */
+    RAX_ERR_SCRATCH = 7      /* the shapes need more than the no-allocation call's static
+                                scratch (RAX_DECODE_SCRATCH_BYTES)                             */
 } rax_status;
 
 typedef enum rax_dtype {
@@ -224,6 +226,38 @@ rax_status rax_decode_attention(rax_dtype dtype, const void* q, void* o, const v
                                 const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
                                 int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                                 float sm_scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * decode_attention_noalloc -- rax_decode_attention with no workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.
+ *
+ * The plan and the partials that rax_decode_attention keeps in the caller's workspace live
+ * instead in a static device array of RAX_DECODE_SCRATCH_BYTES inside the library; each GPU the
+ * library runs on holds its own copy until the process ends. The call allocates and frees
+ * nothing. Its first call on a device looks up that device's copy (not a stream operation:
+ * make the first call outside graph capture). Every call on one GPU shares that GPU's array,
+ * which keeps the last call's contents; nothing in it needs to start at any value. Calls that
+ * overlap on one GPU (on different streams, or from different threads, until the stream has
+ * passed the call) race on the array: serialise them. Arguments, kernels and results are those
+ * of rax_decode_attention (the same bits).
+ *
+ * Errors: as rax_decode_attention; RAX_ERR_SCRATCH when rax_decode_workspace_bytes(dtype, ...)
+ *   of these shapes exceeds RAX_DECODE_SCRATCH_BYTES (for example 64 requests of up to 4,096
+ *   keys with 32 q / 8 kv heads and head_dim 128 need 7.1 MiB, 128 requests of up to 8,192
+ *   keys 8.1 MiB, 8 requests of up to 131,072 keys with 64 q heads 12.3 MiB; 1,000 requests of
+ *   up to 8,192 keys with 32 q heads need 47 MiB and are refused); RAX_ERR_LAUNCH when the
+ *   array cannot be found on the stream's device.
+ */
+#define RAX_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+
+rax_status rax_decode_attention_noalloc(rax_dtype dtype, const void* q, void* o, const void* k_pool,
+                                        const void* v_pool, int64_t num_slots,
+                                        const int32_t* req_to_token, int64_t r2t_stride,
+                                        const int32_t* req_pool_indices, const int32_t* seq_lens,
+                                        int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                                        int32_t n_kv_heads, int32_t head_dim, float sm_scale,
+                                        hipStream_t stream);
 
 /*
  * Page tables -- the same EXTEND and DECODE over a pool allocated in pages of P slots ("A

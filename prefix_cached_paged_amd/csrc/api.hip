@@ -42,6 +42,7 @@ const char* rax_status_str(rax_status status) {
         case RAX_ERR_UNSUPPORTED: return "RAX_ERR_UNSUPPORTED";
         case RAX_ERR_WORKSPACE: return "RAX_ERR_WORKSPACE";
         case RAX_ERR_LAUNCH: return "RAX_ERR_LAUNCH";
+        case RAX_ERR_SCRATCH: return "RAX_ERR_SCRATCH";
         default: return "unknown status";
     }
 }
@@ -141,7 +142,8 @@ rax_status decode_call(int dtype, bool kv8, const void* q, void* o, const void* 
                 const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
                 int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                 float sm_scale, float k_scale, float v_scale, void* workspace,
-                size_t workspace_bytes, hipStream_t stream, int32_t page_shift = 0) {
+                size_t workspace_bytes, hipStream_t stream, int32_t page_shift = 0,
+                bool static_scratch = false) {
     if (!dtype_ok(dtype)) return RAX_ERR_DTYPE;
     if (batch < 0 || batch > kMaxGridYZ || max_seq_len < 0 || num_slots <= 0 || r2t_stride <= 0 ||
         max_seq_len > (r2t_stride << page_shift))
@@ -160,6 +162,13 @@ rax_status decode_call(int dtype, bool kv8, const void* q, void* o, const void* 
         return RAX_ERR_NULL;
     const size_t need = rax_decode_workspace_bytes(kv8 ? RAX_FP8_E4M3 : (rax_dtype)dtype, batch, max_seq_len,
                                                    n_q_heads, n_kv_heads, head_dim);
+    if (static_scratch && need > 0) {
+        // the library's static scratch takes the place of the workspace
+        if (need > RAX_DECODE_SCRATCH_BYTES) return RAX_ERR_SCRATCH;
+        workspace = rax::decode_scratch(stream);
+        if (workspace == nullptr) return RAX_ERR_LAUNCH;
+        workspace_bytes = RAX_DECODE_SCRATCH_BYTES;
+    }
     if (need > 0 && (!workspace || workspace_bytes < need)) return RAX_ERR_WORKSPACE;
 
     rax::AttnArgs a{};
@@ -189,6 +198,18 @@ rax_status rax_decode_attention(rax_dtype dtype, const void* q, void* o, const v
     return decode_call(dtype, false, q, o, k_pool, v_pool, num_slots, req_to_token, r2t_stride,
                        req_pool_indices, seq_lens, batch, max_seq_len, n_q_heads, n_kv_heads, head_dim,
                        sm_scale, 1.f, 1.f, workspace, workspace_bytes, stream);
+}
+
+rax_status rax_decode_attention_noalloc(rax_dtype dtype, const void* q, void* o, const void* k_pool,
+                                        const void* v_pool, int64_t num_slots,
+                                        const int32_t* req_to_token, int64_t r2t_stride,
+                                        const int32_t* req_pool_indices, const int32_t* seq_lens,
+                                        int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                                        int32_t n_kv_heads, int32_t head_dim, float sm_scale,
+                                        hipStream_t stream) {
+    return decode_call(dtype, false, q, o, k_pool, v_pool, num_slots, req_to_token, r2t_stride,
+                       req_pool_indices, seq_lens, batch, max_seq_len, n_q_heads, n_kv_heads, head_dim,
+                       sm_scale, 1.f, 1.f, nullptr, 0, stream, 0, true);
 }
 
 rax_status rax_kv_store_fp8(const void* k_new, const void* v_new, const int32_t* loc, int64_t n_new,

@@ -36,8 +36,10 @@
 //    staged in LDS once with global-to-LDS copies; each lane then reads the slots it needs with
 //    ds_read, off the memory-counter path of the K/V row loads. Padding keys past a request's
 //    end reuse its last valid slot and get -inf scores, so no load leaves the request's slots.
+#include <mutex>
 #include <type_traits>
 
+#include "librax.h"
 #include "rax_device.h"
 #include "rax_launch.h"
 
@@ -642,7 +644,39 @@ DecLayout decode_layout(int32_t batch, int32_t grid, int32_t n_q_heads, int32_t 
     return l;
 }
 
+// Scratch of the no-allocation DECODE call: the plan and the partials, laid out as the
+// workspace. One copy per device, held until the process ends; host code never uses this name
+// as an address (it is a host-side stand-in): only the per-device address looked up below.
+static __device__ __align__(256) char scratch[RAX_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+void* decode_scratch(hipStream_t stream) {
+    int dev = -1;
+    if (stream != nullptr) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        // each device holds its own copy at its own address: look it up with that device current
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || p == nullptr) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
 
 bool decode_bf16_supported(int32_t group, int32_t head_dim) {
     return group >= 1 && group <= 16 && (head_dim == 64 || head_dim == 128);

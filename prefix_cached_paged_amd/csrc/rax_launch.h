@@ -77,8 +77,12 @@ int32_t decode_grid(int32_t batch, int32_t max_seq_len, int32_t n_kv_heads, bool
 size_t decode_workspace(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
                         int32_t head_dim, bool kv8);
 int launch_decode_bf16(const AttnArgs& a, hipStream_t stream);
+// Address of the static DECODE scratch array (RAX_DECODE_SCRATCH_BYTES) on the device of
+// `stream` (the current device for the null stream), looked up once per device; nullptr if it
+// cannot be found.
+void* decode_scratch(hipStream_t stream);
 
-// fp32 path (vector ALU, fp32 throughout).
+// fp32 path (vector ALU; fp32 data, scores formed in double).
 int launch_extend_fp32(const AttnArgs& a, hipStream_t stream);
 int launch_decode_fp32(const AttnArgs& a, hipStream_t stream);
 

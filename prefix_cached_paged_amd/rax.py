@@ -17,7 +17,8 @@ import torch  # imported before the library so that one HIP runtime serves the p
 
 __all__ = [
     "RaxError", "BF16", "FP32", "load", "version", "kv_store", "extend_attention",
-    "decode_attention", "extend_workspace_bytes", "decode_workspace_bytes", "decode_num_splits",
+    "decode_attention", "decode_attention_noalloc", "DECODE_SCRATCH_BYTES", "extend_workspace_bytes",
+    "decode_workspace_bytes", "decode_num_splits",
     "library_path", "declared_symbols", "FP8_E4M3", "kv_store_fp8", "decode_attention_fp8",
     "extend_attention_fp8", "extend_attention_ragged", "extend_attention_paged", "decode_attention_paged",
     "CHECK_ITEMS", "check_kv_store", "check_extend", "check_decode",
@@ -26,6 +27,7 @@ __all__ = [
 BF16 = 0
 FP32 = 1
 FP8_E4M3 = 2   # pool element of the *_fp8 calls (uint8 tensors)
+DECODE_SCRATCH_BYTES = 32 << 20   # RAX_DECODE_SCRATCH_BYTES: the no-allocation DECODE's static scratch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_PKG), "include", "librax.h")
 _lib = None
@@ -56,6 +58,9 @@ _SIGS = {
     "rax_decode_attention": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64,
                                             _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f,
                                             _c_p, _c_sz, _c_p]),
+    "rax_decode_attention_noalloc": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64,
+                                                    _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f,
+                                                    _c_p]),
     "rax_decode_num_splits": (_c_i32, [ctypes.c_int, _c_i32, _c_i32, _c_i32]),
     "rax_kv_store_fp8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_f,
                                         _c_f, _c_p]),
@@ -327,6 +332,21 @@ def decode_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, seq_l
                                        int(max_seq_len), Hq, Hkv, D, float(sm_scale), _ptr(workspace), wbytes,
                                        _stream(stream, q.device)),
            "rax_decode_attention")
+
+
+def decode_attention_noalloc(q, o, k_pool, v_pool, req_to_token, req_pool_indices, seq_lens, max_seq_len,
+                             sm_scale, stream=None):
+    """decode_attention without a workspace: the plan and partials go to the library's static
+    per-device scratch (no allocation at all; calls on one GPU must not overlap)."""
+    B, Hq, D, S, Hkv = _attn_shapes(q, o, k_pool, v_pool)
+    dt = _dtype(q, o, k_pool, v_pool)
+    _per_request(B, req_pool_indices, seq_lens)
+    _table(req_to_token)
+    _check(load().rax_decode_attention_noalloc(dt, _ptr(q), _ptr(o), _ptr(k_pool), _ptr(v_pool), S,
+                                               _idx(req_to_token), req_to_token.shape[1], _idx(req_pool_indices),
+                                               _idx(seq_lens), B, int(max_seq_len), Hq, Hkv, D, float(sm_scale),
+                                               _stream(stream, q.device)),
+           "rax_decode_attention_noalloc")
 
 
 def _fp8_pool(t):

@@ -26,7 +26,7 @@ def test_every_declared_symbol_is_exported():
                           "rax_decode_attention_fp8", "rax_extend_attention_ragged",
                           "rax_extend_attention_paged", "rax_decode_attention_paged",
                           "rax_check_workspace_bytes", "rax_check_kv_store", "rax_check_extend",
-                          "rax_check_decode"}
+                          "rax_check_decode", "rax_decode_attention_noalloc"}
     out = subprocess.run(["nm", "-D", "--defined-only", R.library_path()], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for n in names:
@@ -37,7 +37,8 @@ def test_every_declared_symbol_is_exported():
 def test_version_and_status_names():
     assert lib().rax_version() == 100
     for code, name in enumerate(["RAX_OK", "RAX_ERR_NULL", "RAX_ERR_SHAPE", "RAX_ERR_DTYPE",
-                                 "RAX_ERR_UNSUPPORTED", "RAX_ERR_WORKSPACE", "RAX_ERR_LAUNCH"]):
+                                 "RAX_ERR_UNSUPPORTED", "RAX_ERR_WORKSPACE", "RAX_ERR_LAUNCH",
+                                 "RAX_ERR_SCRATCH"]):
         assert lib().rax_status_str(code).decode() == name
     assert lib().rax_status_str(99).decode() == "unknown status"
 
@@ -285,3 +286,31 @@ def test_check_calls_validate_before_launching():
     assert dec(slots=0) == 2
     assert dec(seq=None) == 1
     assert dec(counts=None) == 1
+
+
+def decode_noalloc(**kw):
+    a = dict(dtype=0, q=FAKE, o=FAKE, k_pool=FAKE, v_pool=FAKE, num_slots=1 << 20, r2t=FAKE, r2t_stride=8192,
+             rpi=FAKE, seq=FAKE, batch=64, max_seq=4096, hq=32, hkv=8, d=128, scale=0.088, stream=None)
+    a.update(kw)
+    return lib().rax_decode_attention_noalloc(*a.values())
+
+
+def test_noalloc_decode_checks_before_looking_up_its_scratch():
+    """Host validation (as rax_decode_attention) and the scratch limit are decided before the
+    static array is looked up or anything is enqueued: no GPU is needed for these."""
+    assert R.DECODE_SCRATCH_BYTES == 32 << 20
+    assert decode_noalloc(dtype=7) == 3
+    assert decode_noalloc(batch=-1) == 2
+    assert decode_noalloc(max_seq=9000) == 2           # beyond the table row
+    assert decode_noalloc(hq=6, hkv=4) == 2
+    assert decode_noalloc(d=96) == 4
+    assert decode_noalloc(q=None) == 1
+    assert decode_noalloc(batch=0) == 0                # empty: no-op
+    # 1,000 requests of up to 8,192 keys need about 47 MiB of partials: refused
+    nb = lib().rax_decode_workspace_bytes(0, 1000, 8192, 32, 8, 128)
+    assert nb > R.DECODE_SCRATCH_BYTES
+    assert decode_noalloc(batch=1000, max_seq=8192) == 7
+    assert lib().rax_status_str(7).decode() == "RAX_ERR_SCRATCH"
+    # the workload shapes fit: 64 requests of up to 4,096 keys, 8 of up to 131,072 with 64 q heads
+    assert lib().rax_decode_workspace_bytes(0, 64, 4096, 32, 8, 128) <= R.DECODE_SCRATCH_BYTES
+    assert lib().rax_decode_workspace_bytes(0, 8, 131072, 64, 8, 128) <= R.DECODE_SCRATCH_BYTES
