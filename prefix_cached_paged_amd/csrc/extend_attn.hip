@@ -109,6 +109,21 @@ __device__ __forceinline__ void lds_dma16(const char* src, void* lds_wave_dst) {
                                      (__attribute__((address_space(3))) void*)lds_wave_dst, 16, 0, 0);
 }
 
+// The same 16-byte-per-lane copy through a buffer resource (buffer_load_dwordx4 ... lds), for
+// pools addressed with 32-bit byte offsets. The wait-count bookkeeping of the compiler treats
+// the global (FLAT-encoded) form as possibly touching LDS through a flat address and, while one
+// is in flight, rounds every LDS and vector-load wait down to zero; the buffer form is a plain
+// vector-memory operation, so waits on LDS reads and on slot loads stay exact.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pool_rsrc(const char* base) {
+    // raw buffer (stride 0), byte range 2^32 - 1 (offsets are below 2^32 by construction),
+    // data format word of gfx9 untyped buffers
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)0xFFFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, void* lds_wave_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_dst, 16,
+                                             off, 0, 0, 0);
+}
+
 template <bool OFF32>
 __device__ __forceinline__ const char* pool_row_ptr(const char* base, int slot, uint32_t row_bytes,
                                                     uint32_t off) {
@@ -198,6 +213,8 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const uint32_t row_bytes = (uint32_t)Hkv * D * EB;
     const char* kbase = k_pool + (int64_t)g * D * EB;
     const char* vbase = v_pool + (int64_t)g * D * EB;
+    const __amdgpu_buffer_rsrc_t krsrc = pool_rsrc(kbase);  // used by the 32-bit-offset copies
+    const __amdgpu_buffer_rsrc_t vrsrc = pool_rsrc(vbase);
     // Ragged suffix: key position j >= p is new row s0 + j - p of k_new / v_new ([tokens, Hkv,
     // D], the same row size as the pool), the prefix comes from the pool.
     const char* knbase = RAG ? k_new + (int64_t)g * D * EB : nullptr;
@@ -229,18 +246,16 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const uint32_t k_src1 = 16u * (uint32_t)(punit ^ (8 * (wave & 1) + 4 + prow));
     const uint32_t v_src = 16u * (uint32_t)unswz_v(prow, punit);
     const int ntiles = (kend + kExtBN - 1) / kExtBN;
-    // Slot numbers come through scalar loads at wave-uniform, clamped positions: the copies
-    // are then the only vector-memory operations in the loop, so waiting for one tile's copies
-    // (vmcnt) never waits for slot loads or for younger copies. Wave w copies tile rows
-    // 8 w .. 8 w + 7; lane row 4 i + prow takes slot number i * 4 + prow of those eight.
+    // FP8 pools: slot numbers come through scalar loads at wave-uniform, clamped positions,
+    // so the copies are the only vector-memory operations in that loop and waiting for one
+    // tile's copies (vmcnt) never waits for slot loads or for younger copies. Wave w copies
+    // tile rows 8 w .. 8 w + 7 (slot numbers nx0 .. nx7 of those eight).
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    int nx0, nx1, nx2, nx3, nx4, nx5, nx6, nx7;  // slots of the next tile to copy (SGPRs)
-    int nxpos = 0;  // key position of the first of those eight rows
+    int nx0, nx1, nx2, nx3, nx4, nx5, nx6, nx7;  // FP8 pools: slots of the next tile to copy (SGPRs)
 #define RAX_SLOTS(TILE)                                                                     \
     {                                                                                       \
         const int pb_ = (TILE) * kExtBN + 8 * wave_u;                                       \
         const int lim_ = kend - 1;                                                          \
-        nxpos = pb_;                                                                        \
         nx0 = slot_at<PG>(row, min(pb_ + 0, lim_), page_shift);                            \
         nx1 = slot_at<PG>(row, min(pb_ + 1, lim_), page_shift);                            \
         nx2 = slot_at<PG>(row, min(pb_ + 2, lim_), page_shift);                            \
@@ -250,26 +265,41 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         nx6 = slot_at<PG>(row, min(pb_ + 6, lim_), page_shift);                            \
         nx7 = slot_at<PG>(row, min(pb_ + 7, lim_), page_shift);                            \
     }
-    // 4 vector-memory operations per wave: K rows (i = 0, 1), then V rows.
-#define RAX_COPY(KB, VB)                                                                    \
+    // bf16 pools: the slot numbers of the two rows a lane copies (tile rows 8 w + prow and
+    // 8 w + 4 + prow) come through per-lane vector loads, one tile before their copy. Scalar
+    // loads would share the LDS counter (lgkmcnt) and, being unordered, turn every LDS operand
+    // wait of the next tile into a wait for all of them; vector loads count on vmcnt, in order
+    // with the copies, so the explicit copy waits below account for them. Tile T's slots are
+    // held in register set T % 2 (S0, S1).
+#define RAX_VSLOTS(TILE, S0, S1)                                                            \
     {                                                                                       \
-        const int sl0_ = prow == 0 ? nx0 : prow == 1 ? nx1 : prow == 2 ? nx2 : nx3;         \
-        const int sl1_ = prow == 0 ? nx4 : prow == 1 ? nx5 : prow == 2 ? nx6 : nx7;         \
+        const int p0_ = min((TILE) * kExtBN + 8 * wave + prow, kend - 1);                  \
+        const int p1_ = min((TILE) * kExtBN + 8 * wave + 4 + prow, kend - 1);              \
+        S0 = slot_at<PG>(row, p0_, page_shift);                                            \
+        S1 = slot_at<PG>(row, p1_, page_shift);                                            \
+    }
+#define RAX_VCOPY(KB, VB, TILE, S0, S1)                                                     \
+    {                                                                                       \
         char* kd_ = (char*)(KB) + (8 * wave_u) * 256;                                       \
         char* vd_ = (char*)(VB) + (8 * wave_u) * 256;                                       \
-        if constexpr (!RAG) {                                                               \
-            lds_dma16(pool_row_ptr<OFF32>(kbase, sl0_, row_bytes, k_src0), kd_);            \
-            lds_dma16(pool_row_ptr<OFF32>(kbase, sl1_, row_bytes, k_src1), kd_ + 1024);     \
-            lds_dma16(pool_row_ptr<OFF32>(vbase, sl0_, row_bytes, v_src), vd_);             \
-            lds_dma16(pool_row_ptr<OFF32>(vbase, sl1_, row_bytes, v_src), vd_ + 1024);      \
+        if constexpr (!RAG && OFF32) {                                                      \
+            const uint32_t o0_ = __umul24((uint32_t)(S0), row_bytes);                       \
+            const uint32_t o1_ = __umul24((uint32_t)(S1), row_bytes);                       \
+            lds_dma16_buf(krsrc, o0_ + k_src0, kd_);                                        \
+            lds_dma16_buf(krsrc, o1_ + k_src1, kd_ + 1024);                                 \
+            lds_dma16_buf(vrsrc, o0_ + v_src, vd_);                                         \
+            lds_dma16_buf(vrsrc, o1_ + v_src, vd_ + 1024);                                  \
+        } else if constexpr (!RAG) {                                                        \
+            lds_dma16(pool_row_ptr<OFF32>(kbase, S0, row_bytes, k_src0), kd_);              \
+            lds_dma16(pool_row_ptr<OFF32>(kbase, S1, row_bytes, k_src1), kd_ + 1024);       \
+            lds_dma16(pool_row_ptr<OFF32>(vbase, S0, row_bytes, v_src), vd_);               \
+            lds_dma16(pool_row_ptr<OFF32>(vbase, S1, row_bytes, v_src), vd_ + 1024);        \
         } else {                                                                            \
-            /* row index (pool slot or new row) and base chosen per lane, the offset */     \
-            /* product shared by K and V */                                                 \
-            const int ps0_ = min(nxpos + prow, kend - 1);                                   \
-            const int ps1_ = min(nxpos + 4 + prow, kend - 1);                               \
+            const int ps0_ = min((TILE) * kExtBN + 8 * wave + prow, kend - 1);             \
+            const int ps1_ = min((TILE) * kExtBN + 8 * wave + 4 + prow, kend - 1);         \
             const bool n0_ = ps0_ >= p, n1_ = ps1_ >= p;                                    \
-            const int64_t r0_ = row_off<OFF32>(n0_ ? s0 + ps0_ - p : sl0_, row_bytes);      \
-            const int64_t r1_ = row_off<OFF32>(n1_ ? s0 + ps1_ - p : sl1_, row_bytes);      \
+            const int64_t r0_ = row_off<OFF32>(n0_ ? s0 + ps0_ - p : S0, row_bytes);        \
+            const int64_t r1_ = row_off<OFF32>(n1_ ? s0 + ps1_ - p : S1, row_bytes);        \
             lds_dma16((n0_ ? knbase : kbase) + (r0_ + k_src0), kd_);                        \
             lds_dma16((n1_ ? knbase : kbase) + (r1_ + k_src1), kd_ + 1024);                 \
             lds_dma16((n0_ ? vnbase : vbase) + (r0_ + v_src), vd_);                         \
@@ -338,16 +368,33 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // are drained before the workgroup ends.
     f32x16 st[2];   // scores of the tile being processed
     uint4 pf[4];    // its probabilities (bf16), the B operand of P V
+    // The two 32-key halves of the tile are independent accumulation chains; each K-dim step
+    // reads both halves' operands and issues both MFMAs, so one pair of LDS reads feeds 64
+    // MFMA cycles and no operand waits in registers for the other chain.
 #define RAX_QK(KB)                                                                          \
     {                                                                                       \
-        _Pragma("unroll") for (int mb = 0; mb < 2; ++mb) {                                  \
-            _Pragma("unroll") for (int i = 0; i < 16; ++i) st[mb][i] = 0.f;                 \
-            const int key = 32 * mb + col;                                                  \
-            _Pragma("unroll") for (int s = 0; s < D / 16; ++s) {                            \
-                const uint4 a = (KB)[key * 16 + swz_k(key, 2 * s + h2)];                    \
-                st[mb] = mfma32x32x16(as_bf16x8(a), qop[s], st[mb]);                        \
+        _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                    \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i) st[mb][i] = 0.f;                     \
+        uint4 ka0_ = (KB)[col * 16 + swz_k(col, h2)];                                       \
+        uint4 ka1_ = (KB)[(32 + col) * 16 + swz_k(32 + col, h2)];                           \
+        _Pragma("unroll") for (int s = 0; s < D / 16; ++s) {                                \
+            uint4 kb0_ = ka0_, kb1_ = ka1_;                                                 \
+            if (s + 1 < D / 16) {     /* the next step's operands, read one step ahead */   \
+                kb0_ = (KB)[col * 16 + swz_k(col, 2 * (s + 1) + h2)];                       \
+                kb1_ = (KB)[(32 + col) * 16 + swz_k(32 + col, 2 * (s + 1) + h2)];           \
             }                                                                               \
+            st[0] = mfma32x32x16(as_bf16x8(ka0_), qop[s], st[0]);                           \
+            st[1] = mfma32x32x16(as_bf16x8(ka1_), qop[s], st[1]);                           \
+            ka0_ = kb0_;                                                                    \
+            ka1_ = kb1_;                                                                    \
         }                                                                                   \
+        /* keep that order: 2 reads, then per step 2 reads of the next step and 2 MFMAs */  \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                  \
+        _Pragma("unroll") for (int s = 0; s < D / 16 - 1; ++s) {                            \
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                              \
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                              \
+        }                                                                                   \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                  \
     }
 #define RAX_SM(IT, MASKABLE)                                                                \
     {                                                                                       \
@@ -384,20 +431,34 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
             lsum = add_bf16x2(pf[kk].w, lsum);                                              \
         }                                                                                   \
     }
+    // V^T operand of step (dt, kk): two transposed reads of keys 16 kk + 4 h2 + jr (+ 8).
+#define RAX_VREAD(VBB, DT, KK)                                                              \
+    ({                                                                                      \
+        const int unit_ = 4 * (DT) + 2 * dh + (cc >> 1);                                    \
+        const int key0_ = 16 * (KK) + 4 * h2 + jr;                                          \
+        const int key1_ = key0_ + 8;                                                        \
+        const uint2 h0_ = ds_read_tr16_b64((VBB) + key0_ * 256 + swz_v(key0_, unit_) * 16 + 8 * (cc & 1)); \
+        const uint2 h1_ = ds_read_tr16_b64((VBB) + key1_ * 256 + swz_v(key1_, unit_) * 16 + 8 * (cc & 1)); \
+        make_uint4(h0_.x, h0_.y, h1_.x, h1_.y);                                             \
+    })
+    // 16 steps (dt, kk), each operand read one step ahead of its MFMA.
 #define RAX_PV(VB)                                                                          \
     {                                                                                       \
         const char* vbb = (const char*)(VB);                                                \
-        _Pragma("unroll") for (int dt = 0; dt < D / 32; ++dt) {                             \
-            const int unit = 4 * dt + 2 * dh + (cc >> 1);                                   \
-            _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                              \
-                const int key0 = 16 * kk + 4 * h2 + jr;                                     \
-                const uint2 h0 = ds_read_tr16_b64(vbb + key0 * 256 + swz_v(key0, unit) * 16 + 8 * (cc & 1)); \
-                const int key1 = key0 + 8;                                                  \
-                const uint2 h1 = ds_read_tr16_b64(vbb + key1 * 256 + swz_v(key1, unit) * 16 + 8 * (cc & 1)); \
-                const uint4 av = make_uint4(h0.x, h0.y, h1.x, h1.y);                        \
-                acc[dt] = mfma32x32x16(as_bf16x8(av), as_bf16x8(pf[kk]), acc[dt]);          \
-            }                                                                               \
+        uint4 va_ = RAX_VREAD(vbb, 0, 0);                                                   \
+        _Pragma("unroll") for (int st_ = 0; st_ < 16; ++st_) {                              \
+            const int dt = st_ >> 2, kk = st_ & 3;                                          \
+            uint4 vb_ = va_;                                                                \
+            if (st_ + 1 < 16) vb_ = RAX_VREAD(vbb, (st_ + 1) >> 2, (st_ + 1) & 3);          \
+            acc[dt] = mfma32x32x16(as_bf16x8(va_), as_bf16x8(pf[kk]), acc[dt]);             \
+            va_ = vb_;                                                                      \
         }                                                                                   \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                  \
+        _Pragma("unroll") for (int st_ = 0; st_ < 15; ++st_) {                              \
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                              \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
+        }                                                                                   \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
     }
 #define RAX_COMPUTE(IT, KB, VB, MASKABLE) { RAX_QK(KB) RAX_SM(IT, MASKABLE) RAX_PV(VB) }
     // Ping-pong (4 LDS buffers): waves w and w + 4 share a SIMD. Waves 0-3 run tile IT whole
@@ -417,15 +478,24 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
             RAX_COMPUTE(IT, KB, VB, MASKABLE)                                               \
         }                                                                                   \
     }
-#define RAX_PTILE(LAG, IT, KB, VB, VP, KN, VN, MASKABLE, STEADY)                            \
+    // Vector-memory operations per wave and tile: at the end of iteration IT, the 2 slot loads
+    // of tile IT+3 (into set (IT+3) % 2), then the 4 copies of tile IT+2 (set (IT+2) % 2). At the
+    // start of iteration IT the copies of tile IT are needed; younger are the slot loads of tile
+    // IT+2 and the copies of tile IT+1 (issued at the end of IT-1, when those tiles exist, and
+    // always in the steady loop): wait until at most 6, 4 or 0 operations are outstanding.
+#define RAX_PTILE(LAG, IT, KB, VB, VP, KN, VN, SU0, SU1, SL0, SL1, MASKABLE, STEADY)        \
     {                                                                                       \
-        if (STEADY || (IT) + 1 < ntiles) { RAX_WAIT_VMCNT(4); } else { RAX_WAIT_VMCNT(0); } \
+        if (STEADY || (IT) + 2 < ntiles) {                                                  \
+            RAX_WAIT_VMCNT(6);                                                              \
+        } else if ((IT) + 1 < ntiles) {                                                     \
+            RAX_WAIT_VMCNT(4);                                                              \
+        } else {                                                                            \
+            RAX_WAIT_VMCNT(0);                                                              \
+        }                                                                                   \
         RAX_BARRIER();                                                                      \
         RAX_PCOMPUTE(LAG, IT, KB, VB, VP, MASKABLE, STEADY)                                 \
-        if (STEADY || (IT) + 2 < ntiles) {                                                  \
-            RAX_COPY(KN, VN)                                                                \
-            if (STEADY || (IT) + 3 < ntiles) RAX_SLOTS((IT) + 3)                            \
-        }                                                                                   \
+        if (STEADY || (IT) + 3 < ntiles) RAX_VSLOTS((IT) + 3, SL0, SL1)                     \
+        if (STEADY || (IT) + 2 < ntiles) RAX_VCOPY(KN, VN, (IT) + 2, SU0, SU1)              \
     }
     // FP8 pools: tile T is staged (E4M3) in buffer T % 2 and widened into bf16 buffer T % 4.
     // Iteration IT: barrier (every wave's widening of tile IT has landed, every wave is done
@@ -482,33 +552,36 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         }                                                                                   \
     }
     if constexpr (!KV8) {
-        RAX_SLOTS(0)
-        RAX_COPY(kb0, vb0)
-        if (ntiles > 1) {
-            RAX_SLOTS(1)
-            RAX_COPY(kb1, vb1)
-        }
-        if (ntiles > 2) RAX_SLOTS(2)
+        // slots of tiles 0 and 1 (the compiler waits for them before the copies), copies of
+        // tiles 0 and 1, then the slots of tile 2 into set 0
+        int sl_a0, sl_a1, sl_b0, sl_b1;  // slot register sets 0 (a) and 1 (b)
+        RAX_VSLOTS(0, sl_a0, sl_a1)
+        if (ntiles > 1) RAX_VSLOTS(1, sl_b0, sl_b1)
+        RAX_VCOPY(kb0, vb0, 0, sl_a0, sl_a1)
+        if (ntiles > 1) RAX_VCOPY(kb1, vb1, 1, sl_b0, sl_b1)
+        if (ntiles > 2) RAX_VSLOTS(2, sl_a0, sl_a1)
         // Tile T lives in buffer T % 4; iteration T starts the copy of tile T+2 into buffer
-        // (T+2) % 4. The first iteration is peeled (waves 4-7 have no previous tile there).
+        // (T+2) % 4 with slot set (T+2) % 2 and loads the slots of tile T+3 into set (T+3) % 2.
+        // The first iteration is peeled (waves 4-7 have no previous tile there); the steady
+        // loop starts at an odd tile and is unrolled by four, so buffers and sets are static.
         // One loop nest per wave group (the same barriers in the same order), so that the
         // scores carried across iterations by waves 4-7 cost registers only there.
 #define RAX_PLOOPS(LAG)                                                                     \
-        RAX_PTILE(LAG, it, kb0, vb0, vb3, kb2, vb2, 1, 0) ++it;                              \
+        RAX_PTILE(LAG, it, kb0, vb0, vb3, kb2, vb2, sl_a0, sl_a1, sl_b0, sl_b1, 1, 0) ++it;  \
         while (it + 4 <= n_full) {                                                          \
-            RAX_PTILE(LAG, it, kb1, vb1, vb0, kb3, vb3, 0, 1) ++it;                          \
-            RAX_PTILE(LAG, it, kb2, vb2, vb1, kb0, vb0, 0, 1) ++it;                          \
-            RAX_PTILE(LAG, it, kb3, vb3, vb2, kb1, vb1, 0, 1) ++it;                          \
-            RAX_PTILE(LAG, it, kb0, vb0, vb3, kb2, vb2, 0, 1) ++it;                          \
+            RAX_PTILE(LAG, it, kb1, vb1, vb0, kb3, vb3, sl_b0, sl_b1, sl_a0, sl_a1, 0, 1) ++it; \
+            RAX_PTILE(LAG, it, kb2, vb2, vb1, kb0, vb0, sl_a0, sl_a1, sl_b0, sl_b1, 0, 1) ++it; \
+            RAX_PTILE(LAG, it, kb3, vb3, vb2, kb1, vb1, sl_b0, sl_b1, sl_a0, sl_a1, 0, 1) ++it; \
+            RAX_PTILE(LAG, it, kb0, vb0, vb3, kb2, vb2, sl_a0, sl_a1, sl_b0, sl_b1, 0, 1) ++it; \
         }                                                                                   \
         while (it < ntiles) {                                                               \
-            RAX_PTILE(LAG, it, kb1, vb1, vb0, kb3, vb3, 1, 0) ++it;                          \
+            RAX_PTILE(LAG, it, kb1, vb1, vb0, kb3, vb3, sl_b0, sl_b1, sl_a0, sl_a1, 1, 0) ++it; \
             if (it >= ntiles) break;                                                        \
-            RAX_PTILE(LAG, it, kb2, vb2, vb1, kb0, vb0, 1, 0) ++it;                          \
+            RAX_PTILE(LAG, it, kb2, vb2, vb1, kb0, vb0, sl_a0, sl_a1, sl_b0, sl_b1, 1, 0) ++it; \
             if (it >= ntiles) break;                                                        \
-            RAX_PTILE(LAG, it, kb3, vb3, vb2, kb1, vb1, 1, 0) ++it;                          \
+            RAX_PTILE(LAG, it, kb3, vb3, vb2, kb1, vb1, sl_b0, sl_b1, sl_a0, sl_a1, 1, 0) ++it; \
             if (it >= ntiles) break;                                                        \
-            RAX_PTILE(LAG, it, kb0, vb0, vb3, kb2, vb2, 1, 0) ++it;                          \
+            RAX_PTILE(LAG, it, kb0, vb0, vb3, kb2, vb2, sl_a0, sl_a1, sl_b0, sl_b1, 1, 0) ++it; \
         }
         if (lag) {
             RAX_PLOOPS(1)
@@ -596,10 +669,12 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     }
 }
 #undef RAX_SLOTS
-#undef RAX_COPY
+#undef RAX_VSLOTS
+#undef RAX_VCOPY
 #undef RAX_QK
 #undef RAX_SM
 #undef RAX_PV
+#undef RAX_VREAD
 #undef RAX_PTILE
 #undef RAX_COPY8
 #undef RAX_CONVERT8
