@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const int cc = i16 & 3;
 
     float m = -INFINITY;
-    float lsum = 0.f;
+    float lsum = 0.f, lsum2 = 0.f;  // row sum in two interleaved parts (shorter dependency chain)
     f32x16 acc[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -415,6 +415,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
             const float alpha = fast_exp2(m - m_new);                                       \
             m = m_new;                                                                      \
             lsum *= alpha;                                                                  \
+            lsum2 *= alpha;                                                                 \
             _Pragma("unroll") for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;         \
         }                                                                                   \
         _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                  \
@@ -426,9 +427,9 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
             pf[kk].z = pack_bf16x2(pv[4], pv[5]);                                           \
             pf[kk].w = pack_bf16x2(pv[6], pv[7]);                                           \
             lsum = add_bf16x2(pf[kk].x, lsum);                                              \
-            lsum = add_bf16x2(pf[kk].y, lsum);                                              \
+            lsum2 = add_bf16x2(pf[kk].y, lsum2);                                            \
             lsum = add_bf16x2(pf[kk].z, lsum);                                              \
-            lsum = add_bf16x2(pf[kk].w, lsum);                                              \
+            lsum2 = add_bf16x2(pf[kk].w, lsum2);                                            \
         }                                                                                   \
     }
     // V^T operand of step (dt, kk): two transposed reads of keys 16 kk + 4 h2 + jr (+ 8).
@@ -441,24 +442,26 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         const uint2 h1_ = ds_read_tr16_b64((VBB) + key1_ * 256 + swz_v(key1_, unit_) * 16 + 8 * (cc & 1)); \
         make_uint4(h0_.x, h0_.y, h1_.x, h1_.y);                                             \
     })
-    // 16 steps (dt, kk), each operand read one step ahead of its MFMA.
+    // 16 steps (dt, kk), each operand read two steps ahead of its MFMA.
 #define RAX_PV(VB)                                                                          \
     {                                                                                       \
         const char* vbb = (const char*)(VB);                                                \
         uint4 va_ = RAX_VREAD(vbb, 0, 0);                                                   \
+        uint4 vb_ = RAX_VREAD(vbb, 0, 1);                                                   \
         _Pragma("unroll") for (int st_ = 0; st_ < 16; ++st_) {                              \
             const int dt = st_ >> 2, kk = st_ & 3;                                          \
-            uint4 vb_ = va_;                                                                \
-            if (st_ + 1 < 16) vb_ = RAX_VREAD(vbb, (st_ + 1) >> 2, (st_ + 1) & 3);          \
+            uint4 vc_ = vb_;                                                                \
+            if (st_ + 2 < 16) vc_ = RAX_VREAD(vbb, (st_ + 2) >> 2, (st_ + 2) & 3);          \
             acc[dt] = mfma32x32x16(as_bf16x8(va_), as_bf16x8(pf[kk]), acc[dt]);             \
             va_ = vb_;                                                                      \
+            vb_ = vc_;                                                                      \
         }                                                                                   \
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                  \
-        _Pragma("unroll") for (int st_ = 0; st_ < 15; ++st_) {                              \
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                                  \
+        _Pragma("unroll") for (int st_ = 0; st_ < 14; ++st_) {                              \
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                              \
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
         }                                                                                   \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                  \
     }
 #define RAX_COMPUTE(IT, KB, VB, MASKABLE) { RAX_QK(KB) RAX_SM(IT, MASKABLE) RAX_PV(VB) }
     // Ping-pong (4 LDS buffers): waves w and w + 4 share a SIMD. Waves 0-3 run tile IT whole
@@ -635,7 +638,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         RAX_WAIT_VMCNT(0);  // as for bf16 pools: copies past the end land before LDS is reused
 #undef RAX_PLOOPS8
     }
-    lsum = sum_pair32(lsum);
+    lsum = sum_pair32(lsum + lsum2);
     if (row_ok) {
         const float inv = out_scale / lsum;
         uint16_t* orow = o + qo_row;
