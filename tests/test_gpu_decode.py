@@ -224,3 +224,40 @@ def test_decode_on_a_side_stream_keeps_its_workspace():
     torch.cuda.synchronize()
     kp, vp = stored_pools(wl)
     assert_close(out_f64(x["o"]), oracle_decode(wl, kp, vp), "bf16", "decode on a side stream")
+
+
+def test_decode_workspace_serves_calls_of_several_shapes():
+    """One workspace, sized for the largest call, serves DECODE calls of different batches and
+    lengths in a row (nothing in it carries over between calls), and an empty request among
+    others gets a zero row while the others still match the oracle."""
+    specs = [W.Spec("ws-a", "bf16", 32, 8, 128, 300000, decode_batch=40, decode_range=(1, 5000)),
+             W.Spec("ws-b", "bf16", 16, 4, 128, 100000, decode_lens=(3, 9000, 700)),
+             W.Spec("ws-c", "bf16", 32, 8, 128, 300000, decode_batch=64, decode_range=(100, 3000))]
+    need = max(R.decode_workspace_bytes(R.BF16, 64, 9000, 32, 8, 128), R.decode_workspace_bytes(R.BF16, 3, 9000, 16, 4, 128))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for i, spec in enumerate(specs + specs[:1]):
+        wl = W.make_workload(spec, 640 + i)
+        dw = upload(wl)
+        store(dw)
+        x = dw.dec
+        R.decode_attention(x["q"], x["o"], dw.k_pool, dw.v_pool, dw.req_to_token, x["req_pool_indices"],
+                           x["seq_lens"], x["max_seq_len"], wl.sm_scale, workspace=ws)
+        torch.cuda.synchronize()
+        kp, vp = stored_pools(wl)
+        assert_close(out_f64(x["o"]), oracle_decode(wl, kp, vp), "bf16", f"shared workspace call {i} ({spec.name})")
+        ws.fill_(0xAB)   # stale contents must not matter to the next call
+    # an empty request (seq_len 0) among others: zero output row, the others unchanged
+    wl = W.make_workload(specs[0], 650)
+    dw = upload(wl)
+    store(dw)
+    x = dw.dec
+    lens = x["seq_lens"].clone()
+    lens[7] = 0
+    x["o"].fill_(float("nan"))
+    R.decode_attention(x["q"], x["o"], dw.k_pool, dw.v_pool, dw.req_to_token, x["req_pool_indices"], lens,
+                       x["max_seq_len"], wl.sm_scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.all(to_host_bits(x["o"])[7] == 0)
+    keep = [b for b in range(wl.decode.batch) if b != 7]
+    kp, vp = stored_pools(wl)
+    assert_close(out_f64(x["o"])[keep], oracle_decode(wl, kp, vp, requests=keep), "bf16", "batch with an empty request")
