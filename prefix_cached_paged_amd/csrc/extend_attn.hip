@@ -246,25 +246,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const uint32_t k_src1 = 16u * (uint32_t)(punit ^ (8 * (wave & 1) + 4 + prow));
     const uint32_t v_src = 16u * (uint32_t)unswz_v(prow, punit);
     const int ntiles = (kend + kExtBN - 1) / kExtBN;
-    // FP8 pools: slot numbers come through scalar loads at wave-uniform, clamped positions,
-    // so the copies are the only vector-memory operations in that loop and waiting for one
-    // tile's copies (vmcnt) never waits for slot loads or for younger copies. Wave w copies
-    // tile rows 8 w .. 8 w + 7 (slot numbers nx0 .. nx7 of those eight).
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    int nx0, nx1, nx2, nx3, nx4, nx5, nx6, nx7;  // FP8 pools: slots of the next tile to copy (SGPRs)
-#define RAX_SLOTS(TILE)                                                                     \
-    {                                                                                       \
-        const int pb_ = (TILE) * kExtBN + 8 * wave_u;                                       \
-        const int lim_ = kend - 1;                                                          \
-        nx0 = slot_at<PG>(row, min(pb_ + 0, lim_), page_shift);                            \
-        nx1 = slot_at<PG>(row, min(pb_ + 1, lim_), page_shift);                            \
-        nx2 = slot_at<PG>(row, min(pb_ + 2, lim_), page_shift);                            \
-        nx3 = slot_at<PG>(row, min(pb_ + 3, lim_), page_shift);                            \
-        nx4 = slot_at<PG>(row, min(pb_ + 4, lim_), page_shift);                            \
-        nx5 = slot_at<PG>(row, min(pb_ + 5, lim_), page_shift);                            \
-        nx6 = slot_at<PG>(row, min(pb_ + 6, lim_), page_shift);                            \
-        nx7 = slot_at<PG>(row, min(pb_ + 7, lim_), page_shift);                            \
-    }
     // bf16 pools: the slot numbers of the two rows a lane copies (tile rows 8 w + prow and
     // 8 w + 4 + prow) come through per-lane vector loads, one tile before their copy. Scalar
     // loads would share the LDS counter (lgkmcnt) and, being unordered, turn every LDS operand
@@ -308,17 +290,24 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     }
     // FP8 pools: a 64-key tile is 8 KB per operand, so one copy instruction per wave moves
     // its eight rows: lane l fetches 16 bytes at offset 16 (l % 8) of row 8 w + l / 8 into
-    // staging unit 64 w + l. 2 vector-memory operations per wave per tile.
+    // staging unit 64 w + l. The lane's slot comes through a per-lane vector load (tile T's in
+    // register set T % 2), as for bf16 pools. Per wave and tile: 1 slot load, 2 copies.
     const int q8 = lane >> 3;
     const uint32_t src8 = 16u * (uint32_t)(lane & 7);
-#define RAX_COPY8(SK, SV)                                                                   \
+#define RAX_VSLOT8(TILE, S)                                                                 \
     {                                                                                       \
-        int sl_ = nx0;                                                                      \
-        sl_ = q8 == 1 ? nx1 : sl_; sl_ = q8 == 2 ? nx2 : sl_; sl_ = q8 == 3 ? nx3 : sl_;    \
-        sl_ = q8 == 4 ? nx4 : sl_; sl_ = q8 == 5 ? nx5 : sl_; sl_ = q8 == 6 ? nx6 : sl_;    \
-        sl_ = q8 == 7 ? nx7 : sl_;                                                          \
-        lds_dma16(pool_row_ptr<OFF32>(kbase, sl_, row_bytes, src8), (char*)(SK) + wave_u * 1024); \
-        lds_dma16(pool_row_ptr<OFF32>(vbase, sl_, row_bytes, src8), (char*)(SV) + wave_u * 1024); \
+        S = slot_at<PG>(row, min((TILE) * kExtBN + 8 * wave + q8, kend - 1), page_shift);   \
+    }
+#define RAX_COPY8(SK, SV, S)                                                                \
+    {                                                                                       \
+        if constexpr (OFF32) {                                                              \
+            const uint32_t o_ = __umul24((uint32_t)(S), row_bytes) + src8;                  \
+            lds_dma16_buf(krsrc, o_, (char*)(SK) + wave_u * 1024);                          \
+            lds_dma16_buf(vrsrc, o_, (char*)(SV) + wave_u * 1024);                          \
+        } else {                                                                            \
+            lds_dma16(pool_row_ptr<OFF32>(kbase, S, row_bytes, src8), (char*)(SK) + wave_u * 1024); \
+            lds_dma16(pool_row_ptr<OFF32>(vbase, S, row_bytes, src8), (char*)(SV) + wave_u * 1024); \
+        }                                                                                   \
     }
     // Each lane widens the staging unit it copied (16 E4M3 values = head_dim 16 u .. 16 u + 15
     // of key 8 w + l / 8) into logical units 2 u and 2 u + 1 of the swizzled bf16 tile. Only
@@ -502,27 +491,36 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     }
     // FP8 pools: tile T is staged (E4M3) in buffer T % 2 and widened into bf16 buffer T % 4.
     // Iteration IT: barrier (every wave's widening of tile IT has landed, every wave is done
-    // with iteration IT-1); compute as above; wait for this wave's copies of tile IT+1 (those
-    // of IT+2 stay in flight) and widen them from staging (SC, SVC) into (KN, VN), free since
-    // tile IT-3; then, once the staging reads have returned, copy tile IT+3 into the staging
-    // buffer just emptied (the compiler may otherwise issue the copy before the widening has
-    // consumed the reads, and a copy that hits in L2 can land first).
-#define RAX_WIDEN8(IT, SC, SVC, KN, VN, STEADY)                                             \
+    // with iteration IT-1); compute as above; wait for this wave's copies of tile IT+1 and
+    // widen them from staging (SC, SVC) into (KN, VN), free since tile IT-3; then load the slot
+    // of tile IT+4 (into set SL) and, once the staging reads have returned, copy tile IT+3
+    // (slot set SU) into the staging buffer just emptied (the compiler may otherwise issue the
+    // copy before the widening has consumed the reads, and a copy that hits in L2 can land
+    // first). When tile IT+1 is widened, the operations younger than its copies are the slot
+    // load of tile IT+3 and the copies of tile IT+2 (issued in iteration IT-1 when those tiles
+    // exist, always in the steady loop): wait until at most 3, 2 or 0 are outstanding.
+#define RAX_WIDEN8(IT, SC, SVC, KN, VN, SU, SL, STEADY)                                     \
     {                                                                                       \
         if (STEADY || (IT) + 1 < ntiles) {                                                  \
-            if (STEADY || (IT) + 2 < ntiles) { RAX_WAIT_VMCNT(2); } else { RAX_WAIT_VMCNT(0); } \
+            if (STEADY || (IT) + 3 < ntiles) {                                              \
+                RAX_WAIT_VMCNT(3);                                                          \
+            } else if ((IT) + 2 < ntiles) {                                                 \
+                RAX_WAIT_VMCNT(2);                                                          \
+            } else {                                                                        \
+                RAX_WAIT_VMCNT(0);                                                          \
+            }                                                                               \
             RAX_CONVERT8(SC, SVC, KN, VN)                                                   \
         }                                                                                   \
+        if (STEADY || (IT) + 4 < ntiles) RAX_VSLOT8((IT) + 4, SL)                           \
         if (STEADY || (IT) + 3 < ntiles) {                                                  \
             RAX_READS_DONE();                                                               \
-            RAX_COPY8(SC, SVC)                                                              \
-            if (STEADY || (IT) + 4 < ntiles) RAX_SLOTS((IT) + 4)                            \
+            RAX_COPY8(SC, SVC, SU)                                                          \
         }                                                                                   \
     }
     // Waves 4-7 widen between their P V and their scores, so that per iteration each wave
     // group alternates MFMA and VALU/LDS blocks in the opposite order to the other group
     // (+1 to +3% over widening at the end of the iteration in both groups).
-#define RAX_PTILE8(LAG, IT, KB, VB, VP, SC, SVC, KN, VN, MASKABLE, STEADY)                  \
+#define RAX_PTILE8(LAG, IT, KB, VB, VP, SC, SVC, KN, VN, SU, SL, MASKABLE, STEADY)          \
     {                                                                                       \
         RAX_WRITES_BARRIER();                                                               \
         if (LAG) {                                                                          \
@@ -530,11 +528,11 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
             } else {                                                                        \
                 RAX_SM((IT) - 1, MASKABLE) RAX_PV(VP)                                       \
             }                                                                               \
-            RAX_WIDEN8(IT, SC, SVC, KN, VN, STEADY)                                         \
+            RAX_WIDEN8(IT, SC, SVC, KN, VN, SU, SL, STEADY)                                 \
             RAX_QK(KB)                                                                      \
         } else {                                                                            \
             RAX_COMPUTE(IT, KB, VB, MASKABLE)                                               \
-            RAX_WIDEN8(IT, SC, SVC, KN, VN, STEADY)                                         \
+            RAX_WIDEN8(IT, SC, SVC, KN, VN, SU, SL, STEADY)                                 \
         }                                                                                   \
     }
 
@@ -595,39 +593,47 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         RAX_WAIT_VMCNT(0);  // the copies past the end land before the workgroup's LDS is reused
 #undef RAX_PLOOPS
     } else {
-        // prologue: copies of tiles 0 and 1 issued, tile 0 widened, the copy of tile 2 issued
-        // into its emptied staging buffer, slots of tile 3 loaded
-        RAX_SLOTS(0)
-        RAX_COPY8(sk0, sv0)
-        if (ntiles > 1) {
-            RAX_SLOTS(1)
-            RAX_COPY8(sk1, sv1)
+        // prologue: slots of tiles 0 and 1, their copies, the slot of tile 2; tile 0 widened
+        // (the younger operations are tile 1's copies and tile 2's slot load); the slot of tile
+        // 3 loaded and the copy of tile 2 issued into its emptied staging buffer
+        int s8a = 0, s8b = 0;  // slot register sets 0 and 1
+        RAX_VSLOT8(0, s8a)
+        if (ntiles > 1) RAX_VSLOT8(1, s8b)
+        RAX_COPY8(sk0, sv0, s8a)
+        if (ntiles > 1) RAX_COPY8(sk1, sv1, s8b)
+        if (ntiles > 2) RAX_VSLOT8(2, s8a)
+        if (ntiles > 2) {
+            RAX_WAIT_VMCNT(3);
+        } else if (ntiles > 1) {
+            RAX_WAIT_VMCNT(2);
+        } else {
+            RAX_WAIT_VMCNT(0);
         }
-        if (ntiles > 2) RAX_SLOTS(2)
-        if (ntiles > 1) { RAX_WAIT_VMCNT(2); } else { RAX_WAIT_VMCNT(0); }
         RAX_CONVERT8(sk0, sv0, kb0, vb0)
+        if (ntiles > 3) RAX_VSLOT8(3, s8b)
         if (ntiles > 2) {
             RAX_READS_DONE();
-            RAX_COPY8(sk0, sv0)
-            if (ntiles > 3) RAX_SLOTS(3)
+            RAX_COPY8(sk0, sv0, s8a)
         }
-        // Tile T: staging T % 2, bf16 buffer T % 4; the first iteration is peeled.
+        // Tile T: staging T % 2, bf16 buffer T % 4, slot set T % 2; the first iteration is
+        // peeled. Iteration IT copies tile IT+3 (set (IT+1) % 2) and loads the slot of tile IT+4
+        // (set IT % 2).
 #define RAX_PLOOPS8(LAG)                                                                    \
-        RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, kb1, vb1, 1, 0) ++it;                   \
+        RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, kb1, vb1, s8b, s8a, 1, 0) ++it;         \
         while (it + 4 <= n_full) {                                                          \
-            RAX_PTILE8(LAG, it, kb1, vb1, vb0, sk0, sv0, kb2, vb2, 0, 1) ++it;               \
-            RAX_PTILE8(LAG, it, kb2, vb2, vb1, sk1, sv1, kb3, vb3, 0, 1) ++it;               \
-            RAX_PTILE8(LAG, it, kb3, vb3, vb2, sk0, sv0, kb0, vb0, 0, 1) ++it;               \
-            RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, kb1, vb1, 0, 1) ++it;               \
+            RAX_PTILE8(LAG, it, kb1, vb1, vb0, sk0, sv0, kb2, vb2, s8a, s8b, 0, 1) ++it;     \
+            RAX_PTILE8(LAG, it, kb2, vb2, vb1, sk1, sv1, kb3, vb3, s8b, s8a, 0, 1) ++it;     \
+            RAX_PTILE8(LAG, it, kb3, vb3, vb2, sk0, sv0, kb0, vb0, s8a, s8b, 0, 1) ++it;     \
+            RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, kb1, vb1, s8b, s8a, 0, 1) ++it;     \
         }                                                                                   \
         while (it < ntiles) {                                                               \
-            RAX_PTILE8(LAG, it, kb1, vb1, vb0, sk0, sv0, kb2, vb2, 1, 0) ++it;               \
+            RAX_PTILE8(LAG, it, kb1, vb1, vb0, sk0, sv0, kb2, vb2, s8a, s8b, 1, 0) ++it;     \
             if (it >= ntiles) break;                                                        \
-            RAX_PTILE8(LAG, it, kb2, vb2, vb1, sk1, sv1, kb3, vb3, 1, 0) ++it;               \
+            RAX_PTILE8(LAG, it, kb2, vb2, vb1, sk1, sv1, kb3, vb3, s8b, s8a, 1, 0) ++it;     \
             if (it >= ntiles) break;                                                        \
-            RAX_PTILE8(LAG, it, kb3, vb3, vb2, sk0, sv0, kb0, vb0, 1, 0) ++it;               \
+            RAX_PTILE8(LAG, it, kb3, vb3, vb2, sk0, sv0, kb0, vb0, s8a, s8b, 1, 0) ++it;     \
             if (it >= ntiles) break;                                                        \
-            RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, kb1, vb1, 1, 0) ++it;               \
+            RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, kb1, vb1, s8b, s8a, 1, 0) ++it;     \
         }
         if (lag) {
             RAX_PLOOPS8(1)
@@ -671,7 +677,6 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         }
     }
 }
-#undef RAX_SLOTS
 #undef RAX_VSLOTS
 #undef RAX_VCOPY
 #undef RAX_QK
@@ -680,6 +685,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
 #undef RAX_VREAD
 #undef RAX_PTILE
 #undef RAX_COPY8
+#undef RAX_VSLOT8
 #undef RAX_CONVERT8
 #undef RAX_PTILE8
 #undef RAX_WIDEN8
