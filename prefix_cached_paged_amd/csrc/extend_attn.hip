@@ -385,6 +385,22 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         }                                                                                   \
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                  \
     }
+    // P = 2^(scale_log2 * s - m) rounded to bf16 into pf (the B operand of P V), added two at a
+    // time into the row sums lsum / lsum2.
+#define RAX_PEXP()                                                                          \
+    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                      \
+        float pv[8];                                                                        \
+        _Pragma("unroll") for (int j = 0; j < 8; ++j)                                       \
+            pv[j] = fast_exp2(fmaf(st[kk >> 1][8 * (kk & 1) + j], scale_log2, -m));         \
+        pf[kk].x = pack_bf16x2(pv[0], pv[1]);                                               \
+        pf[kk].y = pack_bf16x2(pv[2], pv[3]);                                               \
+        pf[kk].z = pack_bf16x2(pv[4], pv[5]);                                               \
+        pf[kk].w = pack_bf16x2(pv[6], pv[7]);                                               \
+        lsum = add_bf16x2(pf[kk].x, lsum);                                                  \
+        lsum2 = add_bf16x2(pf[kk].y, lsum2);                                                \
+        lsum = add_bf16x2(pf[kk].z, lsum);                                                  \
+        lsum2 = add_bf16x2(pf[kk].w, lsum2);                                                \
+    }
 #define RAX_SM(IT, MASKABLE)                                                                \
     {                                                                                       \
         if (MASKABLE && __builtin_amdgcn_readfirstlane((IT) * kExtBN + kExtBN - 1 > diag_from)) { \
@@ -395,30 +411,27 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
                 if (j0_ + 32 * mb + 8 * jj + 4 * h2 + i > last_q) st[mb][4 * jj + i] = -INFINITY; \
             }                                                                               \
         }                                                                                   \
+        /* P is formed against the current reference maximum m while the tile's maximum is  */ \
+        /* found, so the exponentials do not wait for the max chain; that P is the result     */ \
+        /* unless the tile raises some row's maximum by more than 2^kLazyLog2 (always on the  */ \
+        /* first tile, m = -inf), when the sums are restored, rescaled and P is formed again. */ \
+        const float l0_ = lsum, l1_ = lsum2;                                                \
         float mx = -INFINITY;                                                               \
         _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                    \
         _Pragma("unroll") for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[mb][i]);           \
-        mx = max_pair32(mx) * scale_log2;                                             \
+        RAX_PEXP()                                                                          \
+        _Pragma("unroll") for (int kk = 0; kk < 4; ++kk)                                    \
+            asm volatile("" : "+v"(pf[kk].x), "+v"(pf[kk].y), "+v"(pf[kk].z), "+v"(pf[kk].w)); \
+        asm volatile("" : "+v"(lsum), "+v"(lsum2));                                         \
+        mx = max_pair32(mx) * scale_log2;                                                   \
         if (__any(mx > m + kLazyLog2)) {                                                    \
             const float m_new = fmaxf(m, mx);                                               \
             const float alpha = fast_exp2(m - m_new);                                       \
             m = m_new;                                                                      \
-            lsum *= alpha;                                                                  \
-            lsum2 *= alpha;                                                                 \
+            lsum = l0_ * alpha;                                                             \
+            lsum2 = l1_ * alpha;                                                            \
             _Pragma("unroll") for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;         \
-        }                                                                                   \
-        _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                  \
-            float pv[8];                                                                    \
-            _Pragma("unroll") for (int j = 0; j < 8; ++j)                                   \
-                pv[j] = fast_exp2(fmaf(st[kk >> 1][8 * (kk & 1) + j], scale_log2, -m));     \
-            pf[kk].x = pack_bf16x2(pv[0], pv[1]);                                           \
-            pf[kk].y = pack_bf16x2(pv[2], pv[3]);                                           \
-            pf[kk].z = pack_bf16x2(pv[4], pv[5]);                                           \
-            pf[kk].w = pack_bf16x2(pv[6], pv[7]);                                           \
-            lsum = add_bf16x2(pf[kk].x, lsum);                                              \
-            lsum2 = add_bf16x2(pf[kk].y, lsum2);                                            \
-            lsum = add_bf16x2(pf[kk].z, lsum);                                              \
-            lsum2 = add_bf16x2(pf[kk].w, lsum2);                                            \
+            RAX_PEXP()                                                                      \
         }                                                                                   \
     }
     // V^T operand of step (dt, kk): two transposed reads of keys 16 kk + 4 h2 + jr (+ 8).
@@ -681,6 +694,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
 #undef RAX_VCOPY
 #undef RAX_QK
 #undef RAX_SM
+#undef RAX_PEXP
 #undef RAX_PV
 #undef RAX_VREAD
 #undef RAX_PTILE
