@@ -161,9 +161,11 @@ __device__ __forceinline__ T row_load(const char* base, int slot, uint32_t row_b
 }
 
 // Keys request b occupies in the stream: its valid keys rounded up to whole iterations.
-__device__ __forceinline__ int64_t padded_len(const int32_t* seq_lens, int b, int32_t max_seq_len) {
-    const int L = min(seq_lens[b], max_seq_len);
+__device__ __forceinline__ int64_t padded_keys(int L) {
     return L > 0 ? (int64_t)((L + kDecKeysPerIter - 1) / kDecKeysPerIter * kDecKeysPerIter) : 0;
+}
+__device__ __forceinline__ int64_t padded_len(const int32_t* seq_lens, int b, int32_t max_seq_len) {
+    return padded_keys(min(seq_lens[b], max_seq_len));
 }
 
 // Range length for a stream of T keys: clamp(64 * ceil(T / (64 * n_target)), min, 4096).
@@ -247,29 +249,44 @@ __global__ __launch_bounds__(64 * kDecWaves, KV8 ? RAX_DEC_WGS_PER_CU8 : RAX_DEC
     int64_t T, chunk, n_active;
     const int64_t* Pr;  // request offsets: LDS (FUSED) or the plan's array
     int b_first;
+    // FUSED: request lengths (clamped) and r2t rows, loaded together by the plan below and
+    // read again by the request listing from LDS.
+    __shared__ int32_t sLen[FUSED ? kDecFusedBatch : 1];
+    __shared__ int32_t sRpi[FUSED ? kDecFusedBatch : 1];
     if constexpr (FUSED) {
         constexpr int NT = 64 * kDecWaves;
         __shared__ int64_t sP[kDecFusedBatch + 1];
-        __shared__ int64_t part[NT];
+        __shared__ int64_t wsum[kDecWaves];
         const int t = threadIdx.x;
         const int per = (B + NT - 1) / NT;
         const int c0 = min(B, t * per);
         const int c1 = min(B, c0 + per);
         int64_t own = 0;
-        for (int b = c0; b < c1; ++b) own += padded_len(seq_lens, b, max_seq_len);
-        part[t] = own;
-        __syncthreads();
-        for (int off = 1; off < NT; off <<= 1) {  // inclusive scan of the thread sums
-            const int64_t v = t >= off ? part[t - off] : 0;
-            __syncthreads();
-            part[t] += v;
-            __syncthreads();
+        for (int b = c0; b < c1; ++b) {
+            const int L = min(seq_lens[b], max_seq_len);
+            sLen[b] = L;
+            sRpi[b] = rpi[b];
+            own += padded_keys(L);
         }
-        T = part[NT - 1];
-        int64_t run = part[t] - own;
+        // inclusive scan of the thread sums: within each wave by shuffles, then over the waves
+        int64_t inc = own;
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int64_t v = __shfl_up(inc, off, kWave);
+            if (lane >= off) inc += v;
+        }
+        if (lane == kWave - 1) wsum[wv] = inc;
+        __syncthreads();
+        int64_t before = 0;
+        T = 0;
+        for (int i = 0; i < kDecWaves; ++i) {
+            const int64_t ws = wsum[i];
+            before += i < wv ? ws : 0;
+            T += ws;
+        }
+        int64_t run = before + inc - own;
         for (int b = c0; b < c1; ++b) {
             sP[b] = run;
-            run += padded_len(seq_lens, b, max_seq_len);
+            run += padded_keys(sLen[b]);
         }
         if (t == 0) sP[B] = T;
         chunk = range_keys(T, n_target);
@@ -315,8 +332,13 @@ __global__ __launch_bounds__(64 * kDecWaves, KV8 ? RAX_DEC_WGS_PER_CU8 : RAX_DEC
             if (bi < B) {
                 pb = Pr[bi];
                 pe = Pr[bi + 1];
-                rp = rpi[bi];
-                len = min(seq_lens[bi], max_seq_len);
+                if constexpr (FUSED) {
+                    rp = sRpi[bi];
+                    len = sLen[bi];
+                } else {
+                    rp = rpi[bi];
+                    len = min(seq_lens[bi], max_seq_len);
+                }
             }
             const bool ov = bi < B && pe > pb && pe > s0 && pb < s1;
             const uint64_t ball = __ballot(ov);
@@ -554,14 +576,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     const int lane = threadIdx.x & 63;
     const int b = wq / Hq;
     const int h = wq - b * Hq;
+    // the length and the plan entries are independent loads: issue them together
     const int L = min(seq_lens[b], max_seq_len);
+    const int64_t chunk = meta[1];
+    const int64_t pb = P[b], pe = P[b + 1];
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.f;
     if (L > 0) {
-        const int64_t chunk = meta[1];
-        const int64_t w0 = P[b] / chunk;
-        const int n = (int)((P[b + 1] - 1) / chunk - w0) + 1;
+        const int64_t w0 = pb / chunk;
+        const int n = (int)((pe - 1) / chunk - w0) + 1;
         const int64_t first = ((int64_t)b + w0) * Hq + h;  // partial c sits at first + c * Hq
         // Partial c's piece of this lane: o_part[(first + c * Hq) * D + PER * lane ..].
         const Piece* orow = (const Piece*)(o_part + first * D) + lane;
