@@ -21,8 +21,9 @@
  *   head h reads kv head h / (n_q_heads / n_kv_heads) (contiguous groups: grouped-query
  *   attention, "Inside SGLang", Step 3).
  * - Kernels exist for (group G = n_q_heads / n_kv_heads): fp32 EXTEND and DECODE, any G and
- *   head_dim 64 or 128; bf16 (and FP8-pool) EXTEND, head_dim 128 and G in {1, 2, 4, 8, 16, 32};
- *   bf16 (and FP8-pool) DECODE, head_dim 64 or 128 and G from 1 to 16. Any other valid shape
+ *   head_dim 64 or 128; bf16 EXTEND (plain, ragged and paged), head_dim 64 or 128, and FP8-pool
+ *   EXTEND, head_dim 128, with G in {1, 2, 4, 8, 16, 32}; bf16 (and FP8-pool) DECODE, head_dim 64
+ *   or 128 and G from 1 to 16. Any other valid shape
  *   returns RAX_ERR_UNSUPPORTED before anything is enqueued.
  * - `stream` is a hipStream_t (NULL = the null stream). Every call only ENQUEUES work on it:
  *   the library never allocates, frees or synchronises, and keeps no state between calls.
@@ -276,7 +277,7 @@ rax_status rax_decode_attention_noalloc(rax_dtype dtype, const void* q, void* o,
  *   page_table    int32 (device), row stride pt_stride entries; pt_stride * P >= max_seq_len.
  *   page_size     P, a power of two from 1 to 2^20 (else RAX_ERR_SHAPE).
  * Device-side CONTRACT: the entries for positions 0 .. L-1 of each used row are pages with
- *   page * P + P <= num_slots. bf16 (MFMA kernels, head_dim 128 for EXTEND) and fp32.
+ *   page * P + P <= num_slots. bf16 (MFMA kernels) and fp32.
  */
 rax_status rax_extend_attention_paged(rax_dtype dtype, const void* q, void* o, const void* k_pool,
                                       const void* v_pool, int64_t num_slots, const int32_t* page_table,

@@ -1,4 +1,4 @@
-// EXTEND attention, bf16, head_dim 128: new suffix rows attend causally to the request's cached
+// EXTEND attention, bf16, head_dim 64 or 128: new suffix rows attend causally to the request's cached
 // prefix and to themselves, every key gathered from the slot pool through req_to_token.
 //
 // With a prefix cache only the missed suffix is computed, and attention reads the prefix's
@@ -14,7 +14,8 @@
 //    256 / G tokens x G heads. Each wave owns 32 rows. Every workgroup reads the whole visible
 //    context once, so the K/V traffic is (query rows / 256) x context: the row count per
 //    workgroup is what keeps the kernel off the memory roofline.
-//  * Key tiles of 64 rows (256 B per kv head per row) are copied HBM -> LDS by the gfx950
+//  * Key tiles of 64 rows (256 B per kv head per row; head_dim 64 fills half of each LDS row)
+//    are copied HBM -> LDS by the gfx950
 //    global_load_lds_dwordx4 (16 B per lane, no registers), each lane fetching the unit that
 //    the LDS swizzle stores at its destination. Four LDS buffers: tile i is consumed while
 //    tiles i+1 and i+2 are in flight, and tile i-1's V is still read (ping-pong, below);
@@ -57,7 +58,6 @@ namespace rax {
 
 namespace {
 
-constexpr int kExtD = 128;
 constexpr int kExtBM = 256;
 constexpr int kExtBN = 64;
 constexpr int kExtWaves = 8;
@@ -166,7 +166,7 @@ __device__ __forceinline__ int64_t row_off(int idx, uint32_t row_bytes) {
 
 // PG: the table is a page table (page size 2^page_shift): position j lives at slot
 // table[row, j >> page_shift] << page_shift | (j & (2^page_shift - 1)).
-template <int G, bool OFF32, bool KV8, bool RAG, bool PG>
+template <int DH, int G, bool OFF32, bool KV8, bool RAG, bool PG>
 __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const char* __restrict__ k_pool,
     const char* __restrict__ v_pool, const char* __restrict__ k_new, const char* __restrict__ v_new,
@@ -175,7 +175,12 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ extend_start_loc,
     int64_t total_tokens, int32_t max_extend_len, int32_t max_seq_len, int32_t Hq, int32_t Hkv,
     int32_t batch, int32_t tiles, float scale_log2, float out_scale, int32_t page_shift) {
-    constexpr int D = kExtD;
+    // head_dim of Q, O and the pool rows. The LDS tiles keep 128-wide rows either way: with
+    // head_dim 64 only logical units 0-7 of a row are used (score steps 0-3, P V blocks 0-1)
+    // and the copy lanes of units 8-15 fetch a copy of units 0-7, so no copy leaves its row.
+    constexpr int D = DH;
+    static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+    static_assert(!(KV8 && D != 128), "FP8 pools: head_dim 128");
     constexpr int BQ = kExtBM / G;  // tokens per workgroup
     constexpr int EB = KV8 ? 1 : 2;  // bytes per pool element
     static_assert(!(KV8 && RAG), "ragged suffix rows are bf16, as the pools");
@@ -242,9 +247,9 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // unit the swizzle stores there: R & 15 = 8 (w & 1) + 4 i + prow, R & 3 = prow.
     const int prow = lane >> 4;
     const int punit = lane & 15;
-    const uint32_t k_src0 = 16u * (uint32_t)(punit ^ (8 * (wave & 1) + prow));
-    const uint32_t k_src1 = 16u * (uint32_t)(punit ^ (8 * (wave & 1) + 4 + prow));
-    const uint32_t v_src = 16u * (uint32_t)unswz_v(prow, punit);
+    const uint32_t k_src0 = 16u * (uint32_t)((punit ^ (8 * (wave & 1) + prow)) & (D / 8 - 1));
+    const uint32_t k_src1 = 16u * (uint32_t)((punit ^ (8 * (wave & 1) + 4 + prow)) & (D / 8 - 1));
+    const uint32_t v_src = 16u * (uint32_t)(unswz_v(prow, punit) & (D / 8 - 1));
     const int ntiles = (kend + kExtBN - 1) / kExtBN;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     // bf16 pools: the slot numbers of the two rows a lane copies (tile rows 8 w + prow and
@@ -450,16 +455,16 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         const char* vbb = (const char*)(VB);                                                \
         uint4 va_ = RAX_VREAD(vbb, 0, 0);                                                   \
         uint4 vb_ = RAX_VREAD(vbb, 0, 1);                                                   \
-        _Pragma("unroll") for (int st_ = 0; st_ < 16; ++st_) {                              \
+        _Pragma("unroll") for (int st_ = 0; st_ < D / 8; ++st_) {                           \
             const int dt = st_ >> 2, kk = st_ & 3;                                          \
             uint4 vc_ = vb_;                                                                \
-            if (st_ + 2 < 16) vc_ = RAX_VREAD(vbb, (st_ + 2) >> 2, (st_ + 2) & 3);          \
+            if (st_ + 2 < D / 8) vc_ = RAX_VREAD(vbb, (st_ + 2) >> 2, (st_ + 2) & 3);       \
             acc[dt] = mfma32x32x16(as_bf16x8(va_), as_bf16x8(pf[kk]), acc[dt]);             \
             va_ = vb_;                                                                      \
             vb_ = vc_;                                                                      \
         }                                                                                   \
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                                  \
-        _Pragma("unroll") for (int st_ = 0; st_ < 14; ++st_) {                              \
+        _Pragma("unroll") for (int st_ = 0; st_ < D / 8 - 2; ++st_) {                       \
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                              \
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
         }                                                                                   \
@@ -679,9 +684,10 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     if constexpr (RAG) {
         if (store_loc != nullptr) {
             const int nrows = t_last - t0 + 1;
-            for (int u = tid; u < nrows * 16; u += kExtThreads) {
-                const int64_t tok = (int64_t)s0 + t0 + (u >> 4);
-                const int64_t col = (int64_t)g * D * EB + 16 * (u & 15);
+            constexpr int UPR = D / 8;  // 16-byte units per (token, kv head) row
+            for (int u = tid; u < nrows * UPR; u += kExtThreads) {
+                const int64_t tok = (int64_t)s0 + t0 + u / UPR;
+                const int64_t col = (int64_t)g * D * EB + 16 * (u % UPR);
                 const int64_t dst = (int64_t)store_loc[tok] * row_bytes + col;
                 const int64_t src = tok * row_bytes + col;
                 *(uint4*)((char*)k_pool + dst) = *(const uint4*)(k_new + src);
@@ -706,7 +712,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
 #undef RAX_PCOMPUTE
 #undef RAX_LAG_TAIL
 
-template <int G, bool OFF32, bool KV8, bool RAG, bool PG>
+template <int DH, int G, bool OFF32, bool KV8, bool RAG, bool PG>
 int launch_g(const AttnArgs& a, hipStream_t stream) {
     constexpr int BQ = kExtBM / G;
     const int tiles = (a.max_extend_len + BQ - 1) / BQ;
@@ -717,7 +723,7 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
     // FP8 pools: the K scale multiplies every score, the V scale every output element.
     const float scale_log2 = a.sm_scale * kLog2e * (KV8 ? a.k_scale : 1.f);
     const float out_scale = KV8 ? a.v_scale : 1.f;
-    hipLaunchKernelGGL((extend_kernel<G, OFF32, KV8, RAG, PG>), dim3((unsigned)blocks), dim3(kExtThreads),
+    hipLaunchKernelGGL((extend_kernel<DH, G, OFF32, KV8, RAG, PG>), dim3((unsigned)blocks), dim3(kExtThreads),
                        0, stream, (const uint16_t*)a.q, (uint16_t*)a.o, (const char*)a.k_pool,
                        (const char*)a.v_pool, (const char*)a.k_new, (const char*)a.v_new, a.store_loc,
                        a.r2t, a.r2t_stride, a.req_pool_indices,
@@ -727,46 +733,57 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-template <int G>
+template <int DH, int G>
 int launch_g(const AttnArgs& a, hipStream_t stream) {
     if (a.kv8) {
-        if (a.ragged || a.page_shift) return -1;
-        return pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 1)
-                   ? launch_g<G, true, true, false, false>(a, stream)
-                   : launch_g<G, false, true, false, false>(a, stream);
+        if constexpr (DH != 128) {
+            return -1;  // FP8 pools: head_dim 128
+        } else {
+            if (a.ragged || a.page_shift) return -1;
+            return pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 1)
+                       ? launch_g<DH, G, true, true, false, false>(a, stream)
+                       : launch_g<DH, G, false, true, false, false>(a, stream);
+        }
     }
     // ragged: the new rows are addressed like pool rows (row index total_tokens - 1 at most)
     const bool off32 = pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 2) &&
                        (!a.ragged || pool_fits_32bit_offsets(a.total_tokens, a.n_kv_heads, a.head_dim, 2));
     if (a.ragged) {
         if (a.page_shift) return -1;
-        return off32 ? launch_g<G, true, false, true, false>(a, stream)
-                     : launch_g<G, false, false, true, false>(a, stream);
+        return off32 ? launch_g<DH, G, true, false, true, false>(a, stream)
+                     : launch_g<DH, G, false, false, true, false>(a, stream);
     }
     if (a.page_shift)
-        return off32 ? launch_g<G, true, false, false, true>(a, stream)
-                     : launch_g<G, false, false, false, true>(a, stream);
-    return off32 ? launch_g<G, true, false, false, false>(a, stream)
-                 : launch_g<G, false, false, false, false>(a, stream);
+        return off32 ? launch_g<DH, G, true, false, false, true>(a, stream)
+                     : launch_g<DH, G, false, false, false, true>(a, stream);
+    return off32 ? launch_g<DH, G, true, false, false, false>(a, stream)
+                 : launch_g<DH, G, false, false, false, false>(a, stream);
 }
 
 }  // namespace
 
 bool extend_bf16_supported(int32_t group, int32_t head_dim) {
-    return head_dim == 128 &&
+    return (head_dim == 64 || head_dim == 128) &&
            (group == 1 || group == 2 || group == 4 || group == 8 || group == 16 || group == 32);
 }
 
-int launch_extend_bf16(const AttnArgs& a, hipStream_t stream) {
+template <int DH>
+int launch_extend_dh(const AttnArgs& a, hipStream_t stream) {
     switch (a.n_q_heads / a.n_kv_heads) {
-        case 1: return launch_g<1>(a, stream);
-        case 2: return launch_g<2>(a, stream);
-        case 4: return launch_g<4>(a, stream);
-        case 8: return launch_g<8>(a, stream);
-        case 16: return launch_g<16>(a, stream);
-        case 32: return launch_g<32>(a, stream);
+        case 1: return launch_g<DH, 1>(a, stream);
+        case 2: return launch_g<DH, 2>(a, stream);
+        case 4: return launch_g<DH, 4>(a, stream);
+        case 8: return launch_g<DH, 8>(a, stream);
+        case 16: return launch_g<DH, 16>(a, stream);
+        case 32: return launch_g<DH, 32>(a, stream);
         default: return -1;
     }
+}
+
+int launch_extend_bf16(const AttnArgs& a, hipStream_t stream) {
+    if (a.head_dim == 128) return launch_extend_dh<128>(a, stream);
+    if (a.head_dim == 64) return launch_extend_dh<64>(a, stream);
+    return -1;
 }
 
 }  // namespace rax

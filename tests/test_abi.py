@@ -80,7 +80,8 @@ def test_extend_validation():
     assert extend(d=96) == 4
     assert extend(hq=6, hkv=2) == 4          # bf16 MFMA path needs a power-of-two group
     assert extend(hq=128, hkv=2) == 4        # group 64 is beyond the 256-row tile
-    assert extend(d=64) == 4                 # bf16 EXTEND has a head_dim 128 kernel only
+    assert extend(d=32) == 4                 # head_dim 64 or 128 only
+    assert extend(d=64, batch=0, q=None) == 0  # bf16 EXTEND: head_dim 64 too
     assert extend(dtype=1, d=64, batch=0, q=None) == 0           # fp32: head_dim 64 ...
     assert extend(dtype=1, hq=6, hkv=2, batch=0, q=None) == 0    # ... and any group
     assert extend(scale=float("nan")) == 2

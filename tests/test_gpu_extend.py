@@ -23,6 +23,12 @@ SMALL = [
     W.Spec("ext-g16", "bf16", 16, 1, 128, 50000, extend_prefix=(129, 0), extend_lens=(20, 17)),
     W.Spec("ext-shared", "bf16", 32, 8, 128, 100000, extend_prefix=(700,) * 5, extend_lens=(100, 1, 64, 129, 3),
            shared_prefix=True),
+    # head_dim 64: the same tiles with half-filled LDS rows
+    W.Spec("ext-d64-g4", "bf16", 32, 8, 64, 100000, extend_prefix=(0, 1, 63, 64, 500, 3000),
+           extend_lens=(1, 40, 65, 128, 77, 300)),
+    W.Spec("ext-d64-g1", "bf16", 4, 4, 64, 50000, extend_prefix=(0, 200, 37), extend_lens=(300, 129, 0)),
+    W.Spec("ext-d64-g8", "bf16", 64, 8, 64, 100000, extend_prefix=(1000, 5), extend_lens=(33, 200)),
+    W.Spec("ext-d64-g32", "bf16", 32, 1, 64, 50000, extend_prefix=(0, 640), extend_lens=(500, 9)),
 ]
 
 

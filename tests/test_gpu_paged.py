@@ -27,6 +27,8 @@ EXT_SPECS = [
     W.Spec("pg64-g8", "bf16", 64, 8, 128, 131072, extend_prefix=(1000, 5), extend_lens=(33, 200), page_size=64),
     W.Spec("pg32-g16", "bf16", 16, 1, 128, 65536, extend_prefix=(129, 0), extend_lens=(20, 17), page_size=32),
     W.Spec("pg2-g32", "bf16", 32, 1, 128, 65536, extend_prefix=(0, 640), extend_lens=(500, 9), page_size=2),
+    W.Spec("pg16-d64-g2", "bf16", 8, 4, 64, 65536, extend_prefix=(0, 208, 1024), extend_lens=(190, 64, 77),
+           page_size=16),
     W.Spec("pg16-shared", "bf16", 32, 8, 128, 131072, extend_prefix=(704,) * 5, extend_lens=(100, 1, 64, 129, 3),
            shared_prefix=True, page_size=16),
     W.Spec("pg4-fp32", "fp32", 4, 4, 64, 4096, extend_prefix=(0, 16, 64, 128), extend_lens=(32, 16, 8, 1),

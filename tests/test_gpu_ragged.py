@@ -32,6 +32,7 @@ SPECS = [
     W.Spec("rag-shared", "bf16", 32, 8, 128, 100000, extend_prefix=(700,) * 5, extend_lens=(100, 1, 64, 129, 3),
            shared_prefix=True),
     W.Spec("rag-prefill", "bf16", 32, 8, 128, 50000, extend_prefix=(0, 0, 0), extend_lens=(1000, 64, 2)),
+    W.Spec("rag-d64-g4", "bf16", 32, 8, 64, 100000, extend_prefix=(0, 63, 500), extend_lens=(129, 65, 300)),
     W.Spec("rag-fp32-d64", "fp32", 4, 4, 64, 4000, extend_prefix=(0, 16, 64, 128), extend_lens=(32, 16, 8, 1)),
     W.Spec("rag-fp32-d128-g3", "fp32", 6, 2, 128, 20000, extend_prefix=(0, 300), extend_lens=(70, 65)),
 ]
@@ -72,7 +73,7 @@ def test_ragged_extend(spec, variant, fused_store):
 
 
 @pytest.mark.parametrize("variant", ["normal", "peaked"])
-@pytest.mark.parametrize("spec", [SPECS[0], SPECS[3], SPECS[6], SPECS[8], SPECS[9]], ids=lambda s: s.name)
+@pytest.mark.parametrize("spec", [SPECS[0], SPECS[3], SPECS[6], SPECS[8], SPECS[9], SPECS[10]], ids=lambda s: s.name)
 def test_ragged_is_bitwise_store_then_extend(spec, variant):
     wl = W.make_workload(spec, 802, variant)
     dw = upload(wl)
