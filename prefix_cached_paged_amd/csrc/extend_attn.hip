@@ -15,9 +15,10 @@
 //    context once, so the K/V traffic is (query rows / 256) x context: the row count per
 //    workgroup is what keeps the kernel off the memory roofline.
 //  * Key tiles of 64 rows (256 B per kv head per row; head_dim 64 fills half of each LDS row)
-//    are copied HBM -> LDS by the gfx950
-//    global_load_lds_dwordx4 (16 B per lane, no registers), each lane fetching the unit that
-//    the LDS swizzle stores at its destination. Four LDS buffers: tile i is consumed while
+//    are copied HBM -> LDS without registers, 16 B per lane (buffer_load_dwordx4 ... lds
+//    through a buffer resource when the pool's byte offsets fit 32 bits, the gfx950
+//    global_load_lds_dwordx4 otherwise), each lane fetching the unit that the LDS swizzle
+//    stores at its destination. Four LDS buffers: tile i is consumed while
 //    tiles i+1 and i+2 are in flight, and tile i-1's V is still read (ping-pong, below);
 //    slot numbers are loaded one tile before their copy. The buffers are separate LDS objects
 //    and the loop is unrolled by four, so every read names its buffer and the compiler does
@@ -28,9 +29,9 @@
 //    tile: in iteration i they run the softmax and P V of tile i-1, then the scores of tile i,
 //    while waves 0-3 run tile i whole; each SIMD's MFMA pipe then meets the other wave's
 //    softmax for two thirds of the iteration (+2 to +8% measured).
-//  * FP8 pools: E4M3 tiles go through three staging buffers and are widened to the bf16
-//    tiles by the lane that copied them; the compute is the same, without the ping-pong
-//    (4 bf16 buffers and 3 staging buffers would exceed the 160 KB of LDS).
+//  * FP8 pools: E4M3 tiles go through two staging buffers per operand (the four bf16 tiles
+//    plus 32 KB of staging fill the 160 KB of LDS) and are widened to the bf16 tiles by the
+//    lane that copied them, between the two halves of the ping-pong; the compute is the same.
 //  * S^T = K Q^T with 32x32x16 bf16 MFMAs: keys are the M dimension (read from LDS), query
 //    rows the N dimension (Q stays in registers for the whole key loop). The C layout puts
 //    one query row per lane column, so the row max/sum are per lane plus one exchange with
@@ -40,8 +41,9 @@
 //    gfx950 transposed LDS read (ds_read_b64_tr_b16), in the key order the P^T fragment has.
 //  * Softmax: sm_scale * log2(e) is folded into one FMA before exp2; the accumulators are only
 //    rescaled when a row max grows by more than 2^8 (exact: P and the row sum share the
-//    reference max). The row max over the two half-waves is one permlane swap (no LDS), the
-//    row sum adds the bf16-rounded P with dot2 instructions.
+//    reference max); P is formed against the current reference while the tile max is found
+//    and formed again only when the tile rescales. The row max over the two half-waves is one
+//    permlane swap (no LDS), the row sum adds the bf16-rounded P with dot2 instructions.
 //  * Causal mask only on the tiles that cross the diagonal (a separate loop, so full tiles run
 //    no mask code); keys past the last visible key of the workgroup reuse a valid slot and are
 //    masked, so no load leaves the request's slots.
