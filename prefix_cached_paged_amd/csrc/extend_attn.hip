@@ -162,9 +162,6 @@ __device__ __forceinline__ int64_t row_off(int idx, uint32_t row_bytes) {
 // Barrier after which other waves read this wave's LDS writes: the wait for them and the
 // barrier are one statement, so no write can be scheduled between the two.
 #define RAX_WRITES_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
-// This wave's LDS reads have returned before anything after this point is issued: a copy into
-// an LDS buffer the wave has just read (the FP8 staging ring) must not overtake those reads.
-#define RAX_READS_DONE() asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory")
 
 // PG: the table is a page table (page size 2^page_shift): position j lives at slot
 // table[row, j >> page_shift] << page_shift | (j & (2^page_shift - 1)).
@@ -509,17 +506,17 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         if (STEADY || (IT) + 3 < ntiles) RAX_VSLOTS((IT) + 3, SL0, SL1)                     \
         if (STEADY || (IT) + 2 < ntiles) RAX_VCOPY(KN, VN, (IT) + 2, SU0, SU1)              \
     }
-    // FP8 pools: tile T is staged (E4M3) in buffer T % 2 and widened into bf16 buffer T % 4.
-    // Iteration IT: barrier (every wave's widening of tile IT has landed, every wave is done
-    // with iteration IT-1); compute as above; wait for this wave's copies of tile IT+1 and
-    // widen them from staging (SC, SVC) into (KN, VN), free since tile IT-3; then load the slot
-    // of tile IT+4 (into set SL) and, once the staging reads have returned, copy tile IT+3
-    // (slot set SU) into the staging buffer just emptied (the compiler may otherwise issue the
-    // copy before the widening has consumed the reads, and a copy that hits in L2 can land
-    // first). When tile IT+1 is widened, the operations younger than its copies are the slot
-    // load of tile IT+3 and the copies of tile IT+2 (issued in iteration IT-1 when those tiles
-    // exist, always in the steady loop): wait until at most 3, 2 or 0 are outstanding.
-#define RAX_WIDEN8(IT, SC, SVC, KN, VN, SU, SL, STEADY)                                     \
+    // FP8 pools: tile T is staged (E4M3) in buffer T % 2 and widened into bf16 buffer T % 4;
+    // its slot is held in register set T % 2. Iteration IT: barrier (every wave's widening of
+    // tile IT has landed, every wave is done with iteration IT-1, whose widening read staging
+    // IT % 2); copy tile IT+2 into staging IT % 2 (slot set SS); compute as above; wait for
+    // this wave's copies of tile IT+1 and widen them from staging (SC, SVC) into (KN, VN), free
+    // since tile IT-3; then load the slot of tile IT+4 into set SS (the copy has taken its
+    // address already). When tile IT+1 is widened, the operations younger than its copies are
+    // the slot load of tile IT+3 (iteration IT-1) and the copies of tile IT+2 (this iteration),
+    // when those tiles exist (always in the steady loop): wait until at most 3, 2 or 0 are
+    // outstanding.
+#define RAX_WIDEN8(IT, SC, SVC, KN, VN, SS, STEADY)                                         \
     {                                                                                       \
         if (STEADY || (IT) + 1 < ntiles) {                                                  \
             if (STEADY || (IT) + 3 < ntiles) {                                              \
@@ -531,28 +528,25 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
             }                                                                               \
             RAX_CONVERT8(SC, SVC, KN, VN)                                                   \
         }                                                                                   \
-        if (STEADY || (IT) + 4 < ntiles) RAX_VSLOT8((IT) + 4, SL)                           \
-        if (STEADY || (IT) + 3 < ntiles) {                                                  \
-            RAX_READS_DONE();                                                               \
-            RAX_COPY8(SC, SVC, SU)                                                          \
-        }                                                                                   \
+        if (STEADY || (IT) + 4 < ntiles) RAX_VSLOT8((IT) + 4, SS)                           \
     }
     // Waves 4-7 widen between their P V and their scores, so that per iteration each wave
     // group alternates MFMA and VALU/LDS blocks in the opposite order to the other group
     // (+1 to +3% over widening at the end of the iteration in both groups).
-#define RAX_PTILE8(LAG, IT, KB, VB, VP, SC, SVC, KN, VN, SU, SL, MASKABLE, STEADY)          \
+#define RAX_PTILE8(LAG, IT, KB, VB, VP, SC, SVC, SCP, SVCP, KN, VN, SS, MASKABLE, STEADY)    \
     {                                                                                       \
         RAX_WRITES_BARRIER();                                                               \
+        if (STEADY || (IT) + 2 < ntiles) RAX_COPY8(SCP, SVCP, SS)                           \
         if (LAG) {                                                                          \
             if (!STEADY && (IT) == 0) {                                                     \
             } else {                                                                        \
                 RAX_SM((IT) - 1, MASKABLE) RAX_PV(VP)                                       \
             }                                                                               \
-            RAX_WIDEN8(IT, SC, SVC, KN, VN, SU, SL, STEADY)                                 \
+            RAX_WIDEN8(IT, SC, SVC, KN, VN, SS, STEADY)                                     \
             RAX_QK(KB)                                                                      \
         } else {                                                                            \
             RAX_COMPUTE(IT, KB, VB, MASKABLE)                                               \
-            RAX_WIDEN8(IT, SC, SVC, KN, VN, SU, SL, STEADY)                                 \
+            RAX_WIDEN8(IT, SC, SVC, KN, VN, SS, STEADY)                                     \
         }                                                                                   \
     }
 
@@ -617,12 +611,18 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         // (the younger operations are tile 1's copies and tile 2's slot load); the slot of tile
         // 3 loaded and the copy of tile 2 issued into its emptied staging buffer
         int s8a = 0, s8b = 0;  // slot register sets 0 and 1
+        // prologue: slots of tiles 0 and 1, the copy of tile 0, the slot of tile 2, the copy of
+        // tile 1, the slot of tile 3 (so that, as in the loop, a tile's copies are followed by
+        // one slot load and the next tile's copies); tile 0 widened once its copies have landed
         RAX_VSLOT8(0, s8a)
         if (ntiles > 1) RAX_VSLOT8(1, s8b)
         RAX_COPY8(sk0, sv0, s8a)
-        if (ntiles > 1) RAX_COPY8(sk1, sv1, s8b)
         if (ntiles > 2) RAX_VSLOT8(2, s8a)
-        if (ntiles > 2) {
+        if (ntiles > 1) RAX_COPY8(sk1, sv1, s8b)
+        if (ntiles > 3) RAX_VSLOT8(3, s8b)
+        if (ntiles > 3) {
+            RAX_WAIT_VMCNT(4);
+        } else if (ntiles > 2) {
             RAX_WAIT_VMCNT(3);
         } else if (ntiles > 1) {
             RAX_WAIT_VMCNT(2);
@@ -630,30 +630,25 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
             RAX_WAIT_VMCNT(0);
         }
         RAX_CONVERT8(sk0, sv0, kb0, vb0)
-        if (ntiles > 3) RAX_VSLOT8(3, s8b)
-        if (ntiles > 2) {
-            RAX_READS_DONE();
-            RAX_COPY8(sk0, sv0, s8a)
-        }
         // Tile T: staging T % 2, bf16 buffer T % 4, slot set T % 2; the first iteration is
-        // peeled. Iteration IT copies tile IT+3 (set (IT+1) % 2) and loads the slot of tile IT+4
-        // (set IT % 2).
+        // peeled. Iteration IT copies tile IT+2 (staging and set IT % 2) and loads the slot of
+        // tile IT+4 into the same set.
 #define RAX_PLOOPS8(LAG)                                                                    \
-        RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, kb1, vb1, s8b, s8a, 1, 0) ++it;         \
+        RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, sk0, sv0, kb1, vb1, s8a, 1, 0) ++it;    \
         while (it + 4 <= n_full) {                                                          \
-            RAX_PTILE8(LAG, it, kb1, vb1, vb0, sk0, sv0, kb2, vb2, s8a, s8b, 0, 1) ++it;     \
-            RAX_PTILE8(LAG, it, kb2, vb2, vb1, sk1, sv1, kb3, vb3, s8b, s8a, 0, 1) ++it;     \
-            RAX_PTILE8(LAG, it, kb3, vb3, vb2, sk0, sv0, kb0, vb0, s8a, s8b, 0, 1) ++it;     \
-            RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, kb1, vb1, s8b, s8a, 0, 1) ++it;     \
+            RAX_PTILE8(LAG, it, kb1, vb1, vb0, sk0, sv0, sk1, sv1, kb2, vb2, s8b, 0, 1) ++it; \
+            RAX_PTILE8(LAG, it, kb2, vb2, vb1, sk1, sv1, sk0, sv0, kb3, vb3, s8a, 0, 1) ++it; \
+            RAX_PTILE8(LAG, it, kb3, vb3, vb2, sk0, sv0, sk1, sv1, kb0, vb0, s8b, 0, 1) ++it; \
+            RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, sk0, sv0, kb1, vb1, s8a, 0, 1) ++it; \
         }                                                                                   \
         while (it < ntiles) {                                                               \
-            RAX_PTILE8(LAG, it, kb1, vb1, vb0, sk0, sv0, kb2, vb2, s8a, s8b, 1, 0) ++it;     \
+            RAX_PTILE8(LAG, it, kb1, vb1, vb0, sk0, sv0, sk1, sv1, kb2, vb2, s8b, 1, 0) ++it; \
             if (it >= ntiles) break;                                                        \
-            RAX_PTILE8(LAG, it, kb2, vb2, vb1, sk1, sv1, kb3, vb3, s8b, s8a, 1, 0) ++it;     \
+            RAX_PTILE8(LAG, it, kb2, vb2, vb1, sk1, sv1, sk0, sv0, kb3, vb3, s8a, 1, 0) ++it; \
             if (it >= ntiles) break;                                                        \
-            RAX_PTILE8(LAG, it, kb3, vb3, vb2, sk0, sv0, kb0, vb0, s8a, s8b, 1, 0) ++it;     \
+            RAX_PTILE8(LAG, it, kb3, vb3, vb2, sk0, sv0, sk1, sv1, kb0, vb0, s8b, 1, 0) ++it; \
             if (it >= ntiles) break;                                                        \
-            RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, kb1, vb1, s8b, s8a, 1, 0) ++it;     \
+            RAX_PTILE8(LAG, it, kb0, vb0, vb3, sk1, sv1, sk0, sv0, kb1, vb1, s8a, 1, 0) ++it; \
         }
         if (lag) {
             RAX_PLOOPS8(1)
