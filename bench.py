@@ -58,7 +58,7 @@ TRAFFIC_SUMMARIES = {
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", TRAFFIC_SUMMARIES[(4, "bf16")])
 CSRC = os.path.join(ROOT, "prefix_cached_paged_amd", "csrc")
 KERNEL_SOURCES = {
-    "extend_kernel": ["extend_attn.hip", "rax_device.h", "rax_launch.h"],
+    "extend_kernel": ["extend_attn_kernel.h", "rax_device.h", "rax_launch.h"],
     "decode_split_kernel": ["decode_attn.hip", "rax_device.h", "rax_launch.h"],
     "decode_merge_kernel": ["decode_attn.hip", "rax_device.h", "rax_launch.h"],
     "decode_plan_kernel": ["decode_attn.hip", "rax_device.h", "rax_launch.h"],

@@ -69,6 +69,13 @@ int launch_kv_store_fp8(const void* k_new, const void* v_new, const int32_t* loc
 // bf16, MFMA paths.
 bool extend_bf16_supported(int32_t group, int32_t head_dim);
 int launch_extend_bf16(const AttnArgs& a, hipStream_t stream);
+// per group size G (extend_g<G>.hip)
+int launch_extend_g1(const AttnArgs& a, hipStream_t stream);
+int launch_extend_g2(const AttnArgs& a, hipStream_t stream);
+int launch_extend_g4(const AttnArgs& a, hipStream_t stream);
+int launch_extend_g8(const AttnArgs& a, hipStream_t stream);
+int launch_extend_g16(const AttnArgs& a, hipStream_t stream);
+int launch_extend_g32(const AttnArgs& a, hipStream_t stream);
 
 bool decode_bf16_supported(int32_t group, int32_t head_dim);
 // Key ranges per group of kv heads the split kernel is launched with (bf16 or FP8 pools, which
