@@ -225,6 +225,8 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // D], the same row size as the pool), the prefix comes from the pool.
     const char* knbase = RAG ? k_new + (int64_t)g * D * EB : nullptr;
     const char* vnbase = RAG ? v_new + (int64_t)g * D * EB : nullptr;
+    const __amdgpu_buffer_rsrc_t knrsrc = pool_rsrc(RAG ? knbase : kbase);
+    const __amdgpu_buffer_rsrc_t vnrsrc = pool_rsrc(RAG ? vnbase : vbase);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -265,6 +267,45 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         const int p1_ = min((TILE) * kExtBN + 8 * wave + 4 + prow, kend - 1);              \
         S0 = slot_at<PG>(row, p0_, page_shift);                                            \
         S1 = slot_at<PG>(row, p1_, page_shift);                                            \
+    }
+    // Ragged suffix with 32-bit offsets: a copied row comes from the pool (prefix position) or
+    // from the new rows (suffix position), each through its own buffer resource. The two forms
+    // are the two arms of a per-lane branch, run under complementary lane masks (both arms only
+    // on the tile that straddles the prefix end), so a tile still issues at least the 4 copies
+    // the explicit waits count. As the compiler must assume either arm may be skipped, its own
+    // waits for the slot registers count no copy: the offsets of both rows are therefore formed
+    // before any of the tile's copies is issued (and, in the loop, before the next slot loads).
+#define RAX_RADDR(TILE, S0, S1, N0, N1, O0, O1)                                             \
+    {                                                                                       \
+        const int ps0_ = min((TILE) * kExtBN + 8 * wave + prow, kend - 1);                 \
+        const int ps1_ = min((TILE) * kExtBN + 8 * wave + 4 + prow, kend - 1);             \
+        N0 = ps0_ >= p;                                                                     \
+        N1 = ps1_ >= p;                                                                     \
+        O0 = __umul24((uint32_t)(N0 ? s0 + ps0_ - p : (S0)), row_bytes);                   \
+        O1 = __umul24((uint32_t)(N1 ? s0 + ps1_ - p : (S1)), row_bytes);                   \
+    }
+#define RAX_RISSUE(KB, VB, N0, N1, O0, O1)                                                  \
+    {                                                                                       \
+        char* kd_ = (char*)(KB) + (8 * wave_u) * 256;                                       \
+        char* vd_ = (char*)(VB) + (8 * wave_u) * 256;                                       \
+        /* the empty statement in one arm keeps the compiler from merging the arms into */  \
+        /* one copy with a per-lane resource (a loop over the distinct resources) */         \
+        if (N0) {                                                                           \
+            lds_dma16_buf(knrsrc, (O0) + k_src0, kd_);                                      \
+            lds_dma16_buf(vnrsrc, (O0) + v_src, vd_);                                       \
+            asm volatile("" ::: "memory");                                                  \
+        } else {                                                                            \
+            lds_dma16_buf(krsrc, (O0) + k_src0, kd_);                                       \
+            lds_dma16_buf(vrsrc, (O0) + v_src, vd_);                                        \
+        }                                                                                   \
+        if (N1) {                                                                           \
+            lds_dma16_buf(knrsrc, (O1) + k_src1, kd_ + 1024);                               \
+            lds_dma16_buf(vnrsrc, (O1) + v_src, vd_ + 1024);                                \
+            asm volatile("" ::: "memory");                                                  \
+        } else {                                                                            \
+            lds_dma16_buf(krsrc, (O1) + k_src1, kd_ + 1024);                                \
+            lds_dma16_buf(vrsrc, (O1) + v_src, vd_ + 1024);                                 \
+        }                                                                                   \
     }
 #define RAX_VCOPY(KB, VB, TILE, S0, S1)                                                     \
     {                                                                                       \
@@ -505,8 +546,19 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         }                                                                                   \
         RAX_BARRIER();                                                                      \
         RAX_PCOMPUTE(LAG, IT, KB, VB, VP, MASKABLE, STEADY)                                 \
-        if (STEADY || (IT) + 3 < ntiles) RAX_VSLOTS((IT) + 3, SL0, SL1)                     \
-        if (STEADY || (IT) + 2 < ntiles) RAX_VCOPY(KN, VN, (IT) + 2, SU0, SU1)              \
+        if constexpr (RAG && OFF32) {                                                       \
+            bool rn0_ = false, rn1_ = false;                                                \
+            uint32_t ro0_ = 0, ro1_ = 0;                                                    \
+            if (STEADY || (IT) + 2 < ntiles) {                                              \
+                RAX_RADDR((IT) + 2, SU0, SU1, rn0_, rn1_, ro0_, ro1_)                       \
+                asm volatile("" ::"v"(ro0_), "v"(ro1_) : "memory");                        \
+            }                                                                               \
+            if (STEADY || (IT) + 3 < ntiles) RAX_VSLOTS((IT) + 3, SL0, SL1)                 \
+            if (STEADY || (IT) + 2 < ntiles) RAX_RISSUE(KN, VN, rn0_, rn1_, ro0_, ro1_)     \
+        } else {                                                                            \
+            if (STEADY || (IT) + 3 < ntiles) RAX_VSLOTS((IT) + 3, SL0, SL1)                 \
+            if (STEADY || (IT) + 2 < ntiles) RAX_VCOPY(KN, VN, (IT) + 2, SU0, SU1)          \
+        }                                                                                   \
     }
     // FP8 pools: tile T is staged (E4M3) in buffer T % 2 and widened into bf16 buffer T % 4;
     // its slot is held in register set T % 2. Iteration IT: barrier (every wave's widening of
@@ -574,8 +626,19 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
         int sl_a0, sl_a1, sl_b0, sl_b1;  // slot register sets 0 (a) and 1 (b)
         RAX_VSLOTS(0, sl_a0, sl_a1)
         if (ntiles > 1) RAX_VSLOTS(1, sl_b0, sl_b1)
-        RAX_VCOPY(kb0, vb0, 0, sl_a0, sl_a1)
-        if (ntiles > 1) RAX_VCOPY(kb1, vb1, 1, sl_b0, sl_b1)
+        if constexpr (RAG && OFF32) {
+            // both tiles' offsets before the first copy (see RAX_RADDR)
+            bool n0a, n1a, n0b = false, n1b = false;
+            uint32_t o0a, o1a, o0b = 0, o1b = 0;
+            RAX_RADDR(0, sl_a0, sl_a1, n0a, n1a, o0a, o1a)
+            if (ntiles > 1) RAX_RADDR(1, sl_b0, sl_b1, n0b, n1b, o0b, o1b)
+            asm volatile("" ::"v"(o0a), "v"(o1a), "v"(o0b), "v"(o1b) : "memory");
+            RAX_RISSUE(kb0, vb0, n0a, n1a, o0a, o1a)
+            if (ntiles > 1) RAX_RISSUE(kb1, vb1, n0b, n1b, o0b, o1b)
+        } else {
+            RAX_VCOPY(kb0, vb0, 0, sl_a0, sl_a1)
+            if (ntiles > 1) RAX_VCOPY(kb1, vb1, 1, sl_b0, sl_b1)
+        }
         if (ntiles > 2) RAX_VSLOTS(2, sl_a0, sl_a1)
         // Tile T lives in buffer T % 4; iteration T starts the copy of tile T+2 into buffer
         // (T+2) % 4 with slot set (T+2) % 2 and loads the slots of tile T+3 into set (T+3) % 2.
@@ -697,6 +760,8 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
 }
 #undef RAX_VSLOTS
 #undef RAX_VCOPY
+#undef RAX_RADDR
+#undef RAX_RISSUE
 #undef RAX_QK
 #undef RAX_SM
 #undef RAX_PEXP
