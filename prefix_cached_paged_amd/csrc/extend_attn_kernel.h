@@ -597,6 +597,8 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
                 RAX_SM((IT) - 1, MASKABLE) RAX_PV(VP)                                       \
             }                                                                               \
             RAX_WIDEN8(IT, SC, SVC, KN, VN, SS, STEADY)                                     \
+            /* the staging reads would fill the first LDS-read group of the scores */       \
+            __builtin_amdgcn_sched_barrier(0);                                              \
             RAX_QK(KB)                                                                      \
         } else {                                                                            \
             RAX_COMPUTE(IT, KB, VB, MASKABLE)                                               \
