@@ -21,8 +21,8 @@
  *   head h reads kv head h / (n_q_heads / n_kv_heads) (contiguous groups: grouped-query
  *   attention, "Inside SGLang", Step 3).
  * - Kernels exist for (group G = n_q_heads / n_kv_heads): fp32 EXTEND and DECODE, any G and
- *   head_dim 64 or 128; bf16 EXTEND (plain, ragged and paged), head_dim 64 or 128, and FP8-pool
- *   EXTEND, head_dim 128, with G in {1, 2, 4, 8, 16, 32}; bf16 (and FP8-pool) DECODE, head_dim 64
+ *   head_dim 64 or 128; bf16 EXTEND (plain, ragged and paged) and FP8-pool EXTEND, head_dim 64
+ *   or 128, with G in {1, 2, 4, 8, 16, 32}; bf16 (and FP8-pool) DECODE, head_dim 64
  *   or 128 and G from 1 to 16. Any other valid shape
  *   returns RAX_ERR_UNSUPPORTED before anything is enqueued.
  * - `stream` is a hipStream_t (NULL = the null stream). Every call only ENQUEUES work on it:
@@ -311,7 +311,7 @@ rax_status rax_decode_attention_paged(rax_dtype dtype, const void* q, void* o, c
  *   computed in double and rounded once to float. Inputs must be finite (NaN inputs give an
  *   undefined byte). Same loc contract as rax_kv_store.
  *
- * rax_extend_attention_fp8 -- rax_extend_attention over FP8 pools (head_dim 128, the same
+ * rax_extend_attention_fp8 -- rax_extend_attention over FP8 pools (the same head_dims and
  *   group sizes as bf16): the scores use k_scale * e4m3(K) and the values v_scale * e4m3(V).
  *   The kernel stages the E4M3 tiles in LDS, widens them to bf16 (exact) and applies k_scale to
  *   the scores and v_scale to the output. Workspace: rax_extend_workspace_bytes(RAX_FP8_E4M3,

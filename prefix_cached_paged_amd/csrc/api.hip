@@ -109,7 +109,6 @@ rax_status extend_call(int dtype, bool kv8, const void* q, void* o, const void* 
     if (st != RAX_OK) return st;
     const int32_t G = n_q_heads / n_kv_heads;
     if (dtype == RAX_BF16 && !rax::extend_bf16_supported(G, head_dim)) return RAX_ERR_UNSUPPORTED;
-    if (kv8 && head_dim != 128) return RAX_ERR_UNSUPPORTED;  // FP8-pool EXTEND: head_dim 128
     if (!(sm_scale == sm_scale)) return RAX_ERR_SHAPE;
     if (kv8 && (!scale_ok(k_scale) || !scale_ok(v_scale))) return RAX_ERR_SHAPE;
     if (batch == 0 || total_extend_tokens == 0 || max_extend_len == 0) return RAX_OK;

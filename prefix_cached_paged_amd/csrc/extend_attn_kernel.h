@@ -181,7 +181,6 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // and the copy lanes of units 8-15 fetch a copy of units 0-7, so no copy leaves its row.
     constexpr int D = DH;
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-    static_assert(!(KV8 && D != 128), "FP8 pools: head_dim 128");
     constexpr int BQ = kExtBM / G;  // tokens per workgroup
     constexpr int EB = KV8 ? 1 : 2;  // bytes per pool element
     static_assert(!(KV8 && RAG), "ragged suffix rows are bf16, as the pools");
@@ -338,9 +337,11 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // FP8 pools: a 64-key tile is 8 KB per operand, so one copy instruction per wave moves
     // its eight rows: lane l fetches 16 bytes at offset 16 (l % 8) of row 8 w + l / 8 into
     // staging unit 64 w + l. The lane's slot comes through a per-lane vector load (tile T's in
-    // register set T % 2), as for bf16 pools. Per wave and tile: 1 slot load, 2 copies.
+    // register set T % 2), as for bf16 pools. Per wave and tile: 1 slot load, 2 copies. With
+    // head_dim 64 a row is 4 units: lanes of units 4-7 fetch a copy of units 0-3, whose
+    // widening lands in logical units 8-15 of the bf16 row, which head_dim 64 does not read.
     const int q8 = lane >> 3;
-    const uint32_t src8 = 16u * (uint32_t)(lane & 7);
+    const uint32_t src8 = 16u * (uint32_t)(lane & 7 & (D / 16 - 1));
 #define RAX_VSLOT8(TILE, S)                                                                 \
     {                                                                                       \
         S = slot_at<PG>(row, min((TILE) * kExtBN + 8 * wave + q8, kend - 1), page_shift);   \
@@ -805,14 +806,10 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
 template <int DH, int G>
 int launch_g(const AttnArgs& a, hipStream_t stream) {
     if (a.kv8) {
-        if constexpr (DH != 128) {
-            return -1;  // FP8 pools: head_dim 128
-        } else {
-            if (a.ragged || a.page_shift) return -1;
-            return pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 1)
-                       ? launch_g<DH, G, true, true, false, false>(a, stream)
-                       : launch_g<DH, G, false, true, false, false>(a, stream);
-        }
+        if (a.ragged || a.page_shift) return -1;
+        return pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 1)
+                   ? launch_g<DH, G, true, true, false, false>(a, stream)
+                   : launch_g<DH, G, false, true, false, false>(a, stream);
     }
     // ragged: the new rows are addressed like pool rows (row index total_tokens - 1 at most)
     const bool off32 = pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 2) &&

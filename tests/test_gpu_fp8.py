@@ -147,6 +147,9 @@ EXT_SPECS = [
     W.Spec("fp8-ext-g16", "bf16", 16, 1, 128, 30000, extend_prefix=(129, 0, 2000), extend_lens=(20, 17, 70)),
     W.Spec("fp8-ext-g32", "bf16", 32, 1, 128, 30000, extend_prefix=(0, 700), extend_lens=(40, 9)),
     W.Spec("fp8-ext-short", "bf16", 32, 8, 128, 30000, extend_prefix=(0, 0, 64, 100), extend_lens=(1, 64, 64, 28)),
+    # head_dim 64: four E4M3 units per row, the copy lanes of units 4-7 repeat units 0-3
+    W.Spec("fp8-ext-d64-g4", "bf16", 32, 8, 64, 60000, extend_prefix=(0, 63, 500), extend_lens=(129, 65, 300)),
+    W.Spec("fp8-ext-d64-g1", "bf16", 4, 4, 64, 30000, extend_prefix=(37, 0), extend_lens=(200, 1)),
 ]
 
 
