@@ -14,7 +14,8 @@ decode_attention_fp8; per-pool scales 4 sigma / 448), the pools converted from t
 before timing. ``--ragged`` runs EXTEND on the ragged path: the suffix K/V read from the new
 rows and stored by the same kernel (extend_attention_ragged with store_loc); kv_store then
 writes only the decode requests' current tokens. ``--page-size P`` draws the workload with
-pages of P slots and runs EXTEND and DECODE through the page table (the _paged calls).
+pages of P slots and runs EXTEND and DECODE through the page table (the _paged calls; with
+``--kv fp8`` the _paged_fp8 calls).
 ``--cold`` sweeps a 1 GiB buffer (read and write, four times the 256 MB last-level cache)
 before every step, outside the kernels' event windows, so the per-kernel figures are
 cold-cache ones; ms_per_step then includes the sweeps.
@@ -446,8 +447,8 @@ def main():
         spec = dataclasses.replace(spec, page_size=args.page_size)
     kv8 = args.kv == "fp8"
     paged = args.page_size != 1
-    if paged and (kv8 or args.ragged):
-        print("--page-size runs the bf16/fp32 pool path only", file=sys.stderr)
+    if paged and args.ragged:
+        print("--ragged reads the prefix through a token table (no --page-size)", file=sys.stderr)
         sys.exit(2)
     if args.ragged and kv8:
         print("--ragged is for bf16/fp32 pools", file=sys.stderr)
@@ -518,7 +519,10 @@ def main():
             e = dw.ext
             ea = (e["q"], e["o"], dw.k_pool, dw.v_pool, dw.req_to_token, e["req_pool_indices"], e["prefix_lens"],
                   e["extend_lens"], e["extend_start_loc"], e["max_extend_len"], e["max_seq_len"], wl.sm_scale)
-            if kv8:
+            if kv8 and paged:
+                rax.extend_attention_paged_fp8(e["q"], e["o"], dw.k_pool, dw.v_pool, pt, args.page_size, *ea[5:],
+                                               k_scale, v_scale)
+            elif kv8:
                 rax.extend_attention_fp8(*ea, k_scale, v_scale)
             elif rag:
                 rax.extend_attention_ragged(e["q"], e["o"], dw.k_new[:n_ext], dw.v_new[:n_ext], dw.k_pool,
@@ -533,7 +537,10 @@ def main():
             d = dw.dec
             da = (d["q"], d["o"], dw.k_pool, dw.v_pool, dw.req_to_token, d["req_pool_indices"], d["seq_lens"],
                   d["max_seq_len"], wl.sm_scale)
-            if kv8:
+            if kv8 and paged:
+                rax.decode_attention_paged_fp8(d["q"], d["o"], dw.k_pool, dw.v_pool, pt, args.page_size, *da[5:],
+                                               k_scale, v_scale, workspace=ws)
+            elif kv8:
                 rax.decode_attention_fp8(*da, k_scale, v_scale, workspace=ws)
             elif paged:
                 rax.decode_attention_paged(d["q"], d["o"], dw.k_pool, dw.v_pool, pt, args.page_size, *da[5:],

@@ -277,7 +277,8 @@ rax_status rax_decode_attention_noalloc(rax_dtype dtype, const void* q, void* o,
  *   page_table    int32 (device), row stride pt_stride entries; pt_stride * P >= max_seq_len.
  *   page_size     P, a power of two from 1 to 2^20 (else RAX_ERR_SHAPE).
  * Device-side CONTRACT: the entries for positions 0 .. L-1 of each used row are pages with
- *   page * P + P <= num_slots. bf16 (MFMA kernels) and fp32.
+ *   page * P + P <= num_slots. bf16 (MFMA kernels) and fp32; FP8 pools through
+ *   rax_extend_attention_paged_fp8 / rax_decode_attention_paged_fp8 (below).
  */
 rax_status rax_extend_attention_paged(rax_dtype dtype, const void* q, void* o, const void* k_pool,
                                       const void* v_pool, int64_t num_slots, const int32_t* page_table,
@@ -341,6 +342,33 @@ rax_status rax_decode_attention_fp8(const void* q, void* o, const void* k_pool, 
                                     int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
                                     int32_t head_dim, float sm_scale, float k_scale, float v_scale,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * rax_extend_attention_paged_fp8, rax_decode_attention_paged_fp8 -- the FP8-pool calls above
+ * with a page table of page_size slots per page in place of the token table: the arguments of
+ * rax_extend_attention_fp8 / rax_decode_attention_fp8 with (page_table, pt_stride, page_size)
+ * as in rax_extend_attention_paged, and the same scales, contract and errors (a page size that
+ * is not a power of two from 1 to 2^20 gives RAX_ERR_SHAPE). The two options of the pages
+ * together: pages of P slots ("A walkthrough of SGLang", Exercises, exercise 2) over an FP8
+ * cache ("Inside SGLang", Step 6).
+ */
+rax_status rax_extend_attention_paged_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                          int64_t num_slots, const int32_t* page_table, int64_t pt_stride,
+                                          int32_t page_size, const int32_t* req_pool_indices,
+                                          const int32_t* prefix_lens, const int32_t* extend_lens,
+                                          const int32_t* extend_start_loc, int32_t batch,
+                                          int64_t total_extend_tokens, int32_t max_extend_len,
+                                          int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                          int32_t head_dim, float sm_scale, float k_scale, float v_scale,
+                                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+rax_status rax_decode_attention_paged_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                          int64_t num_slots, const int32_t* page_table, int64_t pt_stride,
+                                          int32_t page_size, const int32_t* req_pool_indices,
+                                          const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                          int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                          float sm_scale, float k_scale, float v_scale, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream);
 
 /* Number of key ranges per group of kv heads that rax_decode_attention launches for these
  * shapes (bf16; 1 for fp32 or empty shapes; -1 if the shapes need more than 2^31 - 1). Ranges

@@ -234,7 +234,6 @@ __global__ __launch_bounds__(64 * kDecWaves, KV8 ? RAX_DEC_WGS_PER_CU8 : RAX_DEC
     float scale_log2, float out_scale, int64_t* __restrict__ meta, int64_t* __restrict__ P,
     const int32_t* __restrict__ first_req, float* __restrict__ o_part,
     float* __restrict__ lse_part, int32_t page_shift) {
-    static_assert(!(PG && KV8), "page tables are read by the bf16 pool path");
     constexpr int S = D / 32;   // 32-wide K-dim steps of the score MFMA
     constexpr int DT = D / 16;  // 16-row output tiles; also head_dim elements per lane per V row
     __shared__ int32_t slot_lds[kDecMaxKeys + kDecKeysPerIter];
@@ -726,7 +725,6 @@ size_t decode_workspace(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, i
 }
 
 int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
-    if (a.kv8 && a.page_shift) return -1;
     const int32_t G = a.n_q_heads / a.n_kv_heads;
     const int32_t groups = decode_groups(a.n_kv_heads);
     const int32_t grid = decode_grid(a.batch, a.max_seq_len, a.n_kv_heads, a.kv8);
@@ -758,7 +756,8 @@ int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
                        n_target, scale_log2, out_scale, meta, P, first, o_part, lse, a.page_shift)
 #define RAX_DEC_SPLIT3(DD, OFF, FU)                                                             \
     do {                                                                                        \
-        if (a.kv8) RAX_DEC_SPLIT4(DD, OFF, FU, true, false);                                    \
+        if (a.kv8 && a.page_shift) RAX_DEC_SPLIT4(DD, OFF, FU, true, true);                     \
+        else if (a.kv8) RAX_DEC_SPLIT4(DD, OFF, FU, true, false);                               \
         else if (a.page_shift) RAX_DEC_SPLIT4(DD, OFF, FU, false, true);                        \
         else RAX_DEC_SPLIT4(DD, OFF, FU, false, false);                                         \
     } while (0)

@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     constexpr int BQ = kExtBM / G;  // tokens per workgroup
     constexpr int EB = KV8 ? 1 : 2;  // bytes per pool element
     static_assert(!(KV8 && RAG), "ragged suffix rows are bf16, as the pools");
-    static_assert(!(PG && (KV8 || RAG)), "page tables are read by the bf16 pool path");
+    static_assert(!(PG && RAG), "the ragged suffix is read through a token table");
 
     // Three K/V tile buffers, row-major [key][16 units of 8 bf16], swizzled. Separate LDS
     // objects, each named statically below.
@@ -806,10 +806,13 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
 template <int DH, int G>
 int launch_g(const AttnArgs& a, hipStream_t stream) {
     if (a.kv8) {
-        if (a.ragged || a.page_shift) return -1;
-        return pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 1)
-                   ? launch_g<DH, G, true, true, false, false>(a, stream)
-                   : launch_g<DH, G, false, true, false, false>(a, stream);
+        if (a.ragged) return -1;
+        const bool off8 = pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 1);
+        if (a.page_shift)
+            return off8 ? launch_g<DH, G, true, true, false, true>(a, stream)
+                        : launch_g<DH, G, false, true, false, true>(a, stream);
+        return off8 ? launch_g<DH, G, true, true, false, false>(a, stream)
+                    : launch_g<DH, G, false, true, false, false>(a, stream);
     }
     // ragged: the new rows are addressed like pool rows (row index total_tokens - 1 at most)
     const bool off32 = pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 2) &&

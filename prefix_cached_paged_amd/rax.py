@@ -70,6 +70,13 @@ _SIGS = {
     "rax_decode_attention_fp8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_p,
                                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f, _c_f, _c_f,
                                                 _c_p, _c_sz, _c_p]),
+    "rax_extend_attention_paged_fp8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_i32,
+                                                      _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64, _c_i32, _c_i32,
+                                                      _c_i32, _c_i32, _c_i32, _c_f, _c_f, _c_f, _c_p, _c_sz,
+                                                      _c_p]),
+    "rax_decode_attention_paged_fp8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_i32,
+                                                      _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f,
+                                                      _c_f, _c_f, _c_p, _c_sz, _c_p]),
     "rax_check_workspace_bytes": (_c_sz, [_c_i64]),
     "rax_check_kv_store": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_sz, _c_p, _c_p]),
     "rax_check_extend": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64,
@@ -406,6 +413,44 @@ def decode_attention_fp8(q, o, k_pool, v_pool, req_to_token, req_pool_indices, s
                                            float(k_scale), float(v_scale), _ptr(workspace), wbytes,
                                            _stream(stream, q.device)),
            "rax_decode_attention_fp8")
+
+
+def extend_attention_paged_fp8(q, o, k_pool, v_pool, page_table, page_size, req_pool_indices, prefix_lens,
+                               extend_lens, extend_start_loc, max_extend_len, max_seq_len, sm_scale, k_scale=1.0,
+                               v_scale=1.0, workspace=None, stream=None):
+    """EXTEND over FP8 E4M3 pools with keys addressed through a page table of ``page_size`` slots."""
+    N, Hq, D, S, Hkv = _attn_shapes(q, o, k_pool, v_pool)
+    B = prefix_lens.shape[0]
+    _per_request(B, req_pool_indices, prefix_lens, extend_lens, extend_start_loc)
+    _table(page_table)
+    need = extend_workspace_bytes(FP8_E4M3, B, N, max_extend_len, max_seq_len, Hq, Hkv, D)
+    workspace = _workspace(need, workspace, q.device, stream)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().rax_extend_attention_paged_fp8(_bf16(q), _bf16(o), _fp8_pool(k_pool), _fp8_pool(v_pool), S,
+                                                 _idx(page_table), page_table.shape[1], int(page_size),
+                                                 _idx(req_pool_indices), _idx(prefix_lens), _idx(extend_lens),
+                                                 _idx(extend_start_loc), B, N, int(max_extend_len),
+                                                 int(max_seq_len), Hq, Hkv, D, float(sm_scale), float(k_scale),
+                                                 float(v_scale), _ptr(workspace), wbytes,
+                                                 _stream(stream, q.device)),
+           "rax_extend_attention_paged_fp8")
+
+
+def decode_attention_paged_fp8(q, o, k_pool, v_pool, page_table, page_size, req_pool_indices, seq_lens,
+                               max_seq_len, sm_scale, k_scale=1.0, v_scale=1.0, workspace=None, stream=None):
+    """DECODE over FP8 E4M3 pools with keys addressed through a page table of ``page_size`` slots."""
+    B, Hq, D, S, Hkv = _attn_shapes(q, o, k_pool, v_pool)
+    _per_request(B, req_pool_indices, seq_lens)
+    _table(page_table)
+    need = decode_workspace_bytes(FP8_E4M3, B, int(max_seq_len), Hq, Hkv, D)
+    workspace = _workspace(need, workspace, q.device, stream)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().rax_decode_attention_paged_fp8(_bf16(q), _bf16(o), _fp8_pool(k_pool), _fp8_pool(v_pool), S,
+                                                 _idx(page_table), page_table.shape[1], int(page_size),
+                                                 _idx(req_pool_indices), _idx(seq_lens), B, int(max_seq_len), Hq,
+                                                 Hkv, D, float(sm_scale), float(k_scale), float(v_scale),
+                                                 _ptr(workspace), wbytes, _stream(stream, q.device)),
+           "rax_decode_attention_paged_fp8")
 
 
 # Debug checks of the device-side contracts: counts per kind (order of rax_check_item).

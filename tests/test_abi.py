@@ -25,6 +25,7 @@ def test_every_declared_symbol_is_exported():
                           "rax_decode_num_splits", "rax_kv_store_fp8", "rax_extend_attention_fp8",
                           "rax_decode_attention_fp8", "rax_extend_attention_ragged",
                           "rax_extend_attention_paged", "rax_decode_attention_paged",
+                          "rax_extend_attention_paged_fp8", "rax_decode_attention_paged_fp8",
                           "rax_check_workspace_bytes", "rax_check_kv_store", "rax_check_extend",
                           "rax_check_decode", "rax_decode_attention_noalloc"}
     out = subprocess.run(["nm", "-D", "--defined-only", R.library_path()], capture_output=True, text=True).stdout
@@ -208,6 +209,34 @@ def test_paged_calls_check_page_size_and_table_width():
                                                     1 << 30, None)
     assert dec(P=48) == 2
     assert dec(L=513) == 2               # 8 pages of 64
+    assert dec(B=0) == 0
+    assert dec(pt=None) == 1
+
+
+def test_paged_fp8_calls_check_page_size_scales_and_table_width():
+    L = lib()
+    # (q, o, kp, vp, S, pt, pt_stride, P, rpi, pre, ext, start, B, N, maxe, maxL, Hq, Hkv, D, sm, ks, vs, ws, wsb,
+    #  stream)
+    ext = lambda **kw: L.rax_extend_attention_paged_fp8(FAKE, FAKE, FAKE, FAKE, 4096, kw.get("pt", FAKE),
+                                                        kw.get("stride", 32), kw.get("P", 16), FAKE, FAKE, FAKE,
+                                                        FAKE, kw.get("B", 3), 100, 50, kw.get("L", 300), 8, 2,
+                                                        kw.get("D", 128), 0.1, kw.get("ks", 1.0), 1.0, None, 0,
+                                                        None)
+    for bad in (0, 3, 12, -16, 1 << 21):
+        assert ext(P=bad) == 2, bad
+    assert ext(L=600) == 2               # 32 pages of 16 cover 512 positions only
+    assert ext(ks=0.0) == 2 and ext(ks=float("inf")) == 2
+    assert ext(D=32) == 4
+    assert ext(B=0) == 0
+    assert ext(pt=None) == 1
+    # (q, o, kp, vp, S, pt, pt_stride, P, rpi, seq, B, maxL, Hq, Hkv, D, sm, ks, vs, ws, wsb, stream)
+    dec = lambda **kw: L.rax_decode_attention_paged_fp8(FAKE, FAKE, FAKE, FAKE, 4096, kw.get("pt", FAKE),
+                                                        kw.get("stride", 8), kw.get("P", 64), FAKE, FAKE,
+                                                        kw.get("B", 3), kw.get("L", 512), 8, 2, 128, 0.1, 1.0,
+                                                        kw.get("vs", 1.0), FAKE, 1 << 30, None)
+    assert dec(P=48) == 2
+    assert dec(L=513) == 2               # 8 pages of 64
+    assert dec(vs=-1.0) == 2
     assert dec(B=0) == 0
     assert dec(pt=None) == 1
 

@@ -176,3 +176,53 @@ def test_extend_fp8_first_row_is_v_times_scale():
     first = np.asarray(wl.extend.extend_start_loc)
     assert np.array_equal(got[first], ref[first])
     assert_close(got, ref, "bf16", "fp8 extend, one key")
+
+
+# FP8 pools through page tables: page sizes 8 to 64, both head_dims, EXTEND and DECODE in one
+# workload. Against the oracle over the same bytes, and bit for bit against the token-table
+# FP8 calls on the same slots.
+PAGED_SPECS = [
+    W.Spec("fp8-pg16-g4", "bf16", 32, 8, 128, 65536, extend_prefix=(0, 63, 500), extend_lens=(129, 65, 300),
+           decode_lens=(1, 17, 2500), page_size=16),
+    W.Spec("fp8-pg64-g8", "bf16", 64, 8, 128, 65536, extend_prefix=(1000, 0), extend_lens=(33, 64),
+           decode_lens=(5, 513, 4000), page_size=64),
+    W.Spec("fp8-pg8-d64-g4", "bf16", 16, 4, 64, 65536, extend_prefix=(37, 0), extend_lens=(200, 1),
+           decode_lens=(64, 999), page_size=8),
+]
+
+
+@pytest.mark.parametrize("variant", ["normal", "peaked", "needle"])
+@pytest.mark.parametrize("spec", PAGED_SPECS, ids=lambda s: s.name)
+def test_paged_fp8(spec, variant):
+    wl = W.make_workload(spec, 706, variant)
+    k_scale = v_scale = 4 * spec.sigma / 448
+    if variant == "needle":
+        k_scale = 16.0 / 448
+    P = spec.page_size
+    say(f"paged fp8 {spec.name}/{variant}: P={P}")
+    kp, vp = fp8_pools(wl, k_scale, v_scale)
+    dk, dv = to_dev(kp), to_dev(vp)
+    R.kv_store_fp8(to_dev(wl.k_new), to_dev(wl.v_new), to_dev(wl.store_loc), dk, dv, k_scale, v_scale)
+    ref_k, ref_v = oracle.kv_store_fp8(kp, vp, wl.k_new, wl.v_new, wl.store_loc, k_scale, v_scale)
+    pt, r2t = to_dev(wl.page_table), to_dev(wl.req_to_token)
+    e, d = wl.extend, wl.decode
+    qe, qd = to_dev(e.q), to_dev(d.q)
+    oe, oe_tok = torch.full_like(qe, float("nan")), torch.full_like(qe, float("nan"))
+    od, od_tok = torch.empty_like(qd), torch.empty_like(qd)
+    per = (to_dev(e.req_pool_indices), to_dev(e.prefix_lens), to_dev(e.extend_lens), to_dev(e.extend_start_loc),
+           int(np.max(e.extend_lens)), int(np.max(e.prefix_lens + e.extend_lens)), wl.sm_scale, k_scale, v_scale)
+    R.extend_attention_paged_fp8(qe, oe, dk, dv, pt, P, *per)
+    R.extend_attention_fp8(qe, oe_tok, dk, dv, r2t, *per)
+    dper = (to_dev(d.req_pool_indices), to_dev(d.seq_lens), d.max_seq_len, wl.sm_scale, k_scale, v_scale)
+    R.decode_attention_paged_fp8(qd, od, dk, dv, pt, P, *dper)
+    R.decode_attention_fp8(qd, od_tok, dk, dv, r2t, *dper)
+    torch.cuda.synchronize()
+    ref_e = oracle.extend_attention_paged(e.q, ref_k, ref_v, wl.page_table, P, e.req_pool_indices, e.prefix_lens,
+                                          e.extend_lens, e.extend_start_loc, spec.n_kv_heads, wl.sm_scale,
+                                          k_scale=k_scale, v_scale=v_scale)
+    ref_d = oracle.decode_attention_paged(d.q, ref_k, ref_v, wl.page_table, P, d.req_pool_indices, d.seq_lens,
+                                          spec.n_kv_heads, wl.sm_scale, k_scale=k_scale, v_scale=v_scale)
+    assert_close(oracle.to_f64(to_host_bits(oe)), ref_e, "bf16", f"{spec.name}/{variant} paged fp8 extend")
+    assert_close(oracle.to_f64(to_host_bits(od)), ref_d, "bf16", f"{spec.name}/{variant} paged fp8 decode")
+    assert torch.equal(oe.view(torch.int16), oe_tok.view(torch.int16)), "paged and token-table FP8 EXTEND differ"
+    assert torch.equal(od.view(torch.int16), od_tok.view(torch.int16)), "paged and token-table FP8 DECODE differ"
