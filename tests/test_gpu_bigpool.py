@@ -1,5 +1,5 @@
-"""Pools above 4 GiB for the token-table, FP8, page-table and ragged calls (the 64-bit addressing
-kernels).
+"""Pools above 4 GiB for the token-table, FP8, page-table (bf16 and FP8) and ragged calls (the
+64-bit addressing kernels).
 
 A small seeded workload is spread over a large device pool by an affine slot map
 s -> a * s + b (for page tables, pages p -> a * p + b, positions inside a page unchanged), so
@@ -74,6 +74,52 @@ def test_fp8_extend_and_decode_pool_beyond_4gib():
                                     wl.sm_scale, k_scale=ks, v_scale=vs)
     assert_close(oracle.to_f64(to_host_bits(oe)), ref_e, "bf16", "big FP8 extend")
     assert_close(oracle.to_f64(to_host_bits(od)), ref_d, "bf16", "big FP8 decode")
+
+
+def test_fp8_paged_pool_beyond_4gib():
+    """FP8 pools through a page table, pages mapped beyond byte 2^32 of the E4M3 pools."""
+    P = 16
+    spec = W.Spec("big-fp8-pg", "bf16", 32, 8, 128, 32768, extend_prefix=(2000, 0), extend_lens=(300, 100),
+                  decode_lens=(3000, 1, 40), page_size=P)
+    wl = W.make_workload(spec, 813)
+    n_big, a, b = 4_600_000, 139, 5              # slots; 4.6 GB per E4M3 pool
+    max_page = (32768 // P - 1) * a + b
+    assert max_page < n_big // P and max_page * P > (1 << 32) // (8 * 128)
+    slot_map = lambda s: np.where(np.asarray(s) >= 0, (np.asarray(s, np.int64) // P * a + b) * P + np.asarray(s) % P,
+                                  -1).astype(np.int64)
+    ks = vs = 4.0 * spec.sigma / 448
+    used = np.unique(wl.req_to_token[wl.req_to_token >= 0]).astype(np.int64)
+    rows = np.setdiff1d(used, wl.store_loc.astype(np.int64))
+    kp8 = np.full(wl.k_pool.shape, 0x7F, np.uint8)
+    vp8 = np.full(wl.v_pool.shape, 0x7F, np.uint8)
+    kp8[rows] = oracle.quantize_bf16(wl.k_pool[rows], ks)
+    vp8[rows] = oracle.quantize_bf16(wl.v_pool[rows], vs)
+    say("big FP8 pools, page table: filling on the device")
+    dk = torch.full((n_big, 8, 128), 0x7F, dtype=torch.uint8, device="cuda")
+    dv = torch.full_like(dk, 0x7F)
+    idx = torch.from_numpy(slot_map(np.arange(32768))).cuda()
+    dk[idx] = to_dev(kp8)
+    dv[idx] = to_dev(vp8)
+    R.kv_store_fp8(to_dev(wl.k_new), to_dev(wl.v_new), to_dev(slot_map(wl.store_loc).astype(np.int32)), dk, dv,
+                   ks, vs)
+    pt = to_dev(remap(wl.page_table, a, b))
+    e, d = wl.extend, wl.decode
+    qe, qd = to_dev(e.q), to_dev(d.q)
+    oe, od = torch.empty_like(qe), torch.empty_like(qd)
+    say("big FP8 pools, page table: extend and decode")
+    R.extend_attention_paged_fp8(qe, oe, dk, dv, pt, P, to_dev(e.req_pool_indices), to_dev(e.prefix_lens),
+                                 to_dev(e.extend_lens), to_dev(e.extend_start_loc), e.max_extend_len, e.max_seq_len,
+                                 wl.sm_scale, ks, vs)
+    R.decode_attention_paged_fp8(qd, od, dk, dv, pt, P, to_dev(d.req_pool_indices), to_dev(d.seq_lens),
+                                 d.max_seq_len, wl.sm_scale, ks, vs)
+    torch.cuda.synchronize()
+    rk, rv = oracle.kv_store_fp8(kp8, vp8, wl.k_new, wl.v_new, wl.store_loc, ks, vs)
+    ref_e = oracle.extend_attention(e.q, rk, rv, wl.req_to_token, e.req_pool_indices, e.prefix_lens, e.extend_lens,
+                                    e.extend_start_loc, spec.n_kv_heads, wl.sm_scale, k_scale=ks, v_scale=vs)
+    ref_d = oracle.decode_attention(d.q, rk, rv, wl.req_to_token, d.req_pool_indices, d.seq_lens, spec.n_kv_heads,
+                                    wl.sm_scale, k_scale=ks, v_scale=vs)
+    assert_close(oracle.to_f64(to_host_bits(oe)), ref_e, "bf16", "big paged FP8 extend")
+    assert_close(oracle.to_f64(to_host_bits(od)), ref_d, "bf16", "big paged FP8 decode")
 
 
 def test_paged_and_ragged_pool_beyond_4gib():
