@@ -344,6 +344,28 @@ rax_status rax_decode_attention_fp8(const void* q, void* o, const void* k_pool, 
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * rax_extend_attention_ragged_paged -- rax_extend_attention_ragged with the cached prefix read
+ * through a page table (page_table, pt_stride, page_size as in rax_extend_attention_paged):
+ * suffix positions come from k_new / v_new, prefix positions from the pool slots the page table
+ * names, and store_loc (optional) still names one token slot per suffix row. The ragged kernel
+ * beside a paged one that "Inside SGLang", Step 3 describes, over the paged pool of "A
+ * walkthrough of SGLang", Exercises, exercise 2. Device-side CONTRACT: the page entries that
+ * cover positions 0 .. p-1 of each used row are pages inside the pool (later entries of the
+ * row are not used as pages); store_loc as in rax_extend_attention_ragged. Same errors as both
+ * calls.
+ */
+rax_status rax_extend_attention_ragged_paged(rax_dtype dtype, const void* q, void* o, const void* k_new,
+                                             const void* v_new, const int32_t* store_loc, void* k_pool,
+                                             void* v_pool, int64_t num_slots, const int32_t* page_table,
+                                             int64_t pt_stride, int32_t page_size,
+                                             const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                             const int32_t* extend_lens, const int32_t* extend_start_loc,
+                                             int32_t batch, int64_t total_extend_tokens, int32_t max_extend_len,
+                                             int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                             int32_t head_dim, float sm_scale, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream);
+
+/*
  * rax_extend_attention_paged_fp8, rax_decode_attention_paged_fp8 -- the FP8-pool calls above
  * with a page table of page_size slots per page in place of the token table: the arguments of
  * rax_extend_attention_fp8 / rax_decode_attention_fp8 with (page_table, pt_stride, page_size)

@@ -316,6 +316,26 @@ rax_status rax_decode_attention_paged(rax_dtype dtype, const void* q, void* o, c
                        sm_scale, 1.f, 1.f, workspace, workspace_bytes, stream, ps);
 }
 
+rax_status rax_extend_attention_ragged_paged(rax_dtype dtype, const void* q, void* o, const void* k_new,
+                                             const void* v_new, const int32_t* store_loc, void* k_pool,
+                                             void* v_pool, int64_t num_slots, const int32_t* page_table,
+                                             int64_t pt_stride, int32_t page_size,
+                                             const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                             const int32_t* extend_lens, const int32_t* extend_start_loc,
+                                             int32_t batch, int64_t total_extend_tokens, int32_t max_extend_len,
+                                             int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                             int32_t head_dim, float sm_scale, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
+    const int ps = page_shift_of(page_size);
+    if (ps < 0 || (pt_stride > 0 && pt_stride > (INT64_MAX >> 21))) return RAX_ERR_SHAPE;
+    if (total_extend_tokens > 0 && store_loc && total_extend_tokens > num_slots) return RAX_ERR_SHAPE;
+    return extend_call(dtype, false, q, o, k_pool, v_pool, num_slots, page_table, pt_stride,
+                       req_pool_indices, prefix_lens, extend_lens, extend_start_loc, batch,
+                       total_extend_tokens, max_extend_len, max_seq_len, n_q_heads, n_kv_heads,
+                       head_dim, sm_scale, 1.f, 1.f, workspace, workspace_bytes, stream, true, k_new,
+                       v_new, store_loc, ps);
+}
+
 rax_status rax_extend_attention_paged_fp8(const void* q, void* o, const void* k_pool, const void* v_pool,
                                           int64_t num_slots, const int32_t* page_table, int64_t pt_stride,
                                           int32_t page_size, const int32_t* req_pool_indices,

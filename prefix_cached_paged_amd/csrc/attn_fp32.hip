@@ -162,15 +162,15 @@ int launch_rows(const AttnArgs& a, hipStream_t stream) {
 // Ragged fp32 EXTEND with a store: the rows are stored by the copy kernel first (no slot it
 // writes is read by the attention kernel, so the order only keeps the pool consistent).
 int launch_extend_fp32(const AttnArgs& a, hipStream_t stream) {
-    if (a.page_shift) return a.ragged ? -1 : launch_rows<true, false, true>(a, stream);
-    if (!a.ragged) return launch_rows<true, false, false>(a, stream);
+    if (!a.ragged)
+        return a.page_shift ? launch_rows<true, false, true>(a, stream) : launch_rows<true, false, false>(a, stream);
     if (a.store_loc != nullptr) {
         const int64_t row_bytes = (int64_t)a.n_kv_heads * a.head_dim * 4;
         if (launch_kv_store(a.k_new, a.v_new, a.store_loc, a.total_tokens, const_cast<void*>(a.k_pool),
                             const_cast<void*>(a.v_pool), row_bytes, stream) != 0)
             return -1;
     }
-    return launch_rows<true, true, false>(a, stream);
+    return a.page_shift ? launch_rows<true, true, true>(a, stream) : launch_rows<true, true, false>(a, stream);
 }
 int launch_decode_fp32(const AttnArgs& a, hipStream_t stream) {
     return a.page_shift ? launch_rows<false, false, true>(a, stream) : launch_rows<false, false, false>(a, stream);

@@ -184,7 +184,6 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     constexpr int BQ = kExtBM / G;  // tokens per workgroup
     constexpr int EB = KV8 ? 1 : 2;  // bytes per pool element
     static_assert(!(KV8 && RAG), "ragged suffix rows are bf16, as the pools");
-    static_assert(!(PG && RAG), "the ragged suffix is read through a token table");
 
     // Three K/V tile buffers, row-major [key][16 units of 8 bf16], swizzled. Separate LDS
     // objects, each named statically below.
@@ -818,7 +817,9 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
     const bool off32 = pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 2) &&
                        (!a.ragged || pool_fits_32bit_offsets(a.total_tokens, a.n_kv_heads, a.head_dim, 2));
     if (a.ragged) {
-        if (a.page_shift) return -1;
+        if (a.page_shift)
+            return off32 ? launch_g<DH, G, true, false, true, true>(a, stream)
+                         : launch_g<DH, G, false, false, true, true>(a, stream);
         return off32 ? launch_g<DH, G, true, false, true, false>(a, stream)
                      : launch_g<DH, G, false, false, true, false>(a, stream);
     }

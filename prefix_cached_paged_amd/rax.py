@@ -70,6 +70,10 @@ _SIGS = {
     "rax_decode_attention_fp8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_p,
                                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f, _c_f, _c_f,
                                                 _c_p, _c_sz, _c_p]),
+    "rax_extend_attention_ragged_paged": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                                         _c_p, _c_i64, _c_p, _c_i64, _c_i32, _c_p, _c_p, _c_p,
+                                                         _c_p, _c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                         _c_i32, _c_f, _c_p, _c_sz, _c_p]),
     "rax_extend_attention_paged_fp8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_i32,
                                                       _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64, _c_i32, _c_i32,
                                                       _c_i32, _c_i32, _c_i32, _c_f, _c_f, _c_f, _c_p, _c_sz,
@@ -284,6 +288,35 @@ def extend_attention_ragged(q, o, k_new, v_new, k_pool, v_pool, req_to_token, re
                                               Hq, Hkv, D, float(sm_scale), _ptr(workspace), wbytes,
                                               _stream(stream, q.device)),
            "rax_extend_attention_ragged")
+
+
+def extend_attention_ragged_paged(q, o, k_new, v_new, k_pool, v_pool, page_table, page_size, req_pool_indices,
+                                  prefix_lens, extend_lens, extend_start_loc, max_extend_len, max_seq_len, sm_scale,
+                                  store_loc=None, workspace=None, stream=None):
+    """Ragged EXTEND (suffix K/V from ``k_new`` / ``v_new``, optional fused store) with the prefix
+    read through a page table of ``page_size`` slots per page."""
+    N, Hq, D, S, Hkv = _attn_shapes(q, o, k_pool, v_pool)
+    dt = _dtype(q, o, k_pool, v_pool)
+    if _dtype(k_new, v_new) != dt or k_new.shape != (N, Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [tokens, n_kv_heads, head_dim] in the pool's dtype")
+    _expect(store_loc is None or (store_loc.dim() == 1 and store_loc.shape[0] == N),
+            "store_loc must hold one slot per suffix row")
+    _same_device(q, k_new, v_new, store_loc)
+    B = prefix_lens.shape[0]
+    _per_request(B, req_pool_indices, prefix_lens, extend_lens, extend_start_loc)
+    _table(page_table)
+    need = extend_workspace_bytes(dt, B, N, max_extend_len, max_seq_len, Hq, Hkv, D)
+    workspace = _workspace(need, workspace, q.device, stream)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().rax_extend_attention_ragged_paged(dt, _ptr(q), _ptr(o), _ptr(k_new), _ptr(v_new),
+                                                    _idx(store_loc) if store_loc is not None else None,
+                                                    _ptr(k_pool), _ptr(v_pool), S, _idx(page_table),
+                                                    page_table.shape[1], int(page_size), _idx(req_pool_indices),
+                                                    _idx(prefix_lens), _idx(extend_lens), _idx(extend_start_loc),
+                                                    B, N, int(max_extend_len), int(max_seq_len), Hq, Hkv, D,
+                                                    float(sm_scale), _ptr(workspace), wbytes,
+                                                    _stream(stream, q.device)),
+           "rax_extend_attention_ragged_paged")
 
 
 def extend_attention_paged(q, o, k_pool, v_pool, page_table, page_size, req_pool_indices, prefix_lens,

@@ -26,6 +26,7 @@ def test_every_declared_symbol_is_exported():
                           "rax_decode_attention_fp8", "rax_extend_attention_ragged",
                           "rax_extend_attention_paged", "rax_decode_attention_paged",
                           "rax_extend_attention_paged_fp8", "rax_decode_attention_paged_fp8",
+                          "rax_extend_attention_ragged_paged",
                           "rax_check_workspace_bytes", "rax_check_kv_store", "rax_check_extend",
                           "rax_check_decode", "rax_decode_attention_noalloc"}
     out = subprocess.run(["nm", "-D", "--defined-only", R.library_path()], capture_output=True, text=True).stdout
