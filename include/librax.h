@@ -22,7 +22,7 @@
  *   attention, "Inside SGLang", Step 3).
  * - Kernels exist for (group G = n_q_heads / n_kv_heads): fp32 EXTEND and DECODE, any G and
  *   head_dim 64 or 128; bf16 EXTEND (plain, ragged and paged) and FP8-pool EXTEND, head_dim 64
- *   or 128, with G in {1, 2, 4, 8, 16, 32}; bf16 (and FP8-pool) DECODE, head_dim 64
+ *   or 128, with G from 1 to 256; bf16 (and FP8-pool) DECODE, head_dim 64
  *   or 128 and G from 1 to 16. Any other valid shape
  *   returns RAX_ERR_UNSUPPORTED before anything is enqueued.
  * - `stream` is a hipStream_t (NULL = the null stream). Every call only ENQUEUES work on it:

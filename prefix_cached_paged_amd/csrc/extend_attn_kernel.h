@@ -11,7 +11,8 @@
 // Design (gfx950, wave64, 512 threads = 8 waves per workgroup, one workgroup per CU):
 //  * Work item: (request b, kv head g, BM = 256 query rows). The rows are (token, head) pairs
 //    of the G query heads sharing kv head g, token-major, so one gathered K/V tile feeds
-//    256 / G tokens x G heads. Each wave owns 32 rows. Every workgroup reads the whole visible
+//    256 / G tokens x G heads (floor(256 / G) tokens when G does not divide 256; the rows past
+//    them are idle). Each wave owns 32 rows. Every workgroup reads the whole visible
 //    context once, so the K/V traffic is (query rows / 256) x context: the row count per
 //    workgroup is what keeps the kernel off the memory roofline.
 //  * Key tiles of 64 rows (256 B per kv head per row; head_dim 64 fills half of each LDS row)
@@ -181,7 +182,10 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // and the copy lanes of units 8-15 fetch a copy of units 0-7, so no copy leaves its row.
     constexpr int D = DH;
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-    constexpr int BQ = kExtBM / G;  // tokens per workgroup
+    // G = 0: the group size is read at run time (Hq / Hkv) and each workgroup takes
+    // floor(256 / G) tokens; the rows past BQ * G of the tile are idle (computed, never stored).
+    const int Gv = G > 0 ? G : Hq / Hkv;
+    const int BQ = kExtBM / Gv;  // tokens per workgroup
     constexpr int EB = KV8 ? 1 : 2;  // bytes per pool element
     static_assert(!(KV8 && RAG), "ragged suffix rows are bf16, as the pools");
 
@@ -234,11 +238,11 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
 
     // ---- this lane's query row
     const int r = 32 * wave + col;
-    const int t = t0 + r / G;
-    const int hl = r % G;
-    const bool row_ok = t < e;
+    const int t = t0 + r / Gv;
+    const int hl = r % Gv;
+    const bool row_ok = (G > 0 || r < BQ * Gv) && t < e;  // with G > 0, BQ * G = 256 rows
     const int t_ld = row_ok ? t : e - 1;
-    const int64_t qo_row = ((int64_t)(s0 + t_ld) * Hq + (int64_t)g * G + hl) * D;
+    const int64_t qo_row = ((int64_t)(s0 + t_ld) * Hq + (int64_t)g * Gv + hl) * D;
     bf16x8 qop[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qop[s] = as_bf16x8(*(const uint4*)(q + qo_row + 16 * s + 8 * h2));
@@ -783,7 +787,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
 
 template <int DH, int G, bool OFF32, bool KV8, bool RAG, bool PG>
 int launch_g(const AttnArgs& a, hipStream_t stream) {
-    constexpr int BQ = kExtBM / G;
+    const int BQ = kExtBM / (G > 0 ? G : a.n_q_heads / a.n_kv_heads);
     const int tiles = (a.max_extend_len + BQ - 1) / BQ;
     const int pairs = a.batch * a.n_kv_heads;
     const int64_t blocks = (int64_t)((pairs + kXcds - 1) / kXcds) * kXcds * tiles;
@@ -831,7 +835,8 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
 }
 
 // Both head_dims of group size G (each group size is instantiated in its own translation unit,
-// extend_g<G>.hip, so that the build compiles them in parallel).
+// extend_g<G>.hip, so that the build compiles them in parallel; G = 0 is the run-time group
+// size that serves every other group up to 256).
 template <int G>
 int launch_extend_group(const AttnArgs& a, hipStream_t stream) {
     if (a.head_dim == 128) return launch_g<128, G>(a, stream);

@@ -76,6 +76,7 @@ int launch_extend_g4(const AttnArgs& a, hipStream_t stream);
 int launch_extend_g8(const AttnArgs& a, hipStream_t stream);
 int launch_extend_g16(const AttnArgs& a, hipStream_t stream);
 int launch_extend_g32(const AttnArgs& a, hipStream_t stream);
+int launch_extend_g0(const AttnArgs& a, hipStream_t stream);  // any other group size up to 256
 
 bool decode_bf16_supported(int32_t group, int32_t head_dim);
 // Key ranges per group of kv heads the split kernel is launched with (bf16 or FP8 pools, which

@@ -80,8 +80,9 @@ def test_extend_validation():
     assert extend(max_ext=65, total=64) == 2
     assert extend(hq=6, hkv=4) == 2          # not a multiple
     assert extend(d=96) == 4
-    assert extend(hq=6, hkv=2) == 4          # bf16 MFMA path needs a power-of-two group
-    assert extend(hq=128, hkv=2) == 4        # group 64 is beyond the 256-row tile
+    assert extend(hq=6, hkv=2, batch=0, q=None) == 0     # group 3: the run-time group kernel
+    assert extend(hq=128, hkv=2, batch=0, q=None) == 0   # group 64: 4 tokens per 256-row tile
+    assert extend(hq=514, hkv=2) == 4        # group 257: not one token's heads per tile
     assert extend(d=32) == 4                 # head_dim 64 or 128 only
     assert extend(d=64, batch=0, q=None) == 0  # bf16 EXTEND: head_dim 64 too
     assert extend(dtype=1, d=64, batch=0, q=None) == 0           # fp32: head_dim 64 ...
@@ -172,7 +173,8 @@ def test_fp8_calls_check_scales_and_shapes_before_launching():
     assert ext(ks=-2.0) == 2 and ext(vs=float("inf")) == 2 and ext(ks=float("nan")) == 2
     assert ext(B=0) == 0
     assert ext(D=32) == 4          # head_dim 64 or 128 only
-    assert ext(Hq=6) == 4          # group 3 has no kernel
+    assert ext(Hq=6, B=0) == 0     # group 3: the run-time group kernel
+    assert ext(Hq=2 * 257) == 4    # group 257 has no kernel
     assert L.rax_extend_workspace_bytes(2, 3, 100, 50, 300, 8, 2, 128) == 0
 
 

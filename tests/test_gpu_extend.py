@@ -29,6 +29,13 @@ SMALL = [
     W.Spec("ext-d64-g1", "bf16", 4, 4, 64, 50000, extend_prefix=(0, 200, 37), extend_lens=(300, 129, 0)),
     W.Spec("ext-d64-g8", "bf16", 64, 8, 64, 100000, extend_prefix=(1000, 5), extend_lens=(33, 200)),
     W.Spec("ext-d64-g32", "bf16", 32, 1, 64, 50000, extend_prefix=(0, 640), extend_lens=(500, 9)),
+    # group sizes without their own kernel (the run-time group size): floor(256 / G) tokens per
+    # workgroup, the rows past them idle
+    W.Spec("ext-g3", "bf16", 6, 2, 128, 50000, extend_prefix=(0, 37, 500), extend_lens=(200, 86, 300)),
+    W.Spec("ext-g7", "bf16", 28, 4, 128, 100000, extend_prefix=(0, 63, 1000), extend_lens=(100, 37, 73)),
+    W.Spec("ext-d64-g5", "bf16", 40, 8, 64, 100000, extend_prefix=(64, 0), extend_lens=(103, 52)),
+    W.Spec("ext-g12", "bf16", 12, 1, 128, 50000, extend_prefix=(129, 0), extend_lens=(43, 21)),
+    W.Spec("ext-g64", "bf16", 64, 1, 128, 50000, extend_prefix=(0, 300), extend_lens=(9, 30)),
 ]
 
 

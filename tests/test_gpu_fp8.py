@@ -150,6 +150,9 @@ EXT_SPECS = [
     # head_dim 64: four E4M3 units per row, the copy lanes of units 4-7 repeat units 0-3
     W.Spec("fp8-ext-d64-g4", "bf16", 32, 8, 64, 60000, extend_prefix=(0, 63, 500), extend_lens=(129, 65, 300)),
     W.Spec("fp8-ext-d64-g1", "bf16", 4, 4, 64, 30000, extend_prefix=(37, 0), extend_lens=(200, 1)),
+    # group sizes of the run-time group kernel
+    W.Spec("fp8-ext-g7", "bf16", 28, 4, 128, 60000, extend_prefix=(0, 63, 1000), extend_lens=(100, 37, 73)),
+    W.Spec("fp8-ext-d64-g3", "bf16", 6, 2, 64, 30000, extend_prefix=(0, 500), extend_lens=(200, 86)),
 ]
 
 

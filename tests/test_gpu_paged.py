@@ -33,6 +33,8 @@ EXT_SPECS = [
            shared_prefix=True, page_size=16),
     W.Spec("pg4-fp32", "fp32", 4, 4, 64, 4096, extend_prefix=(0, 16, 64, 128), extend_lens=(32, 16, 8, 1),
            page_size=4),
+    W.Spec("pg16-g7", "bf16", 28, 4, 128, 131072, extend_prefix=(0, 63, 1000), extend_lens=(100, 37, 73),
+           page_size=16),
 ]
 DEC_SPECS = [
     W.Spec("pg16-dec", "bf16", 32, 8, 128, 131072, decode_lens=(1, 2, 15, 16, 17, 257, 1000, 2500), page_size=16),

@@ -35,6 +35,7 @@ SPECS = [
     W.Spec("rag-d64-g4", "bf16", 32, 8, 64, 100000, extend_prefix=(0, 63, 500), extend_lens=(129, 65, 300)),
     W.Spec("rag-fp32-d64", "fp32", 4, 4, 64, 4000, extend_prefix=(0, 16, 64, 128), extend_lens=(32, 16, 8, 1)),
     W.Spec("rag-fp32-d128-g3", "fp32", 6, 2, 128, 20000, extend_prefix=(0, 300), extend_lens=(70, 65)),
+    W.Spec("rag-g7", "bf16", 28, 4, 128, 100000, extend_prefix=(0, 63, 500), extend_lens=(100, 37, 73)),
 ]
 
 
@@ -97,6 +98,7 @@ PAGED_SPECS = [
     W.Spec("ragpg8-d64", "bf16", 32, 8, 64, 65536, extend_prefix=(63, 208), extend_lens=(65, 190), page_size=8),
     W.Spec("ragpg4-fp32", "fp32", 4, 4, 64, 8192, extend_prefix=(0, 16, 64, 130), extend_lens=(32, 16, 8, 1),
            page_size=4),
+    W.Spec("ragpg16-g5", "bf16", 40, 8, 128, 131072, extend_prefix=(70, 0), extend_lens=(103, 52), page_size=16),
 ]
 
 
