@@ -23,7 +23,7 @@
  * - Kernels exist for (group G = n_q_heads / n_kv_heads): fp32 EXTEND and DECODE, any G and
  *   head_dim 64 or 128; bf16 EXTEND (plain, ragged and paged) and FP8-pool EXTEND, head_dim 64
  *   or 128, with G from 1 to 256; bf16 (and FP8-pool) DECODE, head_dim 64
- *   or 128 and G from 1 to 16. Any other valid shape
+ *   or 128 and G from 1 to 256 (above 16, ceil(G / 16) waves per kv head). Any other valid shape
  *   returns RAX_ERR_UNSUPPORTED before anything is enqueued.
  * - `stream` is a hipStream_t (NULL = the null stream). Every call only ENQUEUES work on it:
  *   the library never allocates, frees or synchronises, and keeps no state between calls.
@@ -394,7 +394,8 @@ rax_status rax_decode_attention_paged_fp8(const void* q, void* o, const void* k_
 
 /* Number of key ranges per group of kv heads that rax_decode_attention launches for these
  * shapes (bf16; 1 for fp32 or empty shapes; -1 if the shapes need more than 2^31 - 1). Ranges
- * past the end of the actual key stream exit at once. For tests and reports. */
+ * past the end of the actual key stream exit at once. For tests and reports. With more than
+ * 16 query heads per kv head, pass n_kv_heads * ceil(G / 16) (the waves per range). */
 int32_t rax_decode_num_splits(rax_dtype dtype, int32_t batch, int32_t max_seq_len, int32_t n_kv_heads);
 
 /*

@@ -156,7 +156,8 @@ rax_status decode_call(int dtype, bool kv8, const void* q, void* o, const void* 
     if (kv8 && (!scale_ok(k_scale) || !scale_ok(v_scale))) return RAX_ERR_SHAPE;
     if (batch == 0) return RAX_OK;
     if (max_seq_len == 0) return RAX_ERR_SHAPE;
-    if (dtype == RAX_BF16 && rax::decode_grid(batch, max_seq_len, n_kv_heads, kv8) < 0)
+    if (dtype == RAX_BF16 &&
+        rax::decode_grid(batch, max_seq_len, rax::decode_wave_heads(n_q_heads, n_kv_heads), kv8) < 0)
         return RAX_ERR_SHAPE;
     if (!q || !o || !k_pool || !v_pool || !req_to_token || !req_pool_indices || !seq_lens)
         return RAX_ERR_NULL;

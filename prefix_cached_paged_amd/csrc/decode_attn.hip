@@ -13,12 +13,14 @@
 //    every wave moves the same number of bytes whatever the mix of context lengths. A range
 //    may hold the tail of one request and the head of the next; each (request, range) overlap
 //    yields one partial (o, lse) in the workspace, and decode_merge_kernel combines a request's
-//    partials with log-sum-exp weights. A workgroup's waves are consecutive kv heads. For
-//    batches up to 1,024 requests every split workgroup computes the plan itself (a scan in
-//    LDS); larger batches get it from decode_plan_kernel.
+//    partials with log-sum-exp weights. A workgroup's waves are consecutive kv heads (or
+//    consecutive sixteen-head parts of them, for groups above 16). For batches up to 1,024
+//    requests every split workgroup computes the plan itself (a scan in LDS); larger batches
+//    get it from decode_plan_kernel.
 //  * The G query heads that share kv head g are the N dimension of 16x16x32 bf16 MFMAs
 //    (grouped-query attention: one gathered K/V row feeds all G heads). Heads beyond G are
-//    zero padding; MFMA throughput is far above what the bandwidth bound needs.
+//    zero padding; MFMA throughput is far above what the bandwidth bound needs. Groups above
+//    16 take ceil(G / 16) waves per kv head, 16 query heads each, reading the same rows.
 //  * K rows are loaded straight into the MFMA A-operand layout: lane (n = lane%16,
 //    kgrp = lane/16) holds 8 consecutive head_dim elements of key n, i.e. 16-byte loads of
 //    64 contiguous bytes per key per instruction.
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(64 * kDecWaves, KV8 ? RAX_DEC_WGS_PER_CU8 : RAX_DEC
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ r2t, int64_t r2t_stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ seq_lens, int32_t max_seq_len,
-    int32_t B, int32_t Hq, int32_t Hkv, int32_t G, int32_t groups, int32_t n_target,
+    int32_t B, int32_t Hq, int32_t Hkv, int32_t G, int32_t SG, int32_t groups, int32_t n_target,
     float scale_log2, float out_scale, int64_t* __restrict__ meta, int64_t* __restrict__ P,
     const int32_t* __restrict__ first_req, float* __restrict__ o_part,
     float* __restrict__ lse_part, int32_t page_shift) {
@@ -380,8 +382,14 @@ __global__ __launch_bounds__(64 * kDecWaves, KV8 ? RAX_DEC_WGS_PER_CU8 : RAX_DEC
     }
     __syncthreads();
 
-    const int g = __builtin_amdgcn_readfirstlane(grp * kDecWaves + wv);
-    if (g >= Hkv) return;
+    // Wave v serves kv head g = v / SG and its query heads 16 sub .. 16 sub + 15 (sub = v % SG):
+    // groups above 16 split into SG = ceil(G / 16) waves that read the same K/V rows.
+    const int v = __builtin_amdgcn_readfirstlane(grp * kDecWaves + wv);
+    if (v >= Hkv * SG) return;
+    const int g = __builtin_amdgcn_readfirstlane(v / SG);
+    const int sub = v - g * SG;
+    const int h0 = g * G + 16 * sub;           // first query head of this wave
+    const int gw = min(G - 16 * sub, 16);      // query heads of this wave
 
     const int n16 = lane & 15;
     const int kg = lane >> 4;
@@ -398,9 +406,9 @@ __global__ __launch_bounds__(64 * kDecWaves, KV8 ? RAX_DEC_WGS_PER_CU8 : RAX_DEC
     const uint32_t k_off = 16u * kg;        // this lane's first 16 bytes of a K row
     constexpr int KL = KV8 ? S / 2 : S;     // 16-byte K loads per key
     const uint32_t v_off = es * DT * n16;   // this lane's DT head_dim elements of a V row
-    // Columns n16 >= G are padding: they load a valid head and zero it with a mask (no branch,
+    // Columns n16 >= gw are padding: they load a valid head and zero it with a mask (no branch,
     // so the loads stay in flight together).
-    const bool q_ok = n16 < G;
+    const bool q_ok = n16 < gw;
     const uint32_t q_keep = q_ok ? 0xFFFFFFFFu : 0u;
 
     // Software pipeline over KPI-key iterations: the next iteration's K rows are requested as
@@ -504,7 +512,7 @@ __global__ __launch_bounds__(64 * kDecWaves, KV8 ? RAX_DEC_WGS_PER_CU8 : RAX_DEC
         // B operand of S^T = K Q^T: lane holds Q[head n16][k_step_elem(s, kg) .. +8].
         bf16x8 qop[S];
         {
-            const uint16_t* qr = q + ((int64_t)b * Hq + (int64_t)g * G + (q_ok ? n16 : 0)) * D;
+            const uint16_t* qr = q + ((int64_t)b * Hq + h0 + (q_ok ? n16 : 0)) * D;
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 uint4 v = *(const uint4*)(qr + k_step_elem<KV8>(s, kg));
@@ -533,7 +541,7 @@ __global__ __launch_bounds__(64 * kDecWaves, KV8 ? RAX_DEC_WGS_PER_CU8 : RAX_DEC
         if (q_ok) {
             // Partial of (request b, range w) sits at index b + w: the overlapping pairs form a
             // monotone staircase in (b, w), so b + w never repeats.
-            const int64_t pidx = ((int64_t)b + w) * Hq + g * G + n16;
+            const int64_t pidx = ((int64_t)b + w) * Hq + h0 + n16;
             const float inv = out_scale / lsum;
             float* op = o_part + pidx * D;
             // acc[dt][i] is O^T row 4kg + i, i.e. head_dim DT*(4kg + i) + dt.
@@ -702,7 +710,12 @@ void* decode_scratch(hipStream_t stream) {
 }
 
 bool decode_bf16_supported(int32_t group, int32_t head_dim) {
-    return group >= 1 && group <= 16 && (head_dim == 64 || head_dim == 128);
+    return group >= 1 && group <= 256 && (head_dim == 64 || head_dim == 128);
+}
+
+int32_t decode_wave_heads(int32_t n_q_heads, int32_t n_kv_heads) {
+    const int32_t G = n_q_heads / n_kv_heads;
+    return n_kv_heads * ((G + 15) / 16);
 }
 
 // Ranges per kv-head group the split kernel is launched with: one resident round, or more when
@@ -719,15 +732,17 @@ int32_t decode_grid(int32_t batch, int32_t max_seq_len, int32_t n_kv_heads, bool
 
 size_t decode_workspace(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
                         int32_t head_dim, bool kv8) {
-    const int32_t grid = decode_grid(batch, max_seq_len, n_kv_heads, kv8);
+    const int32_t grid = decode_grid(batch, max_seq_len, decode_wave_heads(n_q_heads, n_kv_heads), kv8);
     if (grid < 0) return 0;
     return decode_layout(batch, grid, n_q_heads, head_dim).total;
 }
 
 int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
     const int32_t G = a.n_q_heads / a.n_kv_heads;
-    const int32_t groups = decode_groups(a.n_kv_heads);
-    const int32_t grid = decode_grid(a.batch, a.max_seq_len, a.n_kv_heads, a.kv8);
+    const int32_t SG = (G + 15) / 16;  // waves per kv head (16 query heads each)
+    const int32_t wheads = a.n_kv_heads * SG;
+    const int32_t groups = decode_groups(wheads);
+    const int32_t grid = decode_grid(a.batch, a.max_seq_len, wheads, a.kv8);
     if (grid < 0) return -1;
     const DecLayout l = decode_layout(a.batch, grid, a.n_q_heads, a.head_dim);
     char* ws = (char*)a.workspace;
@@ -738,7 +753,7 @@ int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
     float* lse = (float*)(ws + l.lse);
     const float scale_log2 = a.sm_scale * kLog2e * (a.kv8 ? a.k_scale : 1.f);
     const float out_scale = a.kv8 ? a.v_scale : 1.f;
-    const int32_t n_target = decode_target(a.n_kv_heads, a.kv8);
+    const int32_t n_target = decode_target(wheads, a.kv8);
     const bool fused = a.batch <= kDecFusedBatch;
     if (!fused) {
         hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.seq_lens,
@@ -752,7 +767,8 @@ int launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_split_kernel<DD, OFF, FU, K8, PGT>), sgrid, dim3(64 * kDecWaves), \
                        0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k_pool,                \
                        (const uint16_t*)a.v_pool, a.r2t, a.r2t_stride, a.req_pool_indices,        \
-                       a.seq_lens, a.max_seq_len, a.batch, a.n_q_heads, a.n_kv_heads, G, groups,  \
+                       a.seq_lens, a.max_seq_len, a.batch, a.n_q_heads, a.n_kv_heads, G, SG,      \
+                       groups,                                                                    \
                        n_target, scale_log2, out_scale, meta, P, first, o_part, lse, a.page_shift)
 #define RAX_DEC_SPLIT3(DD, OFF, FU)                                                             \
     do {                                                                                        \

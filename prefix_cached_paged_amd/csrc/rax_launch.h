@@ -79,6 +79,8 @@ int launch_extend_g32(const AttnArgs& a, hipStream_t stream);
 int launch_extend_g0(const AttnArgs& a, hipStream_t stream);  // any other group size up to 256
 
 bool decode_bf16_supported(int32_t group, int32_t head_dim);
+// Waves per range of the split kernel: one per kv head, ceil(G / 16) for groups above 16.
+int32_t decode_wave_heads(int32_t n_q_heads, int32_t n_kv_heads);
 // Key ranges per group of kv heads the split kernel is launched with (bf16 or FP8 pools, which
 // differ in resident workgroups); -1 if too many.
 int32_t decode_grid(int32_t batch, int32_t max_seq_len, int32_t n_kv_heads, bool kv8);

@@ -108,7 +108,8 @@ def test_decode_validation():
     assert decode(max_seq=0) == 2
     assert decode(hq=8, hkv=3) == 2
     assert decode(d=32) == 4
-    assert decode(hq=34, hkv=2) == 4         # group 17 is beyond the 16-wide head tile
+    assert decode(hq=34, hkv=2, batch=0, q=None) == 0   # group 17: two waves of heads per kv head
+    assert decode(hq=2 * 257, hkv=2) == 4    # group 257 has no kernel
     assert decode(dtype=1, hq=34, hkv=2, batch=0, q=None) == 0   # fp32: any group
     assert decode(d=64, batch=0, q=None) == 0                     # bf16 DECODE: head_dim 64 too
     assert decode(seq=None) == 1

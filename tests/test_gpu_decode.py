@@ -21,6 +21,11 @@ SMALL = [
     W.Spec("dec-g8", "bf16", 64, 8, 128, 300000, decode_lens=(5, 513, 20000)),
     W.Spec("dec-g16", "bf16", 16, 1, 128, 100000, decode_lens=(77, 4096, 12345)),
     W.Spec("dec-d64", "bf16", 16, 4, 64, 100000, decode_lens=(1, 64, 999, 5000)),
+    # groups above 16: ceil(G / 16) waves of up to 16 query heads per kv head
+    W.Spec("dec-g17", "bf16", 34, 2, 128, 100000, decode_lens=(1, 300, 4097)),
+    W.Spec("dec-g24", "bf16", 48, 2, 128, 100000, decode_lens=(64, 2500, 700)),
+    W.Spec("dec-g48", "bf16", 48, 1, 128, 100000, decode_lens=(5, 9000, 65)),
+    W.Spec("dec-d64-g32", "bf16", 64, 2, 64, 100000, decode_lens=(129, 3000)),
     W.Spec("dec-many", "bf16", 32, 8, 128, 400000, decode_batch=96, decode_range=(1, 3000)),
     # head_dim 64 with more than 1,024 requests: the separate plan kernel
     W.Spec("dec-d64-plan", "bf16", 16, 4, 64, 100000, decode_batch=1200, decode_range=(1, 40)),
