@@ -71,10 +71,12 @@ COPY_BYTES = 1 << 30
 
 def source_sha(kernel: str) -> str:
     """Hash of the kernel's sources with comments and blank lines removed (an edit of a comment
-    does not change the kernel the counters were taken on)."""
+    does not change the kernel the counters were taken on), and of the compiler flags."""
     import hashlib
     import re
+    from prefix_cached_paged_amd.build import HIPCC_FLAGS
     h = hashlib.sha256()
+    h.update(" ".join(f for f in HIPCC_FLAGS if os.sep not in f).encode())
     for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(CSRC, f)) as fh:
             text = fh.read()

@@ -28,6 +28,9 @@ HIPCC_FLAGS = [
     "-Wno-unused-function",
     # Packed FP32 VALU ops (v_pk_*_f32) are kept out of generated code on purpose.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Loop heads on 64-byte boundaries: without it the hot loops' placement, and their speed
+    # (by 1-2%), shifts with the length of whatever code precedes them.
+    "-falign-loops=64",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -176,7 +176,8 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
     const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ extend_start_loc,
     int64_t total_tokens, int32_t max_extend_len, int32_t max_seq_len, int32_t Hq, int32_t Hkv,
-    int32_t batch, int32_t tiles, float scale_log2, float out_scale, int32_t page_shift) {
+    int32_t batch, int32_t tiles, float scale_log2, float out_scale, int32_t page_shift,
+    int32_t spread_shift) {
     // head_dim of Q, O and the pool rows. The LDS tiles keep 128-wide rows either way: with
     // head_dim 64 only logical units 0-7 of a row are used (score steps 0-3, P V blocks 0-1)
     // and the copy lanes of units 8-15 fetch a copy of units 0-7, so no copy leaves its row.
@@ -199,13 +200,27 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     constexpr int SU = KV8 ? kExtBN * 8 : 1;
     __shared__ uint4 sk0[SU], sk1[SU], sv0[SU], sv1[SU];
 
-    // ---- workgroup -> (pair = b * Hkv + g, tile), XCD-aware
+    // ---- workgroup -> (pair = b * Hkv + g, tile), XCD-aware. Consecutive workgroup ids go
+    // to different XCDs; XCD x takes every tile of pairs x, x + 8, ... of the first multiple of
+    // 8 pairs (one L2 per pair), longest tile first. The rem = pairs % 8 pairs past that
+    // multiple (all of them when there are fewer than 8) are spread: each takes
+    // 2^spread_shift XCDs (the power of two at most 8 / rem), which share its tiles round
+    // robin, so no XCD stays idle for want of a pair.
     const int pairs = batch * Hkv;
     const int xcd = blockIdx.x % kXcds;
     const int k = blockIdx.x / kXcds;
-    const int pair = xcd + kXcds * (k / tiles);
-    if (pair >= pairs) return;
-    const int tq = tiles - 1 - (k % tiles);
+    const int full = pairs & ~(kXcds - 1);
+    const int rounds = (pairs / kXcds) * tiles;  // per-XCD slots of the full groups of 8
+    int pair, jt;
+    if (k < rounds) {
+        pair = xcd + kXcds * (k / tiles);
+        jt = k % tiles;
+    } else {
+        pair = full + (xcd >> spread_shift);
+        jt = ((k - rounds) << spread_shift) + (xcd & ((1 << spread_shift) - 1));
+        if (pair >= pairs || jt >= tiles) return;
+    }
+    const int tq = tiles - 1 - jt;
     const int b = pair / Hkv;
     const int g = pair - b * Hkv;
 
@@ -790,7 +805,12 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
     const int BQ = kExtBM / (G > 0 ? G : a.n_q_heads / a.n_kv_heads);
     const int tiles = (a.max_extend_len + BQ - 1) / BQ;
     const int pairs = a.batch * a.n_kv_heads;
-    const int64_t blocks = (int64_t)((pairs + kXcds - 1) / kXcds) * kXcds * tiles;
+    // The last pairs % 8 pairs take 2^spread XCDs each (see the kernel).
+    const int rem = pairs % kXcds;
+    int spread = 0;
+    while (rem && (rem << (spread + 1)) <= kXcds) ++spread;
+    const int64_t per_xcd = (int64_t)(pairs / kXcds) * tiles + (rem ? ((tiles - 1) >> spread) + 1 : 0);
+    const int64_t blocks = per_xcd * kXcds;
     if (blocks <= 0) return 0;
     if (blocks > 0x7fffffff) return -1;
     // FP8 pools: the K scale multiplies every score, the V scale every output element.
@@ -802,7 +822,7 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
                        a.r2t, a.r2t_stride, a.req_pool_indices,
                        a.prefix_lens, a.extend_lens, a.extend_start_loc, a.total_tokens,
                        a.max_extend_len, a.max_seq_len, a.n_q_heads, a.n_kv_heads, a.batch, tiles,
-                       scale_log2, out_scale, a.page_shift);
+                       scale_log2, out_scale, a.page_shift, spread);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -36,6 +36,12 @@ SMALL = [
     W.Spec("ext-d64-g5", "bf16", 40, 8, 64, 100000, extend_prefix=(64, 0), extend_lens=(103, 52)),
     W.Spec("ext-g12", "bf16", 12, 1, 128, 50000, extend_prefix=(129, 0), extend_lens=(43, 21)),
     W.Spec("ext-g64", "bf16", 64, 1, 128, 50000, extend_prefix=(0, 300), extend_lens=(9, 30)),
+    # (request, kv head) pair counts that are not a multiple of 8: the tiles of the last pairs
+    # are shared out over several XCDs (1 pair on 8, 3 pairs on 2 each, 13 = 8 + 5 pairs)
+    W.Spec("ext-1pair", "bf16", 8, 1, 128, 50000, extend_prefix=(300,), extend_lens=(1000,)),
+    W.Spec("ext-3pair", "bf16", 12, 3, 128, 50000, extend_prefix=(77,), extend_lens=(700,)),
+    W.Spec("ext-13pair", "bf16", 16, 1, 128, 50000, extend_prefix=(0, 5, 64, 100, 129, 1, 2, 300, 0, 7, 40, 63, 8),
+           extend_lens=(40, 17, 33, 1, 64, 90, 16, 5, 77, 2, 48, 31, 100)),
 ]
 
 
