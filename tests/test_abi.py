@@ -129,13 +129,16 @@ def test_decode_workspace_size():
     # ranges per kv-head group: one resident round (768 workgroups of 4 kv heads, 3 per CU, for
     # bf16 and FP8 pools alike), or enough 4096-key ranges for every request at max_seq_len,
     # whichever is larger
+    # (one wave per kv head and 16 query heads: wave heads = hkv * ceil(G / 16))
     for B, L, hq, hkv in [(64, 4096, 32, 8), (8, 131072, 64, 8), (1, 1, 4, 4), (128, 8192, 32, 8),
-                          (4096, 32768, 32, 8), (16, 1000, 64, 32)]:
+                          (4096, 32768, 32, 8), (16, 1000, 64, 32), (8, 4096, 16, 1), (8, 4096, 32, 1),
+                          (4, 1000, 8, 2), (4, 1000, 48, 1)]:
         for dtype, resident in ((0, 768), (2, 768)):
-            groups = (hkv + 3) // 4
+            wheads = hkv * ((hq // hkv + 15) // 16)
+            groups = (wheads + 3) // 4
             worst = B * ((L + 63) // 64 * 64)
             grid = max(max(1, resident // groups), (worst + 4095) // 4096)
-            assert lib().rax_decode_num_splits(dtype, B, L, hkv) == grid
+            assert lib().rax_decode_num_splits(dtype, B, L, wheads) == grid
             parts = (B + grid) * hq
             want = 256 + a256((B + 1) * 8) + a256(grid * 4) + a256(parts * 128 * 4) + parts * 4
             assert lib().rax_decode_workspace_bytes(dtype, B, L, hq, hkv, 128) == want

@@ -26,6 +26,13 @@ SMALL = [
     W.Spec("dec-g24", "bf16", 48, 2, 128, 100000, decode_lens=(64, 2500, 700)),
     W.Spec("dec-g48", "bf16", 48, 1, 128, 100000, decode_lens=(5, 9000, 65)),
     W.Spec("dec-d64-g32", "bf16", 64, 2, 64, 100000, decode_lens=(129, 3000)),
+    # one or two waves of work per range (kv heads x ceil(G / 16)): the other waves of each
+    # workgroup exit at once
+    W.Spec("dec-1kv-g8", "bf16", 8, 1, 128, 100000, decode_lens=(1, 2, 31, 32, 33, 97, 128, 129, 5000)),
+    W.Spec("dec-2kv-g4", "bf16", 8, 2, 128, 100000, decode_lens=(1, 50, 300, 7000)),
+    W.Spec("dec-1kv-g32-d64", "bf16", 32, 1, 64, 100000, decode_lens=(3, 65, 2000)),
+    W.Spec("dec-1kv-many", "bf16", 16, 1, 128, 200000, decode_batch=200, decode_range=(1, 300)),
+    W.Spec("dec-1kv-plan", "bf16", 8, 1, 64, 100000, decode_batch=1100, decode_range=(1, 40)),
     W.Spec("dec-many", "bf16", 32, 8, 128, 400000, decode_batch=96, decode_range=(1, 3000)),
     # head_dim 64 with more than 1,024 requests: the separate plan kernel
     W.Spec("dec-d64-plan", "bf16", 16, 4, 64, 100000, decode_batch=1200, decode_range=(1, 40)),

@@ -86,6 +86,8 @@ SPECS = [
     W.Spec("fp8-dec-g16", "bf16", 16, 1, 128, 60000, decode_lens=(77, 4096, 12345)),
     W.Spec("fp8-dec-d64", "bf16", 16, 4, 64, 60000, decode_lens=(1, 64, 999, 5000)),
     W.Spec("fp8-dec-g48", "bf16", 48, 1, 128, 60000, decode_lens=(5, 4000, 65)),
+    W.Spec("fp8-dec-1kv-g8", "bf16", 8, 1, 128, 60000, decode_lens=(1, 64, 65, 200, 3000)),
+    W.Spec("fp8-dec-2kv-d64", "bf16", 8, 2, 64, 60000, decode_lens=(2, 129, 2500)),
     W.Spec("fp8-dec-many", "bf16", 32, 8, 128, 60000, decode_batch=64, decode_range=(1, 120)),
     W.Spec("fp8-dec-long", "bf16", 8, 1, 128, 120000, decode_lens=(50000, 3)),
     # more than 1,024 requests: the plan runs as its own kernel before the split

@@ -42,6 +42,7 @@ DEC_SPECS = [
     W.Spec("pg8-dec-many", "bf16", 32, 8, 128, 262144, decode_batch=1500, decode_range=(1, 120), page_size=8),
     W.Spec("pg32-dec-d64", "bf16", 16, 4, 64, 65536, decode_lens=(1, 64, 999, 5000), page_size=32),
     W.Spec("pg16-dec-g24", "bf16", 48, 2, 128, 65536, decode_lens=(17, 2500, 700), page_size=16),
+    W.Spec("pg16-dec-1kv", "bf16", 8, 1, 128, 65536, decode_lens=(1, 40, 130, 3000), page_size=16),
     W.Spec("pg16-dec-fp32", "fp32", 8, 2, 128, 16384, decode_lens=(1, 40, 700), page_size=16),
 ]
 
