@@ -75,6 +75,12 @@ constexpr int kXcds = 8;
 // lag wave's softmax. Same bits; +1.0-1.6% on the long, mixed and shared-prefix EXTEND steps.
 // Raising the lag group's MFMAs above the lead group's measured -3.7%; both at 1, or lead at
 // 2 over lag at 1, measured within 0.5% of this.
+// FP8 pools: the lead waves widen their share of the next tile between their softmax and their
+// P V (rather than after it), so the widened LDS writes land under their own P V MFMAs instead
+// of in front of the next iteration's barrier. Same bits; +0.6 to +1.2% on the FP8 EXTEND.
+#ifndef RAX_F8_LEAD_EARLY
+#define RAX_F8_LEAD_EARLY 1
+#endif
 #ifndef RAX_EXT_PRIO
 #define RAX_EXT_PRIO 1
 #endif
@@ -637,7 +643,9 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     }
     // Waves 4-7 widen between their P V and their scores, so that per iteration each wave
     // group alternates MFMA and VALU/LDS blocks in the opposite order to the other group
-    // (+1 to +3% over widening at the end of the iteration in both groups).
+    // (+1 to +3% over widening at the end of the iteration in both groups); waves 0-3 widen
+    // between their softmax and their P V (RAX_F8_LEAD_EARLY). Widening first thing in the
+    // iteration (waves 4-7) measured the same.
 #define RAX_PTILE8(LAG, IT, KB, VB, VP, SC, SVC, SCP, SVCP, KN, VN, SS, MASKABLE, STEADY)    \
     {                                                                                       \
         RAX_WRITES_BARRIER();                                                               \
@@ -651,6 +659,12 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
             /* the staging reads would fill the first LDS-read group of the scores */       \
             __builtin_amdgcn_sched_barrier(0);                                              \
             RAX_QKP(KB, RAX_PRIO_LAG)                                                       \
+        } else if (RAX_F8_LEAD_EARLY) {                                                     \
+            RAX_QK(KB)                                                                      \
+            RAX_SM(IT, MASKABLE)                                                            \
+            RAX_WIDEN8(IT, SC, SVC, KN, VN, SS, STEADY)                                     \
+            __builtin_amdgcn_sched_barrier(0);                                              \
+            RAX_PV(VB)                                                                      \
         } else {                                                                            \
             RAX_COMPUTE(IT, KB, VB, MASKABLE)                                               \
             RAX_WIDEN8(IT, SC, SVC, KN, VN, SS, STEADY)                                     \
