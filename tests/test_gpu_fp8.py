@@ -156,6 +156,8 @@ EXT_SPECS = [
     # group sizes of the run-time group kernel
     W.Spec("fp8-ext-g7", "bf16", 28, 4, 128, 60000, extend_prefix=(0, 63, 1000), extend_lens=(100, 37, 73)),
     W.Spec("fp8-ext-d64-g3", "bf16", 6, 2, 64, 30000, extend_prefix=(0, 500), extend_lens=(200, 86)),
+    # one (request, kv head) pair: its 32 row tiles shared out over all XCDs
+    W.Spec("fp8-ext-1pair", "bf16", 8, 1, 128, 30000, extend_prefix=(300,), extend_lens=(1000,)),
 ]
 
 

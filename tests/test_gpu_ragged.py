@@ -36,6 +36,8 @@ SPECS = [
     W.Spec("rag-fp32-d64", "fp32", 4, 4, 64, 4000, extend_prefix=(0, 16, 64, 128), extend_lens=(32, 16, 8, 1)),
     W.Spec("rag-fp32-d128-g3", "fp32", 6, 2, 128, 20000, extend_prefix=(0, 300), extend_lens=(70, 65)),
     W.Spec("rag-g7", "bf16", 28, 4, 128, 100000, extend_prefix=(0, 63, 500), extend_lens=(100, 37, 73)),
+    # one (request, kv head) pair whose row tiles are shared out over all XCDs (fused store)
+    W.Spec("rag-1pair", "bf16", 8, 1, 128, 50000, extend_prefix=(200,), extend_lens=(900,)),
 ]
 
 
@@ -99,6 +101,7 @@ PAGED_SPECS = [
     W.Spec("ragpg4-fp32", "fp32", 4, 4, 64, 8192, extend_prefix=(0, 16, 64, 130), extend_lens=(32, 16, 8, 1),
            page_size=4),
     W.Spec("ragpg16-g5", "bf16", 40, 8, 128, 131072, extend_prefix=(70, 0), extend_lens=(103, 52), page_size=16),
+    W.Spec("ragpg16-3pair", "bf16", 12, 3, 128, 65536, extend_prefix=(50,), extend_lens=(600,), page_size=16),
 ]
 
 
