@@ -64,9 +64,14 @@ rax_status rax_kv_store(rax_dtype dtype, const void* k_new, const void* v_new, c
 size_t rax_extend_workspace_bytes(rax_dtype dtype, int32_t batch, int64_t total_extend_tokens,
                                   int32_t max_extend_len, int32_t max_seq_len, int32_t n_q_heads,
                                   int32_t n_kv_heads, int32_t head_dim) {
-    (void)dtype; (void)batch; (void)total_extend_tokens; (void)max_extend_len; (void)max_seq_len;
-    (void)n_q_heads; (void)n_kv_heads; (void)head_dim;
-    return 0;
+    // bf16 pools read through a table: the partials of the key splits (0 when unsplit); FP8
+    // pools and the fp32 path use none.
+    if (dtype != RAX_BF16 || batch <= 0 || total_extend_tokens <= 0 || max_extend_len <= 0 ||
+        n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0 ||
+        !rax::extend_bf16_supported(n_q_heads / n_kv_heads, head_dim))
+        return 0;
+    const int32_t S = rax::extend_splits(batch, n_q_heads, n_kv_heads, max_extend_len, max_seq_len);
+    return rax::extend_split_workspace(S, total_extend_tokens, n_q_heads, head_dim);
 }
 
 size_t rax_decode_workspace_bytes(rax_dtype dtype, int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
@@ -116,8 +121,11 @@ rax_status extend_call(int dtype, bool kv8, const void* q, void* o, const void* 
         !extend_lens || !extend_start_loc)
         return RAX_ERR_NULL;
     if (ragged && (!k_new || !v_new)) return RAX_ERR_NULL;
-    const size_t need = rax_extend_workspace_bytes((rax_dtype)dtype, batch, total_extend_tokens, max_extend_len,
-                                                   max_seq_len, n_q_heads, n_kv_heads, head_dim);
+    // FP8 pools and the ragged calls never split their keys: no workspace needed there
+    const size_t need = kv8 || ragged ? 0
+                                      : rax_extend_workspace_bytes((rax_dtype)dtype, batch, total_extend_tokens,
+                                                                   max_extend_len, max_seq_len, n_q_heads,
+                                                                   n_kv_heads, head_dim);
     if (need > 0 && (!workspace || workspace_bytes < need)) return RAX_ERR_WORKSPACE;
 
     rax::AttnArgs a{};

@@ -197,7 +197,9 @@ __device__ __forceinline__ int64_t row_off(int idx, uint32_t row_bytes) {
 
 // PG: the table is a page table (page size 2^page_shift): position j lives at slot
 // table[row, j >> page_shift] << page_shift | (j & (2^page_shift - 1)).
-template <int DH, int G, bool OFF32, bool KV8, bool RAG, bool PG>
+// SPL: the key range of each row tile is split over nsplit workgroups, which write partial
+// outputs (fp32, normalised) and their log2-sum-exps to o_part / lse_part for merge_kernel.
+template <int DH, int G, bool OFF32, bool KV8, bool RAG, bool PG, bool SPL>
 __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const char* __restrict__ k_pool,
     const char* __restrict__ v_pool, const char* __restrict__ k_new, const char* __restrict__ v_new,
@@ -206,12 +208,21 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ extend_start_loc,
     int64_t total_tokens, int32_t max_extend_len, int32_t max_seq_len, int32_t Hq, int32_t Hkv,
     int32_t batch, int32_t tiles, float scale_log2, float out_scale, int32_t page_shift,
-    int32_t spread_shift) {
+    int32_t spread_shift, int32_t nsplit, float* __restrict__ o_part, float* __restrict__ lse_part) {
     // head_dim of Q, O and the pool rows. The LDS tiles keep 128-wide rows either way: with
     // head_dim 64 only logical units 0-7 of a row are used (score steps 0-3, P V blocks 0-1)
     // and the copy lanes of units 8-15 fetch a copy of units 0-7, so no copy leaves its row.
     constexpr int D = DH;
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+    static_assert(!SPL || (!KV8 && !RAG), "key splits over bf16 pools read through a table");
+    // Score of a masked key. A split's tiles can hold no visible key for some rows (all past
+    // the row's diagonal): with a finite mask value those rows keep a finite running max and
+    // finite sums, and a log2-sum-exp near -2^100 * scale that gives their partial weight 0
+    // in the merge, where -inf would turn the online softmax into NaN. A power of two keeps
+    // the scaled value exact: the running max (a rounded product) and the exponent argument
+    // (a fused multiply-add with the unrounded product) then cancel to exactly 0 instead of
+    // leaving a rounding residual of order 1e21.
+    constexpr float kMasked = SPL ? -0x1p100f : -INFINITY;
     // G = 0: the group size is read at run time (Hq / Hkv) and each workgroup takes
     // floor(256 / G) tokens; the rows past BQ * G of the tile are idle (computed, never stored).
     const int Gv = G > 0 ? G : Hq / Hkv;
@@ -236,8 +247,16 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // 2^spread_shift XCDs (the power of two at most 8 / rem), which share its tiles round
     // robin, so no XCD stays idle for want of a pair.
     const int pairs = batch * Hkv;
-    const int xcd = blockIdx.x % kXcds;
-    const int k = blockIdx.x / kXcds;
+    // SPL: split sp of the key range; the grid is nsplit copies of the unsplit one, each a
+    // multiple of 8 workgroups long, so a workgroup keeps its XCD.
+    int bid = blockIdx.x, sp = 0;
+    if constexpr (SPL) {
+        const int per_split = gridDim.x / nsplit;
+        sp = bid / per_split;
+        bid -= sp * per_split;
+    }
+    const int xcd = bid % kXcds;
+    const int k = bid / kXcds;
     const int full = pairs & ~(kXcds - 1);
     const int rounds = (pairs / kXcds) * tiles;  // per-XCD slots of the full groups of 8
     int pair, jt;
@@ -299,7 +318,16 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const uint32_t k_src0 = 16u * (uint32_t)((punit ^ (8 * (wave & 1) + prow)) & (D / 8 - 1));
     const uint32_t k_src1 = 16u * (uint32_t)((punit ^ (8 * (wave & 1) + 4 + prow)) & (D / 8 - 1));
     const uint32_t v_src = 16u * (uint32_t)(unswz_v(prow, punit) & (D / 8 - 1));
-    const int ntiles = (kend + kExtBN - 1) / kExtBN;
+    // SPL: this workgroup takes key tiles [it_lo, it_lo + ntiles) of the row tile's, split sp
+    // of nsplit near-equal blocks (possibly none); kofs is the first key's position.
+    int ntiles = (kend + kExtBN - 1) / kExtBN;
+    int it_lo = 0;
+    if constexpr (SPL) {
+        const int all = ntiles;
+        it_lo = (int)((int64_t)all * sp / nsplit);
+        ntiles = (int)((int64_t)all * (sp + 1) / nsplit) - it_lo;
+    }
+    const int kofs = it_lo * kExtBN;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     // bf16 pools: the slot numbers of the two rows a lane copies (tile rows 8 w + prow and
     // 8 w + 4 + prow) come through per-lane vector loads, one tile before their copy. Scalar
@@ -309,8 +337,8 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // held in register set T % 2 (S0, S1).
 #define RAX_VSLOTS(TILE, S0, S1)                                                            \
     {                                                                                       \
-        const int p0_ = min((TILE) * kExtBN + 8 * wave + prow, kend - 1);                  \
-        const int p1_ = min((TILE) * kExtBN + 8 * wave + 4 + prow, kend - 1);              \
+        const int p0_ = min(kofs + (TILE) * kExtBN + 8 * wave + prow, kend - 1);           \
+        const int p1_ = min(kofs + (TILE) * kExtBN + 8 * wave + 4 + prow, kend - 1);       \
         S0 = slot_at<PG>(row, p0_, page_shift);                                            \
         S1 = slot_at<PG>(row, p1_, page_shift);                                            \
     }
@@ -323,8 +351,8 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // before any of the tile's copies is issued (and, in the loop, before the next slot loads).
 #define RAX_RADDR(TILE, S0, S1, N0, N1, O0, O1)                                             \
     {                                                                                       \
-        const int ps0_ = min((TILE) * kExtBN + 8 * wave + prow, kend - 1);                 \
-        const int ps1_ = min((TILE) * kExtBN + 8 * wave + 4 + prow, kend - 1);             \
+        const int ps0_ = min(kofs + (TILE) * kExtBN + 8 * wave + prow, kend - 1);          \
+        const int ps1_ = min(kofs + (TILE) * kExtBN + 8 * wave + 4 + prow, kend - 1);      \
         N0 = ps0_ >= p;                                                                     \
         N1 = ps1_ >= p;                                                                     \
         O0 = __umul24((uint32_t)(N0 ? s0 + ps0_ - p : (S0)), row_bytes);                   \
@@ -370,8 +398,8 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
             lds_dma16(pool_row_ptr<OFF32>(vbase, S0, row_bytes, v_src), vd_);               \
             lds_dma16(pool_row_ptr<OFF32>(vbase, S1, row_bytes, v_src), vd_ + 1024);        \
         } else {                                                                            \
-            const int ps0_ = min((TILE) * kExtBN + 8 * wave + prow, kend - 1);             \
-            const int ps1_ = min((TILE) * kExtBN + 8 * wave + 4 + prow, kend - 1);         \
+            const int ps0_ = min(kofs + (TILE) * kExtBN + 8 * wave + prow, kend - 1);      \
+            const int ps1_ = min(kofs + (TILE) * kExtBN + 8 * wave + 4 + prow, kend - 1);  \
             const bool n0_ = ps0_ >= p, n1_ = ps1_ >= p;                                    \
             const int64_t r0_ = row_off<OFF32>(n0_ ? s0 + ps0_ - p : S0, row_bytes);        \
             const int64_t r1_ = row_off<OFF32>(n1_ ? s0 + ps1_ - p : S1, row_bytes);        \
@@ -391,7 +419,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const uint32_t src8 = 16u * (uint32_t)(lane & 7 & (D / 16 - 1));
 #define RAX_VSLOT8(TILE, S)                                                                 \
     {                                                                                       \
-        S = slot_at<PG>(row, min((TILE) * kExtBN + 8 * wave + q8, kend - 1), page_shift);   \
+        S = slot_at<PG>(row, min(kofs + (TILE) * kExtBN + 8 * wave + q8, kend - 1), page_shift); \
     }
 #define RAX_COPY8(SK, SV, S)                                                                \
     {                                                                                       \
@@ -500,12 +528,12 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     }
 #define RAX_SM(IT, MASKABLE)                                                                \
     {                                                                                       \
-        if (MASKABLE && __builtin_amdgcn_readfirstlane((IT) * kExtBN + kExtBN - 1 > diag_from)) { \
-            const int j0_ = (IT) * kExtBN;                                                  \
+        if (MASKABLE && __builtin_amdgcn_readfirstlane(kofs + (IT) * kExtBN + kExtBN - 1 > diag_from)) { \
+            const int j0_ = kofs + (IT) * kExtBN;                                           \
             _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                \
             _Pragma("unroll") for (int jj = 0; jj < 4; ++jj)                                \
             _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                 \
-                if (j0_ + 32 * mb + 8 * jj + 4 * h2 + i > last_q) st[mb][4 * jj + i] = -INFINITY; \
+                if (j0_ + 32 * mb + 8 * jj + 4 * h2 + i > last_q) st[mb][4 * jj + i] = kMasked; \
             }                                                                               \
         }                                                                                   \
         /* P is formed against the current reference maximum m while the tile's maximum is  */ \
@@ -672,9 +700,24 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     }
 
 
-    const int n_full = min(ntiles, (diag_from + 1) / kExtBN);  // tiles with every key <= p + t0
+    // tiles with every key <= p + t0
+    const int n_full = max(0, min(ntiles, (diag_from + 1) / kExtBN - it_lo));
     int it = 0;
     const bool lag = __builtin_amdgcn_readfirstlane(wave) >= 4;
+    if constexpr (SPL) {
+        if (ntiles == 0) {  // no key of this split: a partial of weight 0 (uniform per workgroup)
+            if (row_ok) {
+                const int64_t prow_ = (int64_t)sp * total_tokens * Hq * D + qo_row;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        *(float4*)(o_part + prow_ + 32 * dt + 8 * jj + 4 * h2) = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (h2 == 0) lse_part[(int64_t)sp * total_tokens * Hq + qo_row / D] = -INFINITY;
+            }
+            return;
+        }
+    }
     // waves 4-7 after their loop: softmax and P V of the last tile (inside their branch, so
     // the scores stay dead after the softmax for waves 0-3)
 #define RAX_LAG_TAIL()                                                                      \
@@ -792,7 +835,19 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
 #undef RAX_PLOOPS8
     }
     lsum = sum_pair32(lsum + lsum2);
-    if (row_ok) {
+    if (SPL && row_ok) {
+        // partial of split sp: the normalised row (fp32) and m + log2(sum)
+        const float inv = out_scale / lsum;
+        float* prow_ = o_part + (int64_t)sp * total_tokens * Hq * D + qo_row;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                *(float4*)(prow_ + 32 * dt + 8 * jj + 4 * h2) =
+                    make_float4(acc[dt][4 * jj + 0] * inv, acc[dt][4 * jj + 1] * inv,
+                                acc[dt][4 * jj + 2] * inv, acc[dt][4 * jj + 3] * inv);
+        if (h2 == 0) lse_part[(int64_t)sp * total_tokens * Hq + qo_row / D] = m + __log2f(lsum);
+    } else if (row_ok) {
         const float inv = out_scale / lsum;
         uint16_t* orow = o + qo_row;
         // acc[dt][4 jj + i] is head_dim 32 dt + 8 jj + 4 h2 + i
@@ -843,8 +898,50 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
 #undef RAX_PCOMPUTE
 #undef RAX_LAG_TAIL
 
-template <int DH, int G, bool OFF32, bool KV8, bool RAG, bool PG>
-int launch_g(const AttnArgs& a, hipStream_t stream) {
+// Merge of the key splits: one wave per (request, suffix token, q head) row combines the
+// nsplit partials, o = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M) with M the largest lse
+// (splits without keys carry lse -inf and weigh 0), and writes the bf16 row.
+template <int D>
+__global__ __launch_bounds__(256) void extend_merge_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part, uint16_t* __restrict__ o,
+    const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ extend_start_loc,
+    int64_t total_tokens, int32_t max_extend_len, int32_t Hq, int32_t batch, int32_t nsplit) {
+    constexpr int PER = D / 64;  // head_dim elements per lane
+    const int64_t wq = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int h = (int)(wq % Hq);
+    const int64_t bt = wq / Hq;
+    const int b = (int)(bt / max_extend_len);
+    const int t = (int)(bt - (int64_t)b * max_extend_len);
+    if (b >= batch) return;
+    const int s0 = extend_start_loc[b];
+    int e = min(extend_lens[b], max_extend_len);
+    e = (int)min((int64_t)e, total_tokens - s0);
+    if (t >= e) return;
+    const int64_t row = (int64_t)(s0 + t) * Hq + h;
+    const int64_t plane = total_tokens * Hq;
+    float M = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, lse_part[sp * plane + row]);
+    float acc[PER] = {};
+    float wsum = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+        const float w = fast_exp2(lse_part[sp * plane + row] - M);
+        wsum += w;
+        const float* pr = o_part + (sp * plane + row) * D + PER * lane;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[k] += w * pr[k];
+    }
+    const float inv = 1.f / wsum;
+    uint16_t* dst = o + row * D + PER * lane;
+    if constexpr (PER == 2) {
+        *(uint32_t*)dst = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    } else {
+        *dst = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xFFFFu);
+    }
+}
+
+template <int DH, int G, bool OFF32, bool KV8, bool RAG, bool PG, bool SPL>
+int launch_g(const AttnArgs& a, hipStream_t stream, int nsplit) {
     const int BQ = kExtBM / (G > 0 ? G : a.n_q_heads / a.n_kv_heads);
     const int tiles = (a.max_extend_len + BQ - 1) / BQ;
     const int pairs = a.batch * a.n_kv_heads;
@@ -855,18 +952,37 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
     const int64_t per_xcd = (int64_t)(pairs / kXcds) * tiles + (rem ? ((tiles - 1) >> spread) + 1 : 0);
     const int64_t blocks = per_xcd * kXcds;
     if (blocks <= 0) return 0;
-    if (blocks > 0x7fffffff) return -1;
+    if (blocks * nsplit > 0x7fffffff) return -1;
     // FP8 pools: the K scale multiplies every score, the V scale every output element.
     const float scale_log2 = a.sm_scale * kLog2e * (KV8 ? a.k_scale : 1.f);
     const float out_scale = KV8 ? a.v_scale : 1.f;
-    hipLaunchKernelGGL((extend_kernel<DH, G, OFF32, KV8, RAG, PG>), dim3((unsigned)blocks), dim3(kExtThreads),
+    float* o_part = nullptr;
+    float* lse_part = nullptr;
+    if constexpr (SPL) {
+        o_part = (float*)a.workspace;
+        lse_part = (float*)((char*)a.workspace +
+                            extend_split_o_bytes(nsplit, a.total_tokens, a.n_q_heads, a.head_dim));
+    }
+    hipLaunchKernelGGL((extend_kernel<DH, G, OFF32, KV8, RAG, PG, SPL>), dim3((unsigned)(blocks * nsplit)), dim3(kExtThreads),
                        0, stream, (const uint16_t*)a.q, (uint16_t*)a.o, (const char*)a.k_pool,
                        (const char*)a.v_pool, (const char*)a.k_new, (const char*)a.v_new, a.store_loc,
                        a.r2t, a.r2t_stride, a.req_pool_indices,
                        a.prefix_lens, a.extend_lens, a.extend_start_loc, a.total_tokens,
                        a.max_extend_len, a.max_seq_len, a.n_q_heads, a.n_kv_heads, a.batch, tiles,
-                       scale_log2, out_scale, a.page_shift, spread);
+                       scale_log2, out_scale, a.page_shift, spread, nsplit, o_part, lse_part);
+    if constexpr (SPL) {
+        if (hipGetLastError() != hipSuccess) return -1;
+        const int64_t rows = (int64_t)a.batch * a.max_extend_len * a.n_q_heads;
+        hipLaunchKernelGGL((extend_merge_kernel<DH>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                           (const float*)o_part, (const float*)lse_part, (uint16_t*)a.o, a.extend_lens,
+                           a.extend_start_loc, a.total_tokens, a.max_extend_len, a.n_q_heads, a.batch, nsplit);
+    }
     return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int DH, int G, bool OFF32, bool KV8, bool RAG, bool PG>
+int launch_g(const AttnArgs& a, hipStream_t stream) {
+    return launch_g<DH, G, OFF32, KV8, RAG, PG, false>(a, stream, 1);
 }
 
 template <int DH, int G>
@@ -889,6 +1005,13 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
                          : launch_g<DH, G, false, false, true, true>(a, stream);
         return off32 ? launch_g<DH, G, true, false, true, false>(a, stream)
                      : launch_g<DH, G, false, false, true, false>(a, stream);
+    }
+    // key splits (32-bit offsets, the workspace the call was given)
+    const int32_t S = extend_splits(a.batch, a.n_q_heads, a.n_kv_heads, a.max_extend_len, a.max_seq_len);
+    if (off32 && S > 1 && a.workspace != nullptr &&
+        a.workspace_bytes >= extend_split_workspace(S, a.total_tokens, a.n_q_heads, a.head_dim)) {
+        if (a.page_shift) return launch_g<DH, G, true, false, false, true, true>(a, stream, S);
+        return launch_g<DH, G, true, false, false, false, true>(a, stream, S);
     }
     if (a.page_shift)
         return off32 ? launch_g<DH, G, true, false, false, true>(a, stream)

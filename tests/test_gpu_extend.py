@@ -42,6 +42,13 @@ SMALL = [
     W.Spec("ext-3pair", "bf16", 12, 3, 128, 50000, extend_prefix=(77,), extend_lens=(700,)),
     W.Spec("ext-13pair", "bf16", 16, 1, 128, 50000, extend_prefix=(0, 5, 64, 100, 129, 1, 2, 300, 0, 7, 40, 63, 8),
            extend_lens=(40, 17, 33, 1, 64, 90, 16, 5, 77, 2, 48, 31, 100)),
+    # too few row tiles to fill the CUs: each row tile's keys are split over up to 16
+    # workgroups and merged (a short suffix on a long prefix; the second request's tiles leave
+    # most splits without keys; head_dim 64; a run-time group size)
+    W.Spec("ext-split-mqa", "bf16", 8, 1, 128, 50000, extend_prefix=(10000,), extend_lens=(100,)),
+    W.Spec("ext-split-g4", "bf16", 32, 8, 128, 50000, extend_prefix=(12000, 0), extend_lens=(100, 37)),
+    W.Spec("ext-split-d64", "bf16", 16, 4, 64, 50000, extend_prefix=(5000, 700), extend_lens=(200, 64)),
+    W.Spec("ext-split-g7", "bf16", 28, 4, 128, 50000, extend_prefix=(3000,), extend_lens=(300,)),
 ]
 
 

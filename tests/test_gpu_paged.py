@@ -21,6 +21,8 @@ from parity import assert_close, decode, extend, out_f64, say, store, stored_poo
 pytestmark = pytest.mark.gpu
 
 EXT_SPECS = [
+    # key splits (few row tiles) through a page table
+    W.Spec("pg16-split", "bf16", 32, 8, 128, 65536, extend_prefix=(9000,), extend_lens=(70,), page_size=16),
     W.Spec("pg16-g4", "bf16", 32, 8, 128, 131072, extend_prefix=(0, 1, 63, 64, 500, 3000),
            extend_lens=(1, 40, 65, 128, 77, 300), page_size=16),
     W.Spec("pg8-g1", "bf16", 4, 4, 128, 65536, extend_prefix=(0, 200, 37), extend_lens=(300, 129, 0), page_size=8),

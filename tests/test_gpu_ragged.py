@@ -78,12 +78,23 @@ def test_ragged_extend(spec, variant, fused_store):
 @pytest.mark.parametrize("variant", ["normal", "peaked"])
 @pytest.mark.parametrize("spec", [SPECS[0], SPECS[3], SPECS[6], SPECS[8], SPECS[9], SPECS[10]], ids=lambda s: s.name)
 def test_ragged_is_bitwise_store_then_extend(spec, variant):
+    """The ragged call with its fused store equals the store followed by the pool-reading call,
+    bit for bit while the latter runs unsplit; where it splits the keys of its few row tiles
+    (a workspace is asked for), the merged splits add in another order, so the two agree to
+    the bf16 bound instead (each is checked against the oracle elsewhere)."""
     wl = W.make_workload(spec, 802, variant)
     dw = upload(wl)
     got = run_ragged(dw, wl, True).clone()
     store(dw)
     want = extend(dw, wl)
     torch.cuda.synchronize()
+    x = dw.ext
+    split = spec.dtype == "bf16" and R.extend_workspace_bytes(
+        R.BF16, wl.extend.batch, wl.extend.total_tokens, int(x["max_extend_len"]), int(x["max_seq_len"]),
+        spec.n_q_heads, spec.n_kv_heads, spec.head_dim) > 0
+    if split:
+        assert_close(out_f64(got), out_f64(want), spec.dtype, f"ragged vs split {spec.name}/{variant}")
+        return
     assert torch.equal(got.view(torch.int16) if spec.dtype == "bf16" else got.view(torch.int32),
                        want.view(torch.int16) if spec.dtype == "bf16" else want.view(torch.int32))
 
