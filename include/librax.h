@@ -134,15 +134,16 @@ rax_status rax_kv_store(rax_dtype dtype, const void* k_new, const void* v_new, c
  *   max_seq_len     >= every p + e, <= r2t_stride (host)
  *   sm_scale      softmax scale applied to the raw score (1/sqrt(head_dim) in the pages).
  *   workspace     scratch of at least rax_extend_workspace_bytes(...) bytes (may be NULL when
- *                 that figure is 0). Over bf16 pools the figure is nonzero when the (request,
- *                 kv head) pairs times the row tiles (256 / G suffix tokens each) number fewer
- *                 than 256 and max_seq_len spans at least 1,024 keys: each row tile's keys are
- *                 then split over S <= 16 workgroups whose partial rows (fp32) and
- *                 log2-sum-exps a second kernel merges, S * total_extend_tokens * n_q_heads *
- *                 (head_dim + 1) * 4 bytes (plus alignment). The workspace must not be used by
- *                 other work until the call has passed on the stream. FP8 pools, the fp32
- *                 path and the ragged calls need none. (Split summation order: the results
- *                 agree with the unsplit ones to bf16 rounding, not bit for bit.)
+ *                 that figure is 0). Over bf16 and FP8 pools (query the *_fp8 calls with
+ *                 RAX_FP8_E4M3) the figure is nonzero when the (request, kv head) pairs times
+ *                 the row tiles (256 / G suffix tokens each) number fewer than 256 and
+ *                 max_seq_len spans at least 1,024 keys: each row tile's keys are then split
+ *                 over S <= 16 workgroups whose partial rows (fp32) and log2-sum-exps a second
+ *                 kernel merges, S * total_extend_tokens * n_q_heads * (head_dim + 1) * 4 bytes
+ *                 (plus alignment). The same holds for the paged and ragged calls. The
+ *                 workspace must not be used by other work until the call has passed on the
+ *                 stream; the fp32 path needs none. (Split summation order: the results agree
+ *                 with the unsplit ones to bf16 rounding, not bit for bit.)
  * Device-side CONTRACT: 0 <= prefix_lens[b], 0 <= extend_lens[b] <= max_extend_len,
  *   prefix_lens[b] + extend_lens[b] <= max_seq_len, extend_start_loc[b] + extend_lens[b] <=
  *   total_extend_tokens, the first p + e entries of each used table row are valid slots.

@@ -64,9 +64,9 @@ rax_status rax_kv_store(rax_dtype dtype, const void* k_new, const void* v_new, c
 size_t rax_extend_workspace_bytes(rax_dtype dtype, int32_t batch, int64_t total_extend_tokens,
                                   int32_t max_extend_len, int32_t max_seq_len, int32_t n_q_heads,
                                   int32_t n_kv_heads, int32_t head_dim) {
-    // bf16 pools read through a table: the partials of the key splits (0 when unsplit); FP8
-    // pools and the fp32 path use none.
-    if (dtype != RAX_BF16 || batch <= 0 || total_extend_tokens <= 0 || max_extend_len <= 0 ||
+    // the partials of the key splits over bf16 or FP8 pools (0 when unsplit); the fp32 path
+    // uses none.
+    if ((dtype != RAX_BF16 && dtype != RAX_FP8_E4M3) || batch <= 0 || total_extend_tokens <= 0 || max_extend_len <= 0 ||
         n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0 ||
         !rax::extend_bf16_supported(n_q_heads / n_kv_heads, head_dim))
         return 0;
@@ -121,11 +121,9 @@ rax_status extend_call(int dtype, bool kv8, const void* q, void* o, const void* 
         !extend_lens || !extend_start_loc)
         return RAX_ERR_NULL;
     if (ragged && (!k_new || !v_new)) return RAX_ERR_NULL;
-    // FP8 pools and the ragged calls never split their keys: no workspace needed there
-    const size_t need = kv8 || ragged ? 0
-                                      : rax_extend_workspace_bytes((rax_dtype)dtype, batch, total_extend_tokens,
-                                                                   max_extend_len, max_seq_len, n_q_heads,
-                                                                   n_kv_heads, head_dim);
+    const size_t need = rax_extend_workspace_bytes(kv8 ? RAX_FP8_E4M3 : (rax_dtype)dtype, batch,
+                                                   total_extend_tokens, max_extend_len, max_seq_len,
+                                                   n_q_heads, n_kv_heads, head_dim);
     if (need > 0 && (!workspace || workspace_bytes < need)) return RAX_ERR_WORKSPACE;
 
     rax::AttnArgs a{};

@@ -198,7 +198,8 @@ __device__ __forceinline__ int64_t row_off(int idx, uint32_t row_bytes) {
 // PG: the table is a page table (page size 2^page_shift): position j lives at slot
 // table[row, j >> page_shift] << page_shift | (j & (2^page_shift - 1)).
 // SPL: the key range of each row tile is split over nsplit workgroups, which write partial
-// outputs (fp32, normalised) and their log2-sum-exps to o_part / lse_part for merge_kernel.
+// outputs (fp32, normalised) and their log2-sum-exps to o_part / lse_part for
+// extend_merge_kernel.
 template <int DH, int G, bool OFF32, bool KV8, bool RAG, bool PG, bool SPL>
 __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const char* __restrict__ k_pool,
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // and the copy lanes of units 8-15 fetch a copy of units 0-7, so no copy leaves its row.
     constexpr int D = DH;
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-    static_assert(!SPL || (!KV8 && !RAG), "key splits over bf16 pools read through a table");
+
     // Score of a masked key. A split's tiles can hold no visible key for some rows (all past
     // the row's diagonal): with a finite mask value those rows keep a finite running max and
     // finite sums, and a log2-sum-exp near -2^100 * scale that gives their partial weight 0
@@ -866,7 +867,8 @@ __global__ __launch_bounds__(kExtThreads, 1) void extend_kernel(
     // workgroup of this launch reads those slots: suffix keys come from the new rows, and
     // prefix slots are disjoint from the store slots.
     if constexpr (RAG) {
-        if (store_loc != nullptr) {
+        // with key splits the last split stores (it always holds a tile; split 0 may not)
+        if (store_loc != nullptr && (!SPL || sp == nsplit - 1)) {
             const int nrows = t_last - t0 + 1;
             constexpr int UPR = D / 8;  // 16-byte units per (token, kv head) row
             for (int u = tid; u < nrows * UPR; u += kExtThreads) {
@@ -985,11 +987,26 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
     return launch_g<DH, G, OFF32, KV8, RAG, PG, false>(a, stream, 1);
 }
 
+// Key splits (see extend_splits) where the call's workspace holds their partials; 32-bit
+// offsets only.
+inline int32_t split_count(const AttnArgs& a) {
+    const int32_t S = extend_splits(a.batch, a.n_q_heads, a.n_kv_heads, a.max_extend_len, a.max_seq_len);
+    if (S <= 1 || a.workspace == nullptr ||
+        a.workspace_bytes < extend_split_workspace(S, a.total_tokens, a.n_q_heads, a.head_dim))
+        return 1;
+    return S;
+}
+
 template <int DH, int G>
 int launch_g(const AttnArgs& a, hipStream_t stream) {
+    const int32_t S = split_count(a);
     if (a.kv8) {
         if (a.ragged) return -1;
         const bool off8 = pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 1);
+        if (off8 && S > 1) {
+            if (a.page_shift) return launch_g<DH, G, true, true, false, true, true>(a, stream, S);
+            return launch_g<DH, G, true, true, false, false, true>(a, stream, S);
+        }
         if (a.page_shift)
             return off8 ? launch_g<DH, G, true, true, false, true>(a, stream)
                         : launch_g<DH, G, false, true, false, true>(a, stream);
@@ -1000,16 +1017,17 @@ int launch_g(const AttnArgs& a, hipStream_t stream) {
     const bool off32 = pool_fits_32bit_offsets(a.num_slots, a.n_kv_heads, a.head_dim, 2) &&
                        (!a.ragged || pool_fits_32bit_offsets(a.total_tokens, a.n_kv_heads, a.head_dim, 2));
     if (a.ragged) {
+        if (off32 && S > 1) {
+            if (a.page_shift) return launch_g<DH, G, true, false, true, true, true>(a, stream, S);
+            return launch_g<DH, G, true, false, true, false, true>(a, stream, S);
+        }
         if (a.page_shift)
             return off32 ? launch_g<DH, G, true, false, true, true>(a, stream)
                          : launch_g<DH, G, false, false, true, true>(a, stream);
         return off32 ? launch_g<DH, G, true, false, true, false>(a, stream)
                      : launch_g<DH, G, false, false, true, false>(a, stream);
     }
-    // key splits (32-bit offsets, the workspace the call was given)
-    const int32_t S = extend_splits(a.batch, a.n_q_heads, a.n_kv_heads, a.max_extend_len, a.max_seq_len);
-    if (off32 && S > 1 && a.workspace != nullptr &&
-        a.workspace_bytes >= extend_split_workspace(S, a.total_tokens, a.n_q_heads, a.head_dim)) {
+    if (off32 && S > 1) {
         if (a.page_shift) return launch_g<DH, G, true, false, false, true, true>(a, stream, S);
         return launch_g<DH, G, true, false, false, false, true>(a, stream, S);
     }

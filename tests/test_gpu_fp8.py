@@ -158,6 +158,9 @@ EXT_SPECS = [
     W.Spec("fp8-ext-d64-g3", "bf16", 6, 2, 64, 30000, extend_prefix=(0, 500), extend_lens=(200, 86)),
     # one (request, kv head) pair: its 32 row tiles shared out over all XCDs
     W.Spec("fp8-ext-1pair", "bf16", 8, 1, 128, 30000, extend_prefix=(300,), extend_lens=(1000,)),
+    # few row tiles: each row tile's keys split over several workgroups and merged
+    W.Spec("fp8-ext-split", "bf16", 32, 8, 128, 30000, extend_prefix=(9000, 0), extend_lens=(100, 30)),
+    W.Spec("fp8-ext-split-mqa", "bf16", 8, 1, 128, 30000, extend_prefix=(6000,), extend_lens=(200,)),
 ]
 
 

@@ -38,6 +38,8 @@ SPECS = [
     W.Spec("rag-g7", "bf16", 28, 4, 128, 100000, extend_prefix=(0, 63, 500), extend_lens=(100, 37, 73)),
     # one (request, kv head) pair whose row tiles are shared out over all XCDs (fused store)
     W.Spec("rag-1pair", "bf16", 8, 1, 128, 50000, extend_prefix=(200,), extend_lens=(900,)),
+    # key splits (few row tiles; the last split of each row tile does the fused store)
+    W.Spec("rag-split", "bf16", 32, 8, 128, 50000, extend_prefix=(9000, 0), extend_lens=(90, 30)),
 ]
 
 
@@ -79,22 +81,13 @@ def test_ragged_extend(spec, variant, fused_store):
 @pytest.mark.parametrize("spec", [SPECS[0], SPECS[3], SPECS[6], SPECS[8], SPECS[9], SPECS[10]], ids=lambda s: s.name)
 def test_ragged_is_bitwise_store_then_extend(spec, variant):
     """The ragged call with its fused store equals the store followed by the pool-reading call,
-    bit for bit while the latter runs unsplit; where it splits the keys of its few row tiles
-    (a workspace is asked for), the merged splits add in another order, so the two agree to
-    the bf16 bound instead (each is checked against the oracle elsewhere)."""
+    bit for bit (both split the keys of few row tiles the same way)."""
     wl = W.make_workload(spec, 802, variant)
     dw = upload(wl)
     got = run_ragged(dw, wl, True).clone()
     store(dw)
     want = extend(dw, wl)
     torch.cuda.synchronize()
-    x = dw.ext
-    split = spec.dtype == "bf16" and R.extend_workspace_bytes(
-        R.BF16, wl.extend.batch, wl.extend.total_tokens, int(x["max_extend_len"]), int(x["max_seq_len"]),
-        spec.n_q_heads, spec.n_kv_heads, spec.head_dim) > 0
-    if split:
-        assert_close(out_f64(got), out_f64(want), spec.dtype, f"ragged vs split {spec.name}/{variant}")
-        return
     assert torch.equal(got.view(torch.int16) if spec.dtype == "bf16" else got.view(torch.int32),
                        want.view(torch.int16) if spec.dtype == "bf16" else want.view(torch.int32))
 
@@ -113,6 +106,7 @@ PAGED_SPECS = [
            page_size=4),
     W.Spec("ragpg16-g5", "bf16", 40, 8, 128, 131072, extend_prefix=(70, 0), extend_lens=(103, 52), page_size=16),
     W.Spec("ragpg16-3pair", "bf16", 12, 3, 128, 65536, extend_prefix=(50,), extend_lens=(600,), page_size=16),
+    W.Spec("ragpg16-split", "bf16", 32, 8, 128, 65536, extend_prefix=(7000,), extend_lens=(80,), page_size=16),
 ]
 
 
