@@ -136,9 +136,9 @@ rax_status rax_kv_store(rax_dtype dtype, const void* k_new, const void* v_new, c
  *   workspace     scratch of at least rax_extend_workspace_bytes(...) bytes (may be NULL when
  *                 that figure is 0). Over bf16 and FP8 pools (query the *_fp8 calls with
  *                 RAX_FP8_E4M3) the figure is nonzero when the (request, kv head) pairs times
- *                 the row tiles (256 / G suffix tokens each) number fewer than 256 and
+ *                 the row tiles (256 / G suffix tokens each) number at most 128 and
  *                 max_seq_len spans at least 1,024 keys: each row tile's keys are then split
- *                 over S <= 16 workgroups whose partial rows (fp32) and log2-sum-exps a second
+ *                 over S = floor(256 / (pairs x tiles)) <= 16 workgroups whose partial rows (fp32) and log2-sum-exps a second
  *                 kernel merges, S * total_extend_tokens * n_q_heads * (head_dim + 1) * 4 bytes
  *                 (plus alignment). The same holds for the paged and ragged calls. The
  *                 workspace must not be used by other work until the call has passed on the

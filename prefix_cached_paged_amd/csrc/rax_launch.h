@@ -66,10 +66,10 @@ int launch_kv_store_fp8(const void* k_new, const void* v_new, const int32_t* loc
                         void* k_pool, void* v_pool, int64_t row_elems, float k_inv, float v_inv,
                         hipStream_t stream);
 
-// EXTEND key splits (bf16 pools read through a token or page table): when the (request, kv
-// head) pairs times the row tiles of 256 query rows (256 / G tokens) fill less than one round
-// of the 256 CUs, each row tile's keys are split over S workgroups, S = ceil(256 / work), at
-// most 16 and at most one per 8 key tiles of 64 keys (so a split streams 512 keys or more).
+// EXTEND key splits: when the (request, kv head) pairs times the row tiles of 256 query rows
+// (256 / G tokens) fill at most half a round of the 256 CUs, each row tile's keys are split
+// over S workgroups, S = floor(256 / work) (so the split grid still fits one round), at most
+// 16 and at most one per 8 key tiles of 64 keys (so a split streams 512 keys or more).
 inline int32_t extend_splits(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                              int32_t max_extend_len, int32_t max_seq_len) {
     if (batch <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0) return 1;
@@ -78,7 +78,7 @@ inline int32_t extend_splits(int32_t batch, int32_t n_q_heads, int32_t n_kv_head
     const int32_t BQ = 256 / G;
     const int64_t work = (int64_t)batch * n_kv_heads * ((max_extend_len + BQ - 1) / BQ);
     if (work <= 0 || work >= 256) return 1;
-    int64_t S = (256 + work - 1) / work;
+    int64_t S = 256 / work;
     const int64_t by_keys = ((int64_t)max_seq_len + 63) / 64 / 8;
     if (S > by_keys) S = by_keys;
     if (S > 16) S = 16;

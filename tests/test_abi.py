@@ -144,15 +144,16 @@ def test_decode_workspace_size():
             assert lib().rax_decode_workspace_bytes(dtype, B, L, hq, hkv, 128) == want
     assert lib().rax_decode_workspace_bytes(1, 64, 4096, 32, 8, 128) == 0   # fp32 path needs none
     assert lib().rax_extend_workspace_bytes(0, 1, 2048, 2048, 16384, 32, 8, 128) == 0
-    # few row tiles: S key splits of fp32 partial rows and log2-sum-exps (S = ceil(256 / (pairs
+    # few row tiles: S key splits of fp32 partial rows and log2-sum-exps (S = floor(256 / (pairs
     # x row tiles)), at most 16 and at most one per 512 keys of max_seq_len), over bf16 and FP8
     # pools alike; none for the fp32 path
     for B, N, E, L, hq, hkv, d in [(1, 100, 100, 10100, 32, 8, 128), (1, 100, 100, 10100, 8, 1, 128),
                                     (2, 137, 100, 12100, 32, 8, 64), (1, 2048, 2048, 4096, 32, 4, 128),
-                                    (1, 64, 64, 700, 32, 8, 128)]:
+                                    (1, 64, 64, 700, 32, 8, 128), (1, 2048, 2048, 16384, 28, 4, 128),
+                                    (1, 2048, 2048, 16384, 16, 1, 128)]:
         bq = 256 // (hq // hkv)
         work = B * hkv * ((E + bq - 1) // bq)
-        S = 1 if work >= 256 else max(1, min((256 + work - 1) // work, (L + 63) // 64 // 8, 16))
+        S = 1 if work >= 256 else max(1, min(256 // work, (L + 63) // 64 // 8, 16))
         want = 0 if S == 1 else a256(S * N * hq * d * 4) + S * N * hq * 4
         assert lib().rax_extend_workspace_bytes(0, B, N, E, L, hq, hkv, d) == want, (B, N, E, L, hq, hkv, d)
         assert lib().rax_extend_workspace_bytes(2, B, N, E, L, hq, hkv, d) == want
