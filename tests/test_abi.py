@@ -92,6 +92,14 @@ def test_extend_validation():
     assert extend(start=None) == 1
     assert extend(batch=0, q=None) == 0      # empty batch
     assert extend(total=0, max_ext=0, q=None) == 0
+    # few row tiles over a long context: the key splits need a workspace, and a missing or short
+    # one is refused before any launch (the fp32 path needs none)
+    big = dict(r2t_stride=16384, max_seq=16000, num_slots=1 << 20)
+    need = lib().rax_extend_workspace_bytes(0, 2, 64, 40, 16000, 8, 2, 128)
+    assert need > 0
+    assert extend(**big) == 5
+    assert extend(ws=FAKE, ws_bytes=need - 1, **big) == 5
+    assert extend(dtype=1, batch=0, q=None, **big) == 0
 
 
 def decode(**kw):
