@@ -325,7 +325,7 @@ rax_status rax_decode_attention_paged(rax_dtype dtype, const void* q, void* o, c
  *   group sizes as bf16): the scores use k_scale * e4m3(K) and the values v_scale * e4m3(V).
  *   The kernel stages the E4M3 tiles in LDS, widens them to bf16 (exact) and applies k_scale to
  *   the scores and v_scale to the output. Workspace: rax_extend_workspace_bytes(RAX_FP8_E4M3,
- *   ...) (0 bytes: NULL is accepted).
+ *   ...) (the key splits' partials, as for bf16 pools; NULL is accepted when it is 0).
  *
  * rax_decode_attention_fp8 -- rax_decode_attention over FP8 pools: the scores use
  *   k_scale * e4m3(K) and the values v_scale * e4m3(V). Every E4M3 value is exactly a bf16
