@@ -1,9 +1,12 @@
 """HIP graph capture of one step of the path: kv_store, EXTEND and DECODE on one stream.
 
 The calls allocate nothing and clear nothing with memsets (the DECODE workspace is the
-caller's), so a step can be captured once and replayed. Every replay is checked bit for bit
-against an eager run of the same step, with eager work and synchronisations between replays,
-and the inputs are changed between replays to show that the graph reads the live buffers.
+caller's), so a step can be captured once and replayed. The EXTEND of the step-replay test
+splits its keys (3 requests x 8 kv heads x 5 row tiles = 120 workgroups: two splits and a
+merge); its workspace comes from the binding, through torch's allocator, which serves it from
+the graph's pool during capture. Every replay is checked bit for bit against an eager run of
+the same step, with eager work and synchronisations between replays, and the inputs are
+changed between replays to show that the graph reads the live buffers.
 """
 
 import pytest
