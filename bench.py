@@ -400,7 +400,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=5, help="workload id (1..5)")
+    ap.add_argument("--config", type=int, default=5, help="workload id (1..5; 6: 100 new tokens on a 10,000-token prefix)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=16.0,
                     help="seconds of wall time for the CPU oracle's samples (about half per call)")
@@ -443,7 +443,7 @@ def main():
     from prefix_cached_paged_amd import workloads as W
 
     cfg = args.config
-    spec = W.CONFIGS[cfg]
+    spec = W.workload_spec(cfg)
     if args.page_size != 1:
         import dataclasses
         spec = dataclasses.replace(spec, page_size=args.page_size)

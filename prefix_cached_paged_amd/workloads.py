@@ -411,4 +411,16 @@ CONFIGS = {
             extend_prefix=(65536,), extend_lens=(8192,),
             decode_batch=8, decode_range=(32768, 131072)),
 }
-TIMING_SEEDS = {1: 1001, 2: 1002, 3: 1003, 4: 1004, 5: 1005}
+TIMING_SEEDS = {1: 1001, 2: 1002, 3: 1003, 4: 1004, 5: 1005, 6: 1006}
+
+# Further workloads, not among the five: 6 is a short suffix on a long cached prefix (the
+# multi-turn case), whose few row tiles take the EXTEND key splits.
+EXTRA = {
+    6: Spec("short-suffix-100on10000-bf16", "bf16", 32, 8, 128, 1048576, 1.0,
+            extend_prefix=(10000,), extend_lens=(100,)),
+}
+
+
+def workload_spec(wid: int) -> Spec:
+    """The Spec of workload `wid` (1..5, or one of EXTRA)."""
+    return CONFIGS[wid] if wid in CONFIGS else EXTRA[wid]
