@@ -922,10 +922,14 @@ __global__ __launch_bounds__(256) void extend_merge_kernel(
     if (t >= e) return;
     const int64_t row = (int64_t)(s0 + t) * Hq + h;
     const int64_t plane = total_tokens * Hq;
+    // unrolled by 4 so that four splits' loads are in flight together (a row's splits are
+    // still added in order)
     float M = -INFINITY;
+#pragma unroll 4
     for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, lse_part[sp * plane + row]);
     float acc[PER] = {};
     float wsum = 0.f;
+#pragma unroll 4
     for (int sp = 0; sp < nsplit; ++sp) {
         const float w = fast_exp2(lse_part[sp * plane + row] - M);
         wsum += w;
