@@ -133,10 +133,12 @@ __device__ __forceinline__ VRow<D> widen_v(VRow<D> x) { return x; }
 
 // One K or V row piece (16 or 8 bytes) at byte offset slot * row_bytes + off from a
 // wave-uniform base. With one wave per kv head every K/V byte is read once per step, so the
-// loads are marked non-temporal (NT, measured 2-6% faster on the long-context batches). When
-// ceil(G / 16) > 1 waves of a workgroup read the same rows, the loads stay cached (NT false):
-// the repeats then hit the CU's cache, +29 to +56% for 24 to 48 query heads per kv head, where
-// non-temporal loads fetched every repeat from L2.
+// loads over bf16 pools are marked non-temporal (NT, measured 2-6% faster on the long-context
+// batches). When ceil(G / 16) > 1 waves of a workgroup read the same rows, the loads stay
+// cached (NT false): the repeats then hit the CU's cache, +29 to +56% for 24 to 48 query heads
+// per kv head, where non-temporal loads fetched every repeat from L2. Over FP8 pools (128-byte
+// rows) cached loads measured +20% on 64 requests of 512-4,096 tokens and -1% on the longer
+// contexts, so they stay cached there too.
 template <bool NT, typename T>
 __device__ __forceinline__ T load_piece(const char* p) {
     if constexpr (NT) {
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(64 * kDecWaves, KV8 ? RAX_DEC_WGS_PER_CU8 : RAX_DEC
     float* __restrict__ lse_part, int32_t page_shift) {
     constexpr int S = D / 32;   // 32-wide K-dim steps of the score MFMA
     constexpr int DT = D / 16;  // 16-row output tiles; also head_dim elements per lane per V row
-    constexpr bool NT = RAX_DEC_NT && !SHR;
+    constexpr bool NT = RAX_DEC_NT && !SHR && !KV8;
     __shared__ int32_t slot_lds[kDecMaxKeys + kDecKeysPerIter];
     __shared__ Seg segs[kDecMaxSegs];
     __shared__ int32_t n_seg_lds;
